@@ -1,0 +1,248 @@
+"""Python binding of libspecprefill (SpecPrefill's token-importance estimator on
+an AMD Instinct MI355X).
+
+Argument marshalling only: every step of scoring and selection runs in the HIP
+kernels of ``libspecprefill.so`` (built in-tree by ``build.py``); torch supplies
+device memory and the current stream. There is no CPU fallback: if the
+library is missing, or a call fails, an exception says so.
+
+The call names follow the C ABI in ``include/specprefill.h``:
+``sp_score``, ``sp_score_varlen``, ``sp_select``, ``sp_select_varlen``,
+``sp_score_workspace_bytes``, ``sp_select_workspace_bytes``,
+``sp_score_plan`` and ``sp_status_string``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libspecprefill.so")
+
+SP_OK, SP_EINVAL, SP_EUNSUPPORTED, SP_EWORKSPACE, SP_EDEVICE = range(5)
+SP_F32, SP_BF16 = 0, 1
+SP_SELECT_TOPK, SP_SELECT_MASS = 0, 1
+
+EXPORTED = ("sp_score", "sp_score_varlen", "sp_select", "sp_select_varlen",
+            "sp_score_workspace_bytes", "sp_select_workspace_bytes", "sp_score_plan",
+            "sp_status_string")
+
+
+class SpError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {sp_status_string(status)}")
+
+
+class ScoreDesc(ctypes.Structure):
+    _fields_ = [("L", ctypes.c_int32), ("H", ctypes.c_int32), ("Hkv", ctypes.c_int32),
+                ("d", ctypes.c_int32), ("N", ctypes.c_int32), ("dtype", ctypes.c_int),
+                ("scale", ctypes.c_float)]
+
+
+class SelectParams(ctypes.Structure):
+    _fields_ = [("chunk", ctypes.c_int32), ("pool_k", ctypes.c_int32), ("mode", ctypes.c_int),
+                ("keep_rate", ctypes.c_float), ("mass", ctypes.c_float),
+                ("boost_first_n", ctypes.c_int32), ("boost_first_mult", ctypes.c_float),
+                ("boost_last_n", ctypes.c_int32), ("boost_last_mult", ctypes.c_float)]
+
+
+_lib = None
+
+
+def load_library():
+    """Loads libspecprefill.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: run attention_token_scoring_amd/build.py "
+                           "(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    P = ctypes.POINTER
+    lib.sp_status_string.argtypes = [ctypes.c_int]
+    lib.sp_status_string.restype = ctypes.c_char_p
+    lib.sp_score_workspace_bytes.argtypes = [P(ScoreDesc), i64]
+    lib.sp_score_workspace_bytes.restype = sz
+    lib.sp_score_plan.argtypes = [P(ScoreDesc), i32, P(ctypes.c_int32)]
+    lib.sp_score.argtypes = [P(ScoreDesc), vp, vp, i32, vp, vp, sz, vp]
+    lib.sp_score_varlen.argtypes = [P(ScoreDesc), i32, vp, vp, P(ctypes.c_int64), vp, vp, sz, vp]
+    lib.sp_select_workspace_bytes.argtypes = [i32, i64, P(SelectParams)]
+    lib.sp_select_workspace_bytes.restype = sz
+    lib.sp_select.argtypes = [vp, i32, P(SelectParams), i32, vp, vp, vp, vp, sz, vp]
+    lib.sp_select_varlen.argtypes = [vp, i32, P(ctypes.c_int64), P(ctypes.c_int32),
+                                     P(SelectParams), vp, vp, vp, vp, sz, vp]
+    for name in ("sp_score_plan", "sp_score", "sp_score_varlen", "sp_select", "sp_select_varlen"):
+        getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def sp_status_string(status: int) -> str:
+    return load_library().sp_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != SP_OK:
+        raise SpError(status, where)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return SP_BF16
+    if t.dtype == torch.float32:
+        return SP_F32
+    raise TypeError(f"unsupported dtype {t.dtype}: Q and K must be bfloat16 or float32")
+
+
+def _require_cuda(*ts):
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def score_desc(L, H, Hkv, d, N, dtype=SP_BF16, scale=0.0) -> ScoreDesc:
+    return ScoreDesc(int(L), int(H), int(Hkv), int(d), int(N), int(dtype), float(scale))
+
+
+def select_params(chunk=32, pool_k=1, mode="topk", keep_rate=0.0, mass=0.0, boost_first_n=0,
+                  boost_first_mult=1.0, boost_last_n=0, boost_last_mult=1.0) -> SelectParams:
+    m = {"topk": SP_SELECT_TOPK, "mass": SP_SELECT_MASS}.get(mode, mode)
+    return SelectParams(int(chunk), int(pool_k), int(m), float(keep_rate), float(mass),
+                        int(boost_first_n), float(boost_first_mult), int(boost_last_n),
+                        float(boost_last_mult))
+
+
+def sp_score_workspace_bytes(desc: ScoreDesc, max_prompt_len: int) -> int:
+    return int(load_library().sp_score_workspace_bytes(ctypes.byref(desc), int(max_prompt_len)))
+
+
+def sp_select_workspace_bytes(R: int, total_prompt_len: int, params: SelectParams) -> int:
+    return int(load_library().sp_select_workspace_bytes(int(R), int(total_prompt_len),
+                                                        ctypes.byref(params)))
+
+
+def sp_score_plan(desc: ScoreDesc, M: int) -> dict:
+    info = (ctypes.c_int32 * 8)()
+    _check(load_library().sp_score_plan(ctypes.byref(desc), int(M), info), "sp_score_plan")
+    keys = ("grid", "g", "ngroups", "keys_per_wg", "rows", "units", "cus")
+    return {k: int(info[i]) for i, k in enumerate(keys)}
+
+
+def _workspace(nbytes: int, device, workspace=None):
+    torch = _torch()
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise SpError(SP_EWORKSPACE, "workspace")
+        return workspace
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def sp_score(Q, K, M: Optional[int] = None, scale: float = 0.0, out=None, workspace=None,
+             stream=None):
+    """importance [M] float32 of one prompt. Q [L,H,N,d], K [L,Hkv,M+N,d] (bf16 or f32)."""
+    torch = _torch()
+    _require_cuda(Q, K)
+    L, H, N, d = Q.shape
+    Hkv = K.shape[1]
+    if M is None:
+        M = K.shape[2] - N
+    desc = score_desc(L, H, Hkv, d, N, _dtype_code(Q), scale)
+    if _dtype_code(K) != desc.dtype or K.shape[0] != L or K.shape[3] != d or K.shape[2] != M + N:
+        raise ValueError("K must be [L, Hkv, M+N, d] with Q's dtype")
+    if out is None:
+        out = torch.empty(M, dtype=torch.float32, device=Q.device)
+    ws = _workspace(sp_score_workspace_bytes(desc, M), Q.device, workspace)
+    st = load_library().sp_score(ctypes.byref(desc), Q.data_ptr(), K.data_ptr(), int(M),
+                                 out.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(),
+                                 _stream(stream))
+    _check(st, "sp_score")
+    return out
+
+
+def sp_score_varlen(Q, K, cu_prompt: Sequence[int], scale: float = 0.0, out=None,
+                    workspace=None, stream=None):
+    """importance [sum M_r] float32 of a ragged batch. Q [R,L,H,N,d], K [L,Hkv,T,d]
+    with T = sum (M_r + N); cu_prompt: host offsets [R+1]."""
+    torch = _torch()
+    _require_cuda(Q, K)
+    R, L, H, N, d = Q.shape
+    Hkv = K.shape[1]
+    cu = np.ascontiguousarray(np.asarray(cu_prompt, dtype=np.int64))
+    if cu.shape != (R + 1,):
+        raise ValueError("cu_prompt must hold R+1 offsets")
+    desc = score_desc(L, H, Hkv, d, N, _dtype_code(Q), scale)
+    if K.shape[2] != int(cu[-1]) + R * N:
+        raise ValueError("K must hold sum(M_r + N) key rows")
+    if out is None:
+        out = torch.empty(int(cu[-1]), dtype=torch.float32, device=Q.device)
+    maxM = int(np.max(np.diff(cu))) if R else 1
+    ws = _workspace(sp_score_workspace_bytes(desc, maxM), Q.device, workspace)
+    st = load_library().sp_score_varlen(
+        ctypes.byref(desc), int(R), Q.data_ptr(), K.data_ptr(),
+        cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), out.data_ptr(), ws.data_ptr(),
+        ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "sp_score_varlen")
+    return out
+
+
+def sp_select(importance, params: SelectParams, pos_base: int = 0, kept_idx=None, pos_ids=None,
+              n_kept=None, stream=None):
+    """(kept_idx [M] int32, pos_ids [M] int32, n_kept [1] int32) on the device; the
+    first n_kept entries are valid."""
+    torch = _torch()
+    _require_cuda(importance)
+    M = importance.shape[0]
+    dev = importance.device
+    kept_idx = torch.empty(M, dtype=torch.int32, device=dev) if kept_idx is None else kept_idx
+    pos_ids = torch.empty(M, dtype=torch.int32, device=dev) if pos_ids is None else pos_ids
+    n_kept = torch.empty(1, dtype=torch.int32, device=dev) if n_kept is None else n_kept
+    st = load_library().sp_select(importance.data_ptr(), int(M), ctypes.byref(params),
+                                  int(pos_base), kept_idx.data_ptr(), pos_ids.data_ptr(),
+                                  n_kept.data_ptr(), None, 0, _stream(stream))
+    _check(st, "sp_select")
+    return kept_idx, pos_ids, n_kept
+
+
+def sp_select_varlen(importance, cu_prompt: Sequence[int], params: SelectParams,
+                     pos_base: Optional[Sequence[int]] = None, kept_idx=None, pos_ids=None,
+                     n_kept=None, stream=None):
+    """Per-request selection of a ragged batch; request r's outputs start at
+    cu_prompt[r]; n_kept [R]."""
+    torch = _torch()
+    _require_cuda(importance)
+    cu = np.ascontiguousarray(np.asarray(cu_prompt, dtype=np.int64))
+    R = cu.shape[0] - 1
+    total = int(cu[-1])
+    dev = importance.device
+    kept_idx = torch.empty(total, dtype=torch.int32, device=dev) if kept_idx is None else kept_idx
+    pos_ids = torch.empty(total, dtype=torch.int32, device=dev) if pos_ids is None else pos_ids
+    n_kept = torch.empty(R, dtype=torch.int32, device=dev) if n_kept is None else n_kept
+    pb = None
+    if pos_base is not None:
+        pb_arr = np.ascontiguousarray(np.asarray(pos_base, dtype=np.int32))
+        pb = pb_arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    st = load_library().sp_select_varlen(
+        importance.data_ptr(), int(R), cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), pb,
+        ctypes.byref(params), kept_idx.data_ptr(), pos_ids.data_ptr(), n_kept.data_ptr(), None,
+        0, _stream(stream))
+    _check(st, "sp_select_varlen")
+    return kept_idx, pos_ids, n_kept

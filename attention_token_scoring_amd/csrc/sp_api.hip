@@ -1,0 +1,328 @@
+// C ABI of libspecprefill: argument validation, launch planning, dispatch.
+// Every argument error is reported before anything is enqueued.
+#include <math.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "sp_internal.h"
+
+namespace sp {
+
+hipError_t launch_score(const ScorePlan& p, const sp_score_desc& d, const void* Q, const void* K,
+                        long long plane_stride, int M, float* importance, void* ws,
+                        hipStream_t stream);
+hipError_t launch_select(const SelectParamsDev& p, const int64_t* cu, const int32_t* pos_base,
+                         int R, const float* importance, int32_t* kept_idx, int32_t* pos_ids,
+                         int32_t* n_kept, hipStream_t stream);
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+constexpr int kDefaultCUs = 256;  // MI355X; used when no device can be queried
+constexpr int kMaxSelectChunks = 4096;
+constexpr int kMaxSelectRequests = 1024;
+
+int g_cus[kMaxDevices];
+std::once_flag g_once[kMaxDevices];
+
+// Compute units of the current device (0 if there is no usable device).
+int device_cus() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+    std::call_once(g_once[dev], [dev] {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            n = 0;
+        g_cus[dev] = n;
+    });
+    return g_cus[dev];
+}
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int esize(sp_dtype t) { return t == SP_BF16 ? 2 : 4; }
+
+// Shape checks shared by every scoring entry point.
+sp_status check_desc(const sp_score_desc* d) {
+    if (!d) return SP_EINVAL;
+    if (d->L < 1 || d->H < 1 || d->Hkv < 1 || d->d < 1 || d->N < 1) return SP_EINVAL;
+    if (d->H % d->Hkv != 0) return SP_EINVAL;
+    if (d->dtype != SP_F32 && d->dtype != SP_BF16) return SP_EINVAL;
+    if (!(d->scale >= 0.f) || !isfinite(d->scale)) return SP_EINVAL;
+    const int G = d->H / d->Hkv;
+    if (d->d != 64 && d->d != 128) return SP_EUNSUPPORTED;
+    if ((G & (G - 1)) != 0 || G * d->N > 32) return SP_EUNSUPPORTED;
+    if ((long long)d->L * d->Hkv > (1 << 20)) return SP_EUNSUPPORTED;
+    return SP_OK;
+}
+
+// Launch plan for one prompt of M keys: choose the number g of workgroups that
+// share a (layer, kv-head) unit so that the slice of each fits its registers,
+// the groups fill the device, and the per-unit barriers stay few; then lay out
+// the workspace.
+sp_status make_plan(const sp_score_desc& d, long long M, int cus, ScorePlan* out) {
+    ScorePlan p;
+    const int G = d.H / d.Hkv;
+    p.rows = G * d.N <= 16 ? 16 : 32;
+    const int tk = p.rows;
+    p.cap = kWaves * (p.rows == 32 ? kTilesPerWave32 : kTilesPerWave16) * tk;
+    p.units = d.L * d.Hkv;
+    if (M < 1) return SP_EINVAL;
+    if ((unsigned long long)(M + d.N) * d.d * esize(d.dtype) >= (1ull << 31)) return SP_EUNSUPPORTED;
+    if (cus < 1) cus = kDefaultCUs;
+    const long long gmin = (M + p.cap - 1) / p.cap;
+    if (gmin > cus) return SP_EUNSUPPORTED;
+    const double bytes_per_key = (double)d.d * esize(d.dtype);
+    const double bw_total = 6.0e12, bw_cu_max = 60.0e9;
+    double best = 1e300;
+    int bg = 0, bkr = 0, bng = 0;
+    for (long long g = gmin; g <= cus; ++g) {
+        long long kr = (M + g - 1) / g;
+        kr = (kr + tk - 1) / tk * tk;
+        if (kr > p.cap) continue;
+        const long long geff = (M + kr - 1) / kr;
+        if (geff != g) continue;  // the same slice with fewer workgroups is planned at geff
+        long long ng = cus / g;
+        if (ng > p.units) ng = p.units;
+        if (ng < 1) continue;
+        const long long iters = (p.units + ng - 1) / ng;
+        const double active = (double)(g * ng);
+        double bw_cu = bw_total / active;
+        if (bw_cu > bw_cu_max) bw_cu = bw_cu_max;
+        const double sync = g == 1 ? 0.0 : (32 % g == 0 ? 2.0e-6 : 4.0e-6);
+        const double cost = iters * (kr * bytes_per_key / bw_cu + sync);
+        if (cost < best * 0.999) {
+            best = cost;
+            bg = (int)g;
+            bkr = (int)kr;
+            bng = (int)ng;
+        }
+    }
+    if (bg == 0) return SP_EUNSUPPORTED;
+    p.g = bg;
+    p.KR = bkr;
+    p.ngroups = bng;
+    p.grid = bg * bng;
+    p.xcd_local = (cus == 256 && 32 % bg == 0 && p.grid == 256) ? 1 : 0;
+    p.ws_cnt = 0;
+    p.ws_part = round_up(4 * (size_t)(p.units + 1), 256);
+    p.ws_tg = p.ws_part + round_up((size_t)p.units * p.g * p.rows * 8, 256);
+    p.ws_total = p.ws_tg + round_up((size_t)p.ngroups * d.N * M * 4, 256);
+    *out = p;
+    return SP_OK;
+}
+
+// Workspace for any prompt of at most max_M keys (bounds that hold for every
+// plan make_plan can choose for M <= max_M).
+size_t workspace_bound(const sp_score_desc& d, long long max_M, int cus) {
+    if (cus < 1) cus = kDefaultCUs;
+    const int G = d.H / d.Hkv;
+    const int rows = G * d.N <= 16 ? 16 : 32;
+    const long long cap = (long long)kWaves * (rows == 32 ? kTilesPerWave32 : kTilesPerWave16) * rows;
+    const long long units = (long long)d.L * d.Hkv;
+    long long tg_elems = (long long)(units < cus ? units : cus) * max_M;
+    if (tg_elems > (long long)cus * cap) tg_elems = (long long)cus * cap;
+    tg_elems *= d.N;
+    return round_up(4 * (size_t)(units + 1), 256) + round_up((size_t)units * cus * rows * 8, 256) +
+           round_up((size_t)tg_elems * 4, 256);
+}
+
+sp_status to_status(hipError_t e) { return e == hipSuccess ? SP_OK : SP_EDEVICE; }
+
+sp_status check_select_params(const sp_select_params* p) {
+    if (!p) return SP_EINVAL;
+    if (p->chunk < 1 || p->pool_k < 1 || (p->pool_k % 2) == 0) return SP_EINVAL;
+    if (p->mode == SP_SELECT_TOPK) {
+        if (!(p->keep_rate > 0.f && p->keep_rate <= 1.f)) return SP_EINVAL;
+    } else if (p->mode == SP_SELECT_MASS) {
+        if (!(p->mass > 0.f && p->mass <= 1.f)) return SP_EINVAL;
+    } else {
+        return SP_EINVAL;
+    }
+    if (p->boost_first_n < 0 || p->boost_last_n < 0) return SP_EINVAL;
+    if (!(p->boost_first_mult >= 0.f) || !(p->boost_last_mult >= 0.f) ||
+        !isfinite(p->boost_first_mult) || !isfinite(p->boost_last_mult))
+        return SP_EINVAL;
+    return SP_OK;
+}
+
+// Per-prompt limits of the selection kernel (see the header).
+sp_status check_select_prompt(const sp_select_params* p, long long M) {
+    if (M < 1) return SP_EINVAL;
+    if (M > (1ll << 24)) return SP_EUNSUPPORTED;
+    const long long nc = (M + p->chunk - 1) / p->chunk;
+    if (nc > kMaxSelectChunks) return SP_EUNSUPPORTED;
+    double vmax = 1.0;
+    const double a = p->boost_first_mult, b = p->boost_last_mult;
+    if (a > vmax) vmax = a;
+    if (b > vmax) vmax = b;
+    if (a * b > vmax) vmax = a * b;
+    const double win = (double)p->pool_k * (double)p->chunk;
+    if (vmax * 4294967296.0 * 1.0000001 * win >= 9007199254740992.0) return SP_EUNSUPPORTED;
+    if (vmax * 4294967296.0 * 1.0000001 * (double)M >= 1.8e19) return SP_EUNSUPPORTED;
+    return SP_OK;
+}
+
+SelectParamsDev to_dev(const sp_select_params* p) {
+    SelectParamsDev q;
+    q.chunk = p->chunk;
+    q.pool_k = p->pool_k;
+    q.mode = p->mode;
+    q.keep_rate = p->keep_rate;
+    q.mass = p->mass;
+    q.first_n = p->boost_first_n;
+    q.first_mult = p->boost_first_mult;
+    q.last_n = p->boost_last_n;
+    q.last_mult = p->boost_last_mult;
+    return q;
+}
+
+}  // namespace
+}  // namespace sp
+
+using namespace sp;
+
+extern "C" {
+
+const char* sp_status_string(sp_status s) {
+    switch (s) {
+        case SP_OK: return "SP_OK";
+        case SP_EINVAL: return "SP_EINVAL: invalid argument";
+        case SP_EUNSUPPORTED: return "SP_EUNSUPPORTED: shape or parameter outside what the kernels implement";
+        case SP_EWORKSPACE: return "SP_EWORKSPACE: workspace missing or too small";
+        case SP_EDEVICE: return "SP_EDEVICE: kernel launch failed";
+    }
+    return "unknown sp_status";
+}
+
+size_t sp_score_workspace_bytes(const sp_score_desc* desc, int64_t max_prompt_len) {
+    if (check_desc(desc) != SP_OK || max_prompt_len < 1) return 0;
+    return workspace_bound(*desc, max_prompt_len, device_cus());
+}
+
+sp_status sp_score_plan(const sp_score_desc* desc, int32_t M, int32_t info[8]) {
+    sp_status s = check_desc(desc);
+    if (s != SP_OK) return s;
+    if (!info) return SP_EINVAL;
+    const int cus = device_cus();
+    ScorePlan p;
+    s = make_plan(*desc, M, cus, &p);
+    if (s != SP_OK) return s;
+    info[0] = p.grid;
+    info[1] = p.g;
+    info[2] = p.ngroups;
+    info[3] = p.KR;
+    info[4] = p.rows;
+    info[5] = p.units;
+    info[6] = cus > 0 ? cus : kDefaultCUs;
+    info[7] = 0;
+    return SP_OK;
+}
+
+sp_status sp_score(const sp_score_desc* desc, const void* Q, const void* K, int32_t M,
+                   float* importance, void* ws, size_t ws_bytes, void* stream) {
+    sp_status s = check_desc(desc);
+    if (s != SP_OK) return s;
+    if (!Q || !K || !importance || M < 1) return SP_EINVAL;
+    if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(importance, 4)) return SP_EINVAL;
+    const int cus = device_cus();
+    if (cus < 1) return SP_EDEVICE;
+    ScorePlan p;
+    s = make_plan(*desc, M, cus, &p);
+    if (s != SP_OK) return s;
+    if (!ws || !aligned(ws, 256) || ws_bytes < p.ws_total) return SP_EWORKSPACE;
+    const long long plane = (long long)(M + desc->N) * desc->d;
+    return to_status(launch_score(p, *desc, Q, K, plane, M, importance, ws, (hipStream_t)stream));
+}
+
+sp_status sp_score_varlen(const sp_score_desc* desc, int32_t R, const void* Q, const void* K,
+                          const int64_t* cu, float* importance, void* ws, size_t ws_bytes,
+                          void* stream) {
+    sp_status s = check_desc(desc);
+    if (s != SP_OK) return s;
+    if (R < 1 || !Q || !K || !cu || !importance) return SP_EINVAL;
+    if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(importance, 4)) return SP_EINVAL;
+    if (cu[0] != 0) return SP_EINVAL;
+    for (int r = 0; r < R; ++r)
+        if (cu[r + 1] - cu[r] < 1) return SP_EINVAL;
+    if (cu[R] + (long long)R * desc->N > (1ll << 40)) return SP_EUNSUPPORTED;
+    const int cus = device_cus();
+    if (cus < 1) return SP_EDEVICE;
+    if (!ws || !aligned(ws, 256)) return SP_EWORKSPACE;
+    // validate every request's plan before enqueueing anything
+    for (int r = 0; r < R; ++r) {
+        ScorePlan p;
+        s = make_plan(*desc, cu[r + 1] - cu[r], cus, &p);
+        if (s != SP_OK) return s;
+        if (ws_bytes < p.ws_total) return SP_EWORKSPACE;
+    }
+    const int es = esize(desc->dtype);
+    const long long T = cu[R] + (long long)R * desc->N;
+    const long long qsz = (long long)desc->L * desc->H * desc->N * desc->d * es;
+    for (int r = 0; r < R; ++r) {
+        const long long M = cu[r + 1] - cu[r];
+        ScorePlan p;
+        make_plan(*desc, M, cus, &p);
+        const char* Qr = (const char*)Q + r * qsz;
+        const char* Kr = (const char*)K + (cu[r] + (long long)r * desc->N) * desc->d * es;
+        s = to_status(launch_score(p, *desc, Qr, Kr, T * desc->d, (int)M, importance + cu[r], ws,
+                                   (hipStream_t)stream));
+        if (s != SP_OK) return s;
+    }
+    return SP_OK;
+}
+
+size_t sp_select_workspace_bytes(int32_t R, int64_t total_prompt_len,
+                                 const sp_select_params* params) {
+    if (R < 1 || total_prompt_len < R || check_select_params(params) != SP_OK) return (size_t)-1;
+    return 0;
+}
+
+sp_status sp_select(const float* importance, int32_t M, const sp_select_params* params,
+                    int32_t pos_base, int32_t* kept_idx, int32_t* pos_ids, int32_t* n_kept,
+                    void* ws, size_t ws_bytes, void* stream) {
+    (void)ws;
+    (void)ws_bytes;
+    sp_status s = check_select_params(params);
+    if (s != SP_OK) return s;
+    if (!importance || !kept_idx || !pos_ids || !n_kept) return SP_EINVAL;
+    s = check_select_prompt(params, M);
+    if (s != SP_OK) return s;
+    if ((long long)pos_base + M > 2147483647ll || (long long)pos_base < -2147483647ll)
+        return SP_EINVAL;
+    if (device_cus() < 1) return SP_EDEVICE;
+    const int64_t cu[2] = {0, M};
+    const SelectParamsDev p = to_dev(params);
+    return to_status(launch_select(p, cu, &pos_base, 1, importance, kept_idx, pos_ids, n_kept,
+                                   (hipStream_t)stream));
+}
+
+sp_status sp_select_varlen(const float* importance, int32_t R, const int64_t* cu,
+                           const int32_t* pos_base_host, const sp_select_params* params,
+                           int32_t* kept_idx, int32_t* pos_ids, int32_t* n_kept, void* ws,
+                           size_t ws_bytes, void* stream) {
+    (void)ws;
+    (void)ws_bytes;
+    sp_status s = check_select_params(params);
+    if (s != SP_OK) return s;
+    if (R < 1 || !cu || !importance || !kept_idx || !pos_ids || !n_kept) return SP_EINVAL;
+    if (R > kMaxSelectRequests) return SP_EUNSUPPORTED;
+    if (cu[0] != 0) return SP_EINVAL;
+    for (int r = 0; r < R; ++r) {
+        if (cu[r + 1] - cu[r] < 1) return SP_EINVAL;
+        s = check_select_prompt(params, cu[r + 1] - cu[r]);
+        if (s != SP_OK) return s;
+        const long long pb = pos_base_host ? pos_base_host[r] : 0;
+        if (pb + (cu[r + 1] - cu[r]) > 2147483647ll) return SP_EINVAL;
+    }
+    if (cu[R] > 2147483647ll) return SP_EUNSUPPORTED;
+    if (device_cus() < 1) return SP_EDEVICE;
+    const SelectParamsDev p = to_dev(params);
+    return to_status(launch_select(p, cu, pos_base_host, R, importance, kept_idx, pos_ids, n_kept,
+                                   (hipStream_t)stream));
+}
+
+}  // extern "C"

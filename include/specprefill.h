@@ -1,0 +1,192 @@
+/*
+ * libspecprefill: SpecPrefill's token-importance estimator on one AMD Instinct
+ * MI355X (gfx950), as a C ABI.
+ *
+ * The method (cited by web-page title and section):
+ *   [SP-R] "Speculative Prefill: Turbocharging TTFT with Lightweight and
+ *          Training-Free Token Importance Estimation" (paper review page),
+ *          sections "Core algorithm" and "Core formulas".
+ *   [SP-G] "SpecPrefill - Implementation Guide", sections "How It Works",
+ *          "v3 Improvements", "v3.1 Optimizations & Bug Fixes" and
+ *          "Configuration Reference".
+ * A small speculator decodes N look-ahead tokens after an M-token prompt; the
+ * softmax attention of those N queries over the prompt keys says which prompt
+ * tokens matter. sp_score turns the queries and keys into one importance score
+ * per prompt token; sp_select turns the scores into the list of prompt tokens a
+ * large model should prefill, with their original position ids.
+ *
+ * Conventions for every call:
+ *  - Pointers marked "device" are HIP device memory (hipMalloc / torch CUDA
+ *    tensors); "host" pointers are ordinary CPU memory read during the call.
+ *    The caller owns every buffer; the library allocates nothing and keeps no
+ *    state between calls. Tensors are dense, row-major, innermost index last.
+ *  - `stream` is a hipStream_t (NULL = the default stream). Calls are
+ *    asynchronous and stream-ordered: they enqueue kernels and return. No call
+ *    synchronises the device.
+ *  - Argument errors are reported synchronously, before anything is enqueued:
+ *    SP_EINVAL (malformed arguments), SP_EUNSUPPORTED (well-formed but outside
+ *    what the kernels implement), SP_EWORKSPACE (workspace missing or too
+ *    small). SP_EDEVICE reports a failed kernel launch; faults during
+ *    execution surface at the caller's next synchronisation, as usual in HIP.
+ *  - Inputs containing NaN or Inf give unspecified (but memory-safe) results.
+ *  - Two calls may run concurrently only with distinct workspaces and outputs.
+ */
+#ifndef SPECPREFILL_H
+#define SPECPREFILL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SP_OK = 0,
+    SP_EINVAL = 1,
+    SP_EUNSUPPORTED = 2,
+    SP_EWORKSPACE = 3,
+    SP_EDEVICE = 4
+} sp_status;
+
+typedef enum { SP_F32 = 0, SP_BF16 = 1 } sp_dtype;
+
+typedef enum { SP_SELECT_TOPK = 0, SP_SELECT_MASS = 1 } sp_select_mode;
+
+/* Shape of the speculator's attention: L attention layers, H query heads,
+ * Hkv key/value heads (H % Hkv == 0; query head h reads kv-head h / (H/Hkv)),
+ * head dimension d, N look-ahead steps. scale multiplies the logits; 0 selects
+ * 1/sqrt(d). Supported: d in {64, 128}; G = H/Hkv a power of two; G*N <= 32. */
+typedef struct {
+    int32_t L, H, Hkv, d, N;
+    sp_dtype dtype;
+    float scale;
+} sp_score_desc;
+
+/* Selection parameters ([SP-G] Configuration Reference gives the pages'
+ * defaults: chunk 32, keep rate 0.3, mass 0.85, boosts first 64 x1.5 and last
+ * 128 x1.3).
+ *   chunk      tokens per chunk (>= 1)
+ *   pool_k     odd width of the average pool over chunk scores (1 = none)
+ *   mode       SP_SELECT_TOPK uses keep_rate in (0,1]; SP_SELECT_MASS uses mass in (0,1]
+ *   boost_*    multipliers >= 0 for the first / last n tokens (1.0 = off) */
+typedef struct {
+    int32_t chunk, pool_k;
+    sp_select_mode mode;
+    float keep_rate, mass;
+    int32_t boost_first_n;
+    float boost_first_mult;
+    int32_t boost_last_n;
+    float boost_last_mult;
+} sp_select_params;
+
+/* Bytes of device workspace sp_score / sp_score_varlen need for prompts of at
+ * most max_prompt_len tokens; 0 if the shape is invalid or unsupported. */
+size_t sp_score_workspace_bytes(const sp_score_desc* desc, int64_t max_prompt_len);
+
+/*
+ * Token importance of one prompt ([SP-R] Core formulas: attention score
+ * a_ij = Softmax(Q_{M+j} K^T)_i and the importance aggregation; [SP-G] How It
+ * Works, token importance):
+ *   importance[i] = (1/N) * sum_{j<N} max_{l<L, h<H} softmax_j(s_{l,h,j,.})[i],
+ *   s_{l,h,j,i} = scale * <Q[l][h][j][:], K[l][h/G][i][:]>,
+ * where row j is the query at position M+j and its softmax runs over the
+ * M+j+1 keys 0..M+j it can see (the look-ahead keys M..M+N-1 enter only the
+ * denominators of the rows that see them); i < M.
+ *   Q           device, [L][H][N][d] of desc->dtype (RoPE already applied)
+ *   K           device, [L][Hkv][M+N][d] of desc->dtype
+ *   M           prompt length, >= 1
+ *   importance  device, [M] float32 (written)
+ *   ws          device workspace of ws_bytes >= sp_score_workspace_bytes(desc, M);
+ *               contents need no initialisation and are clobbered
+ */
+sp_status sp_score(const sp_score_desc* desc, const void* Q, const void* K, int32_t M,
+                   float* importance, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * sp_score for a ragged batch of R requests (R >= 1), each scored exactly as
+ * sp_score would score it alone.
+ *   Q              device, [R][L][H][N][d]
+ *   K              device, [L][Hkv][T][d], T = sum_r (M_r + N); request r's
+ *                  M_r prompt keys followed by its N look-ahead keys start at
+ *                  key row cu_prompt_host[r] + r*N
+ *   cu_prompt_host host, [R+1] prompt offsets: cu_prompt_host[0] = 0,
+ *                  M_r = cu_prompt_host[r+1] - cu_prompt_host[r] >= 1
+ *   importance     device, [cu_prompt_host[R]] float32; request r's scores at
+ *                  offset cu_prompt_host[r]
+ *   ws             as for sp_score with max_prompt_len = max_r M_r
+ */
+sp_status sp_score_varlen(const sp_score_desc* desc, int32_t R, const void* Q, const void* K,
+                          const int64_t* cu_prompt_host, float* importance, void* ws,
+                          size_t ws_bytes, void* stream);
+
+/* Bytes of device workspace sp_select / sp_select_varlen need (currently 0 for
+ * every valid argument set; (size_t)-1 if the arguments are invalid). */
+size_t sp_select_workspace_bytes(int32_t R, int64_t total_prompt_len,
+                                 const sp_select_params* params);
+
+/*
+ * Chunk selection and compaction for one prompt ([SP-G] How It Works and v3
+ * Improvements; [SP-R] Core algorithm: chunk selection, pooling, position-ID
+ * recovery). With x = importance:
+ *  1. v_i = (x_i - min x) / (max x - min x) in float32 (all 1 if max == min);
+ *  2. v_i *= first_mult for i < first_n, then v_i *= last_mult for i >= M - last_n;
+ *  3. q_i = round_half_even(v_i * 2^32) as uint64;
+ *  4. chunk c holds tokens [c*chunk, min((c+1)*chunk, M)); C_c = sum q_i;
+ *  5. key_c = (double) sum_{c'} C_c' / (double) sum_{c'} len_c' over the pool
+ *     window c' in [c - (pool_k-1)/2, c + (pool_k-1)/2] clipped to [0, nc);
+ *  6. chunks ranked by key descending, ties by smaller index;
+ *     top-K keeps the first K = min(nc, max(1, ceil((double)keep_rate * nc)));
+ *     mass keeps ranked chunks until (double)(sum of their C) >=
+ *     (double)mass * (double)(sum of all C), the crossing chunk included;
+ *  7. every token i of every kept chunk, ascending:
+ *     kept_idx[n] = i, pos_ids[n] = pos_base + i. The first decode position
+ *     afterwards is pos_base + M.
+ * The result is a pure function of the float32 scores: identical inputs give
+ * identical outputs on every run.
+ *   importance  device, [M] float32
+ *   kept_idx, pos_ids  device, [M] int32 each (first *n_kept entries written)
+ *   n_kept      device, [1] int32 (written)
+ * Supported: M <= 2^24, nc = ceil(M/chunk) <= 4096, and boost multipliers
+ * with max(1, first_mult, last_mult, first_mult*last_mult) * 2^32 * pool_k *
+ * chunk < 2^53 (so the pooled sums stay exact in double).
+ */
+sp_status sp_select(const float* importance, int32_t M, const sp_select_params* params,
+                    int32_t pos_base, int32_t* kept_idx, int32_t* pos_ids, int32_t* n_kept,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * sp_select applied independently to each request of a ragged batch (one
+ * workgroup per request; R <= 1024).
+ *   importance      device, [cu_prompt_host[R]] float32
+ *   cu_prompt_host  host, [R+1] prompt offsets (as for sp_score_varlen)
+ *   pos_base_host   host, [R] position of each request's first prompt token,
+ *                   or NULL for all 0
+ *   kept_idx        device, [cu_prompt_host[R]] int32: request r writes its
+ *                   kept tokens as packed indices cu_prompt_host[r] + i, from
+ *                   offset cu_prompt_host[r]
+ *   pos_ids         device, [cu_prompt_host[R]] int32: pos_base_r + i, same offsets
+ *   n_kept          device, [R] int32
+ */
+sp_status sp_select_varlen(const float* importance, int32_t R, const int64_t* cu_prompt_host,
+                           const int32_t* pos_base_host, const sp_select_params* params,
+                           int32_t* kept_idx, int32_t* pos_ids, int32_t* n_kept, void* ws,
+                           size_t ws_bytes, void* stream);
+
+/* Static, human-readable name of a status code. */
+const char* sp_status_string(sp_status status);
+
+/*
+ * Launch plan sp_score would use for one prompt of M tokens (for reports and
+ * tests): info[0] workgroups, info[1] workgroups per (layer, kv-head) unit,
+ * info[2] groups working in parallel, info[3] prompt keys per workgroup,
+ * info[4] query rows per tile (16 or 32), info[5] units, info[6] device
+ * compute units, info[7] reserved (0). No device work is enqueued.
+ */
+sp_status sp_score_plan(const sp_score_desc* desc, int32_t M, int32_t info[8]);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECPREFILL_H */

@@ -1,0 +1,144 @@
+"""The C-ABI library loads, exports every call the header declares, and rejects
+bad arguments synchronously (no GPU needed: every checked error returns before
+any device call)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import attention_token_scoring_amd as sp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "specprefill.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(sp.LIB_PATH):
+        pytest.skip("libspecprefill.so not built (run __graft_entry__.build())")
+    return sp.load_library()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sp_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_names():
+    assert header_functions() == sorted(sp.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", sp.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (sp_\w+)", out))
+    for name in header_functions():
+        assert name in exported, name
+        getattr(lib, name)
+
+
+def test_status_strings(lib):
+    for s in range(5):
+        assert sp.sp_status_string(s).startswith("SP_")
+    assert "unknown" in sp.sp_status_string(99)
+
+
+def desc(**kw):
+    base = dict(L=2, H=4, Hkv=2, d=64, N=8, dtype=sp.SP_BF16, scale=0.0)
+    base.update(kw)
+    return sp.score_desc(**base)
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every case below fails validation first
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(H=3, Hkv=2), sp.SP_EINVAL),
+    (dict(L=0), sp.SP_EINVAL),
+    (dict(N=0), sp.SP_EINVAL),
+    (dict(dtype=7), sp.SP_EINVAL),
+    (dict(scale=-1.0), sp.SP_EINVAL),
+    (dict(scale=float("inf")), sp.SP_EINVAL),
+    (dict(d=96), sp.SP_EUNSUPPORTED),
+    (dict(H=12, Hkv=4), sp.SP_EUNSUPPORTED),       # G = 3, not a power of two
+    (dict(H=32, Hkv=8, N=16), sp.SP_EUNSUPPORTED),  # G*N = 64 > 32
+])
+def test_score_rejects_descriptors(lib, kw, status):
+    d = desc(**kw)
+    st = lib.sp_score(ctypes.byref(d), FAKE, FAKE, 100, FAKE, FAKE, 1 << 30, None)
+    assert st == status
+    assert lib.sp_score_workspace_bytes(ctypes.byref(d), 100) == 0
+
+
+def test_score_rejects_pointers_and_sizes(lib):
+    d = desc()
+    assert lib.sp_score(ctypes.byref(d), None, FAKE, 100, FAKE, FAKE, 1 << 30, None) == sp.SP_EINVAL
+    assert lib.sp_score(ctypes.byref(d), FAKE, FAKE, 0, FAKE, FAKE, 1 << 30, None) == sp.SP_EINVAL
+    mis = ctypes.c_void_p(0x1008)  # not 16-byte aligned
+    assert lib.sp_score(ctypes.byref(d), mis, FAKE, 100, FAKE, FAKE, 1 << 30, None) == sp.SP_EINVAL
+    assert lib.sp_score(None, FAKE, FAKE, 100, FAKE, FAKE, 1 << 30, None) == sp.SP_EINVAL
+
+
+def test_varlen_rejects_offsets(lib):
+    d = desc()
+    for cu in ([1, 10], [0, 10, 10], [0, 5, 3]):
+        arr = (ctypes.c_int64 * len(cu))(*cu)
+        st = lib.sp_score_varlen(ctypes.byref(d), len(cu) - 1, FAKE, FAKE, arr, FAKE, FAKE,
+                                 1 << 30, None)
+        assert st == sp.SP_EINVAL, cu
+    assert lib.sp_score_varlen(ctypes.byref(d), 0, FAKE, FAKE, None, FAKE, FAKE, 1, None) \
+        == sp.SP_EINVAL
+
+
+def test_workspace_bytes_grows_with_prompt(lib):
+    d = desc(L=32, H=32, Hkv=8, d=128)
+    a = sp.sp_score_workspace_bytes(d, 1024)
+    b = sp.sp_score_workspace_bytes(d, 32768)
+    assert 0 < a <= b < (64 << 20)
+
+
+def test_plan_for_the_8b_shape(lib):
+    """At L=32, Hkv=8, d=128, M=32768 one unit spans 32 workgroups of 1024 keys,
+    8 groups fill the 256 CUs (one group per XCD)."""
+    p = sp.sp_score_plan(desc(L=32, H=32, Hkv=8, d=128), 32768)
+    assert p["rows"] == 32 and p["units"] == 256
+    assert p["g"] * p["keys_per_wg"] >= 32768 and p["keys_per_wg"] <= 1024
+    assert p["grid"] <= p["cus"]
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(chunk=0), sp.SP_EINVAL),
+    (dict(pool_k=4), sp.SP_EINVAL),
+    (dict(pool_k=0), sp.SP_EINVAL),
+    (dict(keep_rate=0.0), sp.SP_EINVAL),
+    (dict(keep_rate=1.01), sp.SP_EINVAL),
+    (dict(mode="mass", mass=0.0), sp.SP_EINVAL),
+    (dict(mode=5), sp.SP_EINVAL),
+    (dict(boost_first_mult=-1.0), sp.SP_EINVAL),
+    (dict(boost_last_n=-3), sp.SP_EINVAL),
+    (dict(chunk=1), sp.SP_EUNSUPPORTED),            # nc = 10000 > 4096
+    (dict(boost_first_mult=3e6), sp.SP_EUNSUPPORTED),  # pooled sums would exceed 2^53
+])
+def test_select_rejects(lib, kw, status):
+    base = dict(chunk=32, pool_k=3, mode="topk", keep_rate=0.3)
+    base.update(kw)
+    p = sp.select_params(**base)
+    st = lib.sp_select(FAKE, 10000, ctypes.byref(p), 0, FAKE, FAKE, FAKE, None, 0, None)
+    assert st == status
+
+
+def test_select_rejects_null_and_sizes(lib):
+    p = sp.select_params(chunk=32, pool_k=3, keep_rate=0.3)
+    assert lib.sp_select(None, 100, ctypes.byref(p), 0, FAKE, FAKE, FAKE, None, 0, None) \
+        == sp.SP_EINVAL
+    assert lib.sp_select(FAKE, 0, ctypes.byref(p), 0, FAKE, FAKE, FAKE, None, 0, None) \
+        == sp.SP_EINVAL
+    assert lib.sp_select(FAKE, 100, ctypes.byref(p), 2147483600, FAKE, FAKE, FAKE, None, 0,
+                         None) == sp.SP_EINVAL
+    cu = (ctypes.c_int64 * 3)(0, 50, 50)
+    assert lib.sp_select_varlen(FAKE, 2, cu, None, ctypes.byref(p), FAKE, FAKE, FAKE, None, 0,
+                                None) == sp.SP_EINVAL
+    assert sp.sp_select_workspace_bytes(1, 100, p) == 0

@@ -1,0 +1,261 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle on the same
+seeded inputs.
+
+Tolerances. Importance: max-abs <= 2e-3 (the target's stated bound), and in
+addition an element-wise relative bound of 1e-3 derived from the arithmetic:
+bf16 x bf16 products are exact in fp32, the fp32 MFMA accumulation of d = 128
+terms bounds the logit error by about d * 2^-24 * sum|q_t k_t| * scale
+(< 1e-4 on these inputs), and p = exp2(s*c - lse) turns an absolute logit
+error e into a relative error of about 2e when the row's log-sum-exp carries a
+similar error; the hardware exp2/log2 add ~1e-7. 1e-3 leaves a 5x margin and
+still catches semantic slips the absolute bound would miss (a softmax over the
+wrong number of keys changes every probability by (M+j+1)/(M+N) - 1, which is
+~4e-3 at M = 1000). Selection: bit-exact (kept indices, position ids, count)
+when the oracle's selection is fed the GPU's float32 importance array.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+import attention_token_scoring_amd as sp  # noqa: E402
+
+ABS_TOL = 2e-3
+REL_TOL = 1e-3
+
+
+def to_dev(a: np.ndarray):
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(a).cuda()
+
+
+def check_importance(gpu: np.ndarray, ref: np.ndarray, label: str):
+    gpu = gpu.astype(np.float64)
+    assert gpu.shape == ref.shape, label
+    assert np.all(np.isfinite(gpu)), label
+    abs_err = np.max(np.abs(gpu - ref))
+    rel = np.abs(gpu - ref) / np.maximum(ref, 1e-30)
+    worst = int(np.argmax(rel))
+    print(f"[{label}] max-abs {abs_err:.3e}  max-rel {rel[worst]:.3e} at {worst}", flush=True)
+    assert abs_err <= ABS_TOL, label
+    assert rel[worst] <= REL_TOL, (label, worst, gpu[worst], ref[worst])
+
+
+def check_selection(imp_gpu_t, sel, label, pos_base=0):
+    params = sp.select_params(**oracle.select_params(sel))
+    kept, pos, n = sp.sp_select(imp_gpu_t, params, pos_base=pos_base)
+    torch.cuda.synchronize()
+    imp_h = imp_gpu_t.cpu().numpy()
+    k_ref, p_ref = oracle.select(imp_h, pos_base=pos_base, **oracle.select_params(sel))
+    nk = int(n.cpu()[0])
+    print(f"[{label}] kept {nk} tokens ({sel.mode})", flush=True)
+    assert nk == len(k_ref), label
+    assert np.array_equal(kept[:nk].cpu().numpy(), k_ref), label
+    assert np.array_equal(pos[:nk].cpu().numpy(), p_ref), label
+    return nk
+
+
+def workload(L, H, Hkv, d, N, M, dtype, seed=11, plant_chunk=32):
+    return synth.Workload("case", L=L, H=H, Hkv=Hkv, d=d, N=N, dtype=dtype, seed=seed, M=M,
+                          plant_frac=0.05, plant_chunk=plant_chunk)
+
+
+BF, F32 = synth.BF16, synth.F32
+
+SMALL_CASES = [
+    # id, L, H, Hkv, d, N, M, dtype
+    ("bf16-d128-G4-N8-M1000", 2, 8, 2, 128, 8, 1000, BF),
+    ("bf16-d128-G4-N8-M4100", 2, 8, 2, 128, 8, 4100, BF),
+    ("bf16-d128-G4-N8-M20000", 1, 8, 2, 128, 8, 20000, BF),
+    ("bf16-d64-G2-N8-M777", 3, 4, 2, 64, 8, 777, BF),
+    ("bf16-d64-G2-N8-M5000", 2, 4, 2, 64, 8, 5000, BF),
+    ("f32-d64-G2-N8-M1024", 2, 4, 2, 64, 8, 1024, F32),
+    ("f32-d128-G4-N8-M300", 2, 8, 2, 128, 8, 300, F32),
+    ("f32-d64-G4-N8-M2100", 1, 8, 2, 64, 8, 2100, F32),
+    ("bf16-d128-G1-N16-M513", 2, 4, 4, 128, 16, 513, BF),
+    ("bf16-d128-G8-N4-M2000", 1, 16, 2, 128, 4, 2000, BF),
+    ("bf16-d64-G16-N2-M900", 1, 16, 1, 64, 2, 900, BF),
+    ("bf16-d128-G32-N1-M700", 1, 32, 1, 128, 1, 700, BF),
+    ("bf16-d128-G4-N6-M999", 2, 8, 2, 128, 6, 999, BF),
+    ("bf16-d64-G1-N3-M1", 1, 2, 2, 64, 3, 1, BF),
+    ("bf16-d64-G2-N1-M17", 2, 4, 2, 64, 1, 17, BF),
+    ("bf16-d128-G2-N4-M33", 3, 4, 2, 128, 4, 33, BF),
+]
+
+
+@pytest.mark.parametrize("case", SMALL_CASES, ids=[c[0] for c in SMALL_CASES])
+def test_score_small_shapes(case):
+    name, L, H, Hkv, d, N, M, dt = case
+    print(f"case {name}", flush=True)
+    w = workload(L, H, Hkv, d, N, M, dt)
+    Qh, Kh, _ = synth.make_request(w)
+    imp = sp.sp_score(to_dev(Qh), to_dev(Kh))
+    torch.cuda.synchronize()
+    check_importance(imp.cpu().numpy(), oracle.score(Qh, Kh), name)
+
+
+def test_score_peaked_logits_with_explicit_scale():
+    """scale = 1 on the planted data gives logits with std ~sqrt(d): rows are
+    sharply peaked; the online statistics must stay stable."""
+    w = workload(2, 8, 2, 128, 8, 1500, BF, seed=21)
+    Qh, Kh, _ = synth.make_request(w)
+    imp = sp.sp_score(to_dev(Qh), to_dev(Kh), scale=1.0)
+    torch.cuda.synchronize()
+    ref = oracle.score(Qh, Kh, scale=1.0)
+    gpu = imp.cpu().numpy().astype(np.float64)
+    big = ref > 1e-6  # relative bound on the probabilities that carry signal
+    assert np.max(np.abs(gpu - ref)) <= ABS_TOL
+    assert np.max(np.abs(gpu[big] - ref[big]) / ref[big]) <= REL_TOL
+
+
+def test_score_is_deterministic():
+    w = workload(2, 8, 2, 128, 8, 3000, BF, seed=5)
+    Qh, Kh, _ = synth.make_request(w)
+    Q, K = to_dev(Qh), to_dev(Kh)
+    a = sp.sp_score(Q, K)
+    b = sp.sp_score(Q, K)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_score_workspace_too_small_is_rejected():
+    w = workload(1, 4, 2, 64, 8, 500, BF)
+    Qh, Kh, _ = synth.make_request(w)
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(sp.SpError) as e:
+        sp.sp_score(to_dev(Qh), to_dev(Kh), workspace=ws)
+    assert e.value.status == sp.SP_EWORKSPACE
+
+
+# ----------------------------------------------------------------------------------------
+# the five workloads at full size
+# ----------------------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["tiny", "spec0.8b_m4608", "spec8b_m32k"])
+def test_workload_full(name):
+    w = synth.WORKLOADS[name]
+    print(f"workload {name}: generating", flush=True)
+    Qh, Kh, M = synth.make_request(w)
+    imp = sp.sp_score(to_dev(Qh), to_dev(Kh))
+    torch.cuda.synchronize()
+    print(f"workload {name}: oracle", flush=True)
+    ref = oracle.score(Qh, Kh)
+    check_importance(imp.cpu().numpy(), ref, name)
+    for sel in w.selects:
+        nk = check_selection(imp, sel, name)
+        if sel.mode == "topk" and M % sel.chunk == 0:
+            nc = M // sel.chunk
+            assert nk == max(1, math.ceil(np.float64(np.float32(sel.keep_rate)) * nc)) * sel.chunk
+
+
+def test_workload_full_128k():
+    w = synth.WORKLOADS["spec8b_m128k"]
+    print("workload spec8b_m128k: generating", flush=True)
+    Qh, Kh, M = synth.make_request(w)
+    Q, K = to_dev(Qh), to_dev(Kh)
+    imp = sp.sp_score(Q, K)
+    torch.cuda.synchronize()
+    del Q, K
+    print("workload spec8b_m128k: oracle", flush=True)
+    ref = oracle.score(Qh, Kh)
+    check_importance(imp.cpu().numpy(), ref, "spec8b_m128k")
+    for sel in w.selects:
+        check_selection(imp, sel, f"spec8b_m128k {sel.mode} {sel.keep_rate or sel.mass}")
+
+
+def test_workload_ragged_batch():
+    """All 16 requests scored in one varlen call. The oracle recomputes the
+    shortest and the longest request in full (each request is independent of
+    the others); every request's selection is checked bit for bit."""
+    w = synth.WORKLOADS["ragged16_8b"]
+    print("workload ragged16_8b: generating", flush=True)
+    Qh, Kh, cu = synth.make_ragged(w)
+    Q, K = to_dev(Qh), to_dev(Kh)
+    imp = sp.sp_score_varlen(Q, K, cu)
+    torch.cuda.synchronize()
+    del Q, K, Kh
+    imp_h = imp.cpu().numpy()
+    Ms = np.diff(cu)
+    for r in sorted({int(np.argmin(Ms)), int(np.argmax(Ms))}):
+        print(f"workload ragged16_8b: oracle for request {r} (M={Ms[r]})", flush=True)
+        q, k, M = synth.make_request(w, r)
+        check_importance(imp_h[cu[r]:cu[r + 1]], oracle.score(q, k), f"ragged r={r}")
+    assert np.all(np.isfinite(imp_h)) and np.all(imp_h >= 0) and np.all(imp_h <= 1)
+    sel = w.selects[0]
+    params = sp.select_params(**oracle.select_params(sel))
+    pos_base = [(7 * r) % 5 for r in range(len(Ms))]
+    kept, pos, n = sp.sp_select_varlen(imp, cu, params, pos_base=pos_base)
+    torch.cuda.synchronize()
+    kept_h, pos_h, n_h = kept.cpu().numpy(), pos.cpu().numpy(), n.cpu().numpy()
+    for r in range(len(Ms)):
+        k_ref, p_ref = oracle.select(imp_h[cu[r]:cu[r + 1]], pos_base=pos_base[r],
+                                     base_index=int(cu[r]), **oracle.select_params(sel))
+        assert n_h[r] == len(k_ref), r
+        off = int(cu[r])
+        assert np.array_equal(kept_h[off:off + n_h[r]], k_ref), r
+        assert np.array_equal(pos_h[off:off + n_h[r]], p_ref), r
+
+
+# ----------------------------------------------------------------------------------------
+# selection on given score arrays (bit-exact against the oracle)
+# ----------------------------------------------------------------------------------------
+def _select_case(x: np.ndarray, pos_base=0, **kw):
+    params = sp.select_params(**kw)
+    t = torch.from_numpy(x.astype(np.float32)).cuda()
+    kept, pos, n = sp.sp_select(t, params, pos_base=pos_base)
+    torch.cuda.synchronize()
+    k_ref, p_ref = oracle.select(x.astype(np.float32), pos_base=pos_base, **kw)
+    nk = int(n.cpu()[0])
+    assert nk == len(k_ref), kw
+    assert np.array_equal(kept[:nk].cpu().numpy(), k_ref), kw
+    assert np.array_equal(pos[:nk].cpu().numpy(), p_ref), kw
+    return k_ref
+
+
+def test_select_position_id_example():
+    x = np.array([0.9, 0.8, 0.1, 0.7, 0.2, 0.3, 0.6, 0.5, 0.05, 0.15])
+    k = _select_case(x, chunk=1, pool_k=1, mode="topk", keep_rate=0.5)
+    assert k.tolist() == [0, 1, 3, 6, 7]
+
+
+SELECT_CASES = [
+    dict(M=32768, chunk=32, pool_k=13, mode="topk", keep_rate=0.1),
+    dict(M=32768, chunk=8, pool_k=5, mode="mass", mass=0.85),       # nc = 4096 (maximum)
+    dict(M=4608, chunk=32, pool_k=5, mode="mass", mass=0.85, boost_first_n=64,
+         boost_first_mult=1.5, boost_last_n=128, boost_last_mult=1.3),
+    dict(M=1000, chunk=24, pool_k=3, mode="topk", keep_rate=0.3),     # chunk not a power of 2
+    dict(M=5000, chunk=100, pool_k=7, mode="mass", mass=0.5),         # > 64, not a power of 2
+    dict(M=9000, chunk=128, pool_k=3, mode="topk", keep_rate=0.25),   # > 64, power of 2
+    dict(M=777, chunk=16, pool_k=41, mode="topk", keep_rate=0.2),     # wide pool
+    dict(M=1, chunk=32, pool_k=3, mode="topk", keep_rate=0.1),
+    dict(M=64, chunk=64, pool_k=1, mode="mass", mass=1.0),
+    dict(M=300, chunk=7, pool_k=1, mode="topk", keep_rate=1.0),
+    dict(M=2049, chunk=32, pool_k=3, mode="mass", mass=0.3, boost_first_n=100,
+         boost_first_mult=2.0, boost_last_n=2000, boost_last_mult=0.5),
+]
+
+
+@pytest.mark.parametrize("dist", ["uniform", "ties", "constant", "spiky"])
+@pytest.mark.parametrize("case", SELECT_CASES,
+                         ids=[f"{c['M']}-{c['chunk']}-{c['mode']}" for c in SELECT_CASES])
+def test_select_matches_oracle(case, dist):
+    kw = dict(case)
+    M = kw.pop("M")
+    rng = np.random.default_rng(M + len(dist))
+    if dist == "uniform":
+        x = rng.random(M)
+    elif dist == "ties":
+        x = rng.integers(0, 4, M) / 3.0
+    elif dist == "constant":
+        x = np.full(M, 0.125)
+    else:
+        x = rng.random(M) ** 8 * 1e-3
+    _select_case(x, pos_base=3, **kw)
