@@ -68,7 +68,7 @@ sp_status make_plan(const sp_score_desc& d, long long M, int cus, ScorePlan* out
     const int G = d.H / d.Hkv;
     p.rows = G * d.N <= 16 ? 16 : 32;
     const int tk = p.rows;
-    p.cap = kWaves * (p.rows == 32 ? kTilesPerWave32 : kTilesPerWave16) * tk;
+    p.cap = kWaves * tiles_per_wave(d.dtype == SP_BF16, p.rows / 16) * kTileKeys;
     p.units = d.L * d.Hkv;
     if (M < 1) return SP_EINVAL;
     if ((unsigned long long)(M + d.N) * d.d * esize(d.dtype) >= (1ull << 31)) return SP_EUNSUPPORTED;
@@ -109,7 +109,10 @@ sp_status make_plan(const sp_score_desc& d, long long M, int cus, ScorePlan* out
     p.xcd_local = (cus == 256 && 32 % bg == 0 && p.grid == 256) ? 1 : 0;
     p.ws_cnt = 0;
     p.ws_part = round_up(4 * (size_t)(p.units + 1), 256);
-    p.ws_tg = p.ws_part + round_up((size_t)p.units * p.g * p.rows * 8, 256);
+    p.ws_tail = p.ws_part + round_up((size_t)p.units * p.g * p.rows * 8, 256);
+    p.ws_lse = p.ws_tail + round_up((size_t)p.units * p.rows * 8, 256);
+    p.ws_flag = p.ws_lse + round_up((size_t)p.units * p.rows * 4, 256);
+    p.ws_tg = p.ws_flag + round_up((size_t)p.units * 4, 256);
     p.ws_total = p.ws_tg + round_up((size_t)p.ngroups * d.N * M * 4, 256);
     *out = p;
     return SP_OK;
@@ -121,13 +124,14 @@ size_t workspace_bound(const sp_score_desc& d, long long max_M, int cus) {
     if (cus < 1) cus = kDefaultCUs;
     const int G = d.H / d.Hkv;
     const int rows = G * d.N <= 16 ? 16 : 32;
-    const long long cap = (long long)kWaves * (rows == 32 ? kTilesPerWave32 : kTilesPerWave16) * rows;
+    const long long cap = (long long)kWaves * tiles_per_wave(d.dtype == SP_BF16, rows / 16) * kTileKeys;
     const long long units = (long long)d.L * d.Hkv;
     long long tg_elems = (long long)(units < cus ? units : cus) * max_M;
     if (tg_elems > (long long)cus * cap) tg_elems = (long long)cus * cap;
     tg_elems *= d.N;
     return round_up(4 * (size_t)(units + 1), 256) + round_up((size_t)units * cus * rows * 8, 256) +
-           round_up((size_t)tg_elems * 4, 256);
+           round_up((size_t)units * rows * 8, 256) + round_up((size_t)units * rows * 4, 256) +
+           round_up((size_t)units * 4, 256) + round_up((size_t)tg_elems * 4, 256);
 }
 
 sp_status to_status(hipError_t e) { return e == hipSuccess ? SP_OK : SP_EDEVICE; }

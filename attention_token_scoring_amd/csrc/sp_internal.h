@@ -8,18 +8,18 @@
 
 namespace sp {
 
-// Waves per scoring workgroup and logit tiles each wave keeps in registers.
-// Query-row tiles are 16 or 32 rows (the MFMA N dimension); a tile covers as
-// many keys as rows, so one workgroup holds the logits of 8*4*32 = 1024 keys
-// (32-row tiles) or 8*16*16 = 2048 keys (16-row tiles) for one (layer,
-// kv-head) unit.
+// Scoring workgroups have 8 waves (two per SIMD, 256 registers each). Keys
+// are processed in tiles of 16 (the M dimension of the 16x16 MFMAs); query
+// rows in 16-row halves (NH = 1 or 2 halves per kv-head). Each wave keeps the
+// logits of three units in registers (a unit is finished two units after it
+// is streamed): 3 * tiles_per_wave * NH * 4 registers.
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
-constexpr int kTilesPerWave32 = 4;
-constexpr int kTilesPerWave16 = 16;
-// Padding (floats) between the look-ahead rows of the per-workgroup running
-// maximum in LDS, to spread the rows over banks.
-constexpr int kRowPad = 8;
+constexpr int kTileKeys = 16;
+constexpr int tiles_per_wave(bool bf16, int nh) { return (bf16 ? 4 : 2) * (nh == 1 ? 2 : 1); }
+// Extra floats per look-ahead row of the LDS running maximum: rows start 16
+// banks apart.
+constexpr int row_stride(int kr) { return (kr + 63) / 64 * 64 + 16; }
 
 // Everything the cooperative scoring kernel needs for one request.
 struct ScoreArgs {
@@ -28,9 +28,12 @@ struct ScoreArgs {
     long long plane_stride;    // elements between consecutive (layer, kv-head) key planes
     float* Tg;                 // [ngroups][N][M]: per-group running max of log2 probabilities
     float2* part;              // [units][g][rows]: per-workgroup (row max, row sum) partials
+    float2* tail;              // [units][rows]: the look-ahead keys' (row max, row sum)
+    float* lse;                // [units][rows]: each row's log2-sum-exp2 (scaled logits)
+    int* flag;                 // [units]: set once the unit's lse is published
     int* cnt;                  // [units]: arrival counters of the per-unit barriers
     int* err;                  // [1]: set when a barrier wait times out
-    int L, H, Hkv, G, N, M;
+    int L, H, Hkv, G, N, M, d;
     int g;                     // workgroups cooperating on one unit
     int ngroups;               // groups working in parallel
     int KR;                    // prompt keys per workgroup (multiple of the tile width)
@@ -44,7 +47,7 @@ struct ScorePlan {
     int cap;       // prompt keys one workgroup can hold
     int g, ngroups, KR, units, grid;
     int xcd_local;
-    size_t ws_cnt, ws_part, ws_tg, ws_total;  // byte offsets / sizes in the workspace
+    size_t ws_cnt, ws_part, ws_tail, ws_lse, ws_flag, ws_tg, ws_total;  // byte offsets / sizes in the workspace
 };
 
 // Selection of one request (one workgroup).

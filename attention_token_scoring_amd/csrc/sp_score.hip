@@ -7,27 +7,35 @@
 // of the scaled logits of query M+j over the M+j+1 keys it sees, then
 //   importance_i = (1/N) sum_j max_{l,h} p_{l,h,j,i},  i < M.
 //
-// How (one pass over K in HBM):
+// How (K is read from HBM once):
 //  * A unit is one (layer, kv-head) plane of K. The G query heads of the plane
-//    and the N look-ahead steps form G*N query rows, padded to a 16- or 32-row
-//    MFMA tile (row = j*G + h_local), so one bf16 MFMA chain computes
-//    K_tile x Q^T for all of them: keys are the MFMA M dimension, query rows
-//    the N dimension, and each lane ends up holding one query row for several
-//    keys, so row statistics are mostly lane-local.
-//  * g workgroups (one per CU, launched cooperatively so all are resident)
-//    share a unit, each holding the logits of its slice of <= 1024 (2048) keys
-//    in registers. Each publishes its slice's (row max, row sum), waits at a
-//    per-unit barrier for the other g-1, combines the g partials into the row
-//    log-sum-exp, and turns its registers into log2 probabilities without
-//    touching K again.
-//  * The max over the G heads of a step is a DPP max across the G adjacent
-//    lanes; the max over kv-heads and layers is a running max in LDS, kept in
-//    the log2 domain (exp2 is monotone, so the exponential is taken once per
-//    (step, key) at the end). Each group writes its running max; a small
-//    kernel takes the max over groups, exponentiates and averages over steps.
+//    and the N look-ahead steps give G*N query rows (row = j*G + h_local),
+//    handled as one or two 16-row halves. Logits come from 16x16x32 bf16 (or
+//    16x16x4 f32) MFMAs with keys as the M dimension: each lane ends up holding
+//    one query row for 4 keys of a tile, so row statistics are lane-local, and
+//    each load instruction reads 64 contiguous bytes of a key row.
+//  * g workgroups (one per CU; launched cooperatively so all are resident)
+//    share a unit, each owning a slice of at most 512 (1024) keys and holding
+//    that slice's logits in registers. A workgroup streams unit u, publishes
+//    its slice's per-row (max, sum) and arrives at the unit's barrier. Unit u
+//    is finished only after units u+1 and u+2 have been streamed (three
+//    register banks rotate): by then everyone has passed its barrier, so the
+//    workgroup loads the g partials (before streaming u+2, hiding the
+//    latency), combines them into each row's log-sum-exp and turns the
+//    registers into log2 probabilities without touching K again. The K tiles
+//    and Q of the next unit are always in flight (a ring of tiles per wave).
+//  * The look-ahead keys M..M+N-1 only enter denominators; a small prep
+//    kernel computes their share of each row's statistics.
+//  * The max over the G heads of a step is a DPP max across G adjacent lanes;
+//    the max over kv-heads and layers is a running max in LDS, in the log2
+//    domain (exp2 is monotone, so one exponential per (step, key) at the end).
+//    Each group writes its running max; a small kernel takes the max over
+//    groups, exponentiates and averages over the steps.
 //  * Groups of g <= 32 workgroups sit on one XCD (blockIdx % 8 picks the XCD),
-//    so a barrier's atomics stay within one L2.
+//    so a barrier's traffic stays within one L2.
 #include <math.h>
+
+#include <type_traits>
 
 #include "sp_internal.h"
 
@@ -35,7 +43,6 @@ namespace sp {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 // 2 s of the 100 MHz constant clock: a barrier wait longer than this is a bug;
@@ -56,114 +63,6 @@ __device__ __forceinline__ i32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) 
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
 
-// ---------------------------------------------------------------------------------------
-// MFMA tile engines. A = K tile (TK keys x d), B = Q^T (d x ROWS query rows),
-// C[key][row]. Lane L supplies key/row L % TK and the contiguous d-range
-// [lg * D/LG, (lg+1) * D/LG) with lg = L / TK for both operands, so A's and B's
-// k-index maps to the same d.
-// ---------------------------------------------------------------------------------------
-template <int D_, bool BF16>
-struct Eng32 {  // 32 rows x 32 keys
-    static constexpr int D = D_, ROWS = 32, TK = 32, NACC = 16, LG = 2;
-    static constexpr int ESZ = BF16 ? 2 : 4;
-    static constexpr int DPL = D / LG;
-    static constexpr int NLD = DPL * ESZ / 16;
-    using Acc = f32x16;
-    struct Frag {
-        i32x4 v[NLD];
-    };
-    __device__ static int qrow(int lane) { return lane & 31; }
-    __device__ static int lgrp(int lane) { return lane >> 5; }
-    __device__ static int key_of(int lane, int r) {
-        return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-    }
-    __device__ static Acc mma(const Frag& q, const Frag& k) {
-        Acc c = {};
-        if constexpr (BF16) {
-#pragma unroll
-            for (int s = 0; s < NLD; ++s)
-                c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, k.v[s]),
-                                                            __builtin_bit_cast(bf16x8, q.v[s]),
-                                                            c, 0, 0, 0);
-        } else {
-#pragma unroll
-            for (int s = 0; s < NLD; ++s) {
-                const f32x4 kv = __builtin_bit_cast(f32x4, k.v[s]);
-                const f32x4 qv = __builtin_bit_cast(f32x4, q.v[s]);
-                c = __builtin_amdgcn_mfma_f32_32x32x2f32(kv.x, qv.x, c, 0, 0, 0);
-                c = __builtin_amdgcn_mfma_f32_32x32x2f32(kv.y, qv.y, c, 0, 0, 0);
-                c = __builtin_amdgcn_mfma_f32_32x32x2f32(kv.z, qv.z, c, 0, 0, 0);
-                c = __builtin_amdgcn_mfma_f32_32x32x2f32(kv.w, qv.w, c, 0, 0, 0);
-            }
-        }
-        return c;
-    }
-};
-
-template <int D_, bool BF16>
-struct Eng16 {  // 16 rows x 16 keys
-    static constexpr int D = D_, ROWS = 16, TK = 16, NACC = 4, LG = 4;
-    static constexpr int ESZ = BF16 ? 2 : 4;
-    static constexpr int DPL = D / LG;
-    static constexpr int NLD = DPL * ESZ / 16;
-    using Acc = f32x4;
-    struct Frag {
-        i32x4 v[NLD];
-    };
-    __device__ static int qrow(int lane) { return lane & 15; }
-    __device__ static int lgrp(int lane) { return lane >> 4; }
-    __device__ static int key_of(int lane, int r) { return 4 * (lane >> 4) + r; }
-    __device__ static Acc mma(const Frag& q, const Frag& k) {
-        Acc c = {};
-        if constexpr (BF16) {
-#pragma unroll
-            for (int s = 0; s < NLD; ++s)
-                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k.v[s]),
-                                                            __builtin_bit_cast(bf16x8, q.v[s]),
-                                                            c, 0, 0, 0);
-        } else {
-#pragma unroll
-            for (int s = 0; s < NLD; ++s) {
-                const f32x4 kv = __builtin_bit_cast(f32x4, k.v[s]);
-                const f32x4 qv = __builtin_bit_cast(f32x4, q.v[s]);
-                c = __builtin_amdgcn_mfma_f32_16x16x4f32(kv.x, qv.x, c, 0, 0, 0);
-                c = __builtin_amdgcn_mfma_f32_16x16x4f32(kv.y, qv.y, c, 0, 0, 0);
-                c = __builtin_amdgcn_mfma_f32_16x16x4f32(kv.z, qv.z, c, 0, 0, 0);
-                c = __builtin_amdgcn_mfma_f32_16x16x4f32(kv.w, qv.w, c, 0, 0, 0);
-            }
-        }
-        return c;
-    }
-};
-
-// K fragment of the tile whose first key is `key0` (zeros when !valid or past
-// the end of the plane: the buffer descriptor bounds the plane).
-template <class E>
-__device__ __forceinline__ void load_k(typename E::Frag& f, __amdgpu_buffer_rsrc_t rs, int key0,
-                                       bool valid, int lane) {
-    const uint32_t off =
-        valid ? (uint32_t)(key0 + (lane % E::TK)) * (uint32_t)(E::D * E::ESZ) +
-                    (uint32_t)(E::lgrp(lane) * E::DPL * E::ESZ)
-              : kOob;
-#pragma unroll
-    for (int s = 0; s < E::NLD; ++s) f.v[s] = load16(rs, off + 16u * s);
-}
-
-// Q fragment of query row (l, kvh*G + hl, j); zeros for padding rows.
-template <class E>
-__device__ __forceinline__ void load_q(typename E::Frag& f, const void* Q, int l, int kvh, int j,
-                                       int hl, bool valid, int H, int G, int N, int lane) {
-    if (valid) {
-        const long long row = ((long long)l * H + (long long)kvh * G + hl) * N + j;
-        const char* p = (const char*)Q + (row * E::D + E::lgrp(lane) * E::DPL) * E::ESZ;
-#pragma unroll
-        for (int s = 0; s < E::NLD; ++s) f.v[s] = *(const i32x4*)(p + 16 * s);
-    } else {
-#pragma unroll
-        for (int s = 0; s < E::NLD; ++s) f.v[s] = i32x4{0, 0, 0, 0};
-    }
-}
-
 // (m, s) <- combination of two partial softmax statistics (raw-logit max m,
 // sum of exp2((x - m) * c)).
 __device__ __forceinline__ void combine(float& m, float& s, float m2, float s2, float c) {
@@ -180,31 +79,116 @@ __device__ __forceinline__ float dpp(float v) {
                                                        false));
 }
 
-// Max over the G adjacent lanes that hold the G heads of one look-ahead step.
-__device__ __forceinline__ float group_max(float v, int G) {
-    if (G >= 2) v = fmaxf(v, dpp<0xb1>(v));   // quad_perm [1,0,3,2]
-    if (G >= 4) v = fmaxf(v, dpp<0x4e>(v));   // quad_perm [2,3,0,1]
-    if (G >= 8) v = fmaxf(v, dpp<0x141>(v));  // row_half_mirror
-    if (G >= 16) v = fmaxf(v, dpp<0x140>(v)); // row_mirror
-    if (G >= 32) v = fmaxf(v, __shfl_xor(v, 16));
+// Max over the G (<= 16) adjacent lanes that hold the G heads of one step.
+template <int G>
+__device__ __forceinline__ float group_max16(float v) {
+    if constexpr (G >= 2) v = fmaxf(v, dpp<0xb1>(v));   // quad_perm [1,0,3,2]
+    if constexpr (G >= 4) v = fmaxf(v, dpp<0x4e>(v));   // quad_perm [2,3,0,1]
+    if constexpr (G >= 8) v = fmaxf(v, dpp<0x141>(v));  // row_half_mirror
+    if constexpr (G >= 16) v = fmaxf(v, dpp<0x140>(v)); // row_mirror
     return v;
 }
 
-template <class E>
-__device__ __forceinline__ void lane_combine(float& m, float& s, float c) {
-    if constexpr (E::LG == 2) {
-        combine(m, s, __shfl_xor(m, 32), __shfl_xor(s, 32), c);
+template <int G, int K>
+__device__ __forceinline__ void group_max16_all(float (&v)[K]) {
+#pragma unroll
+    for (int i = 0; i < K; ++i) v[i] = group_max16<G>(v[i]);
+}
+
+// ---------------------------------------------------------------------------------------
+// 16-key tiles. A = K tile (16 keys x d), B = Q^T (d x 16 rows), C[key][row].
+// Lane L supplies key (and row) L % 16; its lane group g = L / 16 reads bytes
+// [64 s + 16 g, 64 s + 16 g + 16) of the row for load s, i.e. the 4 lane groups
+// of one load instruction read 64 contiguous bytes of each of 16 key rows. For
+// bf16 one load is one 32-deep MFMA k-step (d = 32 s + 8 g + e); for f32 it is
+// four 4-deep k-steps (d = 16 s + 4 g + e). Both operands use the same mapping.
+// C layout: lane L holds rows L % 16 of keys 4 (L / 16) + r, r = 0..3.
+// ---------------------------------------------------------------------------------------
+template <int D_, bool BF16_, int NH_>
+struct Cfg {
+    static constexpr int D = D_, NH = NH_;
+    static constexpr bool BF16 = BF16_;
+    static constexpr int ESZ = BF16 ? 2 : 4;
+    static constexpr int KB = D * ESZ;    // bytes per key row
+    static constexpr int NLD = KB / 64;   // 16-byte loads per lane per tile
+    static constexpr int TPW = tiles_per_wave(BF16, NH);
+    static constexpr int NBUF = TPW < (BF16 ? 4 : 3) ? TPW : (BF16 ? 4 : 3);  // tiles in flight per wave
+    static constexpr int ROWS = 16 * NH;
+};
+
+template <class C>
+struct Frag {
+    i32x4 v[C::NLD];
+};
+
+template <class C>
+__device__ __forceinline__ void mma(f32x4& acc, const i32x4& q, const i32x4& k) {
+    if constexpr (C::BF16) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k),
+                                                      __builtin_bit_cast(bf16x8, q), acc, 0, 0, 0);
     } else {
-        combine(m, s, __shfl_xor(m, 16), __shfl_xor(s, 16), c);
-        combine(m, s, __shfl_xor(m, 32), __shfl_xor(s, 32), c);
+        const f32x4 kv = __builtin_bit_cast(f32x4, k);
+        const f32x4 qv = __builtin_bit_cast(f32x4, q);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kv.x, qv.x, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kv.y, qv.y, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kv.z, qv.z, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kv.w, qv.w, acc, 0, 0, 0);
     }
 }
 
-template <class E, int TPW>
+// K fragment of the 16-key tile starting at key0 (zeros when !valid; the
+// buffer descriptor bounds the plane, so reads past its end are zeros too).
+template <class C>
+__device__ __forceinline__ void load_k(Frag<C>& f, __amdgpu_buffer_rsrc_t rs, int key0,
+                                       bool valid, int lane) {
+    const uint32_t off = valid ? (uint32_t)(key0 + (lane & 15)) * (uint32_t)C::KB +
+                                     (uint32_t)(16 * (lane >> 4))
+                               : kOob;
+#pragma unroll
+    for (int s = 0; s < C::NLD; ++s) f.v[s] = load16(rs, off + 64u * s);
+}
+
+// Per-unit geometry shared by the helpers below.
+struct Unit {
+    __amdgpu_buffer_rsrc_t rs;  // this unit's key plane
+    int u;                      // unit index, or -1 when the group has no such unit
+};
+
+__device__ __forceinline__ Unit unit_at(const ScoreArgs& a, int group, int it, uint32_t plane_bytes,
+                                        int esz) {
+    Unit x;
+    x.u = group + it * a.ngroups;
+    if (it >= (1 << 27) || x.u >= a.units) x.u = -1;
+    const int uu = x.u < 0 ? 0 : x.u;
+    const char* plane = (const char*)a.K + (long long)uu * a.plane_stride * esz;
+    x.rs = make_rsrc(plane, x.u < 0 ? 0u : plane_bytes);
+    return x;
+}
+
+// Q fragments of unit u (both row halves): row = half*16 + lane%16 = j*G + hl.
+template <class C>
+__device__ __forceinline__ void load_q(Frag<C> (&qf)[C::NH], const ScoreArgs& a, int u, int lane) {
+#pragma unroll
+    for (int hf = 0; hf < C::NH; ++hf) {
+        const int qr = hf * 16 + (lane & 15);
+        const int j = qr / a.G, hl = qr - (qr / a.G) * a.G;
+        if (u >= 0 && j < a.N) {
+            const int l = u / a.Hkv, kvh = u - (u / a.Hkv) * a.Hkv;
+            const long long row = ((long long)l * a.H + (long long)kvh * a.G + hl) * a.N + j;
+            const char* p = (const char*)a.Q + row * C::KB + 16 * (lane >> 4);
+#pragma unroll
+            for (int s = 0; s < C::NLD; ++s) qf[hf].v[s] = *(const i32x4*)(p + 64 * s);
+        } else {
+#pragma unroll
+            for (int s = 0; s < C::NLD; ++s) qf[hf].v[s] = i32x4{0, 0, 0, 0};
+        }
+    }
+}
+
+template <class C>
 __global__ __launch_bounds__(kThreads, 2) void score_kernel(ScoreArgs a) {
-    constexpr int ROWS = E::ROWS, TK = E::TK, NACC = E::NACC;
-    constexpr int NSUB = kThreads / ROWS;
-    extern __shared__ float Trun[];  // [N][KR + kRowPad], log2-domain running max
+    constexpr int TPW = C::TPW, NH = C::NH, NBUF = C::NBUF, ROWS = C::ROWS;
+    extern __shared__ float Trun[];  // [N][row_stride(KR)], log2-domain running max
     __shared__ float2 red[kWaves][ROWS];
     __shared__ float2 red2[kThreads];
     __shared__ float lse_s[ROWS];
@@ -219,132 +203,252 @@ __global__ __launch_bounds__(kThreads, 2) void score_kernel(ScoreArgs a) {
         group = blockIdx.x / a.g;
         rank = blockIdx.x % a.g;
     }
-    const int KRP = a.KR + kRowPad;
+    const int KRP = row_stride(a.KR);
     for (int x = tid; x < a.N * KRP; x += kThreads) Trun[x] = -INFINITY;
 
     const int r0 = rank * a.KR;
     const int r1 = min(r0 + a.KR, a.M);
     const int nkeys = max(r1 - r0, 0);
-    const int ntiles = (nkeys + TK - 1) / TK;
-    const bool tail_owner = (r0 < a.M) && (r1 == a.M);
-    const int qr = E::qrow(lane);
-    const int j = qr / a.G, hl = qr - (qr / a.G) * a.G;
-    const bool qvalid = j < a.N;
-    const uint32_t plane_bytes = (uint32_t)(a.M + a.N) * (uint32_t)(E::D * E::ESZ);
+    const int ntiles = (nkeys + kTileKeys - 1) / kTileKeys;
+    const uint32_t plane_bytes = (uint32_t)(a.M + a.N) * (uint32_t)C::KB;
     const float c = a.c;
+    const int g4 = lane >> 4;  // lane group
 
-    for (int it = 0;; ++it) {
-        const int u = group + it * a.ngroups;
-        if (u >= a.units) break;
-        const int l = u / a.Hkv, kvh = u - (u / a.Hkv) * a.Hkv;
+    // Per-lane query rows of the halves, and whether the lane writes the
+    // running max of its step (it holds the step's first head; for G = 32 both
+    // halves hold one step and half 0 writes).
+    int jrow[NH];
+    bool own[NH];
+#pragma unroll
+    for (int hf = 0; hf < NH; ++hf) {
+        const int qr = hf * 16 + (lane & 15);
+        jrow[hf] = qr / a.G;
+        own[hf] = (qr - jrow[hf] * a.G) == 0 && jrow[hf] < a.N && !(NH == 2 && a.G == 32 && hf == 1);
+    }
 
-        typename E::Frag qf;
-        load_q<E>(qf, a.Q, l, kvh, j, hl, qvalid, a.H, a.G, a.N, lane);
-        const char* plane =
-            (const char*)a.K + (long long)(l * a.Hkv + kvh) * a.plane_stride * E::ESZ;
-        const auto rs = make_rsrc(plane, plane_bytes);
+    f32x4 acc0[TPW][NH], acc1[TPW][NH], acc2[TPW][NH];
+    Frag<C> qf[NH];
+    Frag<C> fb[NBUF];
 
-        // logits of this workgroup's key slice, kept in registers
-        typename E::Acc acc[TPW];
+    // prime: Q and the first NBUF tiles of the first unit
+    {
+        const Unit first = unit_at(a, group, 0, plane_bytes, C::ESZ);
+        load_q<C>(qf, a, first.u, lane);
+#pragma unroll
+        for (int t = 0; t < NBUF; ++t) {
+            const int tile = w + kWaves * t;
+            load_k<C>(fb[t], first.rs, r0 + tile * kTileKeys, first.u >= 0 && tile < ntiles, lane);
+        }
+    }
+
+    // Stream unit `cur` into acc (the ring runs ahead into `nxt`), publish the
+    // slice's row statistics and arrive at the unit's barrier. The last of the
+    // g workgroups to arrive combines all partials (and the look-ahead keys'
+    // share) into the unit's log-sum-exp and raises the unit's flag.
+    auto stream = [&](f32x4 (&acc)[TPW][NH], const Unit& cur, const Unit& nxt) {
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
-            const int tile = w + t * kWaves;
-            typename E::Frag kf;
-            load_k<E>(kf, rs, r0 + tile * TK, tile < ntiles, lane);
-            acc[t] = E::mma(qf, kf);
-        }
-        float m = -INFINITY;
 #pragma unroll
-        for (int t = 0; t < TPW; ++t)
+            for (int hf = 0; hf < NH; ++hf) {
+                acc[t][hf] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int r = 0; r < NACC; ++r) {
-                const int key = r0 + (w + t * kWaves) * TK + E::key_of(lane, r);
-                if (key >= r1) acc[t][r] = -INFINITY;
-                m = fmaxf(m, acc[t][r]);
+                for (int s = 0; s < C::NLD; ++s) mma<C>(acc[t][hf], qf[hf].v[s], fb[t % NBUF].v[s]);
             }
-        float s = 0.f;
-        if (m != -INFINITY) {
-            const float mc = m * c;
-#pragma unroll
-            for (int t = 0; t < TPW; ++t)
-#pragma unroll
-                for (int r = 0; r < NACC; ++r) s += exp2_hw(fmaf(acc[t][r], c, -mc));
-        }
-        // look-ahead keys M..M+N-1: in the denominators of the rows that see them
-        if (tail_owner && w == kWaves - 1) {
-            typename E::Frag kf;
-            load_k<E>(kf, rs, a.M, true, lane);
-            typename E::Acc at = E::mma(qf, kf);
-            float mt = -INFINITY;
-#pragma unroll
-            for (int r = 0; r < NACC; ++r) {
-                const int tk = E::key_of(lane, r);
-                if (!(tk < a.N && tk <= j)) at[r] = -INFINITY;
-                mt = fmaxf(mt, at[r]);
-            }
-            if (mt != -INFINITY) {
-                float st = 0.f;
-#pragma unroll
-                for (int r = 0; r < NACC; ++r) st += exp2_hw(fmaf(at[r], c, -mt * c));
-                combine(m, s, mt, st, c);
+            const int tn = t + NBUF;  // refill the slot with the tile NBUF ahead
+            if (tn < TPW) {
+                const int tile = w + kWaves * tn;
+                load_k<C>(fb[t % NBUF], cur.rs, r0 + tile * kTileKeys, tile < ntiles, lane);
+            } else {
+                const int tile = w + kWaves * (tn - TPW);
+                load_k<C>(fb[t % NBUF], nxt.rs, r0 + tile * kTileKeys, nxt.u >= 0 && tile < ntiles,
+                          lane);
             }
         }
-        lane_combine<E>(m, s, c);
-        if (E::lgrp(lane) == 0) red[w][qr] = make_float2(m, s);
+        load_q<C>(qf, a, nxt.u, lane);  // the Q registers are free
+
+        float m[NH], sm[NH];
+#pragma unroll
+        for (int hf = 0; hf < NH; ++hf) {
+            m[hf] = -INFINITY;
+            sm[hf] = 0.f;
+        }
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            const int kt = (w + kWaves * t) * kTileKeys;  // first key of the tile in the slice
+            if (kt + kTileKeys > nkeys) {                 // partial or empty tile: mask
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+#pragma unroll
+                    for (int hf = 0; hf < NH; ++hf)
+                        if (kt + 4 * g4 + r >= nkeys) acc[t][hf][r] = -INFINITY;
+            }
+#pragma unroll
+            for (int hf = 0; hf < NH; ++hf)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) m[hf] = fmaxf(m[hf], acc[t][hf][r]);
+        }
+#pragma unroll
+        for (int hf = 0; hf < NH; ++hf) {
+            if (m[hf] != -INFINITY) {
+                const float mc = m[hf] * c;
+#pragma unroll
+                for (int t = 0; t < TPW; ++t)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) sm[hf] += exp2_hw(fmaf(acc[t][hf][r], c, -mc));
+            }
+            // lanes L, L^16, L^32, L^48 hold the same row
+            combine(m[hf], sm[hf], __shfl_xor(m[hf], 16), __shfl_xor(sm[hf], 16), c);
+            combine(m[hf], sm[hf], __shfl_xor(m[hf], 32), __shfl_xor(sm[hf], 32), c);
+            if (g4 == 0) red[w][hf * 16 + lane] = make_float2(m[hf], sm[hf]);
+        }
         __syncthreads();
         if (tid < ROWS) {
             float mm = red[0][tid].x, ss = red[0][tid].y;
             for (int x = 1; x < kWaves; ++x) combine(mm, ss, red[x][tid].x, red[x][tid].y, c);
-            a.part[((size_t)u * a.g + rank) * ROWS + tid] = make_float2(mm, ss);
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            a.part[((size_t)cur.u * a.g + rank) * ROWS + tid] = make_float2(mm, ss);
         }
         __syncthreads();
-        // per-unit barrier across the g workgroups of the group
+        if (tid == 0)
+            __hip_atomic_fetch_add(a.cnt + cur.u, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    };
+
+    // Partials of unit fu: wait for its barrier (passed by everyone a unit
+    // ago, normally), then load this thread's share of the g partials; they
+    // are combined after the next stream, which hides the loads' latency.
+    constexpr int NSUB = kThreads / ROWS;  // threads per row
+    constexpr int PF = 4;                   // partials a thread prefetches (g <= NSUB * PF)
+    auto part_fetch = [&](int fu, float2 (&pf)[PF]) {
         if (tid == 0) {
-            __hip_atomic_fetch_add(a.cnt + u, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
             const unsigned long long t0 = wall_clock64();
-            while (__hip_atomic_load(a.cnt + u, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < a.g) {
+            while (__hip_atomic_load(a.cnt + fu, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < a.g) {
                 __builtin_amdgcn_s_sleep(1);
                 if (wall_clock64() - t0 > kSpinTicks) {
                     __hip_atomic_store(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     break;
                 }
             }
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         }
         __syncthreads();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        {
-            const int row = tid % ROWS, sub = tid / ROWS;
-            float mm = -INFINITY, ss = 0.f;
-            for (int rr = sub; rr < a.g; rr += NSUB) {
-                float* src = (float*)(a.part + ((size_t)u * a.g + rr) * ROWS + row);
-                const float pm = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                const float ps =
-                    __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                combine(mm, ss, pm, ps, c);
-            }
-            red2[tid] = make_float2(mm, ss);
+        const int row = tid % ROWS, sub = tid / ROWS;
+#pragma unroll
+        for (int x = 0; x < PF; ++x) {
+            const int rr = sub + x * NSUB;
+            pf[x] = rr < a.g ? a.part[((size_t)fu * a.g + rr) * ROWS + row]
+                             : make_float2(-INFINITY, 0.f);
         }
+    };
+    // Row log-sum-exp of unit fu from the prefetched partials (plus, for
+    // g > NSUB * PF, the rest loaded now) and the look-ahead keys' share.
+    auto part_combine = [&](int fu, const float2 (&pf)[PF]) -> float {
+        const int row = tid % ROWS, sub = tid / ROWS;
+        float mm = -INFINITY, ss = 0.f;
+        if (sub == 0) {
+            const float2 ts = a.tail[(size_t)fu * ROWS + row];
+            mm = ts.x;
+            ss = ts.y;
+        }
+#pragma unroll
+        for (int x = 0; x < PF; ++x) combine(mm, ss, pf[x].x, pf[x].y, c);
+        for (int rr = sub + PF * NSUB; rr < a.g; rr += NSUB) {
+            const float2 p2 = a.part[((size_t)fu * a.g + rr) * ROWS + row];
+            combine(mm, ss, p2.x, p2.y, c);
+        }
+        red2[tid] = make_float2(mm, ss);
         __syncthreads();
+        float v = 0.f;
         if (tid < ROWS) {
-            float mm = red2[tid].x, ss = red2[tid].y;
+            mm = red2[tid].x;
+            ss = red2[tid].y;
             for (int x = 1; x < NSUB; ++x)
                 combine(mm, ss, red2[tid + x * ROWS].x, red2[tid + x * ROWS].y, c);
-            lse_s[tid] = mm * c + log2_hw(ss);
+            v = mm * c + log2_hw(ss);
         }
+        return v;
+    };
+
+    // Finish a unit: log2 probabilities, max over the G heads of each step,
+    // running max over units in LDS (read-modify-write in batches of tiles).
+    auto finish = [&](f32x4 (&acc)[TPW][NH], float lse_row) {
+        if (tid < ROWS) lse_s[tid] = lse_row;
         __syncthreads();
-        // log2 probabilities; max over the G heads of a step; running max over units
-        const float lse = lse_s[qr];
+        float lse[NH];
+#pragma unroll
+        for (int hf = 0; hf < NH; ++hf) lse[hf] = lse_s[hf * 16 + (lane & 15)];
+        const bool g32 = NH == 2 && a.G == 32;  // both halves hold the one step
+        constexpr int TB = 1;
+#pragma unroll
+        for (int t0 = 0; t0 < TPW; t0 += TB) {
+#pragma unroll
+            for (int hf = 0; hf < NH; ++hf) {
+                if (hf == 1 && g32) break;
+                float v[TB * 4];
+#pragma unroll
+                for (int tt = 0; tt < TB; ++tt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        v[tt * 4 + r] = fmaf(acc[t0 + tt][hf][r], c, -lse[hf]);
+                        if (g32)
+                            v[tt * 4 + r] =
+                                fmaxf(v[tt * 4 + r], fmaf(acc[t0 + tt][NH - 1][r], c, -lse[NH - 1]));
+                    }
+                switch (a.G) {
+                    case 1: break;
+                    case 2: group_max16_all<2>(v); break;
+                    case 4: group_max16_all<4>(v); break;
+                    case 8: group_max16_all<8>(v); break;
+                    default: group_max16_all<16>(v); break;
+                }
+                if (!own[hf]) continue;
+                float* row = Trun + jrow[hf] * KRP + 4 * g4;
+                const int kt0 = (w + kWaves * t0) * kTileKeys;
+                if (kt0 + kWaves * kTileKeys * (TB - 1) + kTileKeys <= nkeys) {  // full tiles
+                    float old[TB * 4];
+#pragma unroll
+                    for (int tt = 0; tt < TB; ++tt)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            old[tt * 4 + r] = row[kt0 + kWaves * kTileKeys * tt + r];
+#pragma unroll
+                    for (int tt = 0; tt < TB; ++tt)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            row[kt0 + kWaves * kTileKeys * tt + r] =
+                                fmaxf(old[tt * 4 + r], v[tt * 4 + r]);
+                } else {
+#pragma unroll
+                    for (int tt = 0; tt < TB; ++tt) {
+                        const int kt = kt0 + kWaves * kTileKeys * tt;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            if (kt + 4 * g4 + r < nkeys)
+                                row[kt + r] = fmaxf(row[kt + r], v[tt * 4 + r]);
+                    }
+                }
+            }
+        }
+    };
+
+    // Unit `it` streams into acc_cur and is finished two units later (from
+    // acc_fin), so its barrier has a whole unit of slack; after every step the
+    // banks rotate (cur -> mid -> fin).
+    f32x4 (&acc_cur)[TPW][NH] = acc0;
+    f32x4 (&acc_mid)[TPW][NH] = acc1;
+    f32x4 (&acc_fin)[TPW][NH] = acc2;
+    const int n_units = group < a.units ? (a.units - group + a.ngroups - 1) / a.ngroups : 0;
+    for (int it = 0; it < n_units + 2; ++it) {
+        const Unit cur = unit_at(a, group, it, plane_bytes, C::ESZ);
+        const int fu = it >= 2 ? unit_at(a, group, it - 2, plane_bytes, C::ESZ).u : -1;
+        float2 pf[PF];
+        if (fu >= 0) part_fetch(fu, pf);
+        if (cur.u >= 0) stream(acc_cur, cur, unit_at(a, group, it + 1, plane_bytes, C::ESZ));
+        if (fu >= 0) finish(acc_fin, part_combine(fu, pf));
 #pragma unroll
         for (int t = 0; t < TPW; ++t)
 #pragma unroll
-            for (int r = 0; r < NACC; ++r) {
-                const float v = group_max(fmaf(acc[t][r], c, -lse), a.G);
-                const int lk = (w + t * kWaves) * TK + E::key_of(lane, r);
-                if (hl == 0 && qvalid && lk < nkeys) {
-                    float* p = &Trun[j * KRP + lk];
-                    *p = fmaxf(*p, v);
-                }
+            for (int hf = 0; hf < NH; ++hf) {
+                acc_fin[t][hf] = acc_mid[t][hf];
+                acc_mid[t][hf] = acc_cur[t][hf];
             }
     }
     __syncthreads();
@@ -354,10 +458,47 @@ __global__ __launch_bounds__(kThreads, 2) void score_kernel(ScoreArgs a) {
     }
 }
 
-__global__ void score_prep_kernel(int* cnt, int units, int* err) {
-    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < units; i += gridDim.x * blockDim.x)
-        cnt[i] = 0;
-    if (blockIdx.x == 0 && threadIdx.x == 0) *err = 0;
+// Before the cooperative kernel: zero its barrier counters, and compute for
+// every unit and query row the share of the look-ahead keys M..M+N-1 in the
+// row's softmax denominator (row j sees look-ahead key t iff t <= j), as a raw
+// max and a sum of exp2((x - max) * c). One wave per unit, one lane per row.
+template <bool BF16>
+__global__ __launch_bounds__(64) void score_prep_kernel(ScoreArgs a, int rows) {
+    const int u = blockIdx.x, lane = threadIdx.x;
+    if (lane == 0) {
+        a.cnt[u] = 0;
+        a.flag[u] = 0;
+    }
+    if (u == 0 && lane == 0) *a.err = 0;
+    if (lane >= rows) return;
+    const int j = lane / a.G, hl = lane - (lane / a.G) * a.G;
+    float m = -INFINITY, s = 0.f;
+    if (j < a.N) {
+        const int l = u / a.Hkv, kvh = u - (u / a.Hkv) * a.Hkv;
+        const int esz = BF16 ? 2 : 4;
+        const long long qrow = ((long long)l * a.H + (long long)kvh * a.G + hl) * a.N + j;
+        const char* q = (const char*)a.Q + qrow * a.d * esz;
+        const char* kp = (const char*)a.K + ((long long)u * a.plane_stride + (long long)a.M * a.d) * esz;
+        float x[32];
+        for (int t = 0; t <= j; ++t) {
+            float acc = 0.f;
+            for (int e = 0; e < a.d; ++e) {
+                float qv, kv;
+                if (BF16) {
+                    qv = __uint_as_float((unsigned)((const unsigned short*)q)[e] << 16);
+                    kv = __uint_as_float((unsigned)((const unsigned short*)kp)[(long long)t * a.d + e] << 16);
+                } else {
+                    qv = ((const float*)q)[e];
+                    kv = ((const float*)kp)[(long long)t * a.d + e];
+                }
+                acc = fmaf(qv, kv, acc);
+            }
+            x[t] = acc;
+            m = fmaxf(m, acc);
+        }
+        for (int t = 0; t <= j; ++t) s += exp2_hw(fmaf(x[t], a.c, -m * a.c));
+    }
+    a.tail[(size_t)u * rows + lane] = make_float2(m, s);
 }
 
 // importance_i = (1/N) sum_j exp2(max_group Tg[group][j][i])
@@ -377,25 +518,19 @@ __global__ void score_finalize_kernel(const float* __restrict__ Tg, int ngroups,
 // ---------------------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------------------
-typedef void (*KernelFn)(ScoreArgs);
-
-template <class E, int TPW>
+template <class C>
 static const void* kernel_ptr() {
-    return (const void*)&score_kernel<E, TPW>;
+    return (const void*)&score_kernel<C>;
 }
 
 static const void* pick_kernel(int dtype, int d, int rows) {
     const bool bf = dtype == SP_BF16;
     if (rows == 32) {
-        if (d == 128) return bf ? kernel_ptr<Eng32<128, true>, kTilesPerWave32>()
-                                : kernel_ptr<Eng32<128, false>, kTilesPerWave32>();
-        if (d == 64) return bf ? kernel_ptr<Eng32<64, true>, kTilesPerWave32>()
-                               : kernel_ptr<Eng32<64, false>, kTilesPerWave32>();
+        if (d == 128) return bf ? kernel_ptr<Cfg<128, true, 2>>() : kernel_ptr<Cfg<128, false, 2>>();
+        if (d == 64) return bf ? kernel_ptr<Cfg<64, true, 2>>() : kernel_ptr<Cfg<64, false, 2>>();
     } else {
-        if (d == 128) return bf ? kernel_ptr<Eng16<128, true>, kTilesPerWave16>()
-                                : kernel_ptr<Eng16<128, false>, kTilesPerWave16>();
-        if (d == 64) return bf ? kernel_ptr<Eng16<64, true>, kTilesPerWave16>()
-                               : kernel_ptr<Eng16<64, false>, kTilesPerWave16>();
+        if (d == 128) return bf ? kernel_ptr<Cfg<128, true, 1>>() : kernel_ptr<Cfg<128, false, 1>>();
+        if (d == 64) return bf ? kernel_ptr<Cfg<64, true, 1>>() : kernel_ptr<Cfg<64, false, 1>>();
     }
     return nullptr;
 }
@@ -412,6 +547,10 @@ hipError_t launch_score(const ScorePlan& p, const sp_score_desc& d, const void* 
     a.cnt = (int*)(base + p.ws_cnt);
     a.err = (int*)(base + p.ws_cnt + 4 * (size_t)p.units);
     a.part = (float2*)(base + p.ws_part);
+    a.tail = (float2*)(base + p.ws_tail);
+    a.lse = (float*)(base + p.ws_lse);
+    a.flag = (int*)(base + p.ws_flag);
+    a.d = d.d;
     a.Tg = (float*)(base + p.ws_tg);
     a.L = d.L;
     a.H = d.H;
@@ -430,14 +569,16 @@ hipError_t launch_score(const ScorePlan& p, const sp_score_desc& d, const void* 
     const void* fn = pick_kernel(d.dtype, d.d, p.rows);
     if (!fn) return hipErrorInvalidValue;
     // Dynamic LDS: the running max, padded so that two workgroups never share a CU.
-    size_t lds = (size_t)d.N * (p.KR + kRowPad) * sizeof(float);
+    size_t lds = (size_t)d.N * row_stride(p.KR) * sizeof(float);
     const size_t min_lds = 96 * 1024;
     if (lds < min_lds) lds = min_lds;
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
 
-    hipLaunchKernelGGL(score_prep_kernel, dim3((p.units + 255) / 256), dim3(256), 0, stream,
-                       a.cnt, p.units, a.err);
+    if (d.dtype == SP_BF16)
+        hipLaunchKernelGGL(score_prep_kernel<true>, dim3(p.units), dim3(64), 0, stream, a, p.rows);
+    else
+        hipLaunchKernelGGL(score_prep_kernel<false>, dim3(p.units), dim3(64), 0, stream, a, p.rows);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     void* args[] = {&a};

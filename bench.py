@@ -1,0 +1,223 @@
+"""Benchmark of the hot path: token scoring (sp_score) + chunk selection
+(sp_select) on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+               [--copy-probe-mib MIB]
+
+A step scores one prompt of the workload (inputs already resident in HBM) and
+selects its tokens. W untimed steps, then exactly K timed steps between device
+synchronisations; prints one JSON line. Throughput = prompt tokens per second.
+Several copies of K are rotated so that no step finds its keys in the 256 MB
+Infinity Cache left over from the previous one.
+
+The roofline block reports the scoring kernel's algorithmic bytes (one read
+of K and Q) over its average duration, measured with HIP events around every
+sp_score call on the stream the kernels run on. HBM traffic comes from the
+rocprofv3 counter summary under profiles/ when it was taken on the current
+kernel source (else null). The CPU baseline times the oracle on the host
+cores on a bounded sample (a subset of layers, scaled to the full workload).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+METRIC = "prompt tokens scored/s (sp_score+select) at 8B shape M=32K; % HBM roofline"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_kernel_traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="spec8b_m32k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-layers", type=int, default=8,
+                    help="layers of the workload the CPU baseline scores")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run one device copy of this size (counter calibration)")
+    return ap.parse_args()
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for name in ("sp_score.hip", "sp_internal.h"):
+        with open(os.path.join(ROOT, "attention_token_scoring_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str):
+    """Counter-measured HBM bytes per launch of the scoring kernel, if the
+    summary matches the current kernel source and workload."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha") != kernel_source_sha() or t.get("workload") != workload:
+        return None
+    return t.get("bytes_per_launch")
+
+
+def workload_desc(w, sel) -> dict:
+    d = {"workload": f"{w.name}: L={w.L} H={w.H} Hkv={w.Hkv} d={w.d} M={w.M} N={w.N} "
+                     f"{'bf16' if w.dtype else 'f32'}; select {sel.mode} "
+                     f"{sel.keep_rate if sel.mode == 'topk' else sel.mass} chunk {sel.chunk} "
+                     f"pool {sel.pool_k}",
+         "L": w.L, "H": w.H, "Hkv": w.Hkv, "d": w.d, "M": w.M, "N": w.N,
+         "select": sel.mode, "chunk": sel.chunk, "pool_k": sel.pool_k}
+    if sel.mode == "topk":
+        d["keep_rate"] = sel.keep_rate
+    else:
+        d["mass"] = sel.mass
+    if sel.boost_first_n or sel.boost_last_n:
+        d["boosts"] = [sel.boost_first_n, sel.boost_first_mult, sel.boost_last_n,
+                       sel.boost_last_mult]
+    return d
+
+
+def cpu_baseline(w, sel, Qh, Kh, layers: int):
+    """The oracle as it is, on the host cores: score the first `layers` layers
+    of the workload and select on the result; scale the scoring time to all L
+    layers (its cost is linear in L)."""
+    import oracle
+    threads = os.cpu_count() or 1
+    layers = max(1, min(layers, w.L))
+    t0 = time.perf_counter()
+    imp = oracle.score(Qh[:layers], Kh[:layers], nthreads=threads)
+    t1 = time.perf_counter()
+    oracle.select(imp.astype(np.float32), **oracle.select_params(sel))
+    t2 = time.perf_counter()
+    t_full = (t1 - t0) * (w.L / layers) + (t2 - t1)
+    return {"value": w.M / t_full, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{w.name}: oracle scoring of layers 0-{layers - 1} of {w.L} "
+                      f"({(t1 - t0):.2f} s, scaled x{w.L / layers:g} to all layers) plus "
+                      f"selection ({(t2 - t1) * 1e3:.1f} ms); fp64, OpenMP over "
+                      f"{threads} threads"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only; --gpus must be 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import attention_token_scoring_amd as sp
+    import synth
+
+    w = synth.WORKLOADS[args.workload]
+    if w.R != 1:
+        raise SystemExit("bench.py times single-prompt workloads")
+    sel = w.selects[0]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    Qh, Kh, M = synth.make_request(w)
+    k_bytes = Kh.nbytes
+    copies = max(2, math.ceil(512e6 / k_bytes) + 1)
+
+    def to_dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    Q = to_dev(Qh)
+    K0 = to_dev(Kh)
+    Ks = [K0] + [K0.clone() for _ in range(copies - 1)]
+    desc = sp.score_desc(w.L, w.H, w.Hkv, w.d, w.N, sp.SP_BF16 if w.dtype else sp.SP_F32)
+    ws = torch.empty(sp.sp_score_workspace_bytes(desc, M), dtype=torch.uint8, device=dev)
+    imp = torch.empty(M, dtype=torch.float32, device=dev)
+    kept = torch.empty(M, dtype=torch.int32, device=dev)
+    pos = torch.empty(M, dtype=torch.int32, device=dev)
+    nk = torch.empty(1, dtype=torch.int32, device=dev)
+    params = sp.select_params(chunk=sel.chunk, pool_k=sel.pool_k, mode=sel.mode,
+                              keep_rate=sel.keep_rate, mass=sel.mass,
+                              boost_first_n=sel.boost_first_n,
+                              boost_first_mult=sel.boost_first_mult,
+                              boost_last_n=sel.boost_last_n, boost_last_mult=sel.boost_last_mult)
+    plan = sp.sp_score_plan(desc, M)
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty(n, dtype=torch.uint8, device=dev)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    def step(i, ev=None):
+        if ev is not None:
+            ev[0].record()
+        sp.sp_score(Q, Ks[i % copies], M, out=imp, workspace=ws)
+        if ev is not None:
+            ev[1].record()
+        sp.sp_select(imp, params, kept_idx=kept, pos_ids=pos, n_kept=nk)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t_begin = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    t_begin.record()
+    for i in range(args.steps):
+        step(i, evs[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    w1 = time.perf_counter()
+
+    ms_total_ev = t_begin.elapsed_time(t_end)
+    ms_wall = (w1 - w0) * 1e3
+    ms_per_step = ms_wall / args.steps
+    score_ms = [a.elapsed_time(b) for a, b in evs]
+    score_avg_s = float(np.mean(score_ms)) / 1e3
+    alg_bytes = (w.L * w.Hkv * (M + w.N) * w.d + w.L * w.H * w.N * w.d) * (2 if w.dtype else 4)
+    achieved = alg_bytes / score_avg_s / 1e9
+    traffic = load_traffic(w.name)
+
+    out = {
+        "metric": METRIC,
+        "value": M / (ms_per_step / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype else "f32",
+        "data": "synthetic",
+        "config": workload_desc(w, sel),
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic},
+        "detail": {"score_ms_avg": score_avg_s * 1e3, "score_ms_min": float(np.min(score_ms)),
+                   "select_and_gaps_ms_avg": ms_total_ev / args.steps - score_avg_s * 1e3,
+                   "ms_per_step_events": ms_total_ev / args.steps,
+                   "alg_bytes_per_score_launch": alg_bytes, "k_copies": copies,
+                   "plan": plan, "n_kept": int(nk.cpu()[0])},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, sel, Qh, Kh, args.cpu_layers)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
