@@ -68,7 +68,7 @@ sp_status make_plan(const sp_score_desc& d, long long M, int cus, ScorePlan* out
     const int G = d.H / d.Hkv;
     p.rows = G * d.N <= 16 ? 16 : 32;
     const int tk = p.rows;
-    p.cap = kWaves * tiles_per_wave(d.dtype == SP_BF16, p.rows / 16) * kTileKeys;
+    p.cap = kStreamWaves * tiles_per_wave(d.dtype == SP_BF16, p.rows / 16) * kTileKeys;
     p.units = d.L * d.Hkv;
     if (M < 1) return SP_EINVAL;
     if ((unsigned long long)(M + d.N) * d.d * esize(d.dtype) >= (1ull << 31)) return SP_EUNSUPPORTED;
@@ -124,7 +124,7 @@ size_t workspace_bound(const sp_score_desc& d, long long max_M, int cus) {
     if (cus < 1) cus = kDefaultCUs;
     const int G = d.H / d.Hkv;
     const int rows = G * d.N <= 16 ? 16 : 32;
-    const long long cap = (long long)kWaves * tiles_per_wave(d.dtype == SP_BF16, rows / 16) * kTileKeys;
+    const long long cap = (long long)kStreamWaves * tiles_per_wave(d.dtype == SP_BF16, rows / 16) * kTileKeys;
     const long long units = (long long)d.L * d.Hkv;
     long long tg_elems = (long long)(units < cus ? units : cus) * max_M;
     if (tg_elems > (long long)cus * cap) tg_elems = (long long)cus * cap;

@@ -8,14 +8,16 @@
 
 namespace sp {
 
-// Scoring workgroups have 8 waves (two per SIMD, 256 registers each). Keys
-// are processed in tiles of 16 (the M dimension of the 16x16 MFMAs); query
-// rows in 16-row halves (NH = 1 or 2 halves per kv-head). Each wave keeps the
-// logits of three units in registers (a unit is finished two units after it
-// is streamed): 3 * tiles_per_wave * NH * 4 registers.
+// Scoring workgroups have 8 waves (two per SIMD, 256 registers each): 7 stream
+// K, one synchronises. Keys are processed in tiles of 16 (the M dimension of
+// the 16x16 MFMAs); query rows in 16-row halves (NH = 1 or 2 halves per
+// kv-head). Each streaming wave keeps the logits of kBanks units in registers
+// (a unit is finished kBanks-1 units after it is streamed).
 constexpr int kWaves = 8;
+constexpr int kStreamWaves = 7;
 constexpr int kThreads = kWaves * 64;
 constexpr int kTileKeys = 16;
+constexpr int kBanks = 3;
 constexpr int tiles_per_wave(bool bf16, int nh) { return (bf16 ? 4 : 2) * (nh == 1 ? 2 : 1); }
 // Extra floats per look-ahead row of the LDS running maximum: rows start 16
 // banks apart.

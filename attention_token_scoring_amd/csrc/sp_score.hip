@@ -15,15 +15,17 @@
 //    one query row for 4 keys of a tile, so row statistics are lane-local, and
 //    each load instruction reads 64 contiguous bytes of a key row.
 //  * g workgroups (one per CU; launched cooperatively so all are resident)
-//    share a unit, each owning a slice of at most 512 (1024) keys and holding
-//    that slice's logits in registers. A workgroup streams unit u, publishes
-//    its slice's per-row (max, sum) and arrives at the unit's barrier. Unit u
-//    is finished only after units u+1 and u+2 have been streamed (three
-//    register banks rotate): by then everyone has passed its barrier, so the
-//    workgroup loads the g partials (before streaming u+2, hiding the
-//    latency), combines them into each row's log-sum-exp and turns the
-//    registers into log2 probabilities without touching K again. The K tiles
-//    and Q of the next unit are always in flight (a ring of tiles per wave).
+//    share a unit, each owning a key slice whose logits stay in registers.
+//    Seven waves stream K; the eighth does all synchronisation, because on
+//    gfx950 a wave's vector-memory counter is in order: a barrier poll or a
+//    release issued by a streaming wave would wait for all of that wave's
+//    prefetches. Per unit the control wave publishes the workgroup's per-row
+//    (max, sum) partial and arrives at the unit's counter; the last of the g
+//    workgroups to arrive combines the partials into each row's log-sum-exp
+//    and raises the unit's flag. A unit is finished (log2 probabilities,
+//    without touching K again) a unit or two after it is streamed, so the
+//    flag is normally up by then; register banks rotate. A ring of K tiles
+//    per streaming wave keeps the next unit in flight.
 //  * The look-ahead keys M..M+N-1 only enter denominators; a small prep
 //    kernel computes their share of each row's statistics.
 //  * The max over the G heads of a step is a DPP max across G adjacent lanes;
@@ -112,7 +114,11 @@ struct Cfg {
     static constexpr int KB = D * ESZ;    // bytes per key row
     static constexpr int NLD = KB / 64;   // 16-byte loads per lane per tile
     static constexpr int TPW = tiles_per_wave(BF16, NH);
-    static constexpr int NBUF = TPW < (BF16 ? 4 : 3) ? TPW : (BF16 ? 4 : 3);  // tiles in flight per wave
+    // tiles in flight per wave; must divide TPW so that tile t of every unit
+    // lands in ring slot t % NBUF
+    static constexpr int NBUF = TPW <= 4 ? TPW : 4;
+    static constexpr int NB = kBanks;
+    static_assert(TPW % NBUF == 0, "ring depth must divide the tiles per wave");
     static constexpr int ROWS = 16 * NH;
 };
 
@@ -187,13 +193,15 @@ __device__ __forceinline__ void load_q(Frag<C> (&qf)[C::NH], const ScoreArgs& a,
 
 template <class C>
 __global__ __launch_bounds__(kThreads, 2) void score_kernel(ScoreArgs a) {
-    constexpr int TPW = C::TPW, NH = C::NH, NBUF = C::NBUF, ROWS = C::ROWS;
-    extern __shared__ float Trun[];  // [N][row_stride(KR)], log2-domain running max
-    __shared__ float2 red[kWaves][ROWS];
-    __shared__ float2 red2[kThreads];
-    __shared__ float lse_s[ROWS];
+    constexpr int TPW = C::TPW, NH = C::NH, NBUF = C::NBUF, ROWS = C::ROWS, NB = C::NB;
+    constexpr int SW = kStreamWaves;  // waves 0..SW-1 stream K; wave SW synchronises
+    constexpr int D = NB - 1;         // a unit is finished D units after it is streamed
+    extern __shared__ float Trun[];   // [N][row_stride(KR)], log2-domain running max
+    __shared__ float2 red[2][SW][ROWS];
+    __shared__ float lse_s[2][ROWS];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const bool ctrl = w == SW;
     int group, rank;
     if (a.xcd_local) {
         const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
@@ -230,22 +238,21 @@ __global__ __launch_bounds__(kThreads, 2) void score_kernel(ScoreArgs a) {
     Frag<C> qf[NH];
     Frag<C> fb[NBUF];
 
-    // prime: Q and the first NBUF tiles of the first unit
-    {
+    const int n_units = group < a.units ? (a.units - group + a.ngroups - 1) / a.ngroups : 0;
+    // prime the streaming waves: Q and the first NBUF tiles of the first unit
+    if (!ctrl) {
         const Unit first = unit_at(a, group, 0, plane_bytes, C::ESZ);
         load_q<C>(qf, a, first.u, lane);
 #pragma unroll
         for (int t = 0; t < NBUF; ++t) {
-            const int tile = w + kWaves * t;
+            const int tile = w + SW * t;
             load_k<C>(fb[t], first.rs, r0 + tile * kTileKeys, first.u >= 0 && tile < ntiles, lane);
         }
     }
 
-    // Stream unit `cur` into acc (the ring runs ahead into `nxt`), publish the
-    // slice's row statistics and arrive at the unit's barrier. The last of the
-    // g workgroups to arrive combines all partials (and the look-ahead keys'
-    // share) into the unit's log-sum-exp and raises the unit's flag.
-    auto stream = [&](f32x4 (&acc)[TPW][NH], const Unit& cur, const Unit& nxt) {
+    // [streaming waves] Stream unit `cur` into acc (the ring runs ahead into
+    // `nxt`) and leave the slice's per-row statistics in red[pb].
+    auto stream = [&](f32x4 (&acc)[TPW][NH], const Unit& cur, const Unit& nxt, int pb) {
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
 #pragma unroll
@@ -256,10 +263,10 @@ __global__ __launch_bounds__(kThreads, 2) void score_kernel(ScoreArgs a) {
             }
             const int tn = t + NBUF;  // refill the slot with the tile NBUF ahead
             if (tn < TPW) {
-                const int tile = w + kWaves * tn;
+                const int tile = w + SW * tn;
                 load_k<C>(fb[t % NBUF], cur.rs, r0 + tile * kTileKeys, tile < ntiles, lane);
             } else {
-                const int tile = w + kWaves * (tn - TPW);
+                const int tile = w + SW * (tn - TPW);
                 load_k<C>(fb[t % NBUF], nxt.rs, r0 + tile * kTileKeys, nxt.u >= 0 && tile < ntiles,
                           lane);
             }
@@ -274,8 +281,8 @@ __global__ __launch_bounds__(kThreads, 2) void score_kernel(ScoreArgs a) {
         }
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
-            const int kt = (w + kWaves * t) * kTileKeys;  // first key of the tile in the slice
-            if (kt + kTileKeys > nkeys) {                 // partial or empty tile: mask
+            const int kt = (w + SW * t) * kTileKeys;  // first key of the tile in the slice
+            if (kt + kTileKeys > nkeys) {             // partial or empty tile: mask
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
 #pragma unroll
@@ -299,99 +306,117 @@ __global__ __launch_bounds__(kThreads, 2) void score_kernel(ScoreArgs a) {
             // lanes L, L^16, L^32, L^48 hold the same row
             combine(m[hf], sm[hf], __shfl_xor(m[hf], 16), __shfl_xor(sm[hf], 16), c);
             combine(m[hf], sm[hf], __shfl_xor(m[hf], 32), __shfl_xor(sm[hf], 32), c);
-            if (g4 == 0) red[w][hf * 16 + lane] = make_float2(m[hf], sm[hf]);
+            if (g4 == 0) red[pb][w][hf * 16 + lane] = make_float2(m[hf], sm[hf]);
         }
-        __syncthreads();
-        if (tid < ROWS) {
-            float mm = red[0][tid].x, ss = red[0][tid].y;
-            for (int x = 1; x < kWaves; ++x) combine(mm, ss, red[x][tid].x, red[x][tid].y, c);
-            a.part[((size_t)cur.u * a.g + rank) * ROWS + tid] = make_float2(mm, ss);
-        }
-        __syncthreads();
-        if (tid == 0)
-            __hip_atomic_fetch_add(a.cnt + cur.u, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     };
 
-    // Partials of unit fu: wait for its barrier (passed by everyone a unit
-    // ago, normally), then load this thread's share of the g partials; they
-    // are combined after the next stream, which hides the loads' latency.
-    constexpr int NSUB = kThreads / ROWS;  // threads per row
-    constexpr int PF = 4;                   // partials a thread prefetches (g <= NSUB * PF)
-    auto part_fetch = [&](int fu, float2 (&pf)[PF]) {
-        if (tid == 0) {
+    // Cross-workgroup data (partials, counters, log-sum-exps, flags) moves
+    // through agent-scope atomic loads and stores, which are coherent across
+    // the XCDs' L2s; a producer waits for its stores to complete (vmcnt(0), this
+    // wave's own operations only) before it signals, and a consumer issues its
+    // loads only after it has seen the signal.
+    auto st64 = [](void* p, float x, float y) {
+        const unsigned long long bits =
+            (unsigned long long)__float_as_uint(x) | ((unsigned long long)__float_as_uint(y) << 32);
+        __hip_atomic_store((unsigned long long*)p, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    auto ld64 = [](const void* p) -> float2 {
+        const unsigned long long bits = __hip_atomic_load((unsigned long long*)p, __ATOMIC_RELAXED,
+                                                          __HIP_MEMORY_SCOPE_AGENT);
+        return make_float2(__uint_as_float((unsigned)bits), __uint_as_float((unsigned)(bits >> 32)));
+    };
+
+    // [control wave] Publish the workgroup's partial of unit u and arrive at
+    // the unit's counter. The last of the g workgroups to arrive combines all
+    // partials and the look-ahead keys' share into each row's log-sum-exp and
+    // raises the unit's flag. Lane L handles row pair q = L % 16 (rows 2q,
+    // 2q+1) for ranks L / 16, L / 16 + 4, ...
+    auto arrive = [&](int u, int pb) {
+        if (lane < ROWS) {
+            float mm = red[pb][0][lane].x, ss = red[pb][0][lane].y;
+            for (int x = 1; x < SW; ++x) combine(mm, ss, red[pb][x][lane].x, red[pb][x][lane].y, c);
+            st64(a.part + ((size_t)u * a.g + rank) * ROWS + lane, mm, ss);
+        }
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the partial is stored
+        int old = 0;
+        if (lane == 0)
+            old = __hip_atomic_fetch_add(a.cnt + u, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        old = __shfl(old, 0);
+        if (old != a.g - 1) return;
+        const int q = lane & 15, sub = lane >> 4;
+        const bool live = 2 * q < ROWS;
+        float m0 = -INFINITY, s0 = 0.f, m1 = -INFINITY, s1 = 0.f;
+        if (sub == 0 && live) {
+            const float4 t = *(const float4*)(a.tail + (size_t)u * ROWS + 2 * q);
+            m0 = t.x; s0 = t.y; m1 = t.z; s1 = t.w;
+        }
+        constexpr int B = 24;  // ranks in flight per lane
+        for (int rr0 = sub; rr0 < a.g; rr0 += 4 * B) {
+            float2 p0[B], p1[B];
+#pragma unroll
+            for (int x = 0; x < B; ++x) {
+                const int rr = rr0 + 4 * x;
+                if (live && rr < a.g) {
+                    const float2* base = a.part + ((size_t)u * a.g + rr) * ROWS + 2 * q;
+                    p0[x] = ld64(base);
+                    p1[x] = ld64(base + 1);
+                } else {
+                    p0[x] = p1[x] = make_float2(-INFINITY, 0.f);
+                }
+            }
+#pragma unroll
+            for (int x = 0; x < B; ++x) {
+                combine(m0, s0, p0[x].x, p0[x].y, c);
+                combine(m1, s1, p1[x].x, p1[x].y, c);
+            }
+        }
+        combine(m0, s0, __shfl_xor(m0, 16), __shfl_xor(s0, 16), c);
+        combine(m1, s1, __shfl_xor(m1, 16), __shfl_xor(s1, 16), c);
+        combine(m0, s0, __shfl_xor(m0, 32), __shfl_xor(s0, 32), c);
+        combine(m1, s1, __shfl_xor(m1, 32), __shfl_xor(s1, 32), c);
+        if (sub == 0 && live)
+            st64(a.lse + (size_t)u * ROWS + 2 * q, m0 * c + log2_hw(s0), m1 * c + log2_hw(s1));
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the log-sum-exps are stored
+        if (lane == 0) __hip_atomic_store(a.flag + u, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+
+    // [control wave] Wait for unit fu's flag, then put its log-sum-exps in
+    // lse_s[pb].
+    auto fetch_lse = [&](int fu, int pb) {
+        if (lane == 0) {
             const unsigned long long t0 = wall_clock64();
-            while (__hip_atomic_load(a.cnt + fu, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < a.g) {
+            while (__hip_atomic_load(a.flag + fu, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
                 __builtin_amdgcn_s_sleep(1);
                 if (wall_clock64() - t0 > kSpinTicks) {
                     __hip_atomic_store(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     break;
                 }
             }
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         }
-        __syncthreads();
-        const int row = tid % ROWS, sub = tid / ROWS;
-#pragma unroll
-        for (int x = 0; x < PF; ++x) {
-            const int rr = sub + x * NSUB;
-            pf[x] = rr < a.g ? a.part[((size_t)fu * a.g + rr) * ROWS + row]
-                             : make_float2(-INFINITY, 0.f);
-        }
-    };
-    // Row log-sum-exp of unit fu from the prefetched partials (plus, for
-    // g > NSUB * PF, the rest loaded now) and the look-ahead keys' share.
-    auto part_combine = [&](int fu, const float2 (&pf)[PF]) -> float {
-        const int row = tid % ROWS, sub = tid / ROWS;
-        float mm = -INFINITY, ss = 0.f;
-        if (sub == 0) {
-            const float2 ts = a.tail[(size_t)fu * ROWS + row];
-            mm = ts.x;
-            ss = ts.y;
-        }
-#pragma unroll
-        for (int x = 0; x < PF; ++x) combine(mm, ss, pf[x].x, pf[x].y, c);
-        for (int rr = sub + PF * NSUB; rr < a.g; rr += NSUB) {
-            const float2 p2 = a.part[((size_t)fu * a.g + rr) * ROWS + row];
-            combine(mm, ss, p2.x, p2.y, c);
-        }
-        red2[tid] = make_float2(mm, ss);
-        __syncthreads();
-        float v = 0.f;
-        if (tid < ROWS) {
-            mm = red2[tid].x;
-            ss = red2[tid].y;
-            for (int x = 1; x < NSUB; ++x)
-                combine(mm, ss, red2[tid + x * ROWS].x, red2[tid + x * ROWS].y, c);
-            v = mm * c + log2_hw(ss);
-        }
-        return v;
+        __builtin_amdgcn_wave_barrier();
+        if (lane < ROWS)
+            lse_s[pb][lane] = __hip_atomic_load(a.lse + (size_t)fu * ROWS + lane, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
     };
 
-    // Finish a unit: log2 probabilities, max over the G heads of each step,
-    // running max over units in LDS (read-modify-write in batches of tiles).
-    auto finish = [&](f32x4 (&acc)[TPW][NH], float lse_row) {
-        if (tid < ROWS) lse_s[tid] = lse_row;
-        __syncthreads();
+    // [streaming waves] Finish a unit: log2 probabilities, max over the G
+    // heads of each step, running max over units in LDS.
+    auto finish = [&](f32x4 (&acc)[TPW][NH], int pb) {
         float lse[NH];
 #pragma unroll
-        for (int hf = 0; hf < NH; ++hf) lse[hf] = lse_s[hf * 16 + (lane & 15)];
+        for (int hf = 0; hf < NH; ++hf) lse[hf] = lse_s[pb][hf * 16 + (lane & 15)];
         const bool g32 = NH == 2 && a.G == 32;  // both halves hold the one step
-        constexpr int TB = 1;
 #pragma unroll
-        for (int t0 = 0; t0 < TPW; t0 += TB) {
+        for (int t = 0; t < TPW; ++t) {
 #pragma unroll
             for (int hf = 0; hf < NH; ++hf) {
                 if (hf == 1 && g32) break;
-                float v[TB * 4];
+                float v[4];
 #pragma unroll
-                for (int tt = 0; tt < TB; ++tt)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        v[tt * 4 + r] = fmaf(acc[t0 + tt][hf][r], c, -lse[hf]);
-                        if (g32)
-                            v[tt * 4 + r] =
-                                fmaxf(v[tt * 4 + r], fmaf(acc[t0 + tt][NH - 1][r], c, -lse[NH - 1]));
-                    }
+                for (int r = 0; r < 4; ++r) {
+                    v[r] = fmaf(acc[t][hf][r], c, -lse[hf]);
+                    if (g32) v[r] = fmaxf(v[r], fmaf(acc[t][NH - 1][r], c, -lse[NH - 1]));
+                }
                 switch (a.G) {
                     case 1: break;
                     case 2: group_max16_all<2>(v); break;
@@ -401,55 +426,56 @@ __global__ __launch_bounds__(kThreads, 2) void score_kernel(ScoreArgs a) {
                 }
                 if (!own[hf]) continue;
                 float* row = Trun + jrow[hf] * KRP + 4 * g4;
-                const int kt0 = (w + kWaves * t0) * kTileKeys;
-                if (kt0 + kWaves * kTileKeys * (TB - 1) + kTileKeys <= nkeys) {  // full tiles
-                    float old[TB * 4];
+                const int kt = (w + SW * t) * kTileKeys;
+                if (kt + kTileKeys <= nkeys) {  // full tile
+                    float old[4];
 #pragma unroll
-                    for (int tt = 0; tt < TB; ++tt)
+                    for (int r = 0; r < 4; ++r) old[r] = row[kt + r];
 #pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            old[tt * 4 + r] = row[kt0 + kWaves * kTileKeys * tt + r];
-#pragma unroll
-                    for (int tt = 0; tt < TB; ++tt)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            row[kt0 + kWaves * kTileKeys * tt + r] =
-                                fmaxf(old[tt * 4 + r], v[tt * 4 + r]);
+                    for (int r = 0; r < 4; ++r) row[kt + r] = fmaxf(old[r], v[r]);
                 } else {
 #pragma unroll
-                    for (int tt = 0; tt < TB; ++tt) {
-                        const int kt = kt0 + kWaves * kTileKeys * tt;
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            if (kt + 4 * g4 + r < nkeys)
-                                row[kt + r] = fmaxf(row[kt + r], v[tt * 4 + r]);
-                    }
+                    for (int r = 0; r < 4; ++r)
+                        if (kt + 4 * g4 + r < nkeys) row[kt + r] = fmaxf(row[kt + r], v[r]);
                 }
             }
         }
     };
 
-    // Unit `it` streams into acc_cur and is finished two units later (from
-    // acc_fin), so its barrier has a whole unit of slack; after every step the
-    // banks rotate (cur -> mid -> fin).
-    f32x4 (&acc_cur)[TPW][NH] = acc0;
-    f32x4 (&acc_mid)[TPW][NH] = acc1;
-    f32x4 (&acc_fin)[TPW][NH] = acc2;
-    const int n_units = group < a.units ? (a.units - group + a.ngroups - 1) / a.ngroups : 0;
-    for (int it = 0; it < n_units + 2; ++it) {
-        const Unit cur = unit_at(a, group, it, plane_bytes, C::ESZ);
-        const int fu = it >= 2 ? unit_at(a, group, it - 2, plane_bytes, C::ESZ).u : -1;
-        float2 pf[PF];
-        if (fu >= 0) part_fetch(fu, pf);
-        if (cur.u >= 0) stream(acc_cur, cur, unit_at(a, group, it + 1, plane_bytes, C::ESZ));
-        if (fu >= 0) finish(acc_fin, part_combine(fu, pf));
-#pragma unroll
-        for (int t = 0; t < TPW; ++t)
-#pragma unroll
-            for (int hf = 0; hf < NH; ++hf) {
-                acc_fin[t][hf] = acc_mid[t][hf];
-                acc_mid[t][hf] = acc_cur[t][hf];
+    // Unit `it` streams into acc0 and is finished D units later; the banks
+    // rotate (acc0 -> acc1 -> acc2) after every step. The streaming waves and
+    // the control wave run separate loops with one workgroup barrier per step
+    // each: before it, streaming (red[pb]) and the control wave's combine
+    // (lse_s[pb]); after it, finishing and arriving. The LDS buffers alternate
+    // by step parity.
+    if (!ctrl) {
+        for (int it = 0; it < n_units + D; ++it) {
+            const int pb = it & 1;
+            const Unit cur = unit_at(a, group, it, plane_bytes, C::ESZ);
+            const int fu = it >= D ? unit_at(a, group, it - D, plane_bytes, C::ESZ).u : -1;
+            if (cur.u >= 0) stream(acc0, cur, unit_at(a, group, it + 1, plane_bytes, C::ESZ), pb);
+            __syncthreads();
+            if (fu >= 0) {
+                if constexpr (NB == 3) finish(acc2, pb);
+                else finish(acc1, pb);
             }
+#pragma unroll
+            for (int t = 0; t < TPW; ++t)
+#pragma unroll
+                for (int hf = 0; hf < NH; ++hf) {
+                    if constexpr (NB == 3) acc2[t][hf] = acc1[t][hf];
+                    acc1[t][hf] = acc0[t][hf];
+                }
+        }
+    } else {
+        for (int it = 0; it < n_units + D; ++it) {
+            const int pb = it & 1;
+            const int cu = it < n_units ? group + it * a.ngroups : -1;
+            const int fu = (it >= D && it - D < n_units) ? group + (it - D) * a.ngroups : -1;
+            if (fu >= 0) fetch_lse(fu, pb);
+            __syncthreads();
+            if (cu >= 0) arrive(cu, pb);
+        }
     }
     __syncthreads();
     for (int x = tid; x < a.N * nkeys; x += kThreads) {
