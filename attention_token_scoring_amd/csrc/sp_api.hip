@@ -22,6 +22,7 @@ constexpr int kMaxDevices = 64;
 constexpr int kDefaultCUs = 256;  // MI355X; used when no device can be queried
 constexpr int kMaxSelectChunks = 4096;
 constexpr int kMaxSelectRequests = 1024;
+constexpr int kMaxCombiners = 4;
 
 int g_cus[kMaxDevices];
 std::once_flag g_once[kMaxDevices];
@@ -60,59 +61,83 @@ sp_status check_desc(const sp_score_desc* d) {
 }
 
 // Launch plan for one prompt of M keys: choose the number g of workgroups that
-// share a (layer, kv-head) unit so that the slice of each fits its registers,
-// the groups fill the device, and the per-unit barriers stay few; then lay out
-// the workspace.
+// share a (layer, kv-head) unit so that each slice fits what one workgroup can
+// keep in flight and park (registers and LDS), the groups fill the device with
+// at least one CU left for combining, and the per-unit exchanges stay few;
+// then lay out LDS and the workspace.
 sp_status make_plan(const sp_score_desc& d, long long M, int cus, ScorePlan* out) {
     ScorePlan p;
     const int G = d.H / d.Hkv;
+    const bool bf = d.dtype == SP_BF16;
     p.rows = G * d.N <= 16 ? 16 : 32;
-    const int tk = p.rows;
-    p.cap = kStreamWaves * tiles_per_wave(d.dtype == SP_BF16, p.rows / 16) * kTileKeys;
+    const int tk = kTileKeys;
+    const int row_bytes = d.d * esize(d.dtype);
     p.units = d.L * d.Hkv;
     if (M < 1) return SP_EINVAL;
     if ((unsigned long long)(M + d.N) * d.d * esize(d.dtype) >= (1ull << 31)) return SP_EUNSUPPORTED;
     if (cus < 1) cus = kDefaultCUs;
-    const long long gmin = (M + p.cap - 1) / p.cap;
-    if (gmin > cus) return SP_EUNSUPPORTED;
-    const double bytes_per_key = (double)d.d * esize(d.dtype);
+    if (cus < 2) return SP_EUNSUPPORTED;
+    const double bytes_per_key = (double)row_bytes;
     const double bw_total = 6.0e12, bw_cu_max = 60.0e9;
+    // fixed cost of one step (barrier, finishing, exchange bookkeeping)
+    const double step_cost = 1.0e-6;
     double best = 1e300;
-    int bg = 0, bkr = 0, bng = 0;
-    for (long long g = gmin; g <= cus; ++g) {
-        long long kr = (M + g - 1) / g;
-        kr = (kr + tk - 1) / tk * tk;
-        if (kr > p.cap) continue;
-        const long long geff = (M + kr - 1) / kr;
-        if (geff != g) continue;  // the same slice with fewer workgroups is planned at geff
-        long long ng = cus / g;
-        if (ng > p.units) ng = p.units;
-        if (ng < 1) continue;
-        const long long iters = (p.units + ng - 1) / ng;
-        const double active = (double)(g * ng);
-        double bw_cu = bw_total / active;
-        if (bw_cu > bw_cu_max) bw_cu = bw_cu_max;
-        const double sync = g == 1 ? 0.0 : (32 % g == 0 ? 2.0e-6 : 4.0e-6);
-        const double cost = iters * (kr * bytes_per_key / bw_cu + sync);
-        if (cost < best * 0.999) {
-            best = cost;
-            bg = (int)g;
-            bkr = (int)kr;
-            bng = (int)ng;
+    int bg = 0, bkr = 0, bng = 0, bdef = 0, btpw = 0;
+    const int tpw0 = tiles_per_wave(bf, d.d);
+    for (int tpw = tpw0; tpw <= tpw0 + 1; ++tpw) {
+        const int cap = kStreamWaves * tpw * kTileKeys;
+        const long long gmin = (M + cap - 1) / cap;
+        for (long long g = gmin; g <= cus - 1; ++g) {
+            long long kr = (M + g - 1) / g;
+            kr = (kr + tk - 1) / tk * tk;
+            if (kr > cap) continue;
+            const long long geff = (M + kr - 1) / kr;
+            if (geff != g) continue;  // the same slice with fewer workgroups is planned at geff
+            int defer = 0;
+            for (int D = kMaxDefer; D >= 1; --D)
+                if (score_lds_layout(D + 1, tpw, p.rows, row_bytes, d.N, (int)kr).total <= kLdsBytes) {
+                    defer = D;
+                    break;
+                }
+            if (defer == 0) continue;
+            long long ng = (cus - 1) / g;
+            if (ng > p.units) ng = p.units;
+            if (ng < 1) continue;
+            const long long iters = (p.units + ng - 1) / ng;
+            const double active = (double)(g * ng);
+            double bw_cu = bw_total / active;
+            if (bw_cu > bw_cu_max) bw_cu = bw_cu_max;
+            // a shallower deferral exposes more of each exchange's latency;
+            // tiles a wave computes but does not need cost MFMA and LDS time
+            const double sync = (kMaxDefer - defer) * 1.0e-6;
+            const double waste = (double)(cap - kr) / cap * 0.5e-6;
+            const double cost = iters * (kr * bytes_per_key / bw_cu + step_cost + sync + waste);
+            if (cost < best * 0.999) {
+                best = cost;
+                bg = (int)g;
+                bkr = (int)kr;
+                bng = (int)ng;
+                bdef = defer;
+                btpw = tpw;
+            }
         }
     }
     if (bg == 0) return SP_EUNSUPPORTED;
+    p.tpw = btpw;
+    p.cap = kStreamWaves * btpw * kTileKeys;
     p.g = bg;
     p.KR = bkr;
     p.ngroups = bng;
-    p.grid = bg * bng;
-    p.xcd_local = (cus == 256 && 32 % bg == 0 && p.grid == 256) ? 1 : 0;
-    p.ws_cnt = 0;
-    p.ws_part = round_up(4 * (size_t)(p.units + 1), 256);
+    p.defer = bdef;
+    p.ncomb = cus - bg * bng;
+    if (p.ncomb > kMaxCombiners) p.ncomb = kMaxCombiners;
+    p.grid = bg * bng + p.ncomb;
+    p.lds = score_lds_layout(bdef + 1, btpw, p.rows, row_bytes, d.N, bkr);
+    p.ws_err = 0;
+    p.ws_part = 256;
     p.ws_tail = p.ws_part + round_up((size_t)p.units * p.g * p.rows * 8, 256);
     p.ws_lse = p.ws_tail + round_up((size_t)p.units * p.rows * 8, 256);
-    p.ws_flag = p.ws_lse + round_up((size_t)p.units * p.rows * 4, 256);
-    p.ws_tg = p.ws_flag + round_up((size_t)p.units * 4, 256);
+    p.ws_tg = p.ws_lse + round_up((size_t)p.units * p.rows * 4, 256);
     p.ws_total = p.ws_tg + round_up((size_t)p.ngroups * d.N * M * 4, 256);
     *out = p;
     return SP_OK;
@@ -124,14 +149,13 @@ size_t workspace_bound(const sp_score_desc& d, long long max_M, int cus) {
     if (cus < 1) cus = kDefaultCUs;
     const int G = d.H / d.Hkv;
     const int rows = G * d.N <= 16 ? 16 : 32;
-    const long long cap = (long long)kStreamWaves * tiles_per_wave(d.dtype == SP_BF16, rows / 16) * kTileKeys;
+    const long long cap = (long long)kStreamWaves * (tiles_per_wave(d.dtype == SP_BF16, d.d) + 1) * kTileKeys;
     const long long units = (long long)d.L * d.Hkv;
     long long tg_elems = (long long)(units < cus ? units : cus) * max_M;
     if (tg_elems > (long long)cus * cap) tg_elems = (long long)cus * cap;
     tg_elems *= d.N;
-    return round_up(4 * (size_t)(units + 1), 256) + round_up((size_t)units * cus * rows * 8, 256) +
-           round_up((size_t)units * rows * 8, 256) + round_up((size_t)units * rows * 4, 256) +
-           round_up((size_t)units * 4, 256) + round_up((size_t)tg_elems * 4, 256);
+    return 256 + round_up((size_t)units * cus * rows * 8, 256) + round_up((size_t)units * rows * 8, 256) +
+           round_up((size_t)units * rows * 4, 256) + round_up((size_t)tg_elems * 4, 256);
 }
 
 sp_status to_status(hipError_t e) { return e == hipSuccess ? SP_OK : SP_EDEVICE; }
@@ -222,7 +246,7 @@ sp_status sp_score_plan(const sp_score_desc* desc, int32_t M, int32_t info[8]) {
     info[4] = p.rows;
     info[5] = p.units;
     info[6] = cus > 0 ? cus : kDefaultCUs;
-    info[7] = 0;
+    info[7] = p.defer;
     return SP_OK;
 }
 

@@ -11,17 +11,45 @@ namespace sp {
 // Scoring workgroups have 8 waves (two per SIMD, 256 registers each): 7 stream
 // K, one synchronises. Keys are processed in tiles of 16 (the M dimension of
 // the 16x16 MFMAs); query rows in 16-row halves (NH = 1 or 2 halves per
-// kv-head). Each streaming wave keeps the logits of kBanks units in registers
-// (a unit is finished kBanks-1 units after it is streamed).
+// kv-head). Each streaming wave owns TPW tiles of its workgroup's key slice
+// in every unit and keeps two units of K tiles in flight.
 constexpr int kWaves = 8;
 constexpr int kStreamWaves = 7;
 constexpr int kThreads = kWaves * 64;
 constexpr int kTileKeys = 16;
-constexpr int kBanks = 3;
-constexpr int tiles_per_wave(bool bf16, int nh) { return (bf16 ? 4 : 2) * (nh == 1 ? 2 : 1); }
-// Extra floats per look-ahead row of the LDS running maximum: rows start 16
-// banks apart.
+constexpr int kMaxDefer = 3;          // units between streaming and finishing a unit
+constexpr int kLdsBytes = 160 * 1024;  // LDS of one CU
+// Tiles per streaming wave and unit: the base value, or one more for long
+// prompts (a deeper slice per workgroup).
+constexpr int tiles_per_wave(bool bf16, int d) { return (!bf16 && d == 128) ? 2 : 4; }
+// Floats per look-ahead row of the LDS running maximum: rows start 16 banks
+// apart.
 constexpr int row_stride(int kr) { return (kr + 63) / 64 * 64 + 16; }
+
+// Byte offsets of the scoring kernel's LDS regions (all 16-byte aligned).
+struct ScoreLds {
+    int bank;   // [nbk][SW][TPW][64 lanes][NH][4 halves]: parked logits, fp16
+    int ref;    // [nbk][SW][rows] float: reference (log2 domain) of the parked logits
+    int q;      // [2][rows][row bytes + 16]: Q of the current and the next unit
+    int trun;   // [N][row_stride(KR)] float: running max of the log2 probabilities
+    int red;    // [2][SW][rows] float2: per-wave (max, sum) of the unit just streamed
+    int lse;    // [2][rows] float: log-sum-exp of the unit being finished
+    int total;
+};
+
+inline ScoreLds score_lds_layout(int nbk, int tpw, int rows, int row_bytes, int N, int KR) {
+    auto up = [](int x) { return (x + 15) / 16 * 16; };
+    const int nh = rows / 16;
+    ScoreLds l;
+    l.bank = 0;
+    l.ref = l.bank + up(nbk * kStreamWaves * tpw * 64 * nh * 8);
+    l.q = l.ref + up(nbk * kStreamWaves * rows * 4);
+    l.trun = l.q + up(2 * rows * (row_bytes + 16));
+    l.red = l.trun + up(N * row_stride(KR) * 4);
+    l.lse = l.red + up(2 * kStreamWaves * rows * 8);
+    l.total = l.lse + up(2 * rows * 4);
+    return l;
+}
 
 // Everything the cooperative scoring kernel needs for one request.
 struct ScoreArgs {
@@ -29,27 +57,31 @@ struct ScoreArgs {
     const void* K;             // key row 0 of (layer 0, kv-head 0) of this request
     long long plane_stride;    // elements between consecutive (layer, kv-head) key planes
     float* Tg;                 // [ngroups][N][M]: per-group running max of log2 probabilities
-    float2* part;              // [units][g][rows]: per-workgroup (row max, row sum) partials
+    float2* part;              // [units][g][rows]: per-workgroup (row max, row sum); sentinel until published
     float2* tail;              // [units][rows]: the look-ahead keys' (row max, row sum)
-    float* lse;                // [units][rows]: each row's log2-sum-exp2 (scaled logits)
-    int* flag;                 // [units]: set once the unit's lse is published
-    int* cnt;                  // [units]: arrival counters of the per-unit barriers
-    int* err;                  // [1]: set when a barrier wait times out
+    float* lse;                // [units][rows]: each row's log2-sum-exp2; sentinel until published
+    int* err;                  // [1]: set when a wait times out
     int L, H, Hkv, G, N, M, d;
     int g;                     // workgroups cooperating on one unit
     int ngroups;               // groups working in parallel
     int KR;                    // prompt keys per workgroup (multiple of the tile width)
     int units;                 // L * Hkv
-    int xcd_local;             // 1: map groups onto the 8 XCDs (g divides 32)
+    int defer;                 // D: a unit is finished D units after it is streamed
+    int nbk;                   // D + 1 banks of parked logits
+    ScoreLds lds;
     float c;                   // scale * log2(e)
 };
 
 struct ScorePlan {
     int rows;      // 16 or 32
+    int tpw;       // tiles per streaming wave and unit
     int cap;       // prompt keys one workgroup can hold
-    int g, ngroups, KR, units, grid;
-    int xcd_local;
-    size_t ws_cnt, ws_part, ws_tail, ws_lse, ws_flag, ws_tg, ws_total;  // byte offsets / sizes in the workspace
+    int g, ngroups, KR, units;
+    int ncomb;     // combiner workgroups (on CUs no group uses)
+    int grid;      // g * ngroups + ncomb
+    int defer;
+    ScoreLds lds;
+    size_t ws_err, ws_part, ws_tail, ws_lse, ws_tg, ws_total;  // byte offsets / sizes in the workspace
 };
 
 // Selection of one request (one workgroup).
@@ -71,5 +103,12 @@ struct SelectParamsDev {
     int last_n;
     float last_mult;
 };
+
+// Cooperative scoring kernels, one translation unit per operand type and head
+// dimension: the instantiation for (rows, G, tiles per wave), or nullptr.
+const void* score_kernel_bf16_d128(int rows, int G, int tpw);
+const void* score_kernel_bf16_d64(int rows, int G, int tpw);
+const void* score_kernel_f32_d128(int rows, int G, int tpw);
+const void* score_kernel_f32_d64(int rows, int G, int tpw);
 
 }  // namespace sp

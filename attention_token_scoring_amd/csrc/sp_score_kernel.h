@@ -1,0 +1,619 @@
+// Look-ahead attention scoring on gfx950.
+//
+// What is computed ("Speculative Prefill" review page, Core formulas: attention
+// score a_ij = Softmax(Q_{M+j} K^T)_i and the max-max-mean importance
+// aggregation; "SpecPrefill - Implementation Guide", How It Works, token
+// importance): for every layer l, query head h and look-ahead step j the softmax
+// of the scaled logits of query M+j over the M+j+1 keys it sees, then
+//   importance_i = (1/N) sum_j max_{l,h} p_{l,h,j,i},  i < M.
+//
+// How (K is read from HBM once):
+//  * A unit is one (layer, kv-head) plane of K. The G query heads of the plane
+//    and the N look-ahead steps give G*N query rows (row = j*G + h_local),
+//    handled as one or two 16-row halves. Logits come from 16x16x32 bf16 (or
+//    16x16x4 f32) MFMAs with keys as the M dimension: each lane ends up holding
+//    one query row for 4 keys of a tile, so row statistics are lane-local, and
+//    each load instruction reads 64 contiguous bytes of 16 key rows.
+//  * g workgroups (one per CU; launched cooperatively so all are resident)
+//    share a unit, each owning a key slice. Seven waves stream K, each keeping
+//    two units of its tiles in flight, so HBM never waits for the rest of the
+//    pipeline. A streamed unit's logits are parked in LDS as 16-bit fixed-point
+//    log2 values relative to each wave-row's maximum (a probability p carries a
+//    relative error of at most 1.7e-4), together with the wave's (max, sum) per
+//    row.
+//  * The eighth wave of each workgroup does the cross-workgroup exchange, off
+//    the streaming waves' instruction stream (a wave's vector-memory counter is
+//    in order on gfx950, so a poll issued by a streaming wave would wait for
+//    all of its prefetches): it publishes the workgroup's per-row (max, sum) of
+//    each unit, stages the next unit's Q in LDS, and fetches log-sum-exps one
+//    step before they are needed.
+//  * Combiner workgroups on CUs no group uses gather the g partials of each unit
+//    (their loads do not queue behind any K stream), add the look-ahead keys'
+//    share, and publish each row's log-sum-exp. Partial and log-sum-exp slots
+//    hold a sentinel until written, so no counters or flags are needed.
+//  * D units after streaming a unit, its parked logits become log2
+//    probabilities; the max over the G heads of a step is a DPP max across G
+//    adjacent lanes; the max over kv-heads and layers is a running max in LDS,
+//    in the log2 domain (exp2 is monotone, so one exponential per (step, key)
+//    at the end). Each group writes its running max; a small kernel takes the
+//    max over groups, exponentiates and averages over the steps.
+//  * The look-ahead keys M..M+N-1 only enter denominators; a small prep kernel
+//    computes their share of each row's statistics.
+#pragma once
+
+#include <math.h>
+
+#include <type_traits>
+
+#include "sp_internal.h"
+
+namespace sp {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// 2 s of the 100 MHz constant clock: a wait longer than this is a bug; the
+// kernel records it in the error word and moves on instead of hanging.
+constexpr unsigned long long kSpinTicks = 200000000ull;
+// Buffer offset that is always out of range: loads there return zeros.
+constexpr uint32_t kOob = 0x7ffffff0u;
+// Content of a partial-statistics or log-sum-exp slot that has not been
+// published yet (a NaN pattern no published value has).
+constexpr unsigned long long kSentinel = ~0ull;
+constexpr unsigned kSentinel32 = ~0u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+__device__ __forceinline__ i32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
+
+// (m, s) <- combination of two partial softmax statistics (raw-logit max m,
+// sum of exp2((x - m) * c)).
+__device__ __forceinline__ void combine(float& m, float& s, float m2, float s2, float c) {
+    const float mn = fmaxf(m, m2);
+    if (mn == -INFINITY) return;
+    s = s * exp2_hw((m - mn) * c) + s2 * exp2_hw((m2 - mn) * c);
+    m = mn;
+}
+
+// Lane permutation within rows of 16 lanes. Every source lane exists, so
+// bound_ctrl is irrelevant; setting it lets the compiler fold the move into
+// the consuming v_max (the score kernels are built without NaN semantics, so
+// no canonicalisation sits between them).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(float,
+                              __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf,
+                                                       true));
+}
+
+// Max over the G (<= 16) adjacent lanes that hold the G heads of one step.
+template <int G>
+__device__ __forceinline__ float group_max16(float v) {
+    if constexpr (G >= 2) v = fmaxf(v, dpp<0xb1>(v));   // quad_perm [1,0,3,2]
+    if constexpr (G >= 4) v = fmaxf(v, dpp<0x4e>(v));   // quad_perm [2,3,0,1]
+    if constexpr (G >= 8) v = fmaxf(v, dpp<0x141>(v));  // row_half_mirror
+    if constexpr (G >= 16) v = fmaxf(v, dpp<0x140>(v)); // row_mirror
+    return v;
+}
+
+__device__ __forceinline__ void st64(void* p, float x, float y) {
+    const unsigned long long bits =
+        (unsigned long long)__float_as_uint(x) | ((unsigned long long)__float_as_uint(y) << 32);
+    __hip_atomic_store((unsigned long long*)p, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ unsigned long long ld64(const void* p) {
+    return __hip_atomic_load((unsigned long long*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ unsigned ld32(const void* p) {
+    return __hip_atomic_load((unsigned*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Parked logits: y = (log2-domain logit) - (row reference) <= 0 as a 16-bit
+// fixed-point code round(-y * 2^11), clamped to [0, 65535] (y in [-32, 0]).
+// The decoded p = exp2(y + offset) then carries a relative error of at most
+// ln2 * 2^-12 (1.7e-4) whenever y >= -32; below that p < 2^-32 and the clamp
+// changes it by less than that. Two codes share one 32-bit word, which travels
+// by value (bit-casting an element of a vector-typed value in place is not
+// reliable with this compiler).
+constexpr float kCodeScale = 2048.f;
+__device__ __forceinline__ unsigned encode_y(float y) {
+    return (unsigned)fminf(fmaf(y, -kCodeScale, 0.5f), 65535.f);
+}
+__device__ __forceinline__ int pack_y2(float lo, float hi) {
+    return (int)(encode_y(lo) | (encode_y(hi) << 16));
+}
+// (lo, hi) codes of a word -> log2 values plus a common offset
+__device__ __forceinline__ void unpack_y2(int word, float off, float& lo, float& hi) {
+    const unsigned w = (unsigned)word;
+    lo = fmaf((float)(w & 0xffffu), -1.f / kCodeScale, off);
+    hi = fmaf((float)(w >> 16), -1.f / kCodeScale, off);
+}
+
+// ---------------------------------------------------------------------------------------
+// 16-key tiles. A = K tile (16 keys x d), B = Q^T (d x 16 rows), C[key][row].
+// Lane L supplies key (and row) L % 16; its lane group g = L / 16 reads bytes
+// [64 s + 16 g, 64 s + 16 g + 16) of the row for load s, i.e. the 4 lane groups
+// of one load instruction read 64 contiguous bytes of each of 16 key rows. For
+// bf16 one load is one 32-deep MFMA k-step (d = 32 s + 8 g + e); for f32 it is
+// four 4-deep k-steps (d = 16 s + 4 g + e). Both operands use the same mapping.
+// C layout: lane L holds rows L % 16 of keys 4 (L / 16) + r, r = 0..3.
+// ---------------------------------------------------------------------------------------
+template <int D_, bool BF16_, int NH_, int G_, int TPW_>
+struct Cfg {
+    static constexpr int D = D_, NH = NH_, G = G_;
+    static constexpr bool BF16 = BF16_;
+    static constexpr int ESZ = BF16 ? 2 : 4;
+    static constexpr int KB = D * ESZ;    // bytes per key (and query) row
+    static constexpr int QS = KB + 16;    // LDS bytes per staged query row
+    static constexpr int NLD = KB / 64;   // 16-byte loads per lane per tile
+    static constexpr int TPW = TPW_;     // tiles per wave and unit
+    static constexpr int NBUF = 2 * TPW;  // ring: two units of this wave's tiles
+    static constexpr int ROWS = 16 * NH;
+    // Q loads of the control wave per unit: ROWS rows of KB bytes, 16 B per lane
+    static constexpr int QLD = ROWS * KB / (64 * 16);
+    // G = 32 (one step per unit) spans both halves; otherwise a step's heads
+    // sit in G adjacent lanes of one half
+    static_assert(G <= 16 || (G == 32 && NH == 2), "unsupported head grouping");
+    static constexpr int GL = G == 32 ? 16 : G;  // heads of a step within one half
+};
+
+template <class C>
+struct Frag {
+    i32x4 v[C::NLD];
+};
+
+template <class C>
+__device__ __forceinline__ void mma(f32x4& acc, const i32x4& q, const i32x4& k) {
+    if constexpr (C::BF16) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k),
+                                                      __builtin_bit_cast(bf16x8, q), acc, 0, 0, 0);
+    } else {
+        const f32x4 kv = __builtin_bit_cast(f32x4, k);
+        const f32x4 qv = __builtin_bit_cast(f32x4, q);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kv.x, qv.x, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kv.y, qv.y, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kv.z, qv.z, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kv.w, qv.w, acc, 0, 0, 0);
+    }
+}
+
+// K fragment of the 16-key tile starting at key0 (zeros when !valid; the
+// buffer descriptor bounds the plane, so reads past its end are zeros too).
+template <class C>
+__device__ __forceinline__ void load_k(Frag<C>& f, __amdgpu_buffer_rsrc_t rs, int key0,
+                                       bool valid, int lane) {
+    const uint32_t off = valid ? (uint32_t)(key0 + (lane & 15)) * (uint32_t)C::KB +
+                                     (uint32_t)(16 * (lane >> 4))
+                               : kOob;
+#pragma unroll
+    for (int s = 0; s < C::NLD; ++s) f.v[s] = load16(rs, off + 64u * s);
+}
+
+// Key plane of unit u (an empty descriptor when u < 0).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t plane_rsrc(const ScoreArgs& a, int u,
+                                                             uint32_t plane_bytes, int esz) {
+    const int uu = u < 0 ? 0 : u;
+    const char* plane = (const char*)a.K + (long long)uu * a.plane_stride * esz;
+    return make_rsrc(plane, u < 0 ? 0u : plane_bytes);
+}
+
+template <class C>
+__global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
+    constexpr int TPW = C::TPW, NH = C::NH, ROWS = C::ROWS, G = C::G, NLD = C::NLD;
+    constexpr int SW = kStreamWaves;  // waves 0..SW-1 stream K; wave SW synchronises
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int g4 = lane >> 4;  // lane group
+    const float c = a.c;
+    const int nstream = a.g * a.ngroups;
+
+    // ---------------------------------------------------------------------------
+    // Combiner workgroups: for units cw, cw + ncw, ... wait until the g
+    // partials are published, combine them with the look-ahead keys' share and
+    // publish each row's log-sum-exp. Lane L handles row L % ROWS for ranks
+    // L / ROWS, L / ROWS + SUBS, ... in batches of B.
+    // ---------------------------------------------------------------------------
+    if ((int)blockIdx.x >= nstream) {
+        constexpr int SUBS = 64 / ROWS;
+        constexpr int B = 16;
+        const int cw = ((int)blockIdx.x - nstream) * kWaves + w;
+        const int ncw = ((int)gridDim.x - nstream) * kWaves;
+        const int row = lane % ROWS, sub = lane / ROWS;
+        for (int u = cw; u < a.units; u += ncw) {
+            float m = -INFINITY, s = 0.f;
+            if (sub == 0) {
+                const float2 t = a.tail[(size_t)u * ROWS + row];
+                m = t.x;
+                s = t.y;
+            }
+            const unsigned long long* slot =
+                (const unsigned long long*)(a.part + (size_t)u * a.g * ROWS) + row;
+            const unsigned long long t0 = wall_clock64();
+            for (int k0 = sub; k0 < a.g; k0 += SUBS * B) {
+                unsigned long long v[B];
+                unsigned pend = 0;  // bit x: rank k0 + SUBS x not seen yet
+#pragma unroll
+                for (int x = 0; x < B; ++x) {
+                    v[x] = kSentinel;
+                    if (k0 + SUBS * x < a.g) pend |= 1u << x;
+                }
+                while (true) {
+#pragma unroll
+                    for (int x = 0; x < B; ++x)
+                        if ((pend >> x) & 1) v[x] = ld64(slot + (size_t)(k0 + SUBS * x) * ROWS);
+                    unsigned np = 0;
+#pragma unroll
+                    for (int x = 0; x < B; ++x)
+                        if (((pend >> x) & 1) && v[x] == kSentinel) np |= 1u << x;
+                    pend = np;
+                    if (__ballot(pend != 0) == 0) break;
+                    __builtin_amdgcn_s_sleep(2);
+                    if (wall_clock64() - t0 > kSpinTicks) {
+                        if (lane == 0) __hip_atomic_store(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        break;
+                    }
+                }
+                float mx = m;
+#pragma unroll
+                for (int x = 0; x < B; ++x)
+                    if (k0 + SUBS * x < a.g && v[x] != kSentinel)
+                        mx = fmaxf(mx, __uint_as_float((unsigned)v[x]));
+                if (mx != -INFINITY) {
+                    float acc = s * exp2_hw((m - mx) * c);
+#pragma unroll
+                    for (int x = 0; x < B; ++x)
+                        if (k0 + SUBS * x < a.g && v[x] != kSentinel)
+                            acc = fmaf(__uint_as_float((unsigned)(v[x] >> 32)),
+                                       exp2_hw((__uint_as_float((unsigned)v[x]) - mx) * c), acc);
+                    m = mx;
+                    s = acc;
+                }
+            }
+            if constexpr (SUBS == 4) combine(m, s, __shfl_xor(m, 16), __shfl_xor(s, 16), c);
+            combine(m, s, __shfl_xor(m, 32), __shfl_xor(s, 32), c);
+            if (sub == 0)
+                __hip_atomic_store((unsigned*)a.lse + (size_t)u * ROWS + row,
+                                   __float_as_uint(m * c + log2_hw(s)), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        }
+        return;
+    }
+
+    // ---------------------------------------------------------------------------
+    // Streaming workgroups.
+    // ---------------------------------------------------------------------------
+    const int group = (int)blockIdx.x / a.g, rank = (int)blockIdx.x % a.g;
+    const int KRP = row_stride(a.KR);
+    float* Trun = (float*)(smem + a.lds.trun);
+    float2* red = (float2*)(smem + a.lds.red);      // [2][SW][ROWS]
+    float* lse_s = (float*)(smem + a.lds.lse);      // [2][ROWS]
+    float* refs = (float*)(smem + a.lds.ref);       // [nbk][SW][ROWS]
+    char* qlds = smem + a.lds.q;                    // [2][ROWS][QS]
+    char* banks = smem + a.lds.bank;                // [nbk][SW][TPW][64][NH][8 B]
+    for (int x = tid; x < a.N * KRP; x += kThreads) Trun[x] = -INFINITY;
+
+    const int r0 = rank * a.KR;
+    const int r1 = min(r0 + a.KR, a.M);
+    const int nkeys = max(r1 - r0, 0);
+    const int ntiles = (nkeys + kTileKeys - 1) / kTileKeys;
+    const uint32_t plane_bytes = (uint32_t)(a.M + a.N) * (uint32_t)C::KB;
+    const int D = a.defer, nbk = a.nbk;
+    const int n_units = group < a.units ? (a.units - group + a.ngroups - 1) / a.ngroups : 0;
+    const int n_steps = (n_units + D + 1) & ~1;  // even: the streaming loop is unrolled by 2
+    auto unit_of = [&](int it) __attribute__((always_inline)) { return it >= 0 && it < n_units ? group + it * a.ngroups : -1; };
+
+    // Per-lane query rows of the halves, and whether the lane writes the
+    // running max of its step (it holds the step's first head; for G = 32 both
+    // halves hold one step and half 0 writes).
+    int jrow[NH];
+    bool own[NH];
+#pragma unroll
+    for (int hf = 0; hf < NH; ++hf) {
+        const int qr = hf * 16 + (lane & 15);
+        jrow[hf] = qr / G;
+        own[hf] = qr % G == 0 && jrow[hf] < a.N && !(G == 32 && hf == 1);
+    }
+
+    if (w < SW) {
+        // ======================= streaming waves =======================
+        Frag<C> fb[C::NBUF];
+        f32x4 acc[TPW][NH];
+        // prime the ring with the first two units
+#pragma unroll
+        for (int P = 0; P < 2; ++P) {
+            const auto rs = plane_rsrc(a, unit_of(P), plane_bytes, C::ESZ);
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) {
+                const int tile = w + SW * t;
+                load_k<C>(fb[P * TPW + t], rs, r0 + tile * kTileKeys, unit_of(P) >= 0 && tile < ntiles, lane);
+            }
+        }
+        __syncthreads();  // Q of unit 0 is staged
+
+        // Stream unit `it` (ring slots of parity P), park its logits in bank
+        // it % nbk and its per-row statistics in red[P].
+        auto stream = [&](auto Pc, int it) __attribute__((always_inline)) {
+            constexpr int P = decltype(Pc)::value;
+            // k-outer: for each 16-byte k-slice, this unit's Q fragments of both
+            // halves come from LDS, then every tile's MFMAs consume them
+            const int u2 = unit_of(it + 2);
+            const auto rs2 = plane_rsrc(a, u2, plane_bytes, C::ESZ);
+#pragma unroll
+            for (int t = 0; t < TPW; ++t)
+#pragma unroll
+                for (int hf = 0; hf < NH; ++hf) acc[t][hf] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < NLD; ++s) {
+                i32x4 q[NH];
+#pragma unroll
+                for (int hf = 0; hf < NH; ++hf)
+                    q[hf] = *(const i32x4*)(qlds + (P * ROWS + hf * 16 + (lane & 15)) * C::QS + 16 * g4 + 64 * s);
+#pragma unroll
+                for (int t = 0; t < TPW; ++t)
+#pragma unroll
+                    for (int hf = 0; hf < NH; ++hf) mma<C>(acc[t][hf], q[hf], fb[P * TPW + t].v[s]);
+            }
+            // refill the slots with the same tiles of the unit two ahead
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) {
+                const int tile = w + SW * t;
+                load_k<C>(fb[P * TPW + t], rs2, r0 + tile * kTileKeys, u2 >= 0 && tile < ntiles, lane);
+            }
+            // mask keys past the slice
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) {
+                const int kt = (w + SW * t) * kTileKeys;
+                if (kt + kTileKeys > nkeys) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+#pragma unroll
+                        for (int hf = 0; hf < NH; ++hf)
+                            if (kt + 4 * g4 + r >= nkeys) acc[t][hf][r] = -INFINITY;
+                }
+            }
+            // per wave-row max (lanes L, L^16, L^32, L^48 hold the same row),
+            // shifted log2 logits y = c x - c max (<= 0), their exp2 sum
+            const int b = it % nbk;
+#pragma unroll
+            for (int hf = 0; hf < NH; ++hf) {
+                float m = -INFINITY;
+#pragma unroll
+                for (int t = 0; t < TPW; ++t)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) m = fmaxf(m, acc[t][hf][r]);
+                m = fmaxf(m, __shfl_xor(m, 16));
+                m = fmaxf(m, __shfl_xor(m, 32));
+                const float cm = m == -INFINITY ? 0.f : m * c;
+                float s = 0.f;
+#pragma unroll
+                for (int t = 0; t < TPW; ++t)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float y = fmaf(acc[t][hf][r], c, -cm);
+                        acc[t][hf][r] = y;
+                        s += exp2_hw(y);
+                    }
+                s += __shfl_xor(s, 16);
+                s += __shfl_xor(s, 32);
+                if (g4 == 0) {
+                    red[(P * SW + w) * ROWS + hf * 16 + lane] = make_float2(m, s);
+                    refs[(b * SW + w) * ROWS + hf * 16 + lane] = cm;
+                }
+            }
+            // park the shifted logits: 4 halves per (tile, half), NH*8 bytes per lane
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) {
+                int* dst = (int*)(banks + ((size_t)((b * SW + w) * TPW + t) * 64 + lane) * (NH * 8));
+                int wd[2 * NH];
+#pragma unroll
+                for (int hf = 0; hf < NH; ++hf) {
+                    wd[2 * hf] = pack_y2(acc[t][hf][0], acc[t][hf][1]);
+                    wd[2 * hf + 1] = pack_y2(acc[t][hf][2], acc[t][hf][3]);
+                }
+                if constexpr (NH == 2) *(int4*)dst = make_int4(wd[0], wd[1], wd[2], wd[3]);
+                else *(int2*)dst = make_int2(wd[0], wd[1]);
+            }
+        };
+
+        // Finish unit `it` (parked in bank it % nbk; its log-sum-exps in
+        // lse_s[pb]): log2 probabilities, max over the G heads of each step,
+        // running max over units in LDS.
+        auto finish = [&](int it, int pb) __attribute__((always_inline)) {
+            const int b = it % nbk;
+            float off[NH];
+#pragma unroll
+            for (int hf = 0; hf < NH; ++hf) {
+                const int row = hf * 16 + (lane & 15);
+                off[hf] = refs[(b * SW + w) * ROWS + row] - lse_s[pb * ROWS + row];
+            }
+            constexpr int NHF = G == 32 ? 1 : NH;  // G = 32: both halves hold the one step
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) {
+                const int* src = (const int*)(banks + ((size_t)((b * SW + w) * TPW + t) * 64 + lane) * (NH * 8));
+                int wd[2 * NH];
+                if constexpr (NH == 2) {
+                    const int4 q4 = *(const int4*)src;
+                    wd[0] = q4.x;
+                    wd[1] = q4.y;
+                    wd[2] = q4.z;
+                    wd[3] = q4.w;
+                } else {
+                    const int2 q2 = *(const int2*)src;
+                    wd[0] = q2.x;
+                    wd[1] = q2.y;
+                }
+                float y[NH][4];  // log2 probabilities
+#pragma unroll
+                for (int hf = 0; hf < NH; ++hf) {
+                    unpack_y2(wd[2 * hf], off[hf], y[hf][0], y[hf][1]);
+                    unpack_y2(wd[2 * hf + 1], off[hf], y[hf][2], y[hf][3]);
+                }
+#pragma unroll
+                for (int hf = 0; hf < NHF; ++hf) {
+                    float v[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        v[r] = y[hf][r];
+                        if constexpr (G == 32) v[r] = fmaxf(v[r], y[1][r]);
+                    }
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) v[r] = group_max16<C::GL>(v[r]);
+                    if (!own[hf]) continue;
+                    float* rowp = Trun + jrow[hf] * KRP + 4 * g4;
+                    const int kt = (w + SW * t) * kTileKeys;
+                    if (kt + kTileKeys <= nkeys) {  // full tile: one 16-byte read and write
+                        float4* p4 = (float4*)(rowp + kt);
+                        float4 o = *p4;
+                        o.x = fmaxf(o.x, v[0]);
+                        o.y = fmaxf(o.y, v[1]);
+                        o.z = fmaxf(o.z, v[2]);
+                        o.w = fmaxf(o.w, v[3]);
+                        *p4 = o;
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            if (kt + 4 * g4 + r < nkeys) rowp[kt + r] = fmaxf(rowp[kt + r], v[r]);
+                    }
+                }
+            }
+        };
+
+        // Step `it`: stream unit it, then (after the workgroup barrier, when
+        // the control wave has put unit it - D's log-sum-exps in LDS) finish
+        // unit it - D.
+        auto step = [&](auto Pc, int it) __attribute__((always_inline)) {
+            if (it < n_units) stream(Pc, it);
+            __syncthreads();
+            const int fu = it - D;
+            if (fu >= 0 && fu < n_units) finish(fu, it & 1);
+        };
+        for (int it = 0; it < n_steps; it += 2) {
+            step(std::integral_constant<int, 0>{}, it);
+            step(std::integral_constant<int, 1>{}, it + 1);
+        }
+    } else {
+        // ======================= control wave =======================
+        // Q of one unit: ROWS rows of KB bytes, 16 bytes per lane and load.
+        i32x4 qc[C::QLD];
+        auto q_issue = [&](int u) __attribute__((always_inline)) {
+#pragma unroll
+            for (int i = 0; i < C::QLD; ++i) {
+                const int e = (i * 64 + lane) * 16;
+                const int row = e / C::KB, col = e % C::KB;
+                const int j = row / G, hl = row % G;
+                if (u >= 0 && j < a.N) {
+                    const int l = u / a.Hkv, kvh = u % a.Hkv;
+                    const long long qrow = ((long long)l * a.H + (long long)kvh * G + hl) * a.N + j;
+                    qc[i] = *(const i32x4*)((const char*)a.Q + qrow * C::KB + col);
+                } else {
+                    qc[i] = i32x4{0, 0, 0, 0};
+                }
+            }
+        };
+        auto q_store = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+            for (int i = 0; i < C::QLD; ++i) {
+                const int e = (i * 64 + lane) * 16;
+                const int row = e / C::KB, col = e % C::KB;
+                *(i32x4*)(qlds + (buf * ROWS + row) * C::QS + col) = qc[i];
+            }
+        };
+        // log-sum-exps: loads issued one step before they are needed
+        unsigned lse_v = kSentinel32;
+        auto lse_issue = [&](int u) __attribute__((always_inline)) {
+            if (u >= 0 && lane < ROWS) lse_v = ld32(a.lse + (size_t)u * ROWS + lane);
+        };
+        auto lse_take = [&](int u, int pb) __attribute__((always_inline)) {
+            bool miss = lane < ROWS && lse_v == kSentinel32;
+            if (__ballot(miss) != 0) {
+                const unsigned long long t0 = wall_clock64();
+                while (true) {
+                    __builtin_amdgcn_s_sleep(2);
+                    if (miss) lse_v = ld32(a.lse + (size_t)u * ROWS + lane);
+                    miss = lane < ROWS && lse_v == kSentinel32;
+                    if (__ballot(miss) == 0) break;
+                    if (wall_clock64() - t0 > kSpinTicks) {
+                        if (lane == 0) __hip_atomic_store(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        break;
+                    }
+                }
+            }
+            if (lane < ROWS) lse_s[pb * ROWS + lane] = __uint_as_float(lse_v);
+        };
+        // the workgroup's partial of unit u: combine the streaming waves' rows
+        auto publish = [&](int u, int pb) __attribute__((always_inline)) {
+            if (lane < ROWS) {
+                float mm = red[(pb * SW + 0) * ROWS + lane].x, ss = red[(pb * SW + 0) * ROWS + lane].y;
+                for (int x = 1; x < SW; ++x)
+                    combine(mm, ss, red[(pb * SW + x) * ROWS + lane].x, red[(pb * SW + x) * ROWS + lane].y, c);
+                st64(a.part + ((size_t)u * a.g + rank) * ROWS + lane, mm, ss);
+            }
+        };
+
+        q_issue(unit_of(0));
+        q_store(0);
+        q_issue(unit_of(1));
+        lse_issue(unit_of(1 - D));
+        __syncthreads();
+        for (int it = 0; it < n_steps; ++it) {
+            const int pb = it & 1;
+            const int fu = it - D;
+            if (fu >= 0 && fu < n_units) lse_take(unit_of(fu), pb);
+            lse_issue(unit_of(it + 1 - D));
+            q_store((it + 1) & 1);
+            q_issue(unit_of(it + 2));
+            __syncthreads();
+            if (it < n_units) publish(unit_of(it), pb);
+        }
+    }
+    __syncthreads();
+    for (int x = tid; x < a.N * nkeys; x += kThreads) {
+        const int jj = x / nkeys, k = x - (x / nkeys) * nkeys;
+        a.Tg[((size_t)group * a.N + jj) * a.M + r0 + k] = Trun[jj * KRP + k];
+    }
+}
+
+template <class C>
+const void* kernel_ptr() {
+    return (const void*)&score_kernel<C>;
+}
+
+// The instantiation for head-group size G (nullptr when unsupported).
+template <int D, bool BF, int NH, int TPW>
+const void* pick_g(int G) {
+    switch (G) {
+        case 1: return kernel_ptr<Cfg<D, BF, NH, 1, TPW>>();
+        case 2: return kernel_ptr<Cfg<D, BF, NH, 2, TPW>>();
+        case 4: return kernel_ptr<Cfg<D, BF, NH, 4, TPW>>();
+        case 8: return kernel_ptr<Cfg<D, BF, NH, 8, TPW>>();
+        case 16: return kernel_ptr<Cfg<D, BF, NH, 16, TPW>>();
+        case 32:
+            if constexpr (NH == 2) return kernel_ptr<Cfg<D, BF, 2, 32, TPW>>();
+            return nullptr;
+        default: return nullptr;
+    }
+}
+
+// The instantiation for (rows, G, tiles per wave) of one operand type and
+// head dimension; TPW is tiles_per_wave(BF, D) or one more.
+template <int D, bool BF>
+const void* pick_kernel_for(int rows, int G, int tpw) {
+    constexpr int T0 = tiles_per_wave(BF, D);
+    if (tpw == T0) return rows == 32 ? pick_g<D, BF, 2, T0>(G) : pick_g<D, BF, 1, T0>(G);
+    if (tpw == T0 + 1) return rows == 32 ? pick_g<D, BF, 2, T0 + 1>(G) : pick_g<D, BF, 1, T0 + 1>(G);
+    return nullptr;
+}
+
+}  // namespace sp
