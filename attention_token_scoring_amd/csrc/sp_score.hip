@@ -10,43 +10,62 @@ namespace sp {
 // partial and log-sum-exp slot to the sentinel, the error word), and compute
 // for every unit and query row the share of the look-ahead keys M..M+N-1 in the
 // row's softmax denominator (row j sees look-ahead key t iff t <= j), as a raw
-// max and a sum of exp2((x - max) * c). One wave per unit, one lane per row.
+// max and a sum of exp2((x - max) * c). One 256-thread block per unit: one
+// thread per (row, look-ahead key) dot product, 16-byte loads.
 template <bool BF16>
-__global__ __launch_bounds__(64) void score_prep_kernel(ScoreArgs a, int rows) {
-    const int u = blockIdx.x, lane = threadIdx.x;
-    if (u == 0 && lane == 0) *a.err = 0;
-    unsigned long long* slots = (unsigned long long*)(a.part + (size_t)u * a.g * rows);
-    for (int x = lane; x < a.g * rows; x += 64) slots[x] = kSentinel;
-    if (lane < rows) ((unsigned*)a.lse)[(size_t)u * rows + lane] = kSentinel32;
-    if (lane >= rows) return;
-    const int j = lane / a.G, hl = lane - (lane / a.G) * a.G;
-    float m = -INFINITY, s = 0.f;
-    if (j < a.N) {
-        const int l = u / a.Hkv, kvh = u - (u / a.Hkv) * a.Hkv;
-        const int esz = BF16 ? 2 : 4;
-        const long long qrow = ((long long)l * a.H + (long long)kvh * a.G + hl) * a.N + j;
-        const char* q = (const char*)a.Q + qrow * a.d * esz;
-        const char* kp = (const char*)a.K + ((long long)u * a.plane_stride + (long long)a.M * a.d) * esz;
-        float x[32];
-        for (int t = 0; t <= j; ++t) {
-            float acc = 0.f;
-            for (int e = 0; e < a.d; ++e) {
-                float qv, kv;
-                if (BF16) {
-                    qv = __uint_as_float((unsigned)((const unsigned short*)q)[e] << 16);
-                    kv = __uint_as_float((unsigned)((const unsigned short*)kp)[(long long)t * a.d + e] << 16);
-                } else {
-                    qv = ((const float*)q)[e];
-                    kv = ((const float*)kp)[(long long)t * a.d + e];
-                }
-                acc = fmaf(qv, kv, acc);
-            }
-            x[t] = acc;
-            m = fmaxf(m, acc);
+__device__ __forceinline__ float dot16(uint4 q, uint4 k, float acc) {
+    if constexpr (BF16) {
+        const unsigned qa[4] = {q.x, q.y, q.z, q.w}, ka[4] = {k.x, k.y, k.z, k.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc = fmaf(__uint_as_float(qa[i] << 16), __uint_as_float(ka[i] << 16), acc);
+            acc = fmaf(__uint_as_float(qa[i] & 0xffff0000u), __uint_as_float(ka[i] & 0xffff0000u), acc);
         }
-        for (int t = 0; t <= j; ++t) s += exp2_hw(fmaf(x[t], a.c, -m * a.c));
+    } else {
+        acc = fmaf(__uint_as_float(q.x), __uint_as_float(k.x), acc);
+        acc = fmaf(__uint_as_float(q.y), __uint_as_float(k.y), acc);
+        acc = fmaf(__uint_as_float(q.z), __uint_as_float(k.z), acc);
+        acc = fmaf(__uint_as_float(q.w), __uint_as_float(k.w), acc);
     }
-    a.tail[(size_t)u * rows + lane] = make_float2(m, s);
+    return acc;
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void score_prep_kernel(ScoreArgs a, int rows) {
+    __shared__ float logit[32][33];  // [row][look-ahead key]
+    const int u = blockIdx.x, tid = threadIdx.x;
+    if (u == 0 && tid == 0) *a.err = 0;
+    // this unit's g * rows partial slots, two per 16-byte store
+    uint4* slots = (uint4*)(a.part + (size_t)u * a.g * rows);
+    for (int x = tid; x < a.g * rows / 2; x += 256) slots[x] = make_uint4(~0u, ~0u, ~0u, ~0u);
+    if (tid < rows) ((unsigned*)a.lse)[(size_t)u * rows + tid] = kSentinel32;
+
+    const int l = u / a.Hkv, kvh = u % a.Hkv;
+    constexpr int esz = BF16 ? 2 : 4;
+    const char* kp = (const char*)a.K + ((long long)u * a.plane_stride + (long long)a.M * a.d) * esz;
+    const int n16 = a.d * esz / 16;
+    for (int x = tid; x < rows * a.N; x += 256) {
+        const int row = x / a.N, t = x % a.N;
+        const int j = row / a.G, hl = row % a.G;
+        if (j < a.N && t <= j) {
+            const long long qrow = ((long long)l * a.H + (long long)kvh * a.G + hl) * a.N + j;
+            const uint4* q = (const uint4*)((const char*)a.Q + qrow * a.d * esz);
+            const uint4* k = (const uint4*)(kp + (long long)t * a.d * esz);
+            float acc = 0.f;
+            for (int e = 0; e < n16; ++e) acc = dot16<BF16>(q[e], k[e], acc);
+            logit[row][t] = acc;
+        }
+    }
+    __syncthreads();
+    if (tid < rows) {
+        const int j = tid / a.G;
+        float m = -INFINITY, s = 0.f;
+        if (j < a.N) {
+            for (int t = 0; t <= j; ++t) m = fmaxf(m, logit[tid][t]);
+            for (int t = 0; t <= j; ++t) s += exp2_hw(fmaf(logit[tid][t], a.c, -m * a.c));
+        }
+        a.tail[(size_t)u * rows + tid] = make_float2(m, s);
+    }
 }
 
 // importance_i = (1/N) sum_j exp2(max_group Tg[group][j][i])
@@ -115,9 +134,9 @@ hipError_t launch_score(const ScorePlan& p, const sp_score_desc& d, const void* 
     if (e != hipSuccess) return e;
 
     if (d.dtype == SP_BF16)
-        hipLaunchKernelGGL(score_prep_kernel<true>, dim3(p.units), dim3(64), 0, stream, a, p.rows);
+        hipLaunchKernelGGL(score_prep_kernel<true>, dim3(p.units), dim3(256), 0, stream, a, p.rows);
     else
-        hipLaunchKernelGGL(score_prep_kernel<false>, dim3(p.units), dim3(64), 0, stream, a, p.rows);
+        hipLaunchKernelGGL(score_prep_kernel<false>, dim3(p.units), dim3(256), 0, stream, a, p.rows);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     void* args[] = {&a};

@@ -120,24 +120,25 @@ __device__ __forceinline__ unsigned ld32(const void* p) {
 }
 
 // Parked logits: y = (log2-domain logit) - (row reference) <= 0 as a 16-bit
-// fixed-point code round(-y * 2^11), clamped to [0, 65535] (y in [-32, 0]).
-// The decoded p = exp2(y + offset) then carries a relative error of at most
-// ln2 * 2^-12 (1.7e-4) whenever y >= -32; below that p < 2^-32 and the clamp
-// changes it by less than that. Two codes share one 32-bit word, which travels
-// by value (bit-casting an element of a vector-typed value in place is not
-// reliable with this compiler).
-constexpr float kCodeScale = 2048.f;
-__device__ __forceinline__ unsigned encode_y(float y) {
-    return (unsigned)fminf(fmaf(y, -kCodeScale, 0.5f), 65535.f);
-}
-__device__ __forceinline__ int pack_y2(float lo, float hi) {
-    return (int)(encode_y(lo) | (encode_y(hi) << 16));
+// unsigned-normalised code of -y / 32 (v_cvt_pknorm_u16_f32 rounds and clamps
+// to [0, 65535]): a step of 32/65535 (about 2^-11) in log2 units over
+// y in [-32, 0]. The decoded p = exp2(y + offset) then carries a relative error
+// of at most ln2 * 16/65535 (1.7e-4) whenever y >= -32; below that p < 2^-32
+// and the clamp changes it by less than that. Two codes share one 32-bit word,
+// which travels by value (bit-casting an element of a vector-typed value in
+// place is not reliable with this compiler).
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+constexpr float kCodeRange = 32.f;
+// u = -y / kCodeRange, in [0, 1] for y in [-kCodeRange, 0]
+__device__ __forceinline__ int pack_u2(float u_lo, float u_hi) {
+    return __builtin_bit_cast(int, __builtin_amdgcn_cvt_pknorm_u16(u_lo, u_hi));
 }
 // (lo, hi) codes of a word -> log2 values plus a common offset
 __device__ __forceinline__ void unpack_y2(int word, float off, float& lo, float& hi) {
     const unsigned w = (unsigned)word;
-    lo = fmaf((float)(w & 0xffffu), -1.f / kCodeScale, off);
-    hi = fmaf((float)(w >> 16), -1.f / kCodeScale, off);
+    constexpr float step = -kCodeRange / 65535.f;
+    lo = fmaf((float)(w & 0xffffu), step, off);
+    hi = fmaf((float)(w >> 16), step, off);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -227,7 +228,7 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
     // ---------------------------------------------------------------------------
     if ((int)blockIdx.x >= nstream) {
         constexpr int SUBS = 64 / ROWS;
-        constexpr int B = 16;
+        constexpr int B = 40;  // ranks polled per lane at once (one round trip for g <= SUBS * B)
         const int cw = ((int)blockIdx.x - nstream) * kWaves + w;
         const int ncw = ((int)gridDim.x - nstream) * kWaves;
         const int row = lane % ROWS, sub = lane / ROWS;
@@ -243,20 +244,20 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
             const unsigned long long t0 = wall_clock64();
             for (int k0 = sub; k0 < a.g; k0 += SUBS * B) {
                 unsigned long long v[B];
-                unsigned pend = 0;  // bit x: rank k0 + SUBS x not seen yet
+                unsigned long long pend = 0;  // bit x: rank k0 + SUBS x not seen yet
 #pragma unroll
                 for (int x = 0; x < B; ++x) {
                     v[x] = kSentinel;
-                    if (k0 + SUBS * x < a.g) pend |= 1u << x;
+                    if (k0 + SUBS * x < a.g) pend |= 1ull << x;
                 }
                 while (true) {
 #pragma unroll
                     for (int x = 0; x < B; ++x)
                         if ((pend >> x) & 1) v[x] = ld64(slot + (size_t)(k0 + SUBS * x) * ROWS);
-                    unsigned np = 0;
+                    unsigned long long np = 0;
 #pragma unroll
                     for (int x = 0; x < B; ++x)
-                        if (((pend >> x) & 1) && v[x] == kSentinel) np |= 1u << x;
+                        if (((pend >> x) & 1) && v[x] == kSentinel) np |= 1ull << x;
                     pend = np;
                     if (__ballot(pend != 0) == 0) break;
                     __builtin_amdgcn_s_sleep(2);
@@ -419,8 +420,9 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
                 int wd[2 * NH];
 #pragma unroll
                 for (int hf = 0; hf < NH; ++hf) {
-                    wd[2 * hf] = pack_y2(acc[t][hf][0], acc[t][hf][1]);
-                    wd[2 * hf + 1] = pack_y2(acc[t][hf][2], acc[t][hf][3]);
+                    constexpr float k = -1.f / kCodeRange;
+                    wd[2 * hf] = pack_u2(acc[t][hf][0] * k, acc[t][hf][1] * k);
+                    wd[2 * hf + 1] = pack_u2(acc[t][hf][2] * k, acc[t][hf][3] * k);
                 }
                 if constexpr (NH == 2) *(int4*)dst = make_int4(wd[0], wd[1], wd[2], wd[3]);
                 else *(int2*)dst = make_int2(wd[0], wd[1]);
@@ -506,8 +508,12 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
     } else {
         // ======================= control wave =======================
         // Q of one unit: ROWS rows of KB bytes, 16 bytes per lane and load.
-        i32x4 qc[C::QLD];
-        auto q_issue = [&](int u) __attribute__((always_inline)) {
+        // Two register sets: Q of unit it+1 is stored to LDS at step it from
+        // loads issued at step it-2 (the loads of this CU's control wave queue
+        // behind its K stream, so they get two steps).
+        i32x4 qc[2][C::QLD];
+        auto q_issue = [&](auto Sc, int u) __attribute__((always_inline)) {
+            constexpr int S = decltype(Sc)::value;
 #pragma unroll
             for (int i = 0; i < C::QLD; ++i) {
                 const int e = (i * 64 + lane) * 16;
@@ -516,33 +522,39 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
                 if (u >= 0 && j < a.N) {
                     const int l = u / a.Hkv, kvh = u % a.Hkv;
                     const long long qrow = ((long long)l * a.H + (long long)kvh * G + hl) * a.N + j;
-                    qc[i] = *(const i32x4*)((const char*)a.Q + qrow * C::KB + col);
+                    qc[S][i] = *(const i32x4*)((const char*)a.Q + qrow * C::KB + col);
                 } else {
-                    qc[i] = i32x4{0, 0, 0, 0};
+                    qc[S][i] = i32x4{0, 0, 0, 0};
                 }
             }
         };
-        auto q_store = [&](int buf) __attribute__((always_inline)) {
+        auto q_store = [&](auto Sc, int buf) __attribute__((always_inline)) {
+            constexpr int S = decltype(Sc)::value;
 #pragma unroll
             for (int i = 0; i < C::QLD; ++i) {
                 const int e = (i * 64 + lane) * 16;
                 const int row = e / C::KB, col = e % C::KB;
-                *(i32x4*)(qlds + (buf * ROWS + row) * C::QS + col) = qc[i];
+                *(i32x4*)(qlds + (buf * ROWS + row) * C::QS + col) = qc[S][i];
             }
         };
-        // log-sum-exps: loads issued one step before they are needed
-        unsigned lse_v = kSentinel32;
-        auto lse_issue = [&](int u) __attribute__((always_inline)) {
-            if (u >= 0 && lane < ROWS) lse_v = ld32(a.lse + (size_t)u * ROWS + lane);
+        // log-sum-exps: loads issued kLseAhead steps before they are needed
+        // (a unit's log-sum-exps appear a few microseconds after the last of
+        // its g workgroups has published; one step later they are there)
+        constexpr int kLseAhead = 1;
+        unsigned lse_v[2] = {kSentinel32, kSentinel32};
+        auto lse_issue = [&](auto Sc, int u) __attribute__((always_inline)) {
+            constexpr int S = decltype(Sc)::value;
+            if (u >= 0 && lane < ROWS) lse_v[S] = ld32(a.lse + (size_t)u * ROWS + lane);
         };
-        auto lse_take = [&](int u, int pb) __attribute__((always_inline)) {
-            bool miss = lane < ROWS && lse_v == kSentinel32;
+        auto lse_take = [&](auto Sc, int u, int pb) __attribute__((always_inline)) {
+            constexpr int S = decltype(Sc)::value;
+            bool miss = lane < ROWS && lse_v[S] == kSentinel32;
             if (__ballot(miss) != 0) {
                 const unsigned long long t0 = wall_clock64();
                 while (true) {
                     __builtin_amdgcn_s_sleep(2);
-                    if (miss) lse_v = ld32(a.lse + (size_t)u * ROWS + lane);
-                    miss = lane < ROWS && lse_v == kSentinel32;
+                    if (miss) lse_v[S] = ld32(a.lse + (size_t)u * ROWS + lane);
+                    miss = lane < ROWS && lse_v[S] == kSentinel32;
                     if (__ballot(miss) == 0) break;
                     if (wall_clock64() - t0 > kSpinTicks) {
                         if (lane == 0) __hip_atomic_store(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -550,7 +562,7 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
                     }
                 }
             }
-            if (lane < ROWS) lse_s[pb * ROWS + lane] = __uint_as_float(lse_v);
+            if (lane < ROWS) lse_s[pb * ROWS + lane] = __uint_as_float(lse_v[S]);
         };
         // the workgroup's partial of unit u: combine the streaming waves' rows
         auto publish = [&](int u, int pb) __attribute__((always_inline)) {
@@ -561,21 +573,34 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
                 st64(a.part + ((size_t)u * a.g + rank) * ROWS + lane, mm, ss);
             }
         };
-
-        q_issue(unit_of(0));
-        q_store(0);
-        q_issue(unit_of(1));
-        lse_issue(unit_of(1 - D));
-        __syncthreads();
-        for (int it = 0; it < n_steps; ++it) {
-            const int pb = it & 1;
+        // Step it (parity P): take unit it-D's log-sum-exps (loaded kLseAhead
+        // steps ago) into lse_s[P] and load unit it+kLseAhead-D's; stage Q of
+        // unit it+1 and load Q of unit it+3; after the barrier publish unit
+        // it's partial.
+        auto ctrl_step = [&](auto Pc, int it) __attribute__((always_inline)) {
+            constexpr int P = decltype(Pc)::value;
+            constexpr std::integral_constant<int, P> sp{};
+            constexpr std::integral_constant<int, 1 - P> so{};
+            constexpr std::integral_constant<int, (P + kLseAhead) & 1> sl{};
             const int fu = it - D;
-            if (fu >= 0 && fu < n_units) lse_take(unit_of(fu), pb);
-            lse_issue(unit_of(it + 1 - D));
-            q_store((it + 1) & 1);
-            q_issue(unit_of(it + 2));
+            if (fu >= 0 && fu < n_units) lse_take(sp, unit_of(fu), P);
+            lse_issue(sl, unit_of(it + kLseAhead - D));
+            q_store(so, 1 - P);             // Q of unit it+1 -> LDS buffer (it+1)&1
+            q_issue(so, unit_of(it + 3));
             __syncthreads();
-            if (it < n_units) publish(unit_of(it), pb);
+            if (it < n_units) publish(unit_of(it), P);
+        };
+
+        q_issue(std::integral_constant<int, 0>{}, unit_of(0));
+        q_store(std::integral_constant<int, 0>{}, 0);
+        q_issue(std::integral_constant<int, 1>{}, unit_of(1));
+        q_issue(std::integral_constant<int, 0>{}, unit_of(2));
+        lse_issue(std::integral_constant<int, 0>{}, unit_of(-D));
+        if constexpr (kLseAhead == 2) lse_issue(std::integral_constant<int, 1>{}, unit_of(1 - D));
+        __syncthreads();
+        for (int it = 0; it < n_steps; it += 2) {
+            ctrl_step(std::integral_constant<int, 0>{}, it);
+            ctrl_step(std::integral_constant<int, 1>{}, it + 1);
         }
     }
     __syncthreads();
