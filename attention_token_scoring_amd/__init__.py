@@ -28,7 +28,7 @@ SP_SELECT_TOPK, SP_SELECT_MASS = 0, 1
 
 EXPORTED = ("sp_score", "sp_score_varlen", "sp_select", "sp_select_varlen",
             "sp_score_workspace_bytes", "sp_select_workspace_bytes", "sp_score_plan",
-            "sp_status_string")
+            "sp_status_string", "sp_profile_score_kernel")
 
 
 class SpError(RuntimeError):
@@ -76,7 +76,9 @@ def load_library():
     lib.sp_select.argtypes = [vp, i32, P(SelectParams), i32, vp, vp, vp, vp, sz, vp]
     lib.sp_select_varlen.argtypes = [vp, i32, P(ctypes.c_int64), P(ctypes.c_int32),
                                      P(SelectParams), vp, vp, vp, vp, sz, vp]
-    for name in ("sp_score_plan", "sp_score", "sp_score_varlen", "sp_select", "sp_select_varlen"):
+    lib.sp_profile_score_kernel.argtypes = [vp, vp]
+    for name in ("sp_score_plan", "sp_score", "sp_score_varlen", "sp_select", "sp_select_varlen",
+                 "sp_profile_score_kernel"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -145,6 +147,15 @@ def sp_score_plan(desc: ScoreDesc, M: int) -> dict:
     _check(load_library().sp_score_plan(ctypes.byref(desc), int(M), info), "sp_score_plan")
     keys = ("grid", "g", "ngroups", "keys_per_wg", "rows", "units", "cus", "defer")
     return {k: int(info[i]) for i, k in enumerate(keys)}
+
+
+def sp_profile_score_kernel(before=None, after=None):
+    """Profiling aid: record torch.cuda.Event `before`/`after` (already
+    recorded once, so that they exist) around each cooperative scoring kernel
+    launched by this thread; call with no arguments to stop."""
+    b = ctypes.c_void_p(before.cuda_event) if before is not None else None
+    a = ctypes.c_void_p(after.cuda_event) if after is not None else None
+    _check(load_library().sp_profile_score_kernel(b, a), "sp_profile_score_kernel")
 
 
 def _workspace(nbytes: int, device, workspace=None):

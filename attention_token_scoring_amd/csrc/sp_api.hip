@@ -231,6 +231,12 @@ size_t sp_score_workspace_bytes(const sp_score_desc* desc, int64_t max_prompt_le
     return workspace_bound(*desc, max_prompt_len, device_cus());
 }
 
+sp_status sp_profile_score_kernel(void* before, void* after) {
+    if ((before == nullptr) != (after == nullptr)) return SP_EINVAL;
+    sp::set_profile_events((hipEvent_t)before, (hipEvent_t)after);
+    return SP_OK;
+}
+
 sp_status sp_score_plan(const sp_score_desc* desc, int32_t M, int32_t info[8]) {
     sp_status s = check_desc(desc);
     if (s != SP_OK) return s;

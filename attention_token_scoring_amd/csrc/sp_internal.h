@@ -104,6 +104,10 @@ struct SelectParamsDev {
     float last_mult;
 };
 
+// Events the calling thread wants recorded around each cooperative scoring
+// kernel launch (profiling aid; both null when unset).
+void set_profile_events(hipEvent_t before, hipEvent_t after);
+
 // Cooperative scoring kernels, one translation unit per operand type and head
 // dimension: the instantiation for (rows, G, tiles per wave), or nullptr.
 const void* score_kernel_bf16_d128(int rows, int G, int tpw);

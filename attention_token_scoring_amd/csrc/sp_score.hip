@@ -96,6 +96,13 @@ static const void* pick_kernel(int dtype, int d, int rows, int G, int tpw) {
     return nullptr;
 }
 
+static thread_local hipEvent_t t_ev_before = nullptr, t_ev_after = nullptr;
+
+void set_profile_events(hipEvent_t before, hipEvent_t after) {
+    t_ev_before = before;
+    t_ev_after = after;
+}
+
 // One request: prep (reset synchronisation state, look-ahead statistics),
 // cooperative scoring, finalize.
 hipError_t launch_score(const ScorePlan& p, const sp_score_desc& d, const void* Q, const void* K,
@@ -140,8 +147,16 @@ hipError_t launch_score(const ScorePlan& p, const sp_score_desc& d, const void* 
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     void* args[] = {&a};
+    if (t_ev_before) {
+        e = hipEventRecord(t_ev_before, stream);
+        if (e != hipSuccess) return e;
+    }
     e = hipLaunchCooperativeKernel(fn, dim3(p.grid), dim3(kThreads), args, (unsigned)p.lds.total, stream);
     if (e != hipSuccess) return e;
+    if (t_ev_after) {
+        e = hipEventRecord(t_ev_after, stream);
+        if (e != hipSuccess) return e;
+    }
     hipLaunchKernelGGL(score_finalize_kernel, dim3((M + 255) / 256), dim3(256), 0, stream,
                        (const float*)a.Tg, p.ngroups, d.N, M, importance);
     return hipGetLastError();

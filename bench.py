@@ -10,12 +10,17 @@ synchronisations; prints one JSON line. Throughput = prompt tokens per second.
 Several copies of K are rotated so that no step finds its keys in the 256 MB
 Infinity Cache left over from the previous one.
 
-The roofline block reports the scoring kernel's algorithmic bytes (one read
-of K and Q) over its average duration, measured with HIP events around every
-sp_score call on the stream the kernels run on. HBM traffic comes from the
-rocprofv3 counter summary under profiles/ when it was taken on the current
-kernel source (else null). The CPU baseline times the oracle on the host
-cores on a bounded sample (a subset of layers, scaled to the full workload).
+The roofline block reports the dominant kernel's algorithmic bytes (one read
+of K and Q) over its average duration. The library records HIP events on the
+scoring stream immediately before and after each launch of its cooperative
+scoring kernel (sp_profile_score_kernel), so the duration excludes the small
+prep and finalize kernels. HBM traffic comes from the rocprofv3 counter
+summary under profiles/ when it was taken on the current kernel sources
+(else null); `--traffic-from FETCH_DB WRITE_DB` writes that summary from two
+rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE) that
+included `--copy-probe-mib` (the copy calibrates the counters' units). The CPU
+baseline times the oracle on the host cores on a bounded sample (a subset of
+layers, scaled to the full workload).
 """
 from __future__ import annotations
 
@@ -44,19 +49,65 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="spec8b_m32k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-layers", type=int, default=8,
-                    help="layers of the workload the CPU baseline scores")
+    ap.add_argument("--cpu-layers", type=int, default=1 << 30,
+                    help="layers of the workload the CPU baseline scores (default: all)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one device copy of this size (counter calibration)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
+                    help="write the traffic summary from two rocprofv3 --pmc databases and exit")
     return ap.parse_args()
 
 
+SCORE_KERNEL = "sp::score_kernel<"
+# the calibration probe is the run's only elementwise add
+PROBE_KERNEL_HINTS = ("elementwise", "add")
+
+
 def kernel_source_sha() -> str:
+    """Fingerprint of every source the scoring kernels and their plan come from."""
+    csrc = os.path.join(ROOT, "attention_token_scoring_amd", "csrc")
+    names = sorted(n for n in os.listdir(csrc)
+                   if n.startswith("sp_score") or n in ("sp_internal.h", "sp_api.hip"))
     h = hashlib.sha256()
-    for name in ("sp_score.hip", "sp_internal.h"):
-        with open(os.path.join(ROOT, "attention_token_scoring_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+    for name in names:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
+
+
+def pmc_per_dispatch(db_path: str, counter: str):
+    """[(kernel name, counter value summed over the dispatch's instances)] in
+    dispatch order, from a rocprofv3 database."""
+    import sqlite3
+    con = sqlite3.connect(db_path)
+    cur = con.cursor()
+    rows = cur.execute(
+        "select kernel_name, sum(value) from counters_collection where counter_name = ? "
+        "group by dispatch_id order by dispatch_id", (counter,)).fetchall()
+    return [(r[0], float(r[1])) for r in rows]
+
+
+def write_traffic(fetch_db: str, write_db: str, workload: str, copy_mib: int):
+    """HBM bytes per scoring-kernel launch from FETCH_SIZE / WRITE_SIZE (KiB per
+    dispatch), each scaled by what the same counter reads for the copy probe
+    (copy_mib MiB read and written)."""
+    out = {"workload": workload, "source_sha": kernel_source_sha(), "copy_probe_mib": copy_mib}
+    for key, db, counter in (("fetch", fetch_db, "FETCH_SIZE"), ("write", write_db, "WRITE_SIZE")):
+        rows = pmc_per_dispatch(db, counter)
+        score = [v for n, v in rows if SCORE_KERNEL in n]
+        probes = [v for n, v in rows if all(h in n.lower() for h in PROBE_KERNEL_HINTS)]
+        if not score or len(probes) != 1:
+            raise SystemExit(f"{db}: no {counter} for the scoring kernel, or not exactly one probe")
+        copy_kib = probes[0]
+        factor = (copy_mib * 1024.0) / copy_kib
+        out[key] = {"counter": counter, "score_kib_per_dispatch": float(np.mean(score)),
+                    "dispatches": len(score), "copy_probe_kib": copy_kib, "scale": factor,
+                    "bytes_per_launch": float(np.mean(score)) * 1024.0 * factor}
+    out["bytes_per_launch"] = out["fetch"]["bytes_per_launch"] + out["write"]["bytes_per_launch"]
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
 
 
 def load_traffic(workload: str):
@@ -89,28 +140,40 @@ def workload_desc(w, sel) -> dict:
     return d
 
 
-def cpu_baseline(w, sel, Qh, Kh, layers: int):
-    """The oracle as it is, on the host cores: score the first `layers` layers
-    of the workload and select on the result; scale the scoring time to all L
-    layers (its cost is linear in L)."""
+def cpu_baseline(w, sel, Qh, Kh, layers: int, min_seconds: float = 10.0):
+    """The oracle as it is, on the host cores: score `layers` layers of the
+    workload (all of them by default) and select on the result, repeated until
+    about min_seconds of CPU work; the scoring time is scaled to all L layers
+    (its cost is linear in L)."""
     import oracle
     threads = os.cpu_count() or 1
     layers = max(1, min(layers, w.L))
-    t0 = time.perf_counter()
-    imp = oracle.score(Qh[:layers], Kh[:layers], nthreads=threads)
-    t1 = time.perf_counter()
-    oracle.select(imp.astype(np.float32), **oracle.select_params(sel))
-    t2 = time.perf_counter()
-    t_full = (t1 - t0) * (w.L / layers) + (t2 - t1)
+    t_score = t_sel = 0.0
+    reps = 0
+    while t_score + t_sel < min_seconds and reps < 100:
+        t0 = time.perf_counter()
+        imp = oracle.score(Qh[:layers], Kh[:layers], nthreads=threads)
+        t1 = time.perf_counter()
+        oracle.select(imp.astype(np.float32), **oracle.select_params(sel))
+        t2 = time.perf_counter()
+        t_score += t1 - t0
+        t_sel += t2 - t1
+        reps += 1
+    t_full = (t_score * (w.L / layers) + t_sel) / reps
     return {"value": w.M / t_full, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{w.name}: oracle scoring of layers 0-{layers - 1} of {w.L} "
-                      f"({(t1 - t0):.2f} s, scaled x{w.L / layers:g} to all layers) plus "
-                      f"selection ({(t2 - t1) * 1e3:.1f} ms); fp64, OpenMP over "
+            "sample": f"{w.name}: {reps} repetitions of oracle scoring of layers 0-{layers - 1} "
+                      f"of {w.L} ({t_score:.1f} s in all"
+                      + (f", scaled x{w.L / layers:g} to all layers" if layers < w.L else "")
+                      + f") plus selection ({t_sel * 1e3:.1f} ms in all); fp64, OpenMP over "
                       f"{threads} threads"}
 
 
 def main():
     args = parse()
+    if args.traffic_from:
+        write_traffic(args.traffic_from[0], args.traffic_from[1], args.workload,
+                      args.copy_probe_mib or 1024)
+        return
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU only; --gpus must be 1", file=sys.stderr)
         sys.exit(2)
@@ -152,19 +215,25 @@ def main():
     plan = sp.sp_score_plan(desc, M)
 
     if args.copy_probe_mib:
+        # counter calibration: one elementwise kernel that reads and writes
+        # exactly copy_probe_mib MiB
         n = args.copy_probe_mib << 20
-        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        a = torch.empty(n, dtype=torch.uint8, device=dev)  # contents do not matter
         b = torch.empty(n, dtype=torch.uint8, device=dev)
-        b.copy_(a)
+        torch.add(a, 1, out=b)
         torch.cuda.synchronize()
         del a, b
 
-    def step(i, ev=None):
+    def step(i, ev=None, kev=None):
+        if kev is not None:
+            sp.sp_profile_score_kernel(kev[0], kev[1])
         if ev is not None:
             ev[0].record()
         sp.sp_score(Q, Ks[i % copies], M, out=imp, workspace=ws)
         if ev is not None:
             ev[1].record()
+        if kev is not None:
+            sp.sp_profile_score_kernel()
         sp.sp_select(imp, params, kept_idx=kept, pos_ids=pos, n_kept=nk)
 
     for i in range(args.warmup):
@@ -172,13 +241,20 @@ def main():
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
+    # events the library records around the cooperative scoring kernel; torch
+    # creates an event on its first record
+    kevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(args.steps)]
+    for a, b in kevs:
+        a.record()
+        b.record()
     t_begin = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     t_begin.record()
     for i in range(args.steps):
-        step(i, evs[i])
+        step(i, evs[i], kevs[i])
     t_end.record()
     torch.cuda.synchronize()
     w1 = time.perf_counter()
@@ -188,8 +264,10 @@ def main():
     ms_per_step = ms_wall / args.steps
     score_ms = [a.elapsed_time(b) for a, b in evs]
     score_avg_s = float(np.mean(score_ms)) / 1e3
+    kernel_ms = [a.elapsed_time(b) for a, b in kevs]
+    kernel_avg_s = float(np.mean(kernel_ms)) / 1e3
     alg_bytes = (w.L * w.Hkv * (M + w.N) * w.d + w.L * w.H * w.N * w.d) * (2 if w.dtype else 4)
-    achieved = alg_bytes / score_avg_s / 1e9
+    achieved = alg_bytes / kernel_avg_s / 1e9
     traffic = load_traffic(w.name)
 
     out = {
@@ -208,7 +286,9 @@ def main():
         "config": workload_desc(w, sel),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic},
-        "detail": {"score_ms_avg": score_avg_s * 1e3, "score_ms_min": float(np.min(score_ms)),
+        "detail": {"score_kernel_ms_avg": kernel_avg_s * 1e3,
+                   "score_kernel_ms_min": float(np.min(kernel_ms)),
+                   "sp_score_ms_avg": score_avg_s * 1e3, "sp_score_ms_min": float(np.min(score_ms)),
                    "select_and_gaps_ms_avg": ms_total_ev / args.steps - score_avg_s * 1e3,
                    "ms_per_step_events": ms_total_ev / args.steps,
                    "alg_bytes_per_score_launch": alg_bytes, "k_copies": copies,

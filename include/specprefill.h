@@ -187,6 +187,19 @@ const char* sp_status_string(sp_status status);
  */
 sp_status sp_score_plan(const sp_score_desc* desc, int32_t M, int32_t info[8]);
 
+/*
+ * Profiling aid, not part of the scoring computation. While set, every
+ * sp_score / sp_score_varlen call made by the calling thread records the HIP
+ * events `before` and `after` (hipEvent_t handles created by the caller) on
+ * its stream immediately before and after each launch of the cooperative
+ * scoring kernel, so that hipEventElapsedTime gives that kernel's duration
+ * apart from the small kernels around it (for sp_score_varlen the events end
+ * up around the last request's kernel). Pass NULL, NULL to stop. The setting
+ * is per thread; the library never creates, waits on or destroys the events.
+ * Returns SP_EINVAL if exactly one of the two is NULL.
+ */
+sp_status sp_profile_score_kernel(void* before, void* after);
+
 #ifdef __cplusplus
 }
 #endif

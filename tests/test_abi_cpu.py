@@ -142,3 +142,9 @@ def test_select_rejects_null_and_sizes(lib):
     assert lib.sp_select_varlen(FAKE, 2, cu, None, ctypes.byref(p), FAKE, FAKE, FAKE, None, 0,
                                 None) == sp.SP_EINVAL
     assert sp.sp_select_workspace_bytes(1, 100, p) == 0
+
+
+def test_profile_events_need_both_or_neither(lib):
+    assert lib.sp_profile_score_kernel(FAKE, None) == sp.SP_EINVAL
+    assert lib.sp_profile_score_kernel(None, FAKE) == sp.SP_EINVAL
+    assert lib.sp_profile_score_kernel(None, None) == sp.SP_OK
