@@ -45,7 +45,10 @@ inline ScoreLds score_lds_layout(int nbk, int tpw, int rows, int row_bytes, int 
     l.ref = l.bank + up(nbk * kStreamWaves * tpw * 64 * nh * 8);
     l.q = l.ref + up(nbk * kStreamWaves * rows * 4);
     l.trun = l.q + up(2 * rows * (row_bytes + 16));
-    l.red = l.trun + up(N * row_stride(KR) * 4);
+    // (a wave reads the running max at all its tiles' columns, also those
+    // past the slice: the last row's reads may run up to one workgroup's
+    // tile span past the rows)
+    l.red = l.trun + up((N * row_stride(KR) + kStreamWaves * tpw * kTileKeys) * 4);
     l.lse = l.red + up(2 * kStreamWaves * rows * 8);
     l.total = l.lse + up(2 * rows * 4);
     return l;

@@ -105,6 +105,27 @@ __device__ __forceinline__ float group_max16(float v) {
     return v;
 }
 
+// Butterfly reductions across lanes L ^ 16 and L ^ 32: the swap instructions
+// exchange rows (16 lanes) or halves (32 lanes) between two registers, so
+// swapping a value with itself leaves each lane holding its own value and its
+// partner's, one in each result register.
+__device__ __forceinline__ float xor16_max(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_max(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor16_sum(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_sum(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ void st64(void* p, float x, float y) {
     const unsigned long long bits =
         (unsigned long long)__float_as_uint(x) | ((unsigned long long)__float_as_uint(y) << 32);
@@ -189,14 +210,14 @@ __device__ __forceinline__ void mma(f32x4& acc, const i32x4& q, const i32x4& k) 
     }
 }
 
-// K fragment of the 16-key tile starting at key0 (zeros when !valid; the
-// buffer descriptor bounds the plane, so reads past its end are zeros too).
+// K fragment of a 16-key tile; off is the lane's byte offset of its first
+// load in the plane (kOob for a tile past the slice: zeros; the buffer
+// descriptor bounds the plane, so reads past its end are zeros too).
 template <class C>
-__device__ __forceinline__ void load_k(Frag<C>& f, __amdgpu_buffer_rsrc_t rs, int key0,
-                                       bool valid, int lane) {
-    const uint32_t off = valid ? (uint32_t)(key0 + (lane & 15)) * (uint32_t)C::KB +
-                                     (uint32_t)(16 * (lane >> 4))
-                               : kOob;
+__device__ __forceinline__ void load_k(Frag<C>& f, __amdgpu_buffer_rsrc_t rs, uint32_t off, int lane) {
+    // one offset register per tile; the 64-byte steps go in the instructions'
+    // offset field (otherwise every (tile, step) offset is kept live)
+    asm volatile("" : "+v"(off));
 #pragma unroll
     for (int s = 0; s < C::NLD; ++s) f.v[s] = load16(rs, off + 64u * s);
 }
@@ -215,7 +236,10 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
     constexpr int SW = kStreamWaves;  // waves 0..SW-1 stream K; wave SW synchronises
     extern __shared__ __attribute__((aligned(16))) char smem[];
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    // the wave index is uniform across the wave: say so, so that everything
+    // derived from it stays in scalar registers and branches
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g4 = lane >> 4;  // lane group
     const float c = a.c;
     const int nstream = a.g * a.ngroups;
@@ -329,6 +353,31 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
 
     if (w < SW) {
         // ======================= streaming waves =======================
+        // This wave's tiles w, w + SW, ...: the first ntv hold keys of the
+        // slice (the rest are read as zeros and masked); when the slice ends
+        // inside tile tpart, that tile's keys past the end are masked too.
+        const int ntv = min(max((ntiles - w + SW - 1) / SW, 0), TPW);
+        const int tpart = (nkeys % kTileKeys != 0 && ntv > 0 && w + SW * (ntv - 1) == ntiles - 1) ? ntv - 1 : -1;
+        // keys of tile tpart this lane's C rows may hold (4 g4 + r < rem)
+        const int rem = nkeys - (w + SW * max(tpart, 0)) * kTileKeys - 4 * g4;
+        uint32_t koff[TPW];  // buffer offset of this lane's first load of tile t
+#pragma unroll
+        for (int t = 0; t < TPW; ++t)
+            koff[t] = t < ntv ? (uint32_t)(r0 + (w + SW * t) * kTileKeys + (lane & 15)) * (uint32_t)C::KB +
+                                    (uint32_t)(16 * g4)
+                              : kOob;
+        // key plane of unit it + 2 for the refill in step it (advanced by one
+        // group stride per step)
+        const long long ustep = (long long)a.ngroups * a.plane_stride * C::ESZ;
+        const char* kb2 = (const char*)a.K + ((long long)group + 2ll * a.ngroups) * a.plane_stride * C::ESZ;
+        asm volatile("" : "+s"(kb2));  // a pointer of its own, not recomputed from a.K in the loop
+
+        // this lane's running-max columns of tile 0 in each half's step row
+        // (tile t: SW * kTileKeys further)
+        float* trow[NH];
+#pragma unroll
+        for (int hf = 0; hf < NH; ++hf) trow[hf] = Trun + jrow[hf] * KRP + 4 * g4 + w * kTileKeys;
+
         Frag<C> fb[C::NBUF];
         f32x4 acc[TPW][NH];
         // prime the ring with the first two units
@@ -336,21 +385,17 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
         for (int P = 0; P < 2; ++P) {
             const auto rs = plane_rsrc(a, unit_of(P), plane_bytes, C::ESZ);
 #pragma unroll
-            for (int t = 0; t < TPW; ++t) {
-                const int tile = w + SW * t;
-                load_k<C>(fb[P * TPW + t], rs, r0 + tile * kTileKeys, unit_of(P) >= 0 && tile < ntiles, lane);
-            }
+            for (int t = 0; t < TPW; ++t) load_k<C>(fb[P * TPW + t], rs, koff[t], lane);
         }
         __syncthreads();  // Q of unit 0 is staged
 
         // Stream unit `it` (ring slots of parity P), park its logits in bank
-        // it % nbk and its per-row statistics in red[P].
-        auto stream = [&](auto Pc, int it) __attribute__((always_inline)) {
+        // b and its per-row statistics in red[P].
+        auto stream = [&](auto Pc, int it, int b) __attribute__((always_inline)) {
             constexpr int P = decltype(Pc)::value;
             // k-outer: for each 16-byte k-slice, this unit's Q fragments of both
             // halves come from LDS, then every tile's MFMAs consume them
-            const int u2 = unit_of(it + 2);
-            const auto rs2 = plane_rsrc(a, u2, plane_bytes, C::ESZ);
+            const auto rs2 = make_rsrc(kb2, it + 2 < n_units ? plane_bytes : 0u);
 #pragma unroll
             for (int t = 0; t < TPW; ++t)
 #pragma unroll
@@ -368,46 +413,57 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
             }
             // refill the slots with the same tiles of the unit two ahead
 #pragma unroll
-            for (int t = 0; t < TPW; ++t) {
-                const int tile = w + SW * t;
-                load_k<C>(fb[P * TPW + t], rs2, r0 + tile * kTileKeys, u2 >= 0 && tile < ntiles, lane);
-            }
-            // mask keys past the slice
-#pragma unroll
-            for (int t = 0; t < TPW; ++t) {
-                const int kt = (w + SW * t) * kTileKeys;
-                if (kt + kTileKeys > nkeys) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-#pragma unroll
-                        for (int hf = 0; hf < NH; ++hf)
-                            if (kt + 4 * g4 + r >= nkeys) acc[t][hf][r] = -INFINITY;
-                }
-            }
-            // per wave-row max (lanes L, L^16, L^32, L^48 hold the same row),
-            // shifted log2 logits y = c x - c max (<= 0), their exp2 sum
-            const int b = it % nbk;
+            for (int t = 0; t < TPW; ++t) load_k<C>(fb[P * TPW + t], rs2, koff[t], lane);
+            // Per wave-row statistics over this wave's keys of the slice (lanes
+            // L, L^16, L^32, L^48 hold the same row): the max m, the shifted
+            // log2 logits y = c x - c m (<= 0 on those keys) and their exp2
+            // sum. Tiles t >= ntv are left out by wave-uniform selects; the
+            // keys of tile tpart past the slice's end, by per-lane masks in a
+            // branch only that tile's wave takes. The logits themselves are not
+            // masked: what is parked for keys outside the slice is never
+            // written out.
 #pragma unroll
             for (int hf = 0; hf < NH; ++hf) {
                 float m = -INFINITY;
 #pragma unroll
-                for (int t = 0; t < TPW; ++t)
+                for (int t = 0; t < TPW; ++t) {
+                    float mt = fmaxf(fmaxf(acc[t][hf][0], acc[t][hf][1]), fmaxf(acc[t][hf][2], acc[t][hf][3]));
+                    if (t == tpart) {
+                        int lim = rem;
+                        asm volatile("" : "+v"(lim));  // keep the per-lane compares in this branch
+                        mt = -INFINITY;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) m = fmaxf(m, acc[t][hf][r]);
-                m = fmaxf(m, __shfl_xor(m, 16));
-                m = fmaxf(m, __shfl_xor(m, 32));
+                        for (int r = 0; r < 4; ++r)
+                            if (r < lim) mt = fmaxf(mt, acc[t][hf][r]);
+                    }
+                    if (t < ntv) m = fmaxf(m, mt);
+                }
+                m = xor16_max(m);
+                m = xor32_max(m);
                 const float cm = m == -INFINITY ? 0.f : m * c;
                 float s = 0.f;
 #pragma unroll
-                for (int t = 0; t < TPW; ++t)
+                for (int t = 0; t < TPW; ++t) {
+                    float e[4];
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const float y = fmaf(acc[t][hf][r], c, -cm);
                         acc[t][hf][r] = y;
-                        s += exp2_hw(y);
+                        e[r] = exp2_hw(y);
                     }
-                s += __shfl_xor(s, 16);
-                s += __shfl_xor(s, 32);
+                    float st = (e[0] + e[1]) + (e[2] + e[3]);
+                    if (t == tpart) {
+                        int lim = rem;
+                        asm volatile("" : "+v"(lim));
+                        st = 0.f;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            if (r < lim) st += e[r];
+                    }
+                    if (t < ntv) s += st;
+                }
+                s = xor16_sum(s);
+                s = xor32_sum(s);
                 if (g4 == 0) {
                     red[(P * SW + w) * ROWS + hf * 16 + lane] = make_float2(m, s);
                     refs[(b * SW + w) * ROWS + hf * 16 + lane] = cm;
@@ -429,11 +485,12 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
             }
         };
 
-        // Finish unit `it` (parked in bank it % nbk; its log-sum-exps in
-        // lse_s[pb]): log2 probabilities, max over the G heads of each step,
-        // running max over units in LDS.
-        auto finish = [&](int it, int pb) __attribute__((always_inline)) {
-            const int b = it % nbk;
+        // Finish the unit parked in bank b (its log-sum-exps in lse_s[pb]):
+        // log2 probabilities, max over the G heads of each step, running max
+        // over units in LDS. Only this wave's first ntv tiles are updated; keys
+        // of tile tpart past the slice's end land in columns that are never
+        // written out.
+        auto finish = [&](int b, int pb) __attribute__((always_inline)) {
             float off[NH];
 #pragma unroll
             for (int hf = 0; hf < NH; ++hf) {
@@ -441,65 +498,74 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
                 off[hf] = refs[(b * SW + w) * ROWS + row] - lse_s[pb * ROWS + row];
             }
             constexpr int NHF = G == 32 ? 1 : NH;  // G = 32: both halves hold the one step
+            int wd[TPW][2 * NH];
 #pragma unroll
             for (int t = 0; t < TPW; ++t) {
                 const int* src = (const int*)(banks + ((size_t)((b * SW + w) * TPW + t) * 64 + lane) * (NH * 8));
-                int wd[2 * NH];
                 if constexpr (NH == 2) {
                     const int4 q4 = *(const int4*)src;
-                    wd[0] = q4.x;
-                    wd[1] = q4.y;
-                    wd[2] = q4.z;
-                    wd[3] = q4.w;
+                    wd[t][0] = q4.x;
+                    wd[t][1] = q4.y;
+                    wd[t][2] = q4.z;
+                    wd[t][3] = q4.w;
                 } else {
                     const int2 q2 = *(const int2*)src;
-                    wd[0] = q2.x;
-                    wd[1] = q2.y;
+                    wd[t][0] = q2.x;
+                    wd[t][1] = q2.y;
                 }
-                float y[NH][4];  // log2 probabilities
+            }
+            // per half: the running-max reads first, then the decode and the
+            // head max while they are in flight, then the updates
 #pragma unroll
-                for (int hf = 0; hf < NH; ++hf) {
-                    unpack_y2(wd[2 * hf], off[hf], y[hf][0], y[hf][1]);
-                    unpack_y2(wd[2 * hf + 1], off[hf], y[hf][2], y[hf][3]);
+            for (int hf = 0; hf < NHF; ++hf) {
+                float4 o[TPW];  // (tiles past the slice read within the padding)
+                if (own[hf]) {
+#pragma unroll
+                    for (int t = 0; t < TPW; ++t) o[t] = *(const float4*)(trow[hf] + t * SW * kTileKeys);
                 }
+                float v[TPW][4];
 #pragma unroll
-                for (int hf = 0; hf < NHF; ++hf) {
-                    float v[4];
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        v[r] = y[hf][r];
-                        if constexpr (G == 32) v[r] = fmaxf(v[r], y[1][r]);
+                for (int t = 0; t < TPW; ++t) {
+                    float y[4], y1[4];  // log2 probabilities (y1: the other half, G = 32)
+                    unpack_y2(wd[t][2 * hf], off[hf], y[0], y[1]);
+                    unpack_y2(wd[t][2 * hf + 1], off[hf], y[2], y[3]);
+                    if constexpr (G == 32) {
+                        unpack_y2(wd[t][2], off[1], y1[0], y1[1]);
+                        unpack_y2(wd[t][3], off[1], y1[2], y1[3]);
                     }
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) v[r] = group_max16<C::GL>(v[r]);
-                    if (!own[hf]) continue;
-                    float* rowp = Trun + jrow[hf] * KRP + 4 * g4;
-                    const int kt = (w + SW * t) * kTileKeys;
-                    if (kt + kTileKeys <= nkeys) {  // full tile: one 16-byte read and write
-                        float4* p4 = (float4*)(rowp + kt);
-                        float4 o = *p4;
-                        o.x = fmaxf(o.x, v[0]);
-                        o.y = fmaxf(o.y, v[1]);
-                        o.z = fmaxf(o.z, v[2]);
-                        o.w = fmaxf(o.w, v[3]);
-                        *p4 = o;
-                    } else {
+                    for (int r = 0; r < 4; ++r) {
+                        float x = y[r];
+                        if constexpr (G == 32) x = fmaxf(x, y1[r]);
+                        v[t][r] = group_max16<C::GL>(x);
+                    }
+                }
+                if (own[hf]) {
 #pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            if (kt + 4 * g4 + r < nkeys) rowp[kt + r] = fmaxf(rowp[kt + r], v[r]);
+                    for (int t = 0; t < TPW; ++t) {
+                        float4 x = o[t];
+                        x.x = fmaxf(x.x, v[t][0]);
+                        x.y = fmaxf(x.y, v[t][1]);
+                        x.z = fmaxf(x.z, v[t][2]);
+                        x.w = fmaxf(x.w, v[t][3]);
+                        if (t < ntv) *(float4*)(trow[hf] + t * SW * kTileKeys) = x;
                     }
                 }
             }
         };
 
-        // Step `it`: stream unit it, then (after the workgroup barrier, when
-        // the control wave has put unit it - D's log-sum-exps in LDS) finish
-        // unit it - D.
+        // Step `it`: stream unit it into bank b, then (after the workgroup
+        // barrier, when the control wave has put unit it - D's log-sum-exps in
+        // LDS) finish unit it - D, parked in bank (it - D) mod (D + 1), the
+        // bank after b.
+        int b = 0;
         auto step = [&](auto Pc, int it) __attribute__((always_inline)) {
-            if (it < n_units) stream(Pc, it);
+            if (it < n_units) stream(Pc, it, b);
+            kb2 += ustep;
+            b = b + 1 == nbk ? 0 : b + 1;
             __syncthreads();
             const int fu = it - D;
-            if (fu >= 0 && fu < n_units) finish(fu, it & 1);
+            if (fu >= 0 && fu < n_units) finish(b, it & 1);
         };
         for (int it = 0; it < n_steps; it += 2) {
             step(std::integral_constant<int, 0>{}, it);
