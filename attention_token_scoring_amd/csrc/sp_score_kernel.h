@@ -86,22 +86,19 @@ __device__ __forceinline__ void combine(float& m, float& s, float m2, float s2, 
 
 // Lane permutation within rows of 16 lanes. Every source lane exists, so
 // bound_ctrl is irrelevant; setting it lets the compiler fold the move into
-// the consuming v_max (the score kernels are built without NaN semantics, so
-// no canonicalisation sits between them).
+// the consuming v_max.
 template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-    return __builtin_bit_cast(float,
-                              __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf,
-                                                       true));
+__device__ __forceinline__ int dpp_i(int v) {
+    return __builtin_amdgcn_mov_dpp(v, CTRL, 0xf, 0xf, true);
 }
 
 // Max over the G (<= 16) adjacent lanes that hold the G heads of one step.
 template <int G>
-__device__ __forceinline__ float group_max16(float v) {
-    if constexpr (G >= 2) v = fmaxf(v, dpp<0xb1>(v));   // quad_perm [1,0,3,2]
-    if constexpr (G >= 4) v = fmaxf(v, dpp<0x4e>(v));   // quad_perm [2,3,0,1]
-    if constexpr (G >= 8) v = fmaxf(v, dpp<0x141>(v));  // row_half_mirror
-    if constexpr (G >= 16) v = fmaxf(v, dpp<0x140>(v)); // row_mirror
+__device__ __forceinline__ int group_max16(int v) {
+    if constexpr (G >= 2) v = max(v, dpp_i<0xb1>(v));   // quad_perm [1,0,3,2]
+    if constexpr (G >= 4) v = max(v, dpp_i<0x4e>(v));   // quad_perm [2,3,0,1]
+    if constexpr (G >= 8) v = max(v, dpp_i<0x141>(v));  // row_half_mirror
+    if constexpr (G >= 16) v = max(v, dpp_i<0x140>(v)); // row_mirror
     return v;
 }
 
@@ -142,24 +139,35 @@ __device__ __forceinline__ unsigned ld32(const void* p) {
 
 // Parked logits: y = (log2-domain logit) - (row reference) <= 0 as a 16-bit
 // unsigned-normalised code of -y / 32 (v_cvt_pknorm_u16_f32 rounds and clamps
-// to [0, 65535]): a step of 32/65535 (about 2^-11) in log2 units over
-// y in [-32, 0]. The decoded p = exp2(y + offset) then carries a relative error
-// of at most ln2 * 16/65535 (1.7e-4) whenever y >= -32; below that p < 2^-32
-// and the clamp changes it by less than that. Two codes share one 32-bit word,
-// which travels by value (bit-casting an element of a vector-typed value in
-// place is not reliable with this compiler).
+// to [0, 65535]): a step of kStep = 32/65535 (about 2^-11) in log2 units over
+// y in [-32, 0]. Two codes share one 32-bit word, which travels by value
+// (bit-casting an element of a vector-typed value in place is not reliable
+// with this compiler).
+//
+// Finishing works in whole steps: a row's offset (reference - log-sum-exp, in
+// log2 units) is rounded to a whole number of steps, so a log2 probability is
+// the integer (offset - code) times kStep, and the max over heads and units is
+// an integer max. Both roundings are at most half a step, so the final
+// p = exp2(kStep * v) carries a relative error of at most ln2 * kStep (3.4e-4)
+// whenever y >= -32; below that p < 2^-32 and the clamp changes it by less.
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 constexpr float kCodeRange = 32.f;
+constexpr float kStep = kCodeRange / 65535.f;
+constexpr int kNegInf = -2147483647 - 1;  // running-max start: below every value
 // u = -y / kCodeRange, in [0, 1] for y in [-kCodeRange, 0]
 __device__ __forceinline__ int pack_u2(float u_lo, float u_hi) {
     return __builtin_bit_cast(int, __builtin_amdgcn_cvt_pknorm_u16(u_lo, u_hi));
 }
-// (lo, hi) codes of a word -> log2 values plus a common offset
-__device__ __forceinline__ void unpack_y2(int word, float off, float& lo, float& hi) {
+// a row's offset in whole steps (clamped far below any probability that
+// survives exp2 in fp32, so that offset - code cannot wrap)
+__device__ __forceinline__ int offset_steps(float off) {
+    return (int)rintf(fmaxf(off * (1.f / kStep), -1.0e9f));
+}
+// (lo, hi) codes of a word -> log2 probabilities in steps
+__device__ __forceinline__ void unpack_v2(int word, int off, int& lo, int& hi) {
     const unsigned w = (unsigned)word;
-    constexpr float step = -kCodeRange / 65535.f;
-    lo = fmaf((float)(w & 0xffffu), step, off);
-    hi = fmaf((float)(w >> 16), step, off);
+    lo = off - (int)(w & 0xffffu);
+    hi = off - (int)(w >> 16);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -321,13 +329,13 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
     // ---------------------------------------------------------------------------
     const int group = (int)blockIdx.x / a.g, rank = (int)blockIdx.x % a.g;
     const int KRP = row_stride(a.KR);
-    float* Trun = (float*)(smem + a.lds.trun);
+    int* Trun = (int*)(smem + a.lds.trun);  // running max, log2 probabilities in steps
     float2* red = (float2*)(smem + a.lds.red);      // [2][SW][ROWS]
     float* lse_s = (float*)(smem + a.lds.lse);      // [2][ROWS]
     float* refs = (float*)(smem + a.lds.ref);       // [nbk][SW][ROWS]
     char* qlds = smem + a.lds.q;                    // [2][ROWS][QS]
     char* banks = smem + a.lds.bank;                // [nbk][SW][TPW][64][NH][8 B]
-    for (int x = tid; x < a.N * KRP; x += kThreads) Trun[x] = -INFINITY;
+    for (int x = tid; x < a.N * KRP; x += kThreads) Trun[x] = kNegInf;
 
     const int r0 = rank * a.KR;
     const int r1 = min(r0 + a.KR, a.M);
@@ -374,7 +382,7 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
 
         // this lane's running-max columns of tile 0 in each half's step row
         // (tile t: SW * kTileKeys further)
-        float* trow[NH];
+        int* trow[NH];
 #pragma unroll
         for (int hf = 0; hf < NH; ++hf) trow[hf] = Trun + jrow[hf] * KRP + 4 * g4 + w * kTileKeys;
 
@@ -491,11 +499,11 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
         // of tile tpart past the slice's end land in columns that are never
         // written out.
         auto finish = [&](int b, int pb) __attribute__((always_inline)) {
-            float off[NH];
+            int off[NH];  // row offsets in whole steps
 #pragma unroll
             for (int hf = 0; hf < NH; ++hf) {
                 const int row = hf * 16 + (lane & 15);
-                off[hf] = refs[(b * SW + w) * ROWS + row] - lse_s[pb * ROWS + row];
+                off[hf] = offset_steps(refs[(b * SW + w) * ROWS + row] - lse_s[pb * ROWS + row]);
             }
             constexpr int NHF = G == 32 ? 1 : NH;  // G = 32: both halves hold the one step
             int wd[TPW][2 * NH];
@@ -518,37 +526,37 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
             // head max while they are in flight, then the updates
 #pragma unroll
             for (int hf = 0; hf < NHF; ++hf) {
-                float4 o[TPW];  // (tiles past the slice read within the padding)
+                int4 o[TPW];  // (tiles past the slice read within the padding)
                 if (own[hf]) {
 #pragma unroll
-                    for (int t = 0; t < TPW; ++t) o[t] = *(const float4*)(trow[hf] + t * SW * kTileKeys);
+                    for (int t = 0; t < TPW; ++t) o[t] = *(const int4*)(trow[hf] + t * SW * kTileKeys);
                 }
-                float v[TPW][4];
+                int v[TPW][4];
 #pragma unroll
                 for (int t = 0; t < TPW; ++t) {
-                    float y[4], y1[4];  // log2 probabilities (y1: the other half, G = 32)
-                    unpack_y2(wd[t][2 * hf], off[hf], y[0], y[1]);
-                    unpack_y2(wd[t][2 * hf + 1], off[hf], y[2], y[3]);
+                    int y[4], y1[4];  // log2 probabilities in steps (y1: the other half, G = 32)
+                    unpack_v2(wd[t][2 * hf], off[hf], y[0], y[1]);
+                    unpack_v2(wd[t][2 * hf + 1], off[hf], y[2], y[3]);
                     if constexpr (G == 32) {
-                        unpack_y2(wd[t][2], off[1], y1[0], y1[1]);
-                        unpack_y2(wd[t][3], off[1], y1[2], y1[3]);
+                        unpack_v2(wd[t][2], off[1], y1[0], y1[1]);
+                        unpack_v2(wd[t][3], off[1], y1[2], y1[3]);
                     }
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        float x = y[r];
-                        if constexpr (G == 32) x = fmaxf(x, y1[r]);
+                        int x = y[r];
+                        if constexpr (G == 32) x = max(x, y1[r]);
                         v[t][r] = group_max16<C::GL>(x);
                     }
                 }
                 if (own[hf]) {
 #pragma unroll
                     for (int t = 0; t < TPW; ++t) {
-                        float4 x = o[t];
-                        x.x = fmaxf(x.x, v[t][0]);
-                        x.y = fmaxf(x.y, v[t][1]);
-                        x.z = fmaxf(x.z, v[t][2]);
-                        x.w = fmaxf(x.w, v[t][3]);
-                        if (t < ntv) *(float4*)(trow[hf] + t * SW * kTileKeys) = x;
+                        int4 x = o[t];
+                        x.x = max(x.x, v[t][0]);
+                        x.y = max(x.y, v[t][1]);
+                        x.z = max(x.z, v[t][2]);
+                        x.w = max(x.w, v[t][3]);
+                        if (t < ntv) *(int4*)(trow[hf] + t * SW * kTileKeys) = x;
                     }
                 }
             }
@@ -573,6 +581,10 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
         }
     } else {
         // ======================= control wave =======================
+        // Its memory instructions are few and latency-critical: let them
+        // issue ahead of the streaming waves' refills when the memory
+        // pipeline is backed up.
+        __builtin_amdgcn_s_setprio(3);
         // Q of one unit: ROWS rows of KB bytes, 16 bytes per lane and load.
         // Two register sets: Q of unit it+1 is stored to LDS at step it from
         // loads issued at step it-2 (the loads of this CU's control wave queue
@@ -640,9 +652,10 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
             }
         };
         // Step it (parity P): take unit it-D's log-sum-exps (loaded kLseAhead
-        // steps ago) into lse_s[P] and load unit it+kLseAhead-D's; stage Q of
-        // unit it+1 and load Q of unit it+3; after the barrier publish unit
-        // it's partial.
+        // steps ago) into lse_s[P]; stage Q of unit it+1 and load Q of unit
+        // it+3; after the barrier publish unit it's partial, then load unit
+        // it+kLseAhead-D's log-sum-exps (as late as possible in the step, so
+        // that they are more likely to be there).
         auto ctrl_step = [&](auto Pc, int it) __attribute__((always_inline)) {
             constexpr int P = decltype(Pc)::value;
             constexpr std::integral_constant<int, P> sp{};
@@ -650,11 +663,11 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
             constexpr std::integral_constant<int, (P + kLseAhead) & 1> sl{};
             const int fu = it - D;
             if (fu >= 0 && fu < n_units) lse_take(sp, unit_of(fu), P);
-            lse_issue(sl, unit_of(it + kLseAhead - D));
             q_store(so, 1 - P);             // Q of unit it+1 -> LDS buffer (it+1)&1
             q_issue(so, unit_of(it + 3));
             __syncthreads();
             if (it < n_units) publish(unit_of(it), P);
+            lse_issue(sl, unit_of(it + kLseAhead - D));
         };
 
         q_issue(std::integral_constant<int, 0>{}, unit_of(0));
@@ -672,7 +685,8 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
     __syncthreads();
     for (int x = tid; x < a.N * nkeys; x += kThreads) {
         const int jj = x / nkeys, k = x - (x / nkeys) * nkeys;
-        a.Tg[((size_t)group * a.N + jj) * a.M + r0 + k] = Trun[jj * KRP + k];
+        const int v = Trun[jj * KRP + k];
+        a.Tg[((size_t)group * a.N + jj) * a.M + r0 + k] = v == kNegInf ? -INFINITY : (float)v * kStep;
     }
 }
 
