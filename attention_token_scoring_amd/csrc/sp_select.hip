@@ -9,7 +9,9 @@
 //   last), q_i = rint(v_i * 2^32) as uint64, chunk sums C_c, pooled keys
 //   key_c = sum C / sum len over the clipped window, rank (key desc, index asc),
 //   keep K chunks (top-K) or the shortest ranked prefix reaching mass * total
-//   (mass), emit kept tokens ascending with their position ids.
+//   (mass), emit kept tokens ascending with their position ids. The ranking
+//   is never materialised: a radix select over the keys' bits finds the key
+//   of the last kept rank, and ties on it are settled by index.
 // Every step is exact or a single IEEE-rounded operation (fp32 sub/div/mul,
 // u64 -> f64 conversion, f64 div and mul), and sums are integer, so the
 // result is the same however the work is split across threads: a CPU doing
@@ -25,6 +27,12 @@ constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kMaxChunks = 4096;
 constexpr int kSelBatch = 256;  // requests per launch (offsets travel in the kernel arguments)
+constexpr int kLd = 16;         // importance loads in flight per thread
+constexpr int kSeg = 16;        // contiguous elements a thread quantises per tile
+constexpr int kTile = kSelThreads * kSeg;  // elements per staged tile
+constexpr int kDigit = 11;                 // radix select: key bits per round
+constexpr int kBins = 1 << kDigit;
+constexpr int kFinal = 64;                 // candidates ranked exactly by one wave
 
 struct SelectBatch {
     int cu[kSelBatch + 1];      // prompt offsets of the requests in this launch
@@ -34,23 +42,88 @@ struct SelectBatch {
 
 struct SelectShared {
     unsigned long long C[kMaxChunks];     // chunk masses
-    unsigned long long S[kMaxChunks + 1]; // prefix sums, then sort keys, then ranked cumsums
-    unsigned int idx[kMaxChunks];         // chunk index in rank order
-    int off[kMaxChunks];                  // kept-token offset of each kept chunk (compacted)
-    int klist[kMaxChunks];                // kept chunks in index order
+    // staged importance tile (one pad word after every kSeg, so that a thread's
+    // contiguous segment reads are bank-conflict free) while chunk masses are
+    // accumulated; afterwards the arrays of the selection
+    union {
+        float stage[kTile + kTile / kSeg];
+        struct {
+            unsigned long long S[kMaxChunks + 1]; // prefix sums, then the ties' exclusive cumulatives
+            int off[kMaxChunks];                  // kept flags, then their exclusive scan
+            int klist[kMaxChunks];                // kept chunks in index order
+        };
+        struct {                                  // radix select rounds
+            unsigned long long hmass[2][kBins];   // mass of each digit's candidates
+            unsigned int hcount[2][kBins];        //   and their count (two sets, alternating rounds)
+        };
+    };
+    unsigned long long ck[kFinal], cmass[kFinal];  // the last candidates: key, mass,
+    unsigned int ci[kFinal];                        //   chunk index,
+    int ckeep[kFinal];                              //   kept or not
+    int ncand;
     unsigned long long wtmp[kSelWaves];
+    unsigned long long bc_prefix, bc_mass; // broadcast of a round's result
+    unsigned int bc_count, bc_ties;
     float fmin[kSelWaves], fmax[kSelWaves];
+    unsigned long long rand_[kSelWaves], ror_[kSelWaves];  // AND / OR of the keys per wave
     int kc;                               // number of kept chunks
 };
 
-template <typename T>
-__device__ __forceinline__ T wave_incl_scan(T v, int lane) {
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const T u = __shfl_up(v, o, 64);
-        if (lane >= o) v += u;
-    }
+// Inclusive scan across a wave with lane moves: shifts within rows of 16,
+// then row 0's total into row 1 (and row 2's into row 3), then rows 0-1's
+// total into rows 2-3 (rows not selected keep the 0 they are given).
+__device__ __forceinline__ unsigned wave_scan_u32(unsigned v) {
+    int x = (int)v;
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+    return (unsigned)x;
+}
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ unsigned long long dpp_u64(unsigned long long v) {
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)(unsigned)v, CTRL, ROWS, 0xf, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(unsigned)(v >> 32), CTRL, ROWS, 0xf, false);
+    return ((unsigned long long)(unsigned)hi << 32) | (unsigned)lo;
+}
+
+// The same scan for 64-bit values (each half moved, then a 64-bit add).
+__device__ __forceinline__ unsigned long long wave_scan_u64(unsigned long long v) {
+    v += dpp_u64<0x111, 0xf>(v);
+    v += dpp_u64<0x112, 0xf>(v);
+    v += dpp_u64<0x114, 0xf>(v);
+    v += dpp_u64<0x118, 0xf>(v);
+    v += dpp_u64<0x142, 0xa>(v);
+    v += dpp_u64<0x143, 0xc>(v);
     return v;
+}
+
+// Bitwise AND and OR across a wave (butterflies: quad swaps, half-row and
+// row mirrors, then the row and half-wave swaps).
+template <bool AND>
+__device__ __forceinline__ unsigned wave_bitwise(unsigned v) {
+    auto op = [](unsigned a, unsigned b) { return AND ? (a & b) : (a | b); };
+    v = op(v, (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0xb1, 0xf, 0xf, true));
+    v = op(v, (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0x4e, 0xf, 0xf, true));
+    v = op(v, (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xf, 0xf, true));
+    v = op(v, (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xf, 0xf, true));
+    const auto r16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    v = op(r16[0], r16[1]);
+    const auto r32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return op(r32[0], r32[1]);
+}
+template <bool AND>
+__device__ __forceinline__ unsigned long long wave_bitwise64(unsigned long long v) {
+    return ((unsigned long long)wave_bitwise<AND>((unsigned)(v >> 32)) << 32) |
+           wave_bitwise<AND>((unsigned)v);
+}
+
+__device__ __forceinline__ bool ranks_before(unsigned long long ka, unsigned int ia,
+                                             unsigned long long kb, unsigned int ib) {
+    return ka > kb || (ka == kb && ia < ib);
 }
 
 // In-place exclusive scan of data[0..n) (n <= 4 * kSelThreads); returns the total.
@@ -65,7 +138,9 @@ __device__ T block_excl_scan(T* data, int n, unsigned long long* wtmp) {
         loc[e] = (i0 + e < n) ? data[i0 + e] : (T)0;
         run += loc[e];
     }
-    T incl = wave_incl_scan<T>(run, lane);
+    T incl;
+    if constexpr (sizeof(T) == 8) incl = (T)wave_scan_u64((unsigned long long)run);
+    else incl = (T)wave_scan_u32((unsigned)run);
     if (lane == 63) wtmp[w] = (unsigned long long)incl;
     __syncthreads();
     T wbase = 0, total = 0;
@@ -84,11 +159,6 @@ __device__ T block_excl_scan(T* data, int n, unsigned long long* wtmp) {
     return total;
 }
 
-__device__ __forceinline__ bool ranks_before(unsigned long long ka, unsigned int ia,
-                                             unsigned long long kb, unsigned int ib) {
-    return ka > kb || (ka == kb && ia < ib);
-}
-
 __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectBatch b, SelectParamsDev p,
                                                              const float* __restrict__ x_all,
                                                              int32_t* __restrict__ kept_all,
@@ -104,12 +174,18 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectBatch b, Sele
     const int chunk = p.chunk;
     const int nc = (M + chunk - 1) / chunk;
 
-    // 1. min and max (exact in any order)
+    // 1. min and max (exact in any order); kLd loads in flight per thread,
+    // indices past the end re-read the last element
     float mn = INFINITY, mx = -INFINITY;
-    for (int i = tid; i < M; i += kSelThreads) {
-        const float v = x[i];
-        mn = fminf(mn, v);
-        mx = fmaxf(mx, v);
+    for (int t0 = 0; t0 < M; t0 += kSelThreads * kLd) {
+        float v[kLd];
+#pragma unroll
+        for (int k = 0; k < kLd; ++k) v[k] = x[min(t0 + k * kSelThreads + tid, M - 1)];
+#pragma unroll
+        for (int k = 0; k < kLd; ++k) {
+            mn = fminf(mn, v[k]);
+            mx = fmaxf(mx, v[k]);
+        }
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
@@ -129,35 +205,100 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectBatch b, Sele
         mx = fmaxf(mx, sh.fmax[x2]);
     }
     const float range = mx - mn;
+    // for the division below: a power of two taking range into [1, 2), the
+    // scaled range and its correctly rounded reciprocal
+    const int rexp = (int)((__float_as_uint(range) >> 23) & 255);  // range's exponent field
+    const bool dfast = range > 0.f && rexp >= 1 && rexp <= 253;    // normal, scale representable
+    const float dscale = dfast ? __uint_as_float((unsigned)(254 - rexp) << 23) : 1.f;
+    const float drange = range * dscale;
+    const float dnms = -mn * dscale;
+    const float drcp = __fdiv_rn(1.0f, drange);
 
-    // 2-3. normalise, boost, fixed point, chunk sums
-    const bool pow2 = (chunk & (chunk - 1)) == 0;
-    const int seg = chunk < 64 ? chunk : 64;
-    for (int blk = w; blk * 64 < M; blk += kSelWaves) {
-        const int i = blk * 64 + lane;
-        unsigned long long q = 0ull;
-        if (i < M) {
-            float v = 1.0f;
-            if (range > 0.f) v = __fdiv_rn(x[i] - mn, range);
-            if (i < p.first_n) v = v * p.first_mult;
-            if (i >= M - p.last_n) v = v * p.last_mult;
-            q = (unsigned long long)rintf(v * 4294967296.0f);
+    // 2-3. normalise, boost, fixed point, chunk sums. Tiles of kTile elements
+    // are staged in LDS with coalesced loads; each thread then takes kSeg
+    // contiguous elements and adds each run of one chunk to that chunk's mass.
+    // (the next tile's loads are issued before this tile is processed)
+    float v[kSeg];
+#pragma unroll
+    for (int k = 0; k < kSeg; ++k) v[k] = x[min(k * kSelThreads + tid, M - 1)];
+    for (int t0 = 0; t0 < M; t0 += kTile) {
+#pragma unroll
+        for (int k = 0; k < kSeg; ++k) {
+            const int l = k * kSelThreads + tid;
+            sh.stage[l + l / kSeg] = v[k];
         }
-        if (pow2) {
-            for (int o = seg >> 1; o > 0; o >>= 1) q += __shfl_xor(q, o);
-            if ((lane & (seg - 1)) == 0 && i < M) {
-                if (chunk <= 64)
-                    sh.C[i / chunk] = q;
-                else
-                    atomicAdd(&sh.C[i / chunk], q);
+        __syncthreads();
+        if (t0 + kTile < M) {
+#pragma unroll
+            for (int k = 0; k < kSeg; ++k) v[k] = x[min(t0 + kTile + k * kSelThreads + tid, M - 1)];
+        }
+        const int g0 = t0 + tid * kSeg;  // first element of this thread's segment
+        if (g0 < M) {
+            float xv[kSeg];
+#pragma unroll
+            for (int e = 0; e < kSeg; ++e) xv[e] = sh.stage[tid * (kSeg + 1) + e];
+            float vq[kSeg];
+            if (dfast) {
+                // the correctly rounded quotient (x - mn) / range by a
+                // reciprocal and one correction (Markstein): with both
+                // operands scaled by a power of two taking range into [1, 2)
+                // (a2 = (x - mn) * scale in one rounding), y = 1/range rounded,
+                // q0 = a2 * y and the exact residual a2 - q0 * range,
+                // q0 + residual * y rounds to the IEEE quotient (a quotient too
+                // small for that is too small to survive the fixed point)
+#pragma unroll
+                for (int e = 0; e < kSeg; ++e) {
+                    const float a2 = fmaf(xv[e], dscale, dnms);
+                    const float q0 = a2 * drcp;
+                    vq[e] = fmaf(fmaf(-q0, drange, a2), drcp, q0);
+                }
+            } else if (range > 0.f) {
+#pragma unroll
+                for (int e = 0; e < kSeg; ++e) vq[e] = __fdiv_rn(xv[e] - mn, range);
+            } else {
+#pragma unroll
+                for (int e = 0; e < kSeg; ++e) vq[e] = 1.0f;
             }
-        } else if (i < M) {
-            atomicAdd(&sh.C[i / chunk], q);
+            const bool boosted = g0 < p.first_n || g0 + kSeg > M - p.last_n;
+            if (!boosted && g0 + kSeg <= M && chunk % kSeg == 0) {
+                // the whole segment lies in one chunk, inside the prompt, unboosted
+                unsigned long long run = 0ull;
+#pragma unroll
+                for (int e = 0; e < kSeg; ++e) run += (unsigned long long)rintf(vq[e] * 4294967296.0f);
+                atomicAdd(&sh.C[g0 / chunk], run);
+            } else {
+                asm volatile("");  // (keep this path a branch)
+                unsigned long long qv[kSeg];
+#pragma unroll
+                for (int e = 0; e < kSeg; ++e) {
+                    const int i = g0 + e;
+                    float q = vq[e];
+                    if (i < p.first_n) q = q * p.first_mult;
+                    if (i >= M - p.last_n) q = q * p.last_mult;
+                    qv[e] = i < M ? (unsigned long long)rintf(q * 4294967296.0f) : 0ull;
+                }
+                int c = g0 / chunk;
+                int next = (c + 1) * chunk;  // first element of the next chunk
+                unsigned long long run = 0ull;
+#pragma unroll
+                for (int e = 0; e < kSeg; ++e) {
+                    if (g0 + e == next && next < M) {  // (past the prompt's end only zeros follow)
+                        atomicAdd(&sh.C[c], run);
+                        run = 0ull;
+                        ++c;
+                        next += chunk;
+                    }
+                    run += qv[e];
+                }
+                atomicAdd(&sh.C[c], run);
+            }
         }
+        __syncthreads();
     }
-    __syncthreads();
 
-    // 4. pooled keys from prefix sums: key_c = (S[hi+1] - S[lo]) / tokens in window
+    // 4. pooled keys from prefix sums: key_c = (S[hi+1] - S[lo]) / tokens in
+    // window, held as the bits of the (non-negative) double, which order like
+    // the values; thread tid holds chunks e * kSelThreads + tid
     for (int c = tid; c < nc; c += kSelThreads) sh.S[c] = sh.C[c];
     __syncthreads();
     const unsigned long long total = block_excl_scan<unsigned long long>(sh.S, nc, sh.wtmp);
@@ -165,120 +306,248 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectBatch b, Sele
     __syncthreads();
     const int hw = (p.pool_k - 1) / 2;
     const int last_len = M - (nc - 1) * chunk;
-    unsigned long long kb[4];
+    constexpr int kPer = kMaxChunks / kSelThreads;
+    unsigned long long key[kPer], cm[kPer];
+    bool valid[kPer];
+    unsigned long long kand = ~0ull, kor = 0ull;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
+    for (int e = 0; e < kPer; ++e) {
         const int c = tid + e * kSelThreads;
-        kb[e] = 0ull;
-        if (c < nc) {
+        valid[e] = c < nc;
+        key[e] = 0ull;
+        cm[e] = 0ull;
+        if (valid[e]) {
             const int lo = c - hw < 0 ? 0 : c - hw;
             const int hi = c + hw > nc - 1 ? nc - 1 : c + hw;
             const unsigned long long P = sh.S[hi + 1] - sh.S[lo];
             const long long T = (long long)(hi - lo + 1) * chunk - (hi == nc - 1 ? chunk - last_len : 0);
-            const double key = (double)P / (double)T;
-            kb[e] = (unsigned long long)__double_as_longlong(key) + 1ull;  // 0 marks padding
+            key[e] = (unsigned long long)__double_as_longlong((double)P / (double)T);
+            cm[e] = sh.C[c];
+            kand &= key[e];
+            kor |= key[e];
         }
     }
-    int ncp = 1;
-    while (ncp < nc) ncp <<= 1;
-    __syncthreads();
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int c = tid + e * kSelThreads;
-        if (c < ncp) {
-            sh.S[c] = kb[e];
-            sh.idx[c] = (unsigned)c;
-        }
-    }
-    __syncthreads();
 
-    // 5. bitonic sort into rank order: key descending, then index ascending
-    for (int k = 2; k <= ncp; k <<= 1) {
-        for (int jj = k >> 1; jj > 0; jj >>= 1) {
-            for (int i = tid; i < ncp; i += kSelThreads) {
-                const int l = i ^ jj;
-                if (l > i) {
-                    const unsigned long long ka = sh.S[i], kl = sh.S[l];
-                    const unsigned ia = sh.idx[i], il = sh.idx[l];
-                    const bool l_first = ranks_before(kl, il, ka, ia);
-                    const bool up = (i & k) == 0;
-                    if (up == l_first) {
-                        sh.S[i] = kl;
-                        sh.S[l] = ka;
-                        sh.idx[i] = il;
-                        sh.idx[l] = ia;
-                    }
-                }
+    // 5. The kept chunks are the first kc in rank order (key descending, then
+    // index ascending): top-K takes kc = max(1, ceil(rate * nc)); mass walks
+    // the ranking adding own masses and stops at the first rank whose
+    // cumulative mass reaches mass * total (all chunks if none does). Instead
+    // of sorting, a radix select over the key bits narrows down the keys
+    // around the last kept rank, with the count and mass of all keys above
+    // them; the few left are ranked exactly (equal keys: lowest index first).
+    const bool topk = p.mode == SP_SELECT_TOPK;
+    long long kc_topk = 0;
+    double thr = 0.0;
+    bool keep_all = false;
+    if (topk) {
+        kc_topk = (long long)ceil((double)p.keep_rate * (double)nc);
+        if (kc_topk < 1) kc_topk = 1;
+        if (kc_topk > nc) kc_topk = nc;
+    } else {
+        thr = (double)p.mass * (double)total;
+        keep_all = !((double)total >= thr);  // no rank reaches the threshold
+    }
+    kand = wave_bitwise64<true>(kand);
+    kor = wave_bitwise64<false>(kor);
+    if (lane == 0) {
+        sh.rand_[w] = kand;
+        sh.ror_[w] = kor;
+    }
+    __syncthreads();
+    kand = ~0ull;
+    kor = 0ull;
+    for (int x2 = 0; x2 < kSelWaves; ++x2) {
+        kand &= sh.rand_[x2];
+        kor |= sh.ror_[x2];
+    }
+    const unsigned long long diff = kand ^ kor;  // bits where the keys differ
+    // Rounds fix kDigit bits at a time from the highest bit where keys
+    // differ, keeping the candidates (keys matching prefix on the bits of
+    // fmask) that contain the last kept rank, until at most kFinal are left or
+    // all bits are fixed. Keys above the candidates rank before all of them.
+    int hi = diff == 0ull ? -1 : 63 - __builtin_clzll(diff);
+    unsigned long long fmask = hi >= 63 ? 0ull : ~0ull << (hi + 1);
+    unsigned long long prefix = kand & fmask;
+    unsigned long long above_mass = 0ull;
+    unsigned int above_count = 0u;
+    unsigned int ncand = (unsigned)nc;
+    for (int rnd = 0; hi >= 0 && ncand > (unsigned)kFinal && !keep_all; ++rnd) {
+        const int hb = rnd & 1;
+        const int lo = hi - (kDigit - 1) > 0 ? hi - (kDigit - 1) : 0;
+        const int nbits = hi - lo + 1;
+        const int nbins = 1 << nbits;
+        const unsigned long long dmask = (unsigned long long)(nbins - 1);
+        if (rnd == 0) {
+            for (int d = tid; d < kBins; d += kSelThreads) {
+                sh.hcount[0][d] = 0u;
+                sh.hmass[0][d] = 0ull;
             }
             __syncthreads();
         }
-    }
-
-    // 6. number of kept chunks
-    if (p.mode == SP_SELECT_TOPK) {
-        if (tid == 0) {
-            long long K = (long long)ceil((double)p.keep_rate * (double)nc);
-            if (K < 1) K = 1;
-            if (K > nc) K = nc;
-            sh.kc = (int)K;
+#pragma unroll
+        for (int e = 0; e < kPer; ++e)
+            if (valid[e] && (key[e] & fmask) == prefix) {
+                const int d = (int)((key[e] >> lo) & dmask);
+                // (transposed: wave 0's lane L reads digits 32 (63 - L) + b
+                // at b * 64 + 63 - L, conflict-free)
+                const int h = (d & 31) * 64 + (d >> 5);
+                atomicAdd(&sh.hcount[hb][h], 1u);
+                if (!topk) atomicAdd(&sh.hmass[hb][h], cm[e]);
+            }
+        __syncthreads();
+        if (w == 0) {
+            // lane L sums digits 32 (63 - L) .. 32 (63 - L) + 31, so lanes
+            // ascend as digits descend (digits >= nbins are empty)
+            const int a0 = 63 - lane;
+            unsigned int lc = 0u;
+            unsigned long long lm = 0ull;
+            if (topk) {
+#pragma unroll
+                for (int j = 0; j < 32; ++j) lc += sh.hcount[hb][j * 64 + a0];
+            } else {
+#pragma unroll
+                for (int j = 0; j < 32; ++j) {
+                    lc += sh.hcount[hb][j * 64 + a0];
+                    lm += sh.hmass[hb][j * 64 + a0];
+                }
+            }
+            const unsigned int ic = wave_scan_u32(lc);
+            const unsigned long long im = topk ? 0ull : wave_scan_u64(lm);
+            // the first digit (descending) whose inclusive cumulative reaches the target
+            const bool reach = topk ? (long long)(above_count + ic) >= kc_topk
+                                    : (double)(above_mass + im) >= thr;
+            const unsigned long long bal = __ballot(reach);
+            const int F = bal ? __builtin_ctzll(bal) : 63;
+            // counts before lane F's digits, then lane F's digits one per lane, descending
+            const unsigned int cF = __shfl(ic - lc, F);
+            const unsigned long long mF = topk ? 0ull : __shfl(im - lm, F);
+            const bool mine = lane < 32;
+            const int hF = (31 - (lane & 31)) * 64 + (63 - F);
+            const unsigned int c1 = mine ? sh.hcount[hb][hF] : 0u;
+            const unsigned long long m1 = (mine && !topk) ? sh.hmass[hb][hF] : 0ull;
+            const unsigned int ic1 = wave_scan_u32(c1);
+            const unsigned long long im1 = topk ? 0ull : wave_scan_u64(m1);
+            const bool reach1 = mine && (topk ? (long long)(above_count + cF + ic1) >= kc_topk
+                                              : (double)(above_mass + mF + im1) >= thr);
+            const unsigned long long bal1 = __ballot(reach1);
+            const int J = bal1 ? __builtin_ctzll(bal1) : 0;
+            if (lane == J) {
+                sh.bc_prefix = prefix | ((unsigned long long)(32 * (63 - F) + 31 - J) << lo);
+                sh.bc_count = above_count + cF + ic1 - c1;
+                sh.bc_mass = above_mass + mF + im1 - m1;
+                sh.bc_ties = c1;
+            }
+        } else {
+            // the next round's histogram set
+            for (int x2 = tid - 64; x2 < kBins; x2 += kSelThreads - 64) {
+                sh.hcount[hb ^ 1][x2] = 0u;
+                sh.hmass[hb ^ 1][x2] = 0ull;
+            }
         }
-    } else {
-        // ranked cumulative own masses; kept = (ranks whose cumsum is still below
-        // the threshold) + 1, since the cumsum only grows
-        for (int i = tid; i < nc; i += kSelThreads) sh.S[i] = sh.C[sh.idx[i]];
-        if (tid == 0) sh.kc = 0;
+        __syncthreads();
+        prefix = sh.bc_prefix;
+        above_count = sh.bc_count;
+        above_mass = sh.bc_mass;
+        ncand = sh.bc_ties;
+        fmask |= dmask << lo;
+        hi = lo - 1;
+    }
+    __syncthreads();  // the histograms alias S
+
+    // The last candidates: at most kFinal are ranked exactly by one wave;
+    // more can only remain when all their bits are fixed, i.e. they are equal
+    // keys, and then their index order decides (a scan).
+    bool keep[kPer];
+    int slot[kPer];
+    const bool exact = !keep_all && ncand <= (unsigned)kFinal;
+    if (exact) {
+        if (tid == 0) sh.ncand = 0;
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) {
+            slot[e] = -1;
+            if (valid[e] && (key[e] & fmask) == prefix) {
+                const int sl = atomicAdd(&sh.ncand, 1);
+                if (sl < kFinal) {
+                    slot[e] = sl;
+                    sh.ck[sl] = key[e];
+                    sh.ci[sl] = (unsigned)(tid + e * kSelThreads);
+                    sh.cmass[sl] = cm[e];
+                }
+            }
+        }
+        __syncthreads();
+        if (w == 0) {
+            const int n = sh.ncand < kFinal ? sh.ncand : kFinal;
+            if (lane < n) {
+                const unsigned long long mk = sh.ck[lane];
+                const unsigned int mi = sh.ci[lane];
+                unsigned int rank = 0u;
+                unsigned long long before = 0ull;
+                for (int j = 0; j < n; ++j) {
+                    if (ranks_before(sh.ck[j], sh.ci[j], mk, mi)) {
+                        ++rank;
+                        before += sh.cmass[j];
+                    }
+                }
+                sh.ckeep[lane] = topk ? (long long)(above_count + rank) < kc_topk
+                                      : (double)(above_mass + before) < thr;
+            }
+        }
+        __syncthreads();
+    } else if (!keep_all) {
+        for (int c = tid; c < nc; c += kSelThreads) sh.S[c] = 0ull;
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < kPer; ++e)
+            if (valid[e] && (key[e] & fmask) == prefix) sh.S[tid + e * kSelThreads] = topk ? 1ull : cm[e];
         __syncthreads();
         block_excl_scan<unsigned long long>(sh.S, nc, sh.wtmp);
-        const double thr = (double)p.mass * (double)total;
-        int below = 0;
-        for (int i = tid; i < nc; i += kSelThreads) {
-            const unsigned long long incl = sh.S[i] + sh.C[sh.idx[i]];
-            below += ((double)incl < thr) ? 1 : 0;
-        }
+    }
 #pragma unroll
-        for (int o = 32; o > 0; o >>= 1) below += __shfl_xor(below, o);
-        if (lane == 0) atomicAdd(&sh.kc, below);
-        __syncthreads();
-        if (tid == 0) sh.kc = sh.kc + 1 > nc ? nc : sh.kc + 1;
-    }
-    __syncthreads();
-
-    // 7. kept flags in chunk order -> offsets of kept tokens
-    const int kc = sh.kc;
-    for (int c = tid; c < nc; c += kSelThreads) sh.off[c] = 0;
-    __syncthreads();
-    for (int i = tid; i < kc; i += kSelThreads) sh.off[sh.idx[i]] = 1;
-    __syncthreads();
-    // klist position of each kept chunk (exclusive scan of the flags)
-    for (int c = tid; c < nc; c += kSelThreads) sh.klist[c] = sh.off[c];
-    __syncthreads();
-    block_excl_scan<int>(sh.klist, nc, sh.wtmp);
-    // kept chunk k (in index order) -> chunk id; token offsets by scan of lengths
-    for (int c = tid; c < nc; c += kSelThreads) {
-        if (sh.off[c]) {
-            const int k = sh.klist[c];
-            sh.idx[k] = (unsigned)c;  // rank order no longer needed
+    for (int e = 0; e < kPer; ++e) {
+        const int c = tid + e * kSelThreads;
+        bool k = false;
+        if (valid[e]) {
+            if (keep_all || (key[e] & fmask) > prefix) {
+                k = true;
+            } else if ((key[e] & fmask) == prefix) {
+                if (exact) {
+                    k = slot[e] >= 0 && sh.ckeep[slot[e]];
+                } else {
+                    const unsigned long long before = sh.S[c];
+                    k = topk ? (long long)(above_count + before) < kc_topk
+                             : (double)(above_mass + before) < thr;
+                }
+            }
         }
+        keep[e] = k;
     }
     __syncthreads();
-    for (int k = tid; k < kc; k += kSelThreads) {
-        const int c = (int)sh.idx[k];
-        sh.off[k] = (c == nc - 1) ? last_len : chunk;
-    }
-    __syncthreads();
-    const int n_kept = block_excl_scan<int>(sh.off, kc, sh.wtmp);
 
-    // 8. emit kept tokens ascending (coalesced over output positions)
+    // 6. kept chunks in index order: klist by an exclusive scan of the flags
+#pragma unroll
+    for (int e = 0; e < kPer; ++e)
+        if (valid[e]) sh.off[tid + e * kSelThreads] = keep[e] ? 1 : 0;
+    __syncthreads();
+    const int kc = block_excl_scan<int>(sh.off, nc, sh.wtmp);
+#pragma unroll
+    for (int e = 0; e < kPer; ++e)
+        if (valid[e] && keep[e]) sh.klist[sh.off[tid + e * kSelThreads]] = tid + e * kSelThreads;
+    __syncthreads();
+
+    // 7. emit kept tokens ascending (coalesced over output positions). Every
+    // kept chunk but chunk nc - 1 (last in the list when kept) holds chunk
+    // tokens, so output o lies in kept chunk min(o / chunk, kc - 1).
+    const bool last_kept = kc > 0 && sh.klist[kc - 1] == nc - 1;
+    const int n_kept = kc * chunk - (last_kept ? chunk - last_len : 0);
     int32_t* kept = kept_all + base;
     int32_t* pos = pos_all + base;
     const int pb = b.pos_base[r];
     for (int o = tid; o < n_kept; o += kSelThreads) {
-        int lo = 0, hi = kc - 1;  // last k with off[k] <= o
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (sh.off[mid] <= o) lo = mid; else hi = mid - 1;
-        }
-        const int i = (int)sh.idx[lo] * chunk + (o - sh.off[lo]);
+        int k = o / chunk;
+        if (k > kc - 1) k = kc - 1;
+        const int i = sh.klist[k] * chunk + (o - k * chunk);
         kept[o] = base + i;
         pos[o] = pb + i;
     }

@@ -266,6 +266,9 @@ SELECT_CASES = [
     dict(M=300, chunk=7, pool_k=1, mode="topk", keep_rate=1.0),
     dict(M=2049, chunk=32, pool_k=3, mode="mass", mass=0.3, boost_first_n=100,
          boost_first_mult=2.0, boost_last_n=2000, boost_last_mult=0.5),
+    dict(M=4096, chunk=1, pool_k=9, mode="topk", keep_rate=0.05),    # one token per chunk
+    dict(M=200000, chunk=512, pool_k=3, mode="mass", mass=0.9),       # many staged tiles
+    dict(M=50000, chunk=20000, pool_k=1, mode="topk", keep_rate=0.5), # three chunks, ragged last
 ]
 
 
