@@ -133,8 +133,8 @@ sp_status make_plan(const sp_score_desc& d, long long M, int cus, ScorePlan* out
     if (p.ncomb > kMaxCombiners) p.ncomb = kMaxCombiners;
     p.grid = bg * bng + p.ncomb;
     p.lds = score_lds_layout(bdef + 1, btpw, p.rows, row_bytes, d.N, bkr);
-    p.ws_err = 0;
-    p.ws_part = 256;
+    p.ws_err = 0;      // error word; then at +128 one slice counter per rank (g <= 480)
+    p.ws_part = 2048;
     p.ws_tail = p.ws_part + round_up((size_t)p.units * p.g * p.rows * 8, 256);
     p.ws_lse = p.ws_tail + round_up((size_t)p.units * p.rows * 8, 256);
     p.ws_tg = p.ws_lse + round_up((size_t)p.units * p.rows * 4, 256);
@@ -154,7 +154,7 @@ size_t workspace_bound(const sp_score_desc& d, long long max_M, int cus) {
     long long tg_elems = (long long)(units < cus ? units : cus) * max_M;
     if (tg_elems > (long long)cus * cap) tg_elems = (long long)cus * cap;
     tg_elems *= d.N;
-    return 256 + round_up((size_t)units * cus * rows * 8, 256) + round_up((size_t)units * rows * 8, 256) +
+    return 2048 + round_up((size_t)units * cus * rows * 8, 256) + round_up((size_t)units * rows * 8, 256) +
            round_up((size_t)units * rows * 4, 256) + round_up((size_t)tg_elems * 4, 256);
 }
 

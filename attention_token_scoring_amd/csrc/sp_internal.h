@@ -59,11 +59,13 @@ struct ScoreArgs {
     const void* Q;             // [L][H][N][d] of this request
     const void* K;             // key row 0 of (layer 0, kv-head 0) of this request
     long long plane_stride;    // elements between consecutive (layer, kv-head) key planes
-    float* Tg;                 // [ngroups][N][M]: per-group running max of log2 probabilities
+    int* Tg;                   // [ngroups][N][M]: per-group running max of log2 probabilities, in code steps
     float2* part;              // [units][g][rows]: per-workgroup (row max, row sum); sentinel until published
     float2* tail;              // [units][rows]: the look-ahead keys' (row max, row sum)
     float* lse;                // [units][rows]: each row's log2-sum-exp2; sentinel until published
     int* err;                  // [1]: set when a wait times out
+    unsigned* done;            // [g]: groups done with each key slice (0 at launch)
+    float* importance;         // [M]: the output
     int L, H, Hkv, G, N, M, d;
     int g;                     // workgroups cooperating on one unit
     int ngroups;               // groups working in parallel

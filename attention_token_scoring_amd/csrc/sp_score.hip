@@ -1,7 +1,7 @@
-// Scoring: the small kernels around the cooperative one (prep: per-unit
-// synchronisation state and the look-ahead keys' statistics; finalize: max over
-// groups, exponential, mean over steps) and the launch sequence. The method
-// and the cooperative kernel are described in sp_score_kernel.h.
+// Scoring: the small kernel before the cooperative one (prep: per-unit
+// synchronisation state and the look-ahead keys' statistics) and the launch
+// sequence. The method and the cooperative kernel are described in
+// sp_score_kernel.h.
 #include "sp_score_kernel.h"
 
 namespace sp {
@@ -35,6 +35,8 @@ __global__ __launch_bounds__(256) void score_prep_kernel(ScoreArgs a, int rows) 
     __shared__ float logit[32][33];  // [row][look-ahead key]
     const int u = blockIdx.x, tid = threadIdx.x;
     if (u == 0 && tid == 0) *a.err = 0;
+    if (u == 0)
+        for (int x = tid; x < a.g; x += 256) a.done[x] = 0u;
     // this unit's g * rows partial slots, two per 16-byte store
     uint4* slots = (uint4*)(a.part + (size_t)u * a.g * rows);
     for (int x = tid; x < a.g * rows / 2; x += 256) slots[x] = make_uint4(~0u, ~0u, ~0u, ~0u);
@@ -68,20 +70,6 @@ __global__ __launch_bounds__(256) void score_prep_kernel(ScoreArgs a, int rows) 
     }
 }
 
-// importance_i = (1/N) sum_j exp2(max_group Tg[group][j][i])
-__global__ void score_finalize_kernel(const float* __restrict__ Tg, int ngroups, int N, int M,
-                                      float* __restrict__ importance) {
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= M) return;
-    float sum = 0.f;
-    for (int jj = 0; jj < N; ++jj) {
-        float mx = -INFINITY;
-        for (int gr = 0; gr < ngroups; ++gr) mx = fmaxf(mx, Tg[((size_t)gr * N + jj) * M + i]);
-        sum += exp2_hw(mx);
-    }
-    importance[i] = sum / (float)N;
-}
-
 // ---------------------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------------------
@@ -104,7 +92,7 @@ void set_profile_events(hipEvent_t before, hipEvent_t after) {
 }
 
 // One request: prep (reset synchronisation state, look-ahead statistics),
-// cooperative scoring, finalize.
+// then the cooperative scoring kernel, which also writes the importance.
 hipError_t launch_score(const ScorePlan& p, const sp_score_desc& d, const void* Q, const void* K,
                         long long plane_stride, int M, float* importance, void* ws,
                         hipStream_t stream) {
@@ -114,10 +102,12 @@ hipError_t launch_score(const ScorePlan& p, const sp_score_desc& d, const void* 
     a.K = K;
     a.plane_stride = plane_stride;
     a.err = (int*)(base + p.ws_err);
+    a.done = (unsigned*)(base + p.ws_err + 128);
+    a.importance = importance;
     a.part = (float2*)(base + p.ws_part);
     a.tail = (float2*)(base + p.ws_tail);
     a.lse = (float*)(base + p.ws_lse);
-    a.Tg = (float*)(base + p.ws_tg);
+    a.Tg = (int*)(base + p.ws_tg);
     a.L = d.L;
     a.H = d.H;
     a.Hkv = d.Hkv;
@@ -157,9 +147,7 @@ hipError_t launch_score(const ScorePlan& p, const sp_score_desc& d, const void* 
         e = hipEventRecord(t_ev_after, stream);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(score_finalize_kernel, dim3((M + 255) / 256), dim3(256), 0, stream,
-                       (const float*)a.Tg, p.ngroups, d.N, M, importance);
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 }  // namespace sp

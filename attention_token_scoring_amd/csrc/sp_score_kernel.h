@@ -35,8 +35,9 @@
 //    probabilities; the max over the G heads of a step is a DPP max across G
 //    adjacent lanes; the max over kv-heads and layers is a running max in LDS,
 //    in the log2 domain (exp2 is monotone, so one exponential per (step, key)
-//    at the end). Each group writes its running max; a small kernel takes the
-//    max over groups, exponentiates and averages over the steps.
+//    at the end). Each group writes its running max; after a grid-wide barrier
+//    every workgroup takes the max over groups, exponentiates and averages
+//    over the steps for its share of the prompt.
 //  * The look-ahead keys M..M+N-1 only enter denominators; a small prep kernel
 //    computes their share of each row's statistics.
 #pragma once
@@ -683,10 +684,41 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
         }
     }
     __syncthreads();
-    for (int x = tid; x < a.N * nkeys; x += kThreads) {
-        const int jj = x / nkeys, k = x - (x / nkeys) * nkeys;
-        const int v = Trun[jj * KRP + k];
-        a.Tg[((size_t)group * a.N + jj) * a.M + r0 + k] = v == kNegInf ? -INFINITY : (float)v * kStep;
+    // The ngroups workgroups of this rank (one per group) hold the running
+    // maxima of the same key slice. Each but the last to finish leaves its
+    // values for the last one (agent-scope stores, complete before the
+    // count); the last takes the max over groups, exponentiates and averages
+    // over the steps: importance_i = (1/N) sum_j exp2(kStep * max v).
+    int& last_s = *(int*)lse_s;  // (the log-sum-exp slots are free by now)
+    if (a.ngroups > 1) {
+        for (int x = tid; x < a.N * nkeys; x += kThreads) {
+            const int jj = x / nkeys, k = x - jj * nkeys;
+            __hip_atomic_store(&a.Tg[((size_t)group * a.N + jj) * a.M + r0 + k], Trun[jj * KRP + k],
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (tid == 0)
+            last_s = __hip_atomic_fetch_add(a.done + rank, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                     (unsigned)(a.ngroups - 1);
+        __syncthreads();
+        if (!last_s) return;
+    }
+    if (a.ngroups > 1) {
+#pragma unroll 4
+        for (int x = tid; x < a.N * nkeys; x += kThreads) {
+            const int jj = x / nkeys, k = x - jj * nkeys;
+            int v = Trun[jj * KRP + k];
+            for (int gr = 0; gr < a.ngroups; ++gr)
+                if (gr != group) v = max(v, (int)ld32(&a.Tg[((size_t)gr * a.N + jj) * a.M + r0 + k]));
+            Trun[jj * KRP + k] = v;
+        }
+        __syncthreads();
+    }
+    for (int k = tid; k < nkeys; k += kThreads) {
+        float sum = 0.f;
+        for (int jj = 0; jj < a.N; ++jj) sum += exp2_hw((float)Trun[jj * KRP + k] * kStep);
+        a.importance[r0 + k] = sum / (float)a.N;
     }
 }
 
