@@ -84,7 +84,9 @@ sp_status make_plan(const sp_score_desc& d, long long M, int cus, ScorePlan* out
     double best = 1e300;
     int bg = 0, bkr = 0, bng = 0, bdef = 0, btpw = 0;
     const int tpw0 = tiles_per_wave(bf, d.d);
-    for (int tpw = tpw0; tpw <= tpw0 + 1; ++tpw) {
+    // (one head per step over two halves: the base tile count only)
+    const int tpw1 = (G == 1 && p.rows == 32) ? tpw0 : tpw0 + 1;
+    for (int tpw = tpw0; tpw <= tpw1; ++tpw) {
         const int cap = kStreamWaves * tpw * kTileKeys;
         const long long gmin = (M + cap - 1) / cap;
         for (long long g = gmin; g <= cus - 1; ++g) {

@@ -28,10 +28,10 @@ constexpr int row_stride(int kr) { return (kr + 63) / 64 * 64 + 16; }
 
 // Byte offsets of the scoring kernel's LDS regions (all 16-byte aligned).
 struct ScoreLds {
-    int bank;   // [nbk][SW][TPW][64 lanes][NH][4 halves]: parked logits, fp16
+    int bank;   // [nbk][SW][TPW][64 lanes][NH][4]: parked logits, 16-bit codes
     int ref;    // [nbk][SW][rows] float: reference (log2 domain) of the parked logits
     int q;      // [2][rows][row bytes + 16]: Q of the current and the next unit
-    int trun;   // [N][row_stride(KR)] float: running max of the log2 probabilities
+    int trun;   // [N][row_stride(KR)] int: running maxima in code steps, written at the end over the banks
     int red;    // [2][SW][rows] float2: per-wave (max, sum) of the unit just streamed
     int lse;    // [2][rows] float: log-sum-exp of the unit being finished
     int total;
@@ -42,13 +42,13 @@ inline ScoreLds score_lds_layout(int nbk, int tpw, int rows, int row_bytes, int 
     const int nh = rows / 16;
     ScoreLds l;
     l.bank = 0;
-    l.ref = l.bank + up(nbk * kStreamWaves * tpw * 64 * nh * 8);
+    // the running maxima are written once, at the end, over the banks
+    l.trun = 0;
+    const int banks = nbk * kStreamWaves * tpw * 64 * nh * 8;
+    const int trun = N * row_stride(KR) * 4;
+    l.ref = l.bank + up(banks > trun ? banks : trun);
     l.q = l.ref + up(nbk * kStreamWaves * rows * 4);
-    l.trun = l.q + up(2 * rows * (row_bytes + 16));
-    // (a wave reads the running max at all its tiles' columns, also those
-    // past the slice: the last row's reads may run up to one workgroup's
-    // tile span past the rows)
-    l.red = l.trun + up((N * row_stride(KR) + kStreamWaves * tpw * kTileKeys) * 4);
+    l.red = l.q + up(2 * rows * (row_bytes + 16));
     l.lse = l.red + up(2 * kStreamWaves * rows * 8);
     l.total = l.lse + up(2 * rows * 4);
     return l;

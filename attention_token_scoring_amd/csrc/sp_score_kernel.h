@@ -330,13 +330,12 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
     // ---------------------------------------------------------------------------
     const int group = (int)blockIdx.x / a.g, rank = (int)blockIdx.x % a.g;
     const int KRP = row_stride(a.KR);
-    int* Trun = (int*)(smem + a.lds.trun);  // running max, log2 probabilities in steps
+    int* Trun = (int*)(smem + a.lds.trun);  // running maxima at the end (over the parked banks)
     float2* red = (float2*)(smem + a.lds.red);      // [2][SW][ROWS]
     float* lse_s = (float*)(smem + a.lds.lse);      // [2][ROWS]
     float* refs = (float*)(smem + a.lds.ref);       // [nbk][SW][ROWS]
     char* qlds = smem + a.lds.q;                    // [2][ROWS][QS]
     char* banks = smem + a.lds.bank;                // [nbk][SW][TPW][64][NH][8 B]
-    for (int x = tid; x < a.N * KRP; x += kThreads) Trun[x] = kNegInf;
 
     const int r0 = rank * a.KR;
     const int r1 = min(r0 + a.KR, a.M);
@@ -348,17 +347,10 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
     const int n_steps = (n_units + D + 1) & ~1;  // even: the streaming loop is unrolled by 2
     auto unit_of = [&](int it) __attribute__((always_inline)) { return it >= 0 && it < n_units ? group + it * a.ngroups : -1; };
 
-    // Per-lane query rows of the halves, and whether the lane writes the
-    // running max of its step (it holds the step's first head; for G = 32 both
-    // halves hold one step and half 0 writes).
+    // Per-lane query rows of the halves: the look-ahead step of each
     int jrow[NH];
-    bool own[NH];
 #pragma unroll
-    for (int hf = 0; hf < NH; ++hf) {
-        const int qr = hf * 16 + (lane & 15);
-        jrow[hf] = qr / G;
-        own[hf] = qr % G == 0 && jrow[hf] < a.N && !(G == 32 && hf == 1);
-    }
+    for (int hf = 0; hf < NH; ++hf) jrow[hf] = (hf * 16 + (lane & 15)) / G;
 
     if (w < SW) {
         // ======================= streaming waves =======================
@@ -381,11 +373,21 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
         const char* kb2 = (const char*)a.K + ((long long)group + 2ll * a.ngroups) * a.plane_stride * C::ESZ;
         asm volatile("" : "+s"(kb2));  // a pointer of its own, not recomputed from a.K in the loop
 
-        // this lane's running-max columns of tile 0 in each half's step row
-        // (tile t: SW * kTileKeys further)
-        int* trow[NH];
+        // Running max over units, in registers. After the head max every lane
+        // of a step's head group holds the maxima of the 4 keys of its lane
+        // group (C rows r = 0..3); lane k of the group keeps key r = k % 4
+        // (G >= 4), keys 2 (k % 2) and 2 (k % 2) + 1 (G = 2), or all four
+        // (G = 1).
+        constexpr int NHF = G == 32 ? 1 : NH;  // G = 32: both halves hold the one step
+        constexpr int KEEP = C::GL >= 4 ? 1 : 4 / C::GL;
+        int trun[TPW][NHF][KEEP];
 #pragma unroll
-        for (int hf = 0; hf < NH; ++hf) trow[hf] = Trun + jrow[hf] * KRP + 4 * g4 + w * kTileKeys;
+        for (int t = 0; t < TPW; ++t)
+#pragma unroll
+            for (int hf = 0; hf < NHF; ++hf)
+#pragma unroll
+                for (int kk = 0; kk < KEEP; ++kk) trun[t][hf][kk] = kNegInf;
+        const bool lb0 = (lane & 1) != 0, lb1 = (lane & 2) != 0;
 
         Frag<C> fb[C::NBUF];
         f32x4 acc[TPW][NH];
@@ -506,7 +508,6 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
                 const int row = hf * 16 + (lane & 15);
                 off[hf] = offset_steps(refs[(b * SW + w) * ROWS + row] - lse_s[pb * ROWS + row]);
             }
-            constexpr int NHF = G == 32 ? 1 : NH;  // G = 32: both halves hold the one step
             int wd[TPW][2 * NH];
 #pragma unroll
             for (int t = 0; t < TPW; ++t) {
@@ -523,16 +524,8 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
                     wd[t][1] = q2.y;
                 }
             }
-            // per half: the running-max reads first, then the decode and the
-            // head max while they are in flight, then the updates
 #pragma unroll
             for (int hf = 0; hf < NHF; ++hf) {
-                int4 o[TPW];  // (tiles past the slice read within the padding)
-                if (own[hf]) {
-#pragma unroll
-                    for (int t = 0; t < TPW; ++t) o[t] = *(const int4*)(trow[hf] + t * SW * kTileKeys);
-                }
-                int v[TPW][4];
 #pragma unroll
                 for (int t = 0; t < TPW; ++t) {
                     int y[4], y1[4];  // log2 probabilities in steps (y1: the other half, G = 32)
@@ -542,22 +535,22 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
                         unpack_v2(wd[t][2], off[1], y1[0], y1[1]);
                         unpack_v2(wd[t][3], off[1], y1[2], y1[3]);
                     }
+                    int v[4];
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         int x = y[r];
                         if constexpr (G == 32) x = max(x, y1[r]);
-                        v[t][r] = group_max16<C::GL>(x);
+                        v[r] = group_max16<C::GL>(x);
                     }
-                }
-                if (own[hf]) {
+                    if constexpr (KEEP == 1) {
+                        const int x01 = lb0 ? v[1] : v[0], x23 = lb0 ? v[3] : v[2];
+                        trun[t][hf][0] = max(trun[t][hf][0], lb1 ? x23 : x01);
+                    } else if constexpr (KEEP == 2) {
+                        trun[t][hf][0] = max(trun[t][hf][0], lb0 ? v[2] : v[0]);
+                        trun[t][hf][1] = max(trun[t][hf][1], lb0 ? v[3] : v[1]);
+                    } else {
 #pragma unroll
-                    for (int t = 0; t < TPW; ++t) {
-                        int4 x = o[t];
-                        x.x = max(x.x, v[t][0]);
-                        x.y = max(x.y, v[t][1]);
-                        x.z = max(x.z, v[t][2]);
-                        x.w = max(x.w, v[t][3]);
-                        if (t < ntv) *(int4*)(trow[hf] + t * SW * kTileKeys) = x;
+                        for (int r = 0; r < 4; ++r) trun[t][hf][r] = max(trun[t][hf][r], v[r]);
                     }
                 }
             }
@@ -580,6 +573,29 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
             step(std::integral_constant<int, 0>{}, it);
             step(std::integral_constant<int, 1>{}, it + 1);
         }
+        __syncthreads();  // every wave is done with the banks, which Trun overlays
+        // lane k of a head group (k < 4: the group's distinct keys) writes
+        // its kept maxima of the tiles in the slice: row jrow, column
+        // tile + 4 g4 + r
+        const int kg = (lane & 15) % C::GL;
+#pragma unroll
+        for (int hf = 0; hf < NHF; ++hf)
+            if (jrow[hf] < a.N && kg < (C::GL >= 4 ? 4 : C::GL)) {
+#pragma unroll
+                for (int t = 0; t < TPW; ++t) {
+                    if (t >= ntv) break;
+                    int* rowp = Trun + jrow[hf] * KRP + (w + SW * t) * kTileKeys + 4 * g4;
+                    if constexpr (KEEP == 1) {
+                        rowp[lane & 3] = trun[t][hf][0];
+                    } else if constexpr (KEEP == 2) {
+                        rowp[2 * (lane & 1)] = trun[t][hf][0];
+                        rowp[2 * (lane & 1) + 1] = trun[t][hf][1];
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) rowp[r] = trun[t][hf][r];
+                    }
+                }
+            }
     } else {
         // ======================= control wave =======================
         // Its memory instructions are few and latency-critical: let them
@@ -682,6 +698,7 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
             ctrl_step(std::integral_constant<int, 0>{}, it);
             ctrl_step(std::integral_constant<int, 1>{}, it + 1);
         }
+        __syncthreads();  // (the streaming waves' barrier before they write the running maxima)
     }
     __syncthreads();
     // The ngroups workgroups of this rank (one per group) hold the running
@@ -731,7 +748,11 @@ const void* kernel_ptr() {
 template <int D, bool BF, int NH, int TPW>
 const void* pick_g(int G) {
     switch (G) {
-        case 1: return kernel_ptr<Cfg<D, BF, NH, 1, TPW>>();
+        case 1:
+            // (one head per step and two halves keep 32 running maxima per
+            // lane: only the base tile count fits the registers)
+            if constexpr (NH == 2 && TPW > tiles_per_wave(BF, D)) return nullptr;
+            else return kernel_ptr<Cfg<D, BF, NH, 1, TPW>>();
         case 2: return kernel_ptr<Cfg<D, BF, NH, 2, TPW>>();
         case 4: return kernel_ptr<Cfg<D, BF, NH, 4, TPW>>();
         case 8: return kernel_ptr<Cfg<D, BF, NH, 8, TPW>>();
