@@ -18,9 +18,8 @@
 //    share a unit, each owning a key slice. Seven waves stream K, each keeping
 //    two units of its tiles in flight, so HBM never waits for the rest of the
 //    pipeline. A streamed unit's logits are parked in LDS as 16-bit fixed-point
-//    log2 values relative to each wave-row's maximum (a probability p carries a
-//    relative error of at most 1.7e-4), together with the wave's (max, sum) per
-//    row.
+//    log2 values relative to each wave-row's maximum, together with the
+//    wave's (max, sum) per row.
 //  * The eighth wave of each workgroup does the cross-workgroup exchange, off
 //    the streaming waves' instruction stream (a wave's vector-memory counter is
 //    in order on gfx950, so a poll issued by a streaming wave would wait for
@@ -32,12 +31,14 @@
 //    share, and publish each row's log-sum-exp. Partial and log-sum-exp slots
 //    hold a sentinel until written, so no counters or flags are needed.
 //  * D units after streaming a unit, its parked logits become log2
-//    probabilities; the max over the G heads of a step is a DPP max across G
-//    adjacent lanes; the max over kv-heads and layers is a running max in LDS,
-//    in the log2 domain (exp2 is monotone, so one exponential per (step, key)
-//    at the end). Each group writes its running max; after a grid-wide barrier
-//    every workgroup takes the max over groups, exponentiates and averages
-//    over the steps for its share of the prompt.
+//    probabilities in whole code steps (integers; a probability p carries a
+//    relative error of at most 3.4e-4); the max over the G heads of a step is
+//    a DPP max across G adjacent lanes; the max over kv-heads and layers is a
+//    running max kept in registers (log2 domain: exp2 is monotone, so one
+//    exponential per (step, key) at the end).
+//  * At the end the ngroups workgroups holding the same key slice (one per
+//    group) meet through a counter: the last to finish takes the max over
+//    groups, exponentiates and averages over the steps for its slice.
 //  * The look-ahead keys M..M+N-1 only enter denominators; a small prep kernel
 //    computes their share of each row's statistics.
 #pragma once

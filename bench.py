@@ -14,9 +14,9 @@ The roofline block reports the dominant kernel's algorithmic bytes (one read
 of K and Q) over its average duration. The library records HIP events on the
 scoring stream immediately before and after each launch of its cooperative
 scoring kernel (sp_profile_score_kernel), so the duration excludes the small
-prep and finalize kernels. HBM traffic comes from the rocprofv3 counter
-summary under profiles/ when it was taken on the current kernel sources
-(else null); `--traffic-from FETCH_DB WRITE_DB` writes that summary from two
+prep kernel (the cooperative kernel itself ends by writing the importance).
+HBM traffic comes from the rocprofv3 counter summary under profiles/ when it
+was taken on the code of the current kernel sources (else null); `--traffic-from FETCH_DB WRITE_DB` writes that summary from two
 rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE) that
 included `--copy-probe-mib` (the copy calibrates the counters' units). The CPU
 baseline times the oracle on the host cores on a bounded sample (a subset of
@@ -63,15 +63,30 @@ SCORE_KERNEL = "sp::score_kernel<"
 PROBE_KERNEL_HINTS = ("elementwise", "add")
 
 
+def _code_only(text: str) -> str:
+    """C/C++ source without // comments and blank lines (a comment edit does
+    not change the code the counters were taken on)."""
+    out = []
+    for line in text.splitlines():
+        i = line.find("//")
+        if i >= 0 and line.count('"', 0, i) % 2 == 0:
+            line = line[:i]
+        line = line.rstrip()
+        if line:
+            out.append(line)
+    return "\n".join(out)
+
+
 def kernel_source_sha() -> str:
-    """Fingerprint of every source the scoring kernels and their plan come from."""
+    """Fingerprint of the code of every source the scoring kernels and their
+    plan come from."""
     csrc = os.path.join(ROOT, "attention_token_scoring_amd", "csrc")
     names = sorted(n for n in os.listdir(csrc)
                    if n.startswith("sp_score") or n in ("sp_internal.h", "sp_api.hip"))
     h = hashlib.sha256()
     for name in names:
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
+            h.update(name.encode() + b"\0" + _code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
