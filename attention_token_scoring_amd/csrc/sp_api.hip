@@ -89,7 +89,7 @@ sp_status make_plan(const sp_score_desc& d, long long M, int cus, ScorePlan* out
     for (int tpw = tpw0; tpw <= tpw1; ++tpw) {
         const int cap = kStreamWaves * tpw * kTileKeys;
         const long long gmin = (M + cap - 1) / cap;
-        for (long long g = gmin; g <= cus - 1; ++g) {
+        for (long long g = gmin; g <= cus - 1 && g <= kMaxRanks; ++g) {
             long long kr = (M + g - 1) / g;
             kr = (kr + tk - 1) / tk * tk;
             if (kr > cap) continue;
@@ -135,7 +135,7 @@ sp_status make_plan(const sp_score_desc& d, long long M, int cus, ScorePlan* out
     if (p.ncomb > kMaxCombiners) p.ncomb = kMaxCombiners;
     p.grid = bg * bng + p.ncomb;
     p.lds = score_lds_layout(bdef + 1, btpw, p.rows, row_bytes, d.N, bkr);
-    p.ws_err = 0;      // error word; then at +128 one slice counter per rank (g <= 480)
+    p.ws_err = 0;      // error word; then at +128 one slice counter per rank (g <= kMaxRanks)
     p.ws_part = 2048;
     p.ws_tail = p.ws_part + round_up((size_t)p.units * p.g * p.rows * 8, 256);
     p.ws_lse = p.ws_tail + round_up((size_t)p.units * p.rows * 8, 256);

@@ -17,6 +17,9 @@ constexpr int kWaves = 8;
 constexpr int kStreamWaves = 7;
 constexpr int kThreads = kWaves * 64;
 constexpr int kTileKeys = 16;
+// Workgroups sharing a unit: at most this many (the combiner gathers 8 waves x
+// 2 lane groups x 32 ranks; the workspace header holds one counter per slice).
+constexpr int kMaxRanks = 480;
 constexpr int kMaxDefer = 3;          // units between streaming and finishing a unit
 constexpr int kLdsBytes = 160 * 1024;  // LDS of one CU
 // Tiles per streaming wave and unit: the base value, or one more for long

@@ -27,8 +27,9 @@
 //    each unit, stages the next unit's Q in LDS, and fetches log-sum-exps one
 //    step before they are needed.
 //  * Combiner workgroups on CUs no group uses gather the g partials of each unit
-//    (their loads do not queue behind any K stream), add the look-ahead keys'
-//    share, and publish each row's log-sum-exp. Partial and log-sum-exp slots
+//    (their loads do not queue behind any K stream; the eight waves of a
+//    combiner split the ranks), add the look-ahead keys' share, and publish
+//    each row's log-sum-exp. Partial and log-sum-exp slots
 //    hold a sentinel until written, so no counters or flags are needed.
 //  * D units after streaming a unit, its parked logits become log2
 //    probabilities in whole code steps (integers; a probability p carries a
@@ -262,27 +263,45 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
     // ---------------------------------------------------------------------------
     if ((int)blockIdx.x >= nstream) {
         constexpr int SUBS = 64 / ROWS;
-        constexpr int B = 40;  // ranks polled per lane at once (one round trip for g <= SUBS * B)
-        const int cw = ((int)blockIdx.x - nstream) * kWaves + w;
-        const int ncw = ((int)gridDim.x - nstream) * kWaves;
+        constexpr int B = 32;  // ranks polled per lane at once
+        const int cg = (int)blockIdx.x - nstream, ncg = (int)gridDim.x - nstream;
         const int row = lane % ROWS, sub = lane / ROWS;
-        for (int u = cw; u < a.units; u += ncw) {
+        // Teams of wpu waves share a unit: each wave gathers at most SUBS * B
+        // ranks [k_lo, k_hi) in one batch, and the team's first wave combines
+        // the team's results through LDS. wpu grows while enough units can
+        // still be gathered at once (two steps' worth: 2 * ngroups).
+        const int need_w = (a.g + SUBS * B - 1) / (SUBS * B);
+        int wpu = 1;
+        while (wpu < kWaves && (wpu < need_w || ncg * (kWaves / (2 * wpu)) >= 2 * a.ngroups)) wpu *= 2;
+        const int teams = kWaves / wpu, team = w / wpu, wt = w % wpu;
+        const int per = (a.g + wpu - 1) / wpu;
+        const int k_lo = min(wt * per, a.g), k_hi = min(k_lo + per, a.g);
+        float2* cred = (float2*)smem;  // [kWaves][ROWS]
+        for (int ub = cg * teams; ub < a.units; ub += ncg * teams) {
+            const int u = ub + team;  // (past the last unit: barriers only)
             float m = -INFINITY, s = 0.f;
-            if (sub == 0) {
-                const float2 t = a.tail[(size_t)u * ROWS + row];
-                m = t.x;
-                s = t.y;
-            }
             const unsigned long long* slot =
                 (const unsigned long long*)(a.part + (size_t)u * a.g * ROWS) + row;
             const unsigned long long t0 = wall_clock64();
-            for (int k0 = sub; k0 < a.g; k0 += SUBS * B) {
+            if (u < a.units && k_lo < k_hi) {
+                // Until this wave's partials start to appear, watch one slot
+                // (its last rank's first row) instead of re-polling all of
+                // them: the combiner CUs' memory queues stay short.
+                const unsigned long long* gate = (const unsigned long long*)(a.part + ((size_t)u * a.g + k_hi - 1) * ROWS);
+                while (ld64(gate) == kSentinel) {
+                    __builtin_amdgcn_s_sleep(8);
+                    if (wall_clock64() - t0 > kSpinTicks) {
+                        if (lane == 0) __hip_atomic_store(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        break;
+                    }
+                }
+                const int k0 = k_lo + sub;
                 unsigned long long v[B];
                 unsigned long long pend = 0;  // bit x: rank k0 + SUBS x not seen yet
 #pragma unroll
                 for (int x = 0; x < B; ++x) {
                     v[x] = kSentinel;
-                    if (k0 + SUBS * x < a.g) pend |= 1ull << x;
+                    if (k0 + SUBS * x < k_hi) pend |= 1ull << x;
                 }
                 while (true) {
 #pragma unroll
@@ -300,28 +319,36 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
                         break;
                     }
                 }
-                float mx = m;
+                float mx = -INFINITY;
 #pragma unroll
                 for (int x = 0; x < B; ++x)
-                    if (k0 + SUBS * x < a.g && v[x] != kSentinel)
+                    if (k0 + SUBS * x < k_hi && v[x] != kSentinel)
                         mx = fmaxf(mx, __uint_as_float((unsigned)v[x]));
                 if (mx != -INFINITY) {
-                    float acc = s * exp2_hw((m - mx) * c);
+                    float acc = 0.f;
 #pragma unroll
                     for (int x = 0; x < B; ++x)
-                        if (k0 + SUBS * x < a.g && v[x] != kSentinel)
+                        if (k0 + SUBS * x < k_hi && v[x] != kSentinel)
                             acc = fmaf(__uint_as_float((unsigned)(v[x] >> 32)),
                                        exp2_hw((__uint_as_float((unsigned)v[x]) - mx) * c), acc);
                     m = mx;
                     s = acc;
                 }
+                if constexpr (SUBS == 4) combine(m, s, __shfl_xor(m, 16), __shfl_xor(s, 16), c);
+                combine(m, s, __shfl_xor(m, 32), __shfl_xor(s, 32), c);
             }
-            if constexpr (SUBS == 4) combine(m, s, __shfl_xor(m, 16), __shfl_xor(s, 16), c);
-            combine(m, s, __shfl_xor(m, 32), __shfl_xor(s, 32), c);
-            if (sub == 0)
-                __hip_atomic_store((unsigned*)a.lse + (size_t)u * ROWS + row,
-                                   __float_as_uint(m * c + log2_hw(s)), __ATOMIC_RELAXED,
+            if (sub == 0) cred[w * ROWS + row] = make_float2(m, s);
+            __syncthreads();
+            if (u < a.units && wt == 0 && lane < ROWS) {
+                const float2 t = a.tail[(size_t)u * ROWS + lane];
+                float mm = t.x, ss = t.y;
+                for (int x = 0; x < wpu; ++x)
+                    combine(mm, ss, cred[(team * wpu + x) * ROWS + lane].x, cred[(team * wpu + x) * ROWS + lane].y, c);
+                __hip_atomic_store((unsigned*)a.lse + (size_t)u * ROWS + lane,
+                                   __float_as_uint(mm * c + log2_hw(ss)), __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
+            }
+            __syncthreads();  // (cred is rewritten for the next unit)
         }
         return;
     }
