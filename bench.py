@@ -4,6 +4,9 @@
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
                [--copy-probe-mib MIB]
 
+--workload takes any workload of synth (default: the 8B shape at M = 32K); the
+ragged batch is timed through sp_score_varlen + sp_select_varlen.
+
 A step scores one prompt of the workload (inputs already resident in HBM) and
 selects its tokens. W untimed steps, then exactly K timed steps between device
 synchronisations; prints one JSON line. Throughput = prompt tokens per second.
@@ -198,11 +201,12 @@ def main():
     import synth
 
     w = synth.WORKLOADS[args.workload]
-    if w.R != 1:
-        raise SystemExit("bench.py times single-prompt workloads")
     sel = w.selects[0]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if w.R != 1:
+        ragged(args, w, sel, sp, torch, dev)
+        return
 
     Qh, Kh, M = synth.make_request(w)
     k_bytes = Kh.nbytes
@@ -311,6 +315,85 @@ def main():
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, sel, Qh, Kh, args.cpu_layers)
+    print(json.dumps(out), flush=True)
+
+
+def ragged(args, w, sel, sp, torch, dev):
+    """A batch of R prompts of different lengths: one step is sp_score_varlen
+    + sp_select_varlen over the whole batch. The batch's keys (tens of GB) are
+    far larger than the Infinity Cache, so one copy suffices. The roofline
+    figure uses the sp_score_varlen call's duration (one cooperative launch per
+    request plus its prep kernel), a lower bound for the kernels' rate."""
+    import synth
+
+    Qh, Kh, cu = synth.make_ragged(w)
+    total = int(cu[-1])
+    R = len(cu) - 1
+
+    def to_dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    Q = to_dev(Qh)
+    K = to_dev(Kh)
+    del Qh, Kh
+    desc = sp.score_desc(w.L, w.H, w.Hkv, w.d, w.N, sp.SP_BF16 if w.dtype else sp.SP_F32)
+    maxM = int(np.max(np.diff(cu)))
+    ws = torch.empty(sp.sp_score_workspace_bytes(desc, maxM), dtype=torch.uint8, device=dev)
+    imp = torch.empty(total, dtype=torch.float32, device=dev)
+    kept = torch.empty(total, dtype=torch.int32, device=dev)
+    pos = torch.empty(total, dtype=torch.int32, device=dev)
+    nk = torch.empty(R, dtype=torch.int32, device=dev)
+    params = sp.select_params(chunk=sel.chunk, pool_k=sel.pool_k, mode=sel.mode,
+                              keep_rate=sel.keep_rate, mass=sel.mass,
+                              boost_first_n=sel.boost_first_n,
+                              boost_first_mult=sel.boost_first_mult,
+                              boost_last_n=sel.boost_last_n, boost_last_mult=sel.boost_last_mult)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        sp.sp_score_varlen(Q, K, cu, out=imp, workspace=ws)
+        if ev is not None:
+            ev[1].record()
+        sp.sp_select_varlen(imp, cu, params, kept_idx=kept, pos_ids=pos, n_kept=nk)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    w0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - w0) * 1e3 / args.steps
+    score_s = float(np.mean([a.elapsed_time(b) for a, b in evs])) / 1e3
+    Ms = np.diff(cu)
+    alg_bytes = int(sum(w.L * w.Hkv * (int(m) + w.N) * w.d + w.L * w.H * w.N * w.d for m in Ms)) * (2 if w.dtype else 4)
+    achieved = alg_bytes / score_s / 1e9
+    out = {
+        "metric": METRIC,
+        "value": total / (ms_per_step / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype else "f32",
+        "data": "synthetic",
+        "config": dict(workload_desc(w, sel), M=total, workload=f"{w.name}: R={R} prompts, M in "
+                       f"[{int(Ms.min())}, {int(Ms.max())}], sum {total}; L={w.L} H={w.H} "
+                       f"Hkv={w.Hkv} d={w.d} N={w.N}"),
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+        "detail": {"sp_score_varlen_ms_avg": score_s * 1e3, "alg_bytes_per_step": alg_bytes,
+                   "requests": R, "n_kept_total": int(nk.sum().cpu())},
+    }
     print(json.dumps(out), flush=True)
 
 
