@@ -28,7 +28,7 @@ SP_SELECT_TOPK, SP_SELECT_MASS = 0, 1
 
 EXPORTED = ("sp_score", "sp_score_varlen", "sp_select", "sp_select_varlen",
             "sp_score_workspace_bytes", "sp_select_workspace_bytes", "sp_score_plan",
-            "sp_status_string", "sp_profile_score_kernel")
+            "sp_status_string", "sp_profile_score_kernel", "sp_score_status")
 
 
 class SpError(RuntimeError):
@@ -77,8 +77,9 @@ def load_library():
     lib.sp_select_varlen.argtypes = [vp, i32, P(ctypes.c_int64), P(ctypes.c_int32),
                                      P(SelectParams), vp, vp, vp, vp, sz, vp]
     lib.sp_profile_score_kernel.argtypes = [vp, vp]
+    lib.sp_score_status.argtypes = [vp, vp, P(ctypes.c_int32)]
     for name in ("sp_score_plan", "sp_score", "sp_score_varlen", "sp_select", "sp_select_varlen",
-                 "sp_profile_score_kernel"):
+                 "sp_profile_score_kernel", "sp_score_status"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -156,6 +157,17 @@ def sp_profile_score_kernel(before=None, after=None):
     b = ctypes.c_void_p(before.cuda_event) if before is not None else None
     a = ctypes.c_void_p(after.cuda_event) if after is not None else None
     _check(load_library().sp_profile_score_kernel(b, a), "sp_profile_score_kernel")
+
+
+def sp_score_status(workspace, stream=None) -> bool:
+    """True if the last scoring call on this workspace timed out in a
+    cross-workgroup wait (its importance is then not valid). Waits for the
+    stream."""
+    _require_cuda(workspace)
+    out = ctypes.c_int32(0)
+    _check(load_library().sp_score_status(workspace.data_ptr(), _stream(stream),
+                                          ctypes.byref(out)), "sp_score_status")
+    return bool(out.value)
 
 
 def _workspace(nbytes: int, device, workspace=None):

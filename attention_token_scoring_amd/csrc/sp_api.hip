@@ -239,6 +239,17 @@ sp_status sp_profile_score_kernel(void* before, void* after) {
     return SP_OK;
 }
 
+sp_status sp_score_status(const void* ws, void* stream, int32_t* timed_out) {
+    if (!ws || !timed_out) return SP_EINVAL;
+    int32_t v = 0;
+    // (the error word sits at the start of the workspace, see make_plan)
+    if (hipMemcpyAsync(&v, ws, sizeof(v), hipMemcpyDeviceToHost, (hipStream_t)stream) != hipSuccess)
+        return SP_EDEVICE;
+    if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return SP_EDEVICE;
+    *timed_out = v != 0 ? 1 : 0;
+    return SP_OK;
+}
+
 sp_status sp_score_plan(const sp_score_desc* desc, int32_t M, int32_t info[8]) {
     sp_status s = check_desc(desc);
     if (s != SP_OK) return s;

@@ -200,6 +200,20 @@ sp_status sp_score_plan(const sp_score_desc* desc, int32_t M, int32_t info[8]);
  */
 sp_status sp_profile_score_kernel(void* before, void* after);
 
+/*
+ * Whether the last sp_score / sp_score_varlen that used workspace ws ran to
+ * completion without any of its bounded cross-workgroup waits running out.
+ * The scoring kernel never hangs: a wait that sees no progress for 2 s (which
+ * would take a workgroup that never runs) gives up and marks the workspace,
+ * and that call's importance is then not valid.
+ *   ws         device workspace passed to that call
+ *   stream     the stream that call was enqueued on
+ *   timed_out  host, written: 0 (complete) or 1 (a wait timed out)
+ * This call waits for the stream (it copies one word back to the host).
+ * SP_EINVAL for null pointers; SP_EDEVICE if the copy fails.
+ */
+sp_status sp_score_status(const void* ws, void* stream, int32_t* timed_out);
+
 #ifdef __cplusplus
 }
 #endif

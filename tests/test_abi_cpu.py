@@ -144,6 +144,13 @@ def test_select_rejects_null_and_sizes(lib):
     assert sp.sp_select_workspace_bytes(1, 100, p) == 0
 
 
+def test_score_status_rejects_null_pointers(lib):
+    out = ctypes.c_int32(7)
+    assert lib.sp_score_status(None, None, ctypes.byref(out)) == sp.SP_EINVAL
+    assert lib.sp_score_status(FAKE, None, None) == sp.SP_EINVAL
+    assert out.value == 7
+
+
 def test_profile_events_need_both_or_neither(lib):
     assert lib.sp_profile_score_kernel(FAKE, None) == sp.SP_EINVAL
     assert lib.sp_profile_score_kernel(None, FAKE) == sp.SP_EINVAL

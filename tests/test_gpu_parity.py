@@ -153,6 +153,17 @@ def test_score_is_deterministic():
     assert torch.equal(a, b)
 
 
+def test_score_status_after_a_normal_call():
+    w = workload(2, 8, 2, 128, 8, 2000, BF, seed=6)
+    Qh, Kh, M = synth.make_request(w)
+    Q, K = to_dev(Qh), to_dev(Kh)
+    desc = sp.score_desc(w.L, w.H, w.Hkv, w.d, w.N)
+    ws = torch.empty(sp.sp_score_workspace_bytes(desc, M), dtype=torch.uint8, device="cuda")
+    ws.fill_(0xff)  # (the prep kernel must clear the error word)
+    sp.sp_score(Q, K, workspace=ws)
+    assert sp.sp_score_status(ws) is False
+
+
 def test_score_workspace_too_small_is_rejected():
     w = workload(1, 4, 2, 64, 8, 500, BF)
     Qh, Kh, _ = synth.make_request(w)
