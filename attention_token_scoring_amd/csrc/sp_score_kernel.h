@@ -626,10 +626,11 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
             }
     } else {
         // ======================= control wave =======================
-        // Its memory instructions are few and latency-critical: let them
-        // issue ahead of the streaming waves' refills when the memory
-        // pipeline is backed up.
-        __builtin_amdgcn_s_setprio(3);
+        // Its memory instructions are few and latency-critical: they are
+        // issued at raised priority (ahead of the streaming waves' refills
+        // when the memory pipeline is backed up), the rest of its work at the
+        // normal one, so that the streaming wave sharing its SIMD is not held
+        // back.
         // Q of one unit: ROWS rows of KB bytes, 16 bytes per lane and load.
         // Two register sets: Q of unit it+1 is stored to LDS at step it from
         // loads issued at step it-2 (the loads of this CU's control wave queue
@@ -709,10 +710,14 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
             const int fu = it - D;
             if (fu >= 0 && fu < n_units) lse_take(sp, unit_of(fu), P);
             q_store(so, 1 - P);             // Q of unit it+1 -> LDS buffer (it+1)&1
+            __builtin_amdgcn_s_setprio(3);
             q_issue(so, unit_of(it + 3));
+            __builtin_amdgcn_s_setprio(0);
             __syncthreads();
+            __builtin_amdgcn_s_setprio(3);
             if (it < n_units) publish(unit_of(it), P);
             lse_issue(sl, unit_of(it + kLseAhead - D));
+            __builtin_amdgcn_s_setprio(0);
         };
 
         q_issue(std::integral_constant<int, 0>{}, unit_of(0));
