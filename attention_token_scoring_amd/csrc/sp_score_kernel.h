@@ -755,13 +755,42 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
         if (!last_s) return;
     }
     if (a.ngroups > 1) {
-#pragma unroll 4
-        for (int x = tid; x < a.N * nkeys; x += kThreads) {
-            const int jj = x / nkeys, k = x - jj * nkeys;
-            int v = Trun[jj * KRP + k];
-            for (int gr = 0; gr < a.ngroups; ++gr)
-                if (gr != group) v = max(v, (int)ld32(&a.Tg[((size_t)gr * a.N + jj) * a.M + r0 + k]));
-            Trun[jj * KRP + k] = v;
+        // XB values per thread, the other groups' copies GB groups at a time:
+        // XB * GB independent loads in flight instead of one round trip each
+        // (waiting workgroups would learn of the last arrival only by polling
+        // the counter, microseconds later than the last one learns it from
+        // its own increment, so one workgroup does the whole slice)
+        constexpr int XB = 8, GB = 8;
+        const int total = a.N * nkeys;
+        const size_t gstride = (size_t)a.N * a.M;
+        for (int x0 = 0; x0 < total; x0 += kThreads * XB) {
+            int v[XB], li[XB], go[XB];
+#pragma unroll
+            for (int i = 0; i < XB; ++i) {
+                const int x = x0 + i * kThreads + tid;
+                const int jj = x / nkeys, k = x - jj * nkeys;
+                li[i] = x < total ? jj * KRP + k : -1;
+                go[i] = jj * a.M + r0 + k;
+                v[i] = x < total ? Trun[li[i]] : kNegInf;
+            }
+            for (int gb = 0; gb < a.ngroups; gb += GB) {
+                int t[GB][XB];
+#pragma unroll
+                for (int y = 0; y < GB; ++y) {
+                    const int gr = gb + y;
+                    const bool use = gr < a.ngroups && gr != group;
+#pragma unroll
+                    for (int i = 0; i < XB; ++i)
+                        t[y][i] = use && li[i] >= 0 ? (int)ld32(a.Tg + gr * gstride + go[i]) : kNegInf;
+                }
+#pragma unroll
+                for (int y = 0; y < GB; ++y)
+#pragma unroll
+                    for (int i = 0; i < XB; ++i) v[i] = max(v[i], t[y][i]);
+            }
+#pragma unroll
+            for (int i = 0; i < XB; ++i)
+                if (li[i] >= 0) Trun[li[i]] = v[i];
         }
         __syncthreads();
     }
