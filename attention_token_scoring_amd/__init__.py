@@ -25,6 +25,7 @@ LIB_PATH = os.path.join(_HERE, "libspecprefill.so")
 SP_OK, SP_EINVAL, SP_EUNSUPPORTED, SP_EWORKSPACE, SP_EDEVICE = range(5)
 SP_F32, SP_BF16 = 0, 1
 SP_SELECT_TOPK, SP_SELECT_MASS = 0, 1
+SP_LAUNCH_RESIDENT, SP_LAUNCH_COOPERATIVE = 0, 1
 
 EXPORTED = ("sp_score", "sp_score_varlen", "sp_select", "sp_select_varlen",
             "sp_score_workspace_bytes", "sp_select_workspace_bytes", "sp_score_plan",
@@ -40,7 +41,7 @@ class SpError(RuntimeError):
 class ScoreDesc(ctypes.Structure):
     _fields_ = [("L", ctypes.c_int32), ("H", ctypes.c_int32), ("Hkv", ctypes.c_int32),
                 ("d", ctypes.c_int32), ("N", ctypes.c_int32), ("dtype", ctypes.c_int),
-                ("scale", ctypes.c_float)]
+                ("scale", ctypes.c_float), ("launch", ctypes.c_int)]
 
 
 class SelectParams(ctypes.Structure):
@@ -122,8 +123,8 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def score_desc(L, H, Hkv, d, N, dtype=SP_BF16, scale=0.0) -> ScoreDesc:
-    return ScoreDesc(int(L), int(H), int(Hkv), int(d), int(N), int(dtype), float(scale))
+def score_desc(L, H, Hkv, d, N, dtype=SP_BF16, scale=0.0, launch=SP_LAUNCH_RESIDENT) -> ScoreDesc:
+    return ScoreDesc(int(L), int(H), int(Hkv), int(d), int(N), int(dtype), float(scale), int(launch))
 
 
 def select_params(chunk=32, pool_k=1, mode="topk", keep_rate=0.0, mass=0.0, boost_first_n=0,
@@ -180,15 +181,16 @@ def _workspace(nbytes: int, device, workspace=None):
 
 
 def sp_score(Q, K, M: Optional[int] = None, scale: float = 0.0, out=None, workspace=None,
-             stream=None):
-    """importance [M] float32 of one prompt. Q [L,H,N,d], K [L,Hkv,M+N,d] (bf16 or f32)."""
+             stream=None, launch: int = SP_LAUNCH_RESIDENT):
+    """importance [M] float32 of one prompt. Q [L,H,N,d], K [L,Hkv,M+N,d] (bf16 or f32).
+    launch: SP_LAUNCH_RESIDENT (ordinary launch) or SP_LAUNCH_COOPERATIVE."""
     torch = _torch()
     _require_cuda(Q, K)
     L, H, N, d = Q.shape
     Hkv = K.shape[1]
     if M is None:
         M = K.shape[2] - N
-    desc = score_desc(L, H, Hkv, d, N, _dtype_code(Q), scale)
+    desc = score_desc(L, H, Hkv, d, N, _dtype_code(Q), scale, launch)
     if _dtype_code(K) != desc.dtype or K.shape[0] != L or K.shape[3] != d or K.shape[2] != M + N:
         raise ValueError("K must be [L, Hkv, M+N, d] with Q's dtype")
     if out is None:
@@ -202,7 +204,7 @@ def sp_score(Q, K, M: Optional[int] = None, scale: float = 0.0, out=None, worksp
 
 
 def sp_score_varlen(Q, K, cu_prompt: Sequence[int], scale: float = 0.0, out=None,
-                    workspace=None, stream=None):
+                    workspace=None, stream=None, launch: int = SP_LAUNCH_RESIDENT):
     """importance [sum M_r] float32 of a ragged batch. Q [R,L,H,N,d], K [L,Hkv,T,d]
     with T = sum (M_r + N); cu_prompt: host offsets [R+1]."""
     torch = _torch()
@@ -212,7 +214,7 @@ def sp_score_varlen(Q, K, cu_prompt: Sequence[int], scale: float = 0.0, out=None
     cu = np.ascontiguousarray(np.asarray(cu_prompt, dtype=np.int64))
     if cu.shape != (R + 1,):
         raise ValueError("cu_prompt must hold R+1 offsets")
-    desc = score_desc(L, H, Hkv, d, N, _dtype_code(Q), scale)
+    desc = score_desc(L, H, Hkv, d, N, _dtype_code(Q), scale, launch)
     if K.shape[2] != int(cu[-1]) + R * N:
         raise ValueError("K must hold sum(M_r + N) key rows")
     if out is None:

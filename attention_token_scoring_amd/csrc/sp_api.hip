@@ -53,6 +53,7 @@ sp_status check_desc(const sp_score_desc* d) {
     if (d->H % d->Hkv != 0) return SP_EINVAL;
     if (d->dtype != SP_F32 && d->dtype != SP_BF16) return SP_EINVAL;
     if (!(d->scale >= 0.f) || !isfinite(d->scale)) return SP_EINVAL;
+    if (d->launch != SP_LAUNCH_RESIDENT && d->launch != SP_LAUNCH_COOPERATIVE) return SP_EINVAL;
     const int G = d->H / d->Hkv;
     if (d->d != 64 && d->d != 128) return SP_EUNSUPPORTED;
     if ((G & (G - 1)) != 0 || G * d->N > 32) return SP_EUNSUPPORTED;
@@ -134,6 +135,7 @@ sp_status make_plan(const sp_score_desc& d, long long M, int cus, ScorePlan* out
     p.ncomb = cus - bg * bng;
     if (p.ncomb > kMaxCombiners) p.ncomb = kMaxCombiners;
     p.grid = bg * bng + p.ncomb;
+    p.cus = cus;
     p.lds = score_lds_layout(bdef + 1, btpw, p.rows, row_bytes, d.N, bkr);
     p.ws_err = 0;      // error word; then at +128 one slice counter per rank (g <= kMaxRanks)
     p.ws_part = 2048;

@@ -88,6 +88,7 @@ struct ScorePlan {
     int ncomb;     // combiner workgroups (on CUs no group uses)
     int grid;      // g * ngroups + ncomb
     int defer;
+    int cus;       // compute units of the device planned for
     ScoreLds lds;
     size_t ws_err, ws_part, ws_tail, ws_lse, ws_tg, ws_total;  // byte offsets / sizes in the workspace
 };
@@ -112,11 +113,11 @@ struct SelectParamsDev {
     float last_mult;
 };
 
-// Events the calling thread wants recorded around each cooperative scoring
-// kernel launch (profiling aid; both null when unset).
+// Events the calling thread wants recorded around each scoring kernel launch
+// (profiling aid; both null when unset).
 void set_profile_events(hipEvent_t before, hipEvent_t after);
 
-// Cooperative scoring kernels, one translation unit per operand type and head
+// Scoring kernels, one translation unit per operand type and head
 // dimension: the instantiation for (rows, G, tiles per wave), or nullptr.
 const void* score_kernel_bf16_d128(int rows, int G, int tpw);
 const void* score_kernel_bf16_d64(int rows, int G, int tpw);

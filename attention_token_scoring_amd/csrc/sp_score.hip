@@ -1,12 +1,12 @@
-// Scoring: the small kernel before the cooperative one (prep: per-unit
+// Scoring: the small kernel before the scoring kernel (prep: per-unit
 // synchronisation state and the look-ahead keys' statistics) and the launch
-// sequence. The method and the cooperative kernel are described in
+// sequence. The method and the scoring kernel are described in
 // sp_score_kernel.h.
 #include "sp_score_kernel.h"
 
 namespace sp {
 
-// Before the cooperative kernel: reset its synchronisation state (every
+// Before the scoring kernel: reset its synchronisation state (every
 // partial and log-sum-exp slot to the sentinel, the error word), and compute
 // for every unit and query row the share of the look-ahead keys M..M+N-1 in the
 // row's softmax denominator (row j sees look-ahead key t iff t <= j), as a raw
@@ -92,7 +92,9 @@ void set_profile_events(hipEvent_t before, hipEvent_t after) {
 }
 
 // One request: prep (reset synchronisation state, look-ahead statistics),
-// then the cooperative scoring kernel, which also writes the importance.
+// then the scoring kernel, which also writes the importance: an ordinary
+// launch (every workgroup resident on an otherwise idle device) or, if the
+// descriptor asks for it, a cooperative one.
 hipError_t launch_score(const ScorePlan& p, const sp_score_desc& d, const void* Q, const void* K,
                         long long plane_stride, int M, float* importance, void* ws,
                         hipStream_t stream) {
@@ -141,7 +143,17 @@ hipError_t launch_score(const ScorePlan& p, const sp_score_desc& d, const void* 
         e = hipEventRecord(t_ev_before, stream);
         if (e != hipSuccess) return e;
     }
-    e = hipLaunchCooperativeKernel(fn, dim3(p.grid), dim3(kThreads), args, (unsigned)p.lds.total, stream);
+    if (d.launch == SP_LAUNCH_COOPERATIVE) {
+        e = hipLaunchCooperativeKernel(fn, dim3(p.grid), dim3(kThreads), args, (unsigned)p.lds.total, stream);
+    } else {
+        // every workgroup must fit on the device at once (one per unit here)
+        int per_cu = 0;
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, p.lds.total);
+        if (e != hipSuccess) return e;
+        if (per_cu < 1 || (long long)p.grid > (long long)per_cu * p.cus)
+            return hipErrorCooperativeLaunchTooLarge;
+        e = hipLaunchKernel(fn, dim3(p.grid), dim3(kThreads), args, (unsigned)p.lds.total, stream);
+    }
     if (e != hipSuccess) return e;
     if (t_ev_after) {
         e = hipEventRecord(t_ev_after, stream);

@@ -14,7 +14,8 @@
 //    16x16x4 f32) MFMAs with keys as the M dimension: each lane ends up holding
 //    one query row for 4 keys of a tile, so row statistics are lane-local, and
 //    each load instruction reads 64 contiguous bytes of 16 key rows.
-//  * g workgroups (one per CU; launched cooperatively so all are resident)
+//  * g workgroups (one per CU, all resident at once: an ordinary launch no
+//    larger than what the device holds at a time, or a cooperative launch)
 //    share a unit, each owning a key slice. Seven waves stream K, each keeping
 //    two units of its tiles in flight, so HBM never waits for the rest of the
 //    pipeline. A streamed unit's logits are parked in LDS as 16-bit fixed-point
@@ -56,9 +57,14 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-// 2 s of the 100 MHz constant clock: a wait longer than this is a bug; the
-// kernel records it in the error word and moves on instead of hanging.
+// 2 s of the 100 MHz constant clock: a wait longer than this means a
+// workgroup it waits for is not running (not resident, or a bug); the kernel
+// records it in the error word and moves on instead of hanging.
 constexpr unsigned long long kSpinTicks = 200000000ull;
+// After 100 us a wait also looks at the error word, so that once one wait of
+// the launch has timed out the others end too and the launch drains in about
+// one time-out.
+constexpr unsigned long long kAbortTicks = 10000ull;
 // Buffer offset that is always out of range: loads there return zeros.
 constexpr uint32_t kOob = 0x7ffffff0u;
 // Content of a partial-statistics or log-sum-exp slot that has not been
@@ -138,6 +144,12 @@ __device__ __forceinline__ unsigned long long ld64(const void* p) {
 
 __device__ __forceinline__ unsigned ld32(const void* p) {
     return __hip_atomic_load((unsigned*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Whether a bounded wait that started at t0 should give up.
+__device__ __forceinline__ bool wait_expired(unsigned long long t0, const int* err) {
+    const unsigned long long dt = wall_clock64() - t0;
+    return dt > kSpinTicks || (dt > kAbortTicks && ld32(err) != 0u);
 }
 
 // Parked logits: y = (log2-domain logit) - (row reference) <= 0 as a 16-bit
@@ -290,7 +302,7 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
                 const unsigned long long* gate = (const unsigned long long*)(a.part + ((size_t)u * a.g + k_hi - 1) * ROWS);
                 while (ld64(gate) == kSentinel) {
                     __builtin_amdgcn_s_sleep(8);
-                    if (wall_clock64() - t0 > kSpinTicks) {
+                    if (wait_expired(t0, a.err)) {
                         if (lane == 0) __hip_atomic_store(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                         break;
                     }
@@ -314,7 +326,7 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
                     pend = np;
                     if (__ballot(pend != 0) == 0) break;
                     __builtin_amdgcn_s_sleep(2);
-                    if (wall_clock64() - t0 > kSpinTicks) {
+                    if (wait_expired(t0, a.err)) {
                         if (lane == 0) __hip_atomic_store(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                         break;
                     }
@@ -680,7 +692,7 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
                     if (miss) lse_v[S] = ld32(a.lse + (size_t)u * ROWS + lane);
                     miss = lane < ROWS && lse_v[S] == kSentinel32;
                     if (__ballot(miss) == 0) break;
-                    if (wall_clock64() - t0 > kSpinTicks) {
+                    if (wait_expired(t0, a.err)) {
                         if (lane == 0) __hip_atomic_store(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                         break;
                     }

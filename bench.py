@@ -2,10 +2,12 @@
 (sp_select) on one MI355X.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
-               [--copy-probe-mib MIB]
+               [--copy-probe-mib MIB] [--cooperative]
 
 --workload takes any workload of synth (default: the 8B shape at M = 32K); the
 ragged batch is timed through sp_score_varlen + sp_select_varlen.
+--cooperative launches the scoring kernel cooperatively (SP_LAUNCH_COOPERATIVE)
+instead of with the default ordinary launch.
 
 A step scores one prompt of the workload (inputs already resident in HBM) and
 selects its tokens. W untimed steps, then exactly K timed steps between device
@@ -15,9 +17,9 @@ Infinity Cache left over from the previous one.
 
 The roofline block reports the dominant kernel's algorithmic bytes (one read
 of K and Q) over its average duration. The library records HIP events on the
-scoring stream immediately before and after each launch of its cooperative
-scoring kernel (sp_profile_score_kernel), so the duration excludes the small
-prep kernel (the cooperative kernel itself ends by writing the importance).
+scoring stream immediately before and after each launch of its scoring
+kernel (sp_profile_score_kernel), so the duration excludes the small prep
+kernel (the scoring kernel itself ends by writing the importance).
 HBM traffic comes from the rocprofv3 counter summary under profiles/ when it
 was taken on the code of the current kernel sources (else null); `--traffic-from FETCH_DB WRITE_DB` writes that summary from two
 rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE) that
@@ -52,6 +54,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="spec8b_m32k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cooperative", action="store_true",
+                    help="launch the scoring kernel cooperatively (SP_LAUNCH_COOPERATIVE)")
     ap.add_argument("--cpu-layers", type=int, default=1 << 30,
                     help="layers of the workload the CPU baseline scores (default: all)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -220,7 +224,8 @@ def main():
     Q = to_dev(Qh)
     K0 = to_dev(Kh)
     Ks = [K0] + [K0.clone() for _ in range(copies - 1)]
-    desc = sp.score_desc(w.L, w.H, w.Hkv, w.d, w.N, sp.SP_BF16 if w.dtype else sp.SP_F32)
+    launch = sp.SP_LAUNCH_COOPERATIVE if args.cooperative else sp.SP_LAUNCH_RESIDENT
+    desc = sp.score_desc(w.L, w.H, w.Hkv, w.d, w.N, sp.SP_BF16 if w.dtype else sp.SP_F32, 0.0, launch)
     ws = torch.empty(sp.sp_score_workspace_bytes(desc, M), dtype=torch.uint8, device=dev)
     imp = torch.empty(M, dtype=torch.float32, device=dev)
     kept = torch.empty(M, dtype=torch.int32, device=dev)
@@ -248,7 +253,7 @@ def main():
             sp.sp_profile_score_kernel(kev[0], kev[1])
         if ev is not None:
             ev[0].record()
-        sp.sp_score(Q, Ks[i % copies], M, out=imp, workspace=ws)
+        sp.sp_score(Q, Ks[i % copies], M, out=imp, workspace=ws, launch=launch)
         if ev is not None:
             ev[1].record()
         if kev is not None:
@@ -260,7 +265,7 @@ def main():
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
-    # events the library records around the cooperative scoring kernel; torch
+    # events the library records around the scoring kernel; torch
     # creates an event on its first record
     kevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
             for _ in range(args.steps)]
@@ -302,7 +307,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype else "f32",
         "data": "synthetic",
-        "config": workload_desc(w, sel),
+        "config": dict(workload_desc(w, sel), launch=launch_name(args)),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic},
         "detail": {"score_kernel_ms_avg": kernel_avg_s * 1e3,
@@ -318,11 +323,15 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+def launch_name(args) -> str:
+    return "cooperative" if args.cooperative else "resident"
+
+
 def ragged(args, w, sel, sp, torch, dev):
     """A batch of R prompts of different lengths: one step is sp_score_varlen
     + sp_select_varlen over the whole batch. The batch's keys (tens of GB) are
     far larger than the Infinity Cache, so one copy suffices. The roofline
-    figure uses the sp_score_varlen call's duration (one cooperative launch per
+    figure uses the sp_score_varlen call's duration (one scoring kernel per
     request plus its prep kernel), a lower bound for the kernels' rate."""
     import synth
 
@@ -338,7 +347,8 @@ def ragged(args, w, sel, sp, torch, dev):
     Q = to_dev(Qh)
     K = to_dev(Kh)
     del Qh, Kh
-    desc = sp.score_desc(w.L, w.H, w.Hkv, w.d, w.N, sp.SP_BF16 if w.dtype else sp.SP_F32)
+    launch = sp.SP_LAUNCH_COOPERATIVE if args.cooperative else sp.SP_LAUNCH_RESIDENT
+    desc = sp.score_desc(w.L, w.H, w.Hkv, w.d, w.N, sp.SP_BF16 if w.dtype else sp.SP_F32, 0.0, launch)
     maxM = int(np.max(np.diff(cu)))
     ws = torch.empty(sp.sp_score_workspace_bytes(desc, maxM), dtype=torch.uint8, device=dev)
     imp = torch.empty(total, dtype=torch.float32, device=dev)
@@ -354,7 +364,7 @@ def ragged(args, w, sel, sp, torch, dev):
     def step(ev=None):
         if ev is not None:
             ev[0].record()
-        sp.sp_score_varlen(Q, K, cu, out=imp, workspace=ws)
+        sp.sp_score_varlen(Q, K, cu, out=imp, workspace=ws, launch=launch)
         if ev is not None:
             ev[1].record()
         sp.sp_select_varlen(imp, cu, params, kept_idx=kept, pos_ids=pos, n_kept=nk)
@@ -386,7 +396,7 @@ def ragged(args, w, sel, sp, torch, dev):
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype else "f32",
         "data": "synthetic",
-        "config": dict(workload_desc(w, sel), M=total, workload=f"{w.name}: R={R} prompts, M in "
+        "config": dict(workload_desc(w, sel), launch=launch_name(args), M=total, workload=f"{w.name}: R={R} prompts, M in "
                        f"[{int(Ms.min())}, {int(Ms.max())}], sum {total}; L={w.L} H={w.H} "
                        f"Hkv={w.Hkv} d={w.d} N={w.N}"),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",

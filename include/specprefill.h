@@ -53,14 +53,31 @@ typedef enum { SP_F32 = 0, SP_BF16 = 1 } sp_dtype;
 
 typedef enum { SP_SELECT_TOPK = 0, SP_SELECT_MASS = 1 } sp_select_mode;
 
+/* How sp_score launches its scoring kernel, whose workgroups wait on each
+ * other and so must all be resident on the device at once.
+ *   SP_LAUNCH_RESIDENT     (0, the default) an ordinary launch of no more
+ *       workgroups than the device holds at a time (one per compute unit; the
+ *       call returns SP_EDEVICE otherwise): on a device not otherwise busy,
+ *       every workgroup is resident from the start. Kernels that occupy compute units for long
+ *       on other streams (or processes) can keep some workgroups waiting for
+ *       a unit; the others' waits are bounded, so the call then ends after at
+ *       most about 2 s with its scores invalid and the time-out reported by
+ *       sp_score_status.
+ *   SP_LAUNCH_COOPERATIVE  (1) a cooperative launch (hipLaunchCooperativeKernel):
+ *       the runtime guarantees co-residency whatever else runs, at a cost of
+ *       about 20 us of device time per call. */
+typedef enum { SP_LAUNCH_RESIDENT = 0, SP_LAUNCH_COOPERATIVE = 1 } sp_launch;
+
 /* Shape of the speculator's attention: L attention layers, H query heads,
  * Hkv key/value heads (H % Hkv == 0; query head h reads kv-head h / (H/Hkv)),
  * head dimension d, N look-ahead steps. scale multiplies the logits; 0 selects
- * 1/sqrt(d). Supported: d in {64, 128}; G = H/Hkv a power of two; G*N <= 32. */
+ * 1/sqrt(d). launch is an sp_launch (0 = SP_LAUNCH_RESIDENT). Supported:
+ * d in {64, 128}; G = H/Hkv a power of two; G*N <= 32. */
 typedef struct {
     int32_t L, H, Hkv, d, N;
     sp_dtype dtype;
     float scale;
+    sp_launch launch;
 } sp_score_desc;
 
 /* Selection parameters ([SP-G] Configuration Reference gives the pages'
@@ -191,7 +208,7 @@ sp_status sp_score_plan(const sp_score_desc* desc, int32_t M, int32_t info[8]);
  * Profiling aid, not part of the scoring computation. While set, every
  * sp_score / sp_score_varlen call made by the calling thread records the HIP
  * events `before` and `after` (hipEvent_t handles created by the caller) on
- * its stream immediately before and after each launch of the cooperative
+ * its stream immediately before and after each launch of the
  * scoring kernel, so that hipEventElapsedTime gives that kernel's duration
  * apart from the small kernels around it (for sp_score_varlen the events end
  * up around the last request's kernel). Pass NULL, NULL to stop. The setting

@@ -62,6 +62,8 @@ FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every case below fails val
     (dict(dtype=7), sp.SP_EINVAL),
     (dict(scale=-1.0), sp.SP_EINVAL),
     (dict(scale=float("inf")), sp.SP_EINVAL),
+    (dict(launch=2), sp.SP_EINVAL),
+    (dict(launch=-1), sp.SP_EINVAL),
     (dict(d=96), sp.SP_EUNSUPPORTED),
     (dict(H=12, Hkv=4), sp.SP_EUNSUPPORTED),       # G = 3, not a power of two
     (dict(H=32, Hkv=8, N=16), sp.SP_EUNSUPPORTED),  # G*N = 64 > 32
@@ -101,8 +103,9 @@ def test_workspace_bytes_grows_with_prompt(lib):
 
 
 def test_plan_for_the_8b_shape(lib):
-    """At L=32, Hkv=8, d=128, M=32768 one unit spans 32 workgroups of 1024 keys,
-    8 groups fill the 256 CUs (one group per XCD)."""
+    """At L=32, Hkv=8, d=128, M=32768 the 256 units are shared by groups of
+    workgroups that each hold one key slice; the grid (groups plus combiners)
+    fits the device, one workgroup per CU."""
     p = sp.sp_score_plan(desc(L=32, H=32, Hkv=8, d=128), 32768)
     assert p["rows"] == 32 and p["units"] == 256
     assert p["g"] * p["keys_per_wg"] >= 32768 and p["keys_per_wg"] <= 1024
@@ -155,3 +158,10 @@ def test_profile_events_need_both_or_neither(lib):
     assert lib.sp_profile_score_kernel(FAKE, None) == sp.SP_EINVAL
     assert lib.sp_profile_score_kernel(None, FAKE) == sp.SP_EINVAL
     assert lib.sp_profile_score_kernel(None, None) == sp.SP_OK
+
+
+def test_plan_does_not_depend_on_the_launch_mode(lib):
+    for M in (1, 4608, 32768, 131072):
+        a = sp.sp_score_plan(desc(L=32, H=32, Hkv=8, d=128), M)
+        b = sp.sp_score_plan(desc(L=32, H=32, Hkv=8, d=128, launch=sp.SP_LAUNCH_COOPERATIVE), M)
+        assert a == b

@@ -153,6 +153,26 @@ def test_score_is_deterministic():
     assert torch.equal(a, b)
 
 
+COOP_CASES = [c for c in SMALL_CASES if c[0] in ("bf16-d128-G4-N8-M4100", "f32-d64-G2-N8-M1024",
+                                                   "bf16-d64-G1-N3-M1")] + MULTI_UNIT_CASES[:2]
+
+
+@pytest.mark.parametrize("case", COOP_CASES, ids=[c[0] for c in COOP_CASES])
+def test_score_cooperative_launch_matches(case):
+    """The two launch modes run the same kernel on the same plan: the scores
+    are identical bit for bit, and match the oracle."""
+    name, L, H, Hkv, d, N, M, dt = case
+    print(f"case {name} (cooperative launch)", flush=True)
+    w = workload(L, H, Hkv, d, N, M, dt, seed=17)
+    Qh, Kh, _ = synth.make_request(w)
+    Q, K = to_dev(Qh), to_dev(Kh)
+    a = sp.sp_score(Q, K, launch=sp.SP_LAUNCH_COOPERATIVE)
+    b = sp.sp_score(Q, K, launch=sp.SP_LAUNCH_RESIDENT)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b), name
+    check_importance(a.cpu().numpy(), oracle.score(Qh, Kh), name)
+
+
 def test_score_status_after_a_normal_call():
     w = workload(2, 8, 2, 128, 8, 2000, BF, seed=6)
     Qh, Kh, M = synth.make_request(w)
