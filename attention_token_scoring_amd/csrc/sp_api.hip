@@ -232,6 +232,9 @@ const char* sp_status_string(sp_status s) {
 
 size_t sp_score_workspace_bytes(const sp_score_desc* desc, int64_t max_prompt_len) {
     if (check_desc(desc) != SP_OK || max_prompt_len < 1) return 0;
+    // (plans get harder as prompts grow: if the longest has none, 0)
+    ScorePlan p;
+    if (make_plan(*desc, max_prompt_len, device_cus(), &p) != SP_OK) return 0;
     return workspace_bound(*desc, max_prompt_len, device_cus());
 }
 

@@ -72,7 +72,10 @@ typedef enum { SP_LAUNCH_RESIDENT = 0, SP_LAUNCH_COOPERATIVE = 1 } sp_launch;
  * Hkv key/value heads (H % Hkv == 0; query head h reads kv-head h / (H/Hkv)),
  * head dimension d, N look-ahead steps. scale multiplies the logits; 0 selects
  * 1/sqrt(d). launch is an sp_launch (0 = SP_LAUNCH_RESIDENT). Supported:
- * d in {64, 128}; G = H/Hkv a power of two; G*N <= 32. */
+ * d in {64, 128}; G = H/Hkv a power of two; G*N <= 32; and prompts of at most
+ * (compute units - 1) x 560 keys (x 336 for f32 at d = 128; fewer for G = 1
+ * with 32 query rows): 142,800 keys on a 256-CU MI355X, 85,680 for f32 at
+ * d = 128. sp_score_plan reports SP_EUNSUPPORTED beyond. */
 typedef struct {
     int32_t L, H, Hkv, d, N;
     sp_dtype dtype;

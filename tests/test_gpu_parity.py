@@ -173,6 +173,32 @@ def test_score_cooperative_launch_matches(case):
     check_importance(a.cpu().numpy(), oracle.score(Qh, Kh), name)
 
 
+# The longest prompts the planner accepts: one workgroup per CU but one (the
+# combiner's), each holding as many keys as its registers and LDS allow.
+LONGEST_CASES = [
+    ("longest-bf16-d128", 1, 4, 1, 128, 8, 142800, BF),
+    ("longest-f32-d128", 1, 4, 1, 128, 8, 85680, F32),
+]
+
+
+@pytest.mark.parametrize("case", LONGEST_CASES, ids=[c[0] for c in LONGEST_CASES])
+def test_score_longest_prompt(case):
+    """g = CUs - 1 workgroups share the unit and a single combiner workgroup
+    gathers their partials: the largest grid and the smallest combiner."""
+    name, L, H, Hkv, d, N, M, dt = case
+    print(f"case {name}", flush=True)
+    desc = sp.score_desc(L, H, Hkv, d, N, sp.SP_BF16 if dt else sp.SP_F32)
+    plan = sp.sp_score_plan(desc, M)
+    assert plan["g"] == plan["cus"] - 1 and plan["grid"] == plan["cus"], plan
+    with pytest.raises(sp.SpError):
+        sp.sp_score_plan(desc, M + 1)
+    w = workload(L, H, Hkv, d, N, M, dt, seed=29)
+    Qh, Kh, _ = synth.make_request(w)
+    imp = sp.sp_score(to_dev(Qh), to_dev(Kh))
+    torch.cuda.synchronize()
+    check_importance(imp.cpu().numpy(), oracle.score(Qh, Kh), name)
+
+
 def test_score_status_after_a_normal_call():
     w = workload(2, 8, 2, 128, 8, 2000, BF, seed=6)
     Qh, Kh, M = synth.make_request(w)
@@ -300,6 +326,7 @@ SELECT_CASES = [
     dict(M=4096, chunk=1, pool_k=9, mode="topk", keep_rate=0.05),    # one token per chunk
     dict(M=200000, chunk=512, pool_k=3, mode="mass", mass=0.9),       # many staged tiles
     dict(M=50000, chunk=20000, pool_k=1, mode="topk", keep_rate=0.5), # three chunks, ragged last
+    dict(M=1 << 24, chunk=4096, pool_k=5, mode="topk", keep_rate=0.3),  # the largest prompt
 ]
 
 
