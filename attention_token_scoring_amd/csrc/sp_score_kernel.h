@@ -413,13 +413,15 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
         const char* kb2 = (const char*)a.K + ((long long)group + 2ll * a.ngroups) * a.plane_stride * C::ESZ;
         asm volatile("" : "+s"(kb2));  // a pointer of its own, not recomputed from a.K in the loop
 
-        // Running max over units, in registers. After the head max every lane
-        // of a step's head group holds the maxima of the 4 keys of its lane
-        // group (C rows r = 0..3); lane k of the group keeps key r = k % 4
-        // (G >= 4), keys 2 (k % 2) and 2 (k % 2) + 1 (G = 2), or all four
-        // (G = 1).
+        // Running max over units, in registers. The max over heads commutes
+        // with the max over units, so each step takes it only over lane pairs
+        // (heads 2m, 2m + 1: one DPP max) and the rest once, at the end.
+        // After the pair max both lanes of a pair hold the maxima of the 4 keys
+        // of their lane group (C rows r = 0..3); lane k keeps keys 2 (k % 2)
+        // and 2 (k % 2) + 1 (G >= 2), or all four (G = 1).
         constexpr int NHF = G == 32 ? 1 : NH;  // G = 32: both halves hold the one step
-        constexpr int KEEP = C::GL >= 4 ? 1 : 4 / C::GL;
+        constexpr int SGL = C::GL >= 2 ? 2 : 1;  // lanes a step's head max spans
+        constexpr int KEEP = 4 / SGL;
         int trun[TPW][NHF][KEEP];
 #pragma unroll
         for (int t = 0; t < TPW; ++t)
@@ -427,7 +429,7 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
             for (int hf = 0; hf < NHF; ++hf)
 #pragma unroll
                 for (int kk = 0; kk < KEEP; ++kk) trun[t][hf][kk] = kNegInf;
-        const bool lb0 = (lane & 1) != 0, lb1 = (lane & 2) != 0;
+        const bool lb0 = (lane & 1) != 0;
 
         Frag<C> fb[C::NBUF];
         f32x4 acc[TPW][NH];
@@ -580,12 +582,9 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
                     for (int r = 0; r < 4; ++r) {
                         int x = y[r];
                         if constexpr (G == 32) x = max(x, y1[r]);
-                        v[r] = group_max16<C::GL>(x);
+                        v[r] = group_max16<SGL>(x);
                     }
-                    if constexpr (KEEP == 1) {
-                        const int x01 = lb0 ? v[1] : v[0], x23 = lb0 ? v[3] : v[2];
-                        trun[t][hf][0] = max(trun[t][hf][0], lb1 ? x23 : x01);
-                    } else if constexpr (KEEP == 2) {
+                    if constexpr (KEEP == 2) {
                         trun[t][hf][0] = max(trun[t][hf][0], lb0 ? v[2] : v[0]);
                         trun[t][hf][1] = max(trun[t][hf][1], lb0 ? v[3] : v[1]);
                     } else {
@@ -614,20 +613,28 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
             step(std::integral_constant<int, 1>{}, it + 1);
         }
         __syncthreads();  // every wave is done with the banks, which Trun overlays
-        // lane k of a head group (k < 4: the group's distinct keys) writes
-        // its kept maxima of the tiles in the slice: row jrow, column
+        // the rest of the head max (lanes k and k ^ m of a head group keep the
+        // same keys for even m), then lanes 0 and 1 of each head group write
+        // their kept maxima of the tiles in the slice: row jrow, column
         // tile + 4 g4 + r
+#pragma unroll
+        for (int m = SGL; m < C::GL; m <<= 1)
+#pragma unroll
+            for (int t = 0; t < TPW; ++t)
+#pragma unroll
+                for (int hf = 0; hf < NHF; ++hf)
+#pragma unroll
+                    for (int kk = 0; kk < KEEP; ++kk)
+                        trun[t][hf][kk] = max(trun[t][hf][kk], __shfl_xor(trun[t][hf][kk], m));
         const int kg = (lane & 15) % C::GL;
 #pragma unroll
         for (int hf = 0; hf < NHF; ++hf)
-            if (jrow[hf] < a.N && kg < (C::GL >= 4 ? 4 : C::GL)) {
+            if (jrow[hf] < a.N && kg < SGL) {
 #pragma unroll
                 for (int t = 0; t < TPW; ++t) {
                     if (t >= ntv) break;
                     int* rowp = Trun + jrow[hf] * KRP + (w + SW * t) * kTileKeys + 4 * g4;
-                    if constexpr (KEEP == 1) {
-                        rowp[lane & 3] = trun[t][hf][0];
-                    } else if constexpr (KEEP == 2) {
+                    if constexpr (KEEP == 2) {
                         rowp[2 * (lane & 1)] = trun[t][hf][0];
                         rowp[2 * (lane & 1) + 1] = trun[t][hf][1];
                     } else {
