@@ -414,13 +414,14 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
         asm volatile("" : "+s"(kb2));  // a pointer of its own, not recomputed from a.K in the loop
 
         // Running max over units, in registers. The max over heads commutes
-        // with the max over units, so each step takes it only over lane pairs
-        // (heads 2m, 2m + 1: one DPP max) and the rest once, at the end.
-        // After the pair max both lanes of a pair hold the maxima of the 4 keys
-        // of their lane group (C rows r = 0..3); lane k keeps keys 2 (k % 2)
-        // and 2 (k % 2) + 1 (G >= 2), or all four (G = 1).
+        // with the max over units, so it is taken once, at the end, where the
+        // registers allow: each lane keeps the running maxima of its own query
+        // row for its 4 keys (C rows r = 0..3). Where the ring and the
+        // accumulators leave no room for that, each step takes the head max
+        // over lane pairs (heads 2m, 2m + 1: one DPP max) and lane k keeps
+        // keys 2 (k % 2) and 2 (k % 2) + 1 of its pair.
         constexpr int NHF = G == 32 ? 1 : NH;  // G = 32: both halves hold the one step
-        constexpr int SGL = C::GL >= 2 ? 2 : 1;  // lanes a step's head max spans
+        constexpr int SGL = C::GL >= 2 && C::NBUF * NLD * 4 + TPW * NH * 4 > 160 ? 2 : 1;
         constexpr int KEEP = 4 / SGL;
         int trun[TPW][NHF][KEEP];
 #pragma unroll
@@ -614,8 +615,8 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
         }
         __syncthreads();  // every wave is done with the banks, which Trun overlays
         // the rest of the head max (lanes k and k ^ m of a head group keep the
-        // same keys for even m), then lanes 0 and 1 of each head group write
-        // their kept maxima of the tiles in the slice: row jrow, column
+        // same keys for m >= SGL), then the first SGL lanes of each head group
+        // write their kept maxima of the tiles in the slice: row jrow, column
         // tile + 4 g4 + r
 #pragma unroll
         for (int m = SGL; m < C::GL; m <<= 1)
