@@ -401,6 +401,7 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
         const int tpart = (nkeys % kTileKeys != 0 && ntv > 0 && w + SW * (ntv - 1) == ntiles - 1) ? ntv - 1 : -1;
         // keys of tile tpart this lane's C rows may hold (4 g4 + r < rem)
         const int rem = nkeys - (w + SW * max(tpart, 0)) * kTileKeys - 4 * g4;
+        const bool full = tpart < 0 && ntv == TPW;  // every tile of this wave inside the slice
         uint32_t koff[TPW];  // buffer offset of this lane's first load of tile t
 #pragma unroll
         for (int t = 0; t < TPW; ++t)
@@ -421,7 +422,8 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
         // over lane pairs (heads 2m, 2m + 1: one DPP max) and lane k keeps
         // keys 2 (k % 2) and 2 (k % 2) + 1 of its pair.
         constexpr int NHF = G == 32 ? 1 : NH;  // G = 32: both halves hold the one step
-        constexpr int SGL = C::GL >= 2 && C::NBUF * NLD * 4 + TPW * NH * 4 > 160 ? 2 : 1;
+        constexpr bool kRoomy = C::NBUF * NLD * 4 + TPW * NH * 4 <= 160;  // K ring + accumulators
+        constexpr int SGL = C::GL >= 2 && !kRoomy ? 2 : 1;
         constexpr int KEEP = 4 / SGL;
         int trun[TPW][NHF][KEEP];
 #pragma unroll
@@ -471,57 +473,75 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
             // Per wave-row statistics over this wave's keys of the slice (lanes
             // L, L^16, L^32, L^48 hold the same row): the max m, the shifted
             // log2 logits y = c x - c m (<= 0 on those keys) and their exp2
-            // sum. Tiles t >= ntv are left out by wave-uniform selects; the
-            // keys of tile tpart past the slice's end, by per-lane masks in a
-            // branch only that tile's wave takes. The logits themselves are not
-            // masked: what is parked for keys outside the slice is never
-            // written out.
+            // sum. When the slice does not fill this wave's tiles (!FULL),
+            // tiles t >= ntv are left out by wave-uniform selects and the keys
+            // of tile tpart past the slice's end by per-lane masks in a branch
+            // only that tile's wave takes; waves whose tiles are all full take
+            // a copy without either. The logits themselves are not masked:
+            // what is parked for keys outside the slice is never written out.
+            auto stats = [&](auto FullC) __attribute__((always_inline)) {
+                constexpr bool FULL = decltype(FullC)::value;
 #pragma unroll
-            for (int hf = 0; hf < NH; ++hf) {
-                float m = -INFINITY;
+                for (int hf = 0; hf < NH; ++hf) {
+                    float m = -INFINITY;
 #pragma unroll
-                for (int t = 0; t < TPW; ++t) {
-                    float mt = fmaxf(fmaxf(acc[t][hf][0], acc[t][hf][1]), fmaxf(acc[t][hf][2], acc[t][hf][3]));
-                    if (t == tpart) {
-                        int lim = rem;
-                        asm volatile("" : "+v"(lim));  // keep the per-lane compares in this branch
-                        mt = -INFINITY;
+                    for (int t = 0; t < TPW; ++t) {
+                        float mt = fmaxf(fmaxf(acc[t][hf][0], acc[t][hf][1]), fmaxf(acc[t][hf][2], acc[t][hf][3]));
+                        if constexpr (FULL) {
+                            m = fmaxf(m, mt);
+                        } else {
+                            if (t == tpart) {
+                                int lim = rem;
+                                asm volatile("" : "+v"(lim));  // keep the per-lane compares in this branch
+                                mt = -INFINITY;
 #pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            if (r < lim) mt = fmaxf(mt, acc[t][hf][r]);
+                                for (int r = 0; r < 4; ++r)
+                                    if (r < lim) mt = fmaxf(mt, acc[t][hf][r]);
+                            }
+                            if (t < ntv) m = fmaxf(m, mt);
+                        }
                     }
-                    if (t < ntv) m = fmaxf(m, mt);
-                }
-                m = xor16_max(m);
-                m = xor32_max(m);
-                const float cm = m == -INFINITY ? 0.f : m * c;
-                float s = 0.f;
+                    m = xor16_max(m);
+                    m = xor32_max(m);
+                    const float cm = m == -INFINITY ? 0.f : m * c;
+                    float s = 0.f;
 #pragma unroll
-                for (int t = 0; t < TPW; ++t) {
-                    float e[4];
+                    for (int t = 0; t < TPW; ++t) {
+                        float e[4];
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const float y = fmaf(acc[t][hf][r], c, -cm);
-                        acc[t][hf][r] = y;
-                        e[r] = exp2_hw(y);
+                        for (int r = 0; r < 4; ++r) {
+                            const float y = fmaf(acc[t][hf][r], c, -cm);
+                            acc[t][hf][r] = y;
+                            e[r] = exp2_hw(y);
+                        }
+                        float st = (e[0] + e[1]) + (e[2] + e[3]);
+                        if constexpr (FULL) {
+                            s += st;
+                        } else {
+                            if (t == tpart) {
+                                int lim = rem;
+                                asm volatile("" : "+v"(lim));
+                                st = 0.f;
+#pragma unroll
+                                for (int r = 0; r < 4; ++r)
+                                    if (r < lim) st += e[r];
+                            }
+                            if (t < ntv) s += st;
+                        }
                     }
-                    float st = (e[0] + e[1]) + (e[2] + e[3]);
-                    if (t == tpart) {
-                        int lim = rem;
-                        asm volatile("" : "+v"(lim));
-                        st = 0.f;
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            if (r < lim) st += e[r];
+                    s = xor16_sum(s);
+                    s = xor32_sum(s);
+                    if (g4 == 0) {
+                        red[(P * SW + w) * ROWS + hf * 16 + lane] = make_float2(m, s);
+                        refs[(b * SW + w) * ROWS + hf * 16 + lane] = cm;
                     }
-                    if (t < ntv) s += st;
                 }
-                s = xor16_sum(s);
-                s = xor32_sum(s);
-                if (g4 == 0) {
-                    red[(P * SW + w) * ROWS + hf * 16 + lane] = make_float2(m, s);
-                    refs[(b * SW + w) * ROWS + hf * 16 + lane] = cm;
-                }
+            };
+            if constexpr (kRoomy) {
+                if (full) stats(std::true_type{});
+                else stats(std::false_type{});
+            } else {
+                stats(std::false_type{});  // (no registers for a second copy)
             }
             // park the shifted logits: 4 halves per (tile, half), NH*8 bytes per lane
 #pragma unroll
