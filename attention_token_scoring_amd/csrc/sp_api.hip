@@ -79,9 +79,13 @@ sp_status make_plan(const sp_score_desc& d, long long M, int cus, ScorePlan* out
     if (cus < 1) cus = kDefaultCUs;
     if (cus < 2) return SP_EUNSUPPORTED;
     const double bytes_per_key = (double)row_bytes;
-    const double bw_total = 6.0e12, bw_cu_max = 60.0e9;
-    // fixed cost of one step (barrier, finishing, exchange bookkeeping)
-    const double step_cost = 1.0e-6;
+    // A step takes the longer of (a) the busiest streaming wave's work on its
+    // tiles (measured on the MI355X: ~4.1 us for 4 tiles, ~5.7 us for 5 tiles
+    // without the registers for the guard-free statistics), and (b) the
+    // step's bytes at the HBM rate the kernel sustains (~6.2 TB/s).
+    const double bw_total = 6.2e12;
+    const double wave_base = 1.0e-6, wave_per_tile = 0.77e-6, wave_tight = 0.85e-6,
+                 wave_partial = 0.1e-6;
     double best = 1e300;
     int bg = 0, bkr = 0, bng = 0, bdef = 0, btpw = 0;
     const int tpw0 = tiles_per_wave(bf, d.d);
@@ -90,9 +94,18 @@ sp_status make_plan(const sp_score_desc& d, long long M, int cus, ScorePlan* out
     for (int tpw = tpw0; tpw <= tpw1; ++tpw) {
         const int cap = kStreamWaves * tpw * kTileKeys;
         const long long gmin = (M + cap - 1) / cap;
-        for (long long g = gmin; g <= cus - 1 && g <= kMaxRanks; ++g) {
+        const bool roomy = score_roomy(row_bytes, tpw, p.rows / 16);
+        for (long long cand = 0; cand < 2 * (cus - gmin + 1); ++cand) {
+            // each g with the smallest slice that covers M, then with a full one
+            // (cap keys; the last workgroup takes the rest)
+            const long long g = gmin + cand / 2;
+            if (g > cus - 1 || g > kMaxRanks) break;
             long long kr = (M + g - 1) / g;
             kr = (kr + tk - 1) / tk * tk;
+            if (cand % 2 == 1) {
+                if (kr == cap) continue;  // (already planned)
+                kr = cap;
+            }
             if (kr > cap) continue;
             const long long geff = (M + kr - 1) / kr;
             if (geff != g) continue;  // the same slice with fewer workgroups is planned at geff
@@ -107,14 +120,16 @@ sp_status make_plan(const sp_score_desc& d, long long M, int cus, ScorePlan* out
             if (ng > p.units) ng = p.units;
             if (ng < 1) continue;
             const long long iters = (p.units + ng - 1) / ng;
-            const double active = (double)(g * ng);
-            double bw_cu = bw_total / active;
-            if (bw_cu > bw_cu_max) bw_cu = bw_cu_max;
-            // a shallower deferral exposes more of each exchange's latency;
-            // tiles a wave computes but does not need cost MFMA and LDS time
+            // where the kernel has a guard-free copy of the statistics for
+            // waves whose tiles all lie inside the slice, a slice that leaves
+            // some wave short puts the slower copy on every step's critical
+            // path; a shallower deferral exposes more of each exchange's latency
+            const long long busiest = (kr / tk + kStreamWaves - 1) / kStreamWaves;  // tiles of the busiest wave
+            const double wave = wave_base + wave_per_tile * busiest + (roomy ? 0.0 : wave_tight) +
+                                (roomy && kr < cap ? wave_partial : 0.0);
+            const double hbm = (double)(g * ng) * kr * bytes_per_key / bw_total;
             const double sync = (kMaxDefer - defer) * 1.0e-6;
-            const double waste = (double)(cap - kr) / cap * 0.5e-6;
-            const double cost = iters * (kr * bytes_per_key / bw_cu + step_cost + sync + waste);
+            const double cost = iters * ((wave > hbm ? wave : hbm) + sync);
             if (cost < best * 0.999) {
                 best = cost;
                 bg = (int)g;

@@ -25,6 +25,14 @@ constexpr int kLdsBytes = 160 * 1024;  // LDS of one CU
 // Tiles per streaming wave and unit: the base value, or one more for long
 // prompts (a deeper slice per workgroup).
 constexpr int tiles_per_wave(bool bf16, int d) { return (!bf16 && d == 128) ? 2 : 4; }
+// Whether a streaming wave's K ring (two units of tpw tiles, row_bytes / 64
+// 16-byte loads each) and MFMA accumulators (tpw tiles x nh halves) leave
+// registers for the scoring kernel's second copy of the row statistics
+// (taken by waves whose tiles all lie inside the slice) and for per-row
+// running maxima (the head max taken once, at the end).
+constexpr bool score_roomy(int row_bytes, int tpw, int nh) {
+    return 2 * tpw * (row_bytes / 64) * 4 + tpw * nh * 4 <= 160;
+}
 // Floats per look-ahead row of the LDS running maximum: rows start 16 banks
 // apart.
 constexpr int row_stride(int kr) { return (kr + 63) / 64 * 64 + 16; }

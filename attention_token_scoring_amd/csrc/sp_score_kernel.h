@@ -422,7 +422,7 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
         // over lane pairs (heads 2m, 2m + 1: one DPP max) and lane k keeps
         // keys 2 (k % 2) and 2 (k % 2) + 1 of its pair.
         constexpr int NHF = G == 32 ? 1 : NH;  // G = 32: both halves hold the one step
-        constexpr bool kRoomy = C::NBUF * NLD * 4 + TPW * NH * 4 <= 160;  // K ring + accumulators
+        constexpr bool kRoomy = score_roomy(C::KB, TPW, NH);  // registers left by K ring + accumulators
         constexpr int SGL = C::GL >= 2 && !kRoomy ? 2 : 1;
         constexpr int KEEP = 4 / SGL;
         int trun[TPW][NHF][KEEP];
@@ -795,12 +795,13 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
         if (!last_s) return;
     }
     if (a.ngroups > 1) {
-        // XB values per thread, the other groups' copies GB groups at a time:
-        // XB * GB independent loads in flight instead of one round trip each
-        // (waiting workgroups would learn of the last arrival only by polling
-        // the counter, microseconds later than the last one learns it from
-        // its own increment, so one workgroup does the whole slice)
-        constexpr int XB = 8, GB = 8;
+        // XB values per thread (one pass covers N x 560 keys at N = 8), the
+        // other groups' copies GB groups at a time: XB * GB = 63 independent
+        // loads in flight (the most a wave can have) instead of one round
+        // trip each (waiting workgroups would learn of the last arrival only
+        // by polling the counter, microseconds later than the last one learns
+        // it from its own increment, so one workgroup does the whole slice)
+        constexpr int XB = 9, GB = 7;
         const int total = a.N * nkeys;
         const size_t gstride = (size_t)a.N * a.M;
         for (int x0 = 0; x0 < total; x0 += kThreads * XB) {
