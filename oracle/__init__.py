@@ -55,7 +55,9 @@ def _load():
         lib.oracle_score.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32, dbl, i32, vp]
         lib.oracle_select.argtypes = [vp, i32, i32, i32, i32, flt, flt, i32, flt, i32, flt, lng,
                                       lng, vp, vp, vp, vp, vp, vp, vp, vp]
-        for f in (lib.oracle_softmax_row, lib.oracle_score, lib.oracle_select):
+        lib.oracle_select_threshold.argtypes = [vp, i32, i32, flt, i32, i32, lng, lng, vp, vp, vp]
+        for f in (lib.oracle_softmax_row, lib.oracle_score, lib.oracle_select,
+                  lib.oracle_select_threshold):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -136,6 +138,25 @@ def select(importance, chunk, pool_k, mode, keep_rate=0.0, mass=0.0, boost_first
     if debug:
         return kept[:k].copy(), pos[:k].copy(), dict(v=v, q=q, C=C[:nc], key=key[:nc],
                                                     kept_chunk=kc[:nc].astype(bool))
+    return kept[:k].copy(), pos[:k].copy()
+
+
+def select_threshold(importance, chunk, keep_rate, min_tok=128, max_keep=0, pos_base=0,
+                     base_index=0):
+    """Threshold selection of one prompt as the Implementation Guide's program
+    performs it (see oracle_select_threshold): (kept_idx int32, pos_ids int32)."""
+    x = np.ascontiguousarray(importance, dtype=np.float32)
+    M = x.shape[0]
+    kept = np.empty(max(M, 1), np.int32)
+    pos = np.empty(max(M, 1), np.int32)
+    n = np.zeros(1, np.int32)
+    rc = _load().oracle_select_threshold(x.ctypes.data, M, int(chunk), float(keep_rate),
+                                         int(min_tok), int(max_keep), int(pos_base),
+                                         int(base_index), kept.ctypes.data, pos.ctypes.data,
+                                         n.ctypes.data)
+    if rc:
+        raise ValueError(f"oracle_select_threshold rejected its arguments ({rc})")
+    k = int(n[0])
     return kept[:k].copy(), pos[:k].copy()
 
 

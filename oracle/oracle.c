@@ -38,7 +38,10 @@
  *    window), rank by (pooled key desc, chunk index asc); top-K keeps
  *    max(1, ceil(rate * nc)) chunks, mass mode walks the ranking adding each
  *    chunk's own mass until it reaches mass * total; kept tokens ascend, with
- *    position id = pos_base + i.
+ *    position id = pos_base + i;
+ *  - threshold selection (oracle_select_threshold) follows the steps of the
+ *    Implementation Guide's own program on the raw scores; the cap keeps
+ *    every (n / max_keep)-th kept token and ends with the last kept one.
  */
 #include <math.h>
 #include <stdint.h>
@@ -305,5 +308,102 @@ int oracle_select(const float* importance, int M, int chunk, int pool_k, int mod
     if (key_out) memcpy(key_out, key, sizeof(double) * (size_t)nc);
     if (kept_chunk_out) memcpy(kept_chunk_out, keep, (size_t)nc);
     free(v); free(C); free(len); free(key); free(rk); free(keep);
+    return 0;
+}
+
+/* float comparison for qsort, descending */
+static int desc_f32(const void* a, const void* b) {
+    const float x = *(const float*)a, y = *(const float*)b;
+    return (x > y) ? -1 : (x < y);
+}
+
+/*
+ * Threshold chunk selection as the Implementation Guide's own program performs
+ * it: [SP-G] "Full Source Code" (its chunk selection and the cap on sparse
+ * tokens), "How It Works" / Chunk Selection (the first 4 and last 2 tokens are
+ * always kept) and "Configuration Reference" (SP_MAX_KEEP). On the raw float32
+ * scores x[0..M):
+ *  1. eff_min = min(min_tok, max(4, M / 10)); with keep_rate >= 1 or
+ *     M <= eff_min every token is kept;
+ *  2. chunk means a_c = (float)(s_c / n_c), s_c the double sum of the chunk's
+ *     scores in index order, n_c its token count;
+ *  3. K = max(1, ceil(nc * keep_rate)) with the product in single precision;
+ *     t = the K-th largest a_c; every chunk with a_c >= t is kept (equal
+ *     means may keep more than K chunks);
+ *  4. tokens 0..3 and, when M > 4, M-2 and M-1 are kept;
+ *  5. while fewer than eff_min tokens are kept, tokens of the chunks with
+ *     a_c < t are added in index order;
+ *  6. the kept tokens ascend; if max_keep > 0 and more than max_keep are kept,
+ *     only every (n / max_keep)-th of them is kept, at most max_keep, the last
+ *     of which is replaced by the last kept token.
+ * Outputs as for oracle_select. Returns 0, or -1 on invalid arguments.
+ */
+int oracle_select_threshold(const float* x, int M, int chunk, float keep_rate, int min_tok,
+                            int max_keep, long pos_base, long base_index, int32_t* kept_idx,
+                            int32_t* pos_ids, int32_t* n_kept) {
+    if (M < 1 || chunk < 1 || !(keep_rate > 0.0f) || min_tok < 0 || max_keep < 0) return -1;
+    const int four = 4, tenth = M / 10;
+    const int floor_min = tenth > four ? tenth : four;
+    const int eff_min = min_tok < floor_min ? min_tok : floor_min;
+    uint8_t* keep = (uint8_t*)calloc((size_t)M, 1);
+    if (!keep) return -2;
+    int all = keep_rate >= 1.0f || M <= eff_min;
+    if (all) {
+        memset(keep, 1, (size_t)M);
+    } else {
+        const long nc = (M + chunk - 1) / chunk;
+        float* a = (float*)malloc(sizeof(float) * (size_t)nc);
+        float* sorted = (float*)malloc(sizeof(float) * (size_t)nc);
+        if (!a || !sorted) {
+            free(a); free(sorted); free(keep);
+            return -2;
+        }
+        for (long c = 0; c < nc; ++c) {
+            const long i0 = c * chunk, i1 = (c + 1) * chunk < M ? (c + 1) * chunk : M;
+            double s = 0.0;
+            for (long i = i0; i < i1; ++i) s += (double)x[i];
+            a[c] = (float)(s / (double)(i1 - i0));
+            sorted[c] = a[c];
+        }
+        const float prod = (float)nc * keep_rate;
+        long K = (long)ceilf(prod);
+        if (K < 1) K = 1;
+        qsort(sorted, (size_t)nc, sizeof(float), desc_f32);
+        const float t = sorted[K - 1];
+        long n = 0;
+        for (long c = 0; c < nc; ++c) {
+            if (!(a[c] >= t)) continue;
+            const long i1 = (c + 1) * chunk < M ? (c + 1) * chunk : M;
+            for (long i = c * chunk; i < i1; ++i) keep[i] = 1, ++n;
+        }
+        const int always[6] = {0, 1, 2, 3, M - 2, M - 1};
+        const int n_always = M > 4 ? 6 : 4;
+        for (int k = 0; k < n_always; ++k)
+            if (always[k] < M && !keep[always[k]]) keep[always[k]] = 1, ++n;
+        for (long c = 0; c < nc && n < eff_min; ++c) {
+            if (a[c] >= t) continue;
+            const long i1 = (c + 1) * chunk < M ? (c + 1) * chunk : M;
+            for (long i = c * chunk; i < i1 && n < eff_min; ++i)
+                if (!keep[i]) keep[i] = 1, ++n;
+        }
+        free(a);
+        free(sorted);
+    }
+    int32_t n = 0;
+    for (long i = 0; i < M; ++i)
+        if (keep[i]) kept_idx[n++] = (int32_t)i;
+    free(keep);
+    if (max_keep > 0 && n > max_keep) {
+        const int32_t step = n / max_keep, last = kept_idx[n - 1];
+        int32_t m = 0;
+        for (int32_t i = 0; i < n && m < max_keep; i += step) kept_idx[m++] = kept_idx[i];
+        kept_idx[m - 1] = last;
+        n = m;
+    }
+    for (int32_t k = 0; k < n; ++k) {
+        pos_ids[k] = (int32_t)(pos_base + kept_idx[k]);
+        kept_idx[k] = (int32_t)(base_index + kept_idx[k]);
+    }
+    *n_kept = n;
     return 0;
 }
