@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(_HERE, "libspecprefill.so")
 
 SP_OK, SP_EINVAL, SP_EUNSUPPORTED, SP_EWORKSPACE, SP_EDEVICE = range(5)
 SP_F32, SP_BF16 = 0, 1
-SP_SELECT_TOPK, SP_SELECT_MASS = 0, 1
+SP_SELECT_TOPK, SP_SELECT_MASS, SP_SELECT_THRESHOLD = 0, 1, 2
 SP_LAUNCH_RESIDENT, SP_LAUNCH_COOPERATIVE = 0, 1
 
 EXPORTED = ("sp_score", "sp_score_varlen", "sp_select", "sp_select_varlen",
@@ -48,7 +48,8 @@ class SelectParams(ctypes.Structure):
     _fields_ = [("chunk", ctypes.c_int32), ("pool_k", ctypes.c_int32), ("mode", ctypes.c_int),
                 ("keep_rate", ctypes.c_float), ("mass", ctypes.c_float),
                 ("boost_first_n", ctypes.c_int32), ("boost_first_mult", ctypes.c_float),
-                ("boost_last_n", ctypes.c_int32), ("boost_last_mult", ctypes.c_float)]
+                ("boost_last_n", ctypes.c_int32), ("boost_last_mult", ctypes.c_float),
+                ("min_tok", ctypes.c_int32), ("max_keep", ctypes.c_int32)]
 
 
 _lib = None
@@ -128,11 +129,13 @@ def score_desc(L, H, Hkv, d, N, dtype=SP_BF16, scale=0.0, launch=SP_LAUNCH_RESID
 
 
 def select_params(chunk=32, pool_k=1, mode="topk", keep_rate=0.0, mass=0.0, boost_first_n=0,
-                  boost_first_mult=1.0, boost_last_n=0, boost_last_mult=1.0) -> SelectParams:
-    m = {"topk": SP_SELECT_TOPK, "mass": SP_SELECT_MASS}.get(mode, mode)
+                  boost_first_mult=1.0, boost_last_n=0, boost_last_mult=1.0, min_tok=0,
+                  max_keep=0) -> SelectParams:
+    m = {"topk": SP_SELECT_TOPK, "mass": SP_SELECT_MASS,
+         "threshold": SP_SELECT_THRESHOLD}.get(mode, mode)
     return SelectParams(int(chunk), int(pool_k), int(m), float(keep_rate), float(mass),
                         int(boost_first_n), float(boost_first_mult), int(boost_last_n),
-                        float(boost_last_mult))
+                        float(boost_last_mult), int(min_tok), int(max_keep))
 
 
 def sp_score_workspace_bytes(desc: ScoreDesc, max_prompt_len: int) -> int:

@@ -186,9 +186,15 @@ sp_status check_select_params(const sp_select_params* p) {
         if (!(p->keep_rate > 0.f && p->keep_rate <= 1.f)) return SP_EINVAL;
     } else if (p->mode == SP_SELECT_MASS) {
         if (!(p->mass > 0.f && p->mass <= 1.f)) return SP_EINVAL;
+    } else if (p->mode == SP_SELECT_THRESHOLD) {
+        // raw scores: no pooling, no boosts
+        if (!(p->keep_rate > 0.f && p->keep_rate <= 1.f)) return SP_EINVAL;
+        if (p->pool_k != 1 || p->boost_first_n != 0 || p->boost_last_n != 0) return SP_EINVAL;
+        if (p->min_tok < 0 || p->max_keep < 0) return SP_EINVAL;
     } else {
         return SP_EINVAL;
     }
+    if (p->mode != SP_SELECT_THRESHOLD && (p->min_tok != 0 || p->max_keep != 0)) return SP_EINVAL;
     if (p->boost_first_n < 0 || p->boost_last_n < 0) return SP_EINVAL;
     if (!(p->boost_first_mult >= 0.f) || !(p->boost_last_mult >= 0.f) ||
         !isfinite(p->boost_first_mult) || !isfinite(p->boost_last_mult))
@@ -202,6 +208,7 @@ sp_status check_select_prompt(const sp_select_params* p, long long M) {
     if (M > (1ll << 24)) return SP_EUNSUPPORTED;
     const long long nc = (M + p->chunk - 1) / p->chunk;
     if (nc > kMaxSelectChunks) return SP_EUNSUPPORTED;
+    if (p->mode == SP_SELECT_THRESHOLD) return SP_OK;  // (no fixed-point sums)
     double vmax = 1.0;
     const double a = p->boost_first_mult, b = p->boost_last_mult;
     if (a > vmax) vmax = a;
@@ -224,6 +231,8 @@ SelectParamsDev to_dev(const sp_select_params* p) {
     q.first_mult = p->boost_first_mult;
     q.last_n = p->boost_last_n;
     q.last_mult = p->boost_last_mult;
+    q.min_tok = p->min_tok;
+    q.max_keep = p->max_keep;
     return q;
 }
 

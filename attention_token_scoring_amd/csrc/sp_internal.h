@@ -119,6 +119,7 @@ struct SelectParamsDev {
     float first_mult;
     int last_n;
     float last_mult;
+    int min_tok, max_keep;  // (threshold mode)
 };
 
 // Events the calling thread wants recorded around each scoring kernel launch

@@ -2,10 +2,13 @@
 (sp_select) on one MI355X.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
-               [--copy-probe-mib MIB] [--cooperative]
+               [--copy-probe-mib MIB] [--cooperative] [--select workload|threshold]
 
 --workload takes any workload of synth (default: the 8B shape at M = 32K); the
 ragged batch is timed through sp_score_varlen + sp_select_varlen.
+--select threshold times the threshold selection (SP_SELECT_THRESHOLD, the
+Implementation Guide program's chunk selection with its 128-token fill and
+2000-token cap) instead of the workload's selection.
 --cooperative launches the scoring kernel cooperatively (SP_LAUNCH_COOPERATIVE)
 instead of with the default ordinary launch.
 
@@ -30,6 +33,7 @@ layers, scaled to the full workload).
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import math
@@ -54,6 +58,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="spec8b_m32k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--select", choices=("workload", "threshold"), default="workload",
+                    help="the workload's selection, or the Implementation Guide program's "
+                         "threshold selection (min_tok 128, max_keep 2000)")
     ap.add_argument("--cooperative", action="store_true",
                     help="launch the scoring kernel cooperatively (SP_LAUNCH_COOPERATIVE)")
     ap.add_argument("--cpu-layers", type=int, default=1 << 30,
@@ -145,17 +152,33 @@ def load_traffic(workload: str):
     return t.get("bytes_per_launch")
 
 
+THRESHOLD_MIN_TOK, THRESHOLD_MAX_KEEP = 128, 2000
+
+
+def select_params(sp, sel):
+    extra = dict(min_tok=THRESHOLD_MIN_TOK, max_keep=THRESHOLD_MAX_KEEP) \
+        if sel.mode == "threshold" else {}
+    return sp.select_params(chunk=sel.chunk, pool_k=sel.pool_k, mode=sel.mode,
+                            keep_rate=sel.keep_rate, mass=sel.mass,
+                            boost_first_n=sel.boost_first_n,
+                            boost_first_mult=sel.boost_first_mult,
+                            boost_last_n=sel.boost_last_n, boost_last_mult=sel.boost_last_mult,
+                            **extra)
+
+
 def workload_desc(w, sel) -> dict:
     d = {"workload": f"{w.name}: L={w.L} H={w.H} Hkv={w.Hkv} d={w.d} M={w.M} N={w.N} "
                      f"{'bf16' if w.dtype else 'f32'}; select {sel.mode} "
-                     f"{sel.keep_rate if sel.mode == 'topk' else sel.mass} chunk {sel.chunk} "
+                     f"{sel.mass if sel.mode == 'mass' else sel.keep_rate} chunk {sel.chunk} "
                      f"pool {sel.pool_k}",
          "L": w.L, "H": w.H, "Hkv": w.Hkv, "d": w.d, "M": w.M, "N": w.N,
          "select": sel.mode, "chunk": sel.chunk, "pool_k": sel.pool_k}
-    if sel.mode == "topk":
-        d["keep_rate"] = sel.keep_rate
-    else:
+    if sel.mode == "mass":
         d["mass"] = sel.mass
+    else:
+        d["keep_rate"] = sel.keep_rate
+    if sel.mode == "threshold":
+        d["min_tok"], d["max_keep"] = THRESHOLD_MIN_TOK, THRESHOLD_MAX_KEEP
     if sel.boost_first_n or sel.boost_last_n:
         d["boosts"] = [sel.boost_first_n, sel.boost_first_mult, sel.boost_last_n,
                        sel.boost_last_mult]
@@ -176,7 +199,11 @@ def cpu_baseline(w, sel, Qh, Kh, layers: int, min_seconds: float = 10.0):
         t0 = time.perf_counter()
         imp = oracle.score(Qh[:layers], Kh[:layers], nthreads=threads)
         t1 = time.perf_counter()
-        oracle.select(imp.astype(np.float32), **oracle.select_params(sel))
+        if sel.mode == "threshold":
+            oracle.select_threshold(imp.astype(np.float32), sel.chunk, sel.keep_rate,
+                                    min_tok=THRESHOLD_MIN_TOK, max_keep=THRESHOLD_MAX_KEEP)
+        else:
+            oracle.select(imp.astype(np.float32), **oracle.select_params(sel))
         t2 = time.perf_counter()
         t_score += t1 - t0
         t_sel += t2 - t1
@@ -206,6 +233,11 @@ def main():
 
     w = synth.WORKLOADS[args.workload]
     sel = w.selects[0]
+    if args.select == "threshold":
+        # the Implementation Guide program's selection at its defaults (keep
+        # rate 0.3 unless the workload fixes one, 128-token fill, 2000-token cap)
+        sel = dataclasses.replace(sel, mode="threshold", pool_k=1, keep_rate=sel.keep_rate or 0.3,
+                                  mass=0.0, boost_first_n=0, boost_last_n=0)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if w.R != 1:
@@ -231,11 +263,7 @@ def main():
     kept = torch.empty(M, dtype=torch.int32, device=dev)
     pos = torch.empty(M, dtype=torch.int32, device=dev)
     nk = torch.empty(1, dtype=torch.int32, device=dev)
-    params = sp.select_params(chunk=sel.chunk, pool_k=sel.pool_k, mode=sel.mode,
-                              keep_rate=sel.keep_rate, mass=sel.mass,
-                              boost_first_n=sel.boost_first_n,
-                              boost_first_mult=sel.boost_first_mult,
-                              boost_last_n=sel.boost_last_n, boost_last_mult=sel.boost_last_mult)
+    params = select_params(sp, sel)
     plan = sp.sp_score_plan(desc, M)
 
     if args.copy_probe_mib:
@@ -355,11 +383,7 @@ def ragged(args, w, sel, sp, torch, dev):
     kept = torch.empty(total, dtype=torch.int32, device=dev)
     pos = torch.empty(total, dtype=torch.int32, device=dev)
     nk = torch.empty(R, dtype=torch.int32, device=dev)
-    params = sp.select_params(chunk=sel.chunk, pool_k=sel.pool_k, mode=sel.mode,
-                              keep_rate=sel.keep_rate, mass=sel.mass,
-                              boost_first_n=sel.boost_first_n,
-                              boost_first_mult=sel.boost_first_mult,
-                              boost_last_n=sel.boost_last_n, boost_last_mult=sel.boost_last_mult)
+    params = select_params(sp, sel)
 
     def step(ev=None):
         if ev is not None:

@@ -51,7 +51,7 @@ typedef enum {
 
 typedef enum { SP_F32 = 0, SP_BF16 = 1 } sp_dtype;
 
-typedef enum { SP_SELECT_TOPK = 0, SP_SELECT_MASS = 1 } sp_select_mode;
+typedef enum { SP_SELECT_TOPK = 0, SP_SELECT_MASS = 1, SP_SELECT_THRESHOLD = 2 } sp_select_mode;
 
 /* How sp_score launches its scoring kernel, whose workgroups wait on each
  * other and so must all be resident on the device at once.
@@ -85,11 +85,15 @@ typedef struct {
 
 /* Selection parameters ([SP-G] Configuration Reference gives the pages'
  * defaults: chunk 32, keep rate 0.3, mass 0.85, boosts first 64 x1.5 and last
- * 128 x1.3).
+ * 128 x1.3, SP_MAX_KEEP 2000).
  *   chunk      tokens per chunk (>= 1)
  *   pool_k     odd width of the average pool over chunk scores (1 = none)
- *   mode       SP_SELECT_TOPK uses keep_rate in (0,1]; SP_SELECT_MASS uses mass in (0,1]
- *   boost_*    multipliers >= 0 for the first / last n tokens (1.0 = off) */
+ *   mode       SP_SELECT_TOPK uses keep_rate in (0,1]; SP_SELECT_MASS uses mass in (0,1];
+ *              SP_SELECT_THRESHOLD uses keep_rate in (0,1], min_tok and max_keep
+ *   boost_*    multipliers >= 0 for the first / last n tokens (1.0 = off)
+ *   min_tok    (threshold mode) >= 0; the fill target is min(min_tok, max(4, M/10))
+ *              tokens (the Guide's program passes 128); 0 in the other modes
+ *   max_keep   (threshold mode) >= 0; cap on kept tokens, 0 = none; 0 in the other modes */
 typedef struct {
     int32_t chunk, pool_k;
     sp_select_mode mode;
@@ -98,6 +102,7 @@ typedef struct {
     float boost_first_mult;
     int32_t boost_last_n;
     float boost_last_mult;
+    int32_t min_tok, max_keep;
 } sp_select_params;
 
 /* Bytes of device workspace sp_score / sp_score_varlen need for prompts of at
@@ -162,6 +167,24 @@ size_t sp_select_workspace_bytes(int32_t R, int64_t total_prompt_len,
  *  7. every token i of every kept chunk, ascending:
  *     kept_idx[n] = i, pos_ids[n] = pos_base + i. The first decode position
  *     afterwards is pos_base + M.
+ * SP_SELECT_THRESHOLD instead follows the Implementation Guide's own program
+ * ([SP-G] Full Source Code, its chunk selection and the cap on sparse tokens;
+ * How It Works, chunk selection; Configuration Reference, SP_MAX_KEEP) on the
+ * raw scores (pool_k must be 1 and the boosts off):
+ *  a. eff_min = min(min_tok, max(4, M/10)); keep_rate >= 1 or M <= eff_min
+ *     keeps every token;
+ *  b. chunk means a_c = (float)(double sum of the chunk's scores in index
+ *     order / its token count);
+ *  c. K = max(1, ceil((float)nc * keep_rate)) (single-precision product);
+ *     every chunk whose mean is >= the K-th largest mean is kept (equal
+ *     means may keep more than K chunks);
+ *  d. tokens 0..3 and, when M > 4, M-2 and M-1 are kept;
+ *  e. while fewer than eff_min tokens are kept, the tokens of the other
+ *     chunks are added in index order;
+ *  f. the kept tokens ascend; with max_keep > 0 and more than max_keep kept,
+ *     only kept[0], kept[s], kept[2s], ... (s = n / max_keep, integer
+ *     division; max_keep of them) remain, the last replaced by the last kept
+ *     token.
  * The result is a pure function of the float32 scores: identical inputs give
  * identical outputs on every run.
  *   importance  device, [M] float32

@@ -124,6 +124,14 @@ def test_plan_for_the_8b_shape(lib):
     (dict(boost_last_n=-3), sp.SP_EINVAL),
     (dict(chunk=1), sp.SP_EUNSUPPORTED),            # nc = 10000 > 4096
     (dict(boost_first_mult=3e6), sp.SP_EUNSUPPORTED),  # pooled sums would exceed 2^53
+    (dict(min_tok=128), sp.SP_EINVAL),              # threshold-mode fields in top-K mode
+    (dict(mode="mass", mass=0.5, max_keep=10), sp.SP_EINVAL),
+    (dict(mode="threshold"), sp.SP_EINVAL),         # threshold mode takes no pooling
+    (dict(mode="threshold", pool_k=1, boost_first_n=4), sp.SP_EINVAL),  # nor boosts
+    (dict(mode="threshold", pool_k=1, min_tok=-1), sp.SP_EINVAL),
+    (dict(mode="threshold", pool_k=1, max_keep=-1), sp.SP_EINVAL),
+    (dict(mode="threshold", pool_k=1, keep_rate=0.0), sp.SP_EINVAL),
+    (dict(mode="threshold", pool_k=1, chunk=1), sp.SP_EUNSUPPORTED),  # nc = 10000 > 4096
 ])
 def test_select_rejects(lib, kw, status):
     base = dict(chunk=32, pool_k=3, mode="topk", keep_rate=0.3)

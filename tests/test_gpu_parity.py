@@ -346,3 +346,77 @@ def test_select_matches_oracle(case, dist):
     else:
         x = rng.random(M) ** 8 * 1e-3
     _select_case(x, pos_base=3, **kw)
+
+
+# ----------------------------------------------------------------------------------------
+# threshold selection (the Implementation Guide program's chunk selection and cap)
+# ----------------------------------------------------------------------------------------
+THRESH_CASES = [
+    dict(M=10, chunk=1, keep_rate=0.5, min_tok=0, max_keep=0),
+    dict(M=32768, chunk=32, keep_rate=0.3, min_tok=128, max_keep=0),
+    dict(M=32768, chunk=32, keep_rate=0.3, min_tok=128, max_keep=2000),  # the Guide's defaults
+    dict(M=4608, chunk=32, keep_rate=0.1, min_tok=128, max_keep=0),
+    dict(M=200, chunk=10, keep_rate=0.05, min_tok=128, max_keep=0),      # the fill
+    dict(M=3, chunk=1, keep_rate=0.3, min_tok=0, max_keep=0),
+    dict(M=5, chunk=5, keep_rate=0.5, min_tok=0, max_keep=0),
+    dict(M=4, chunk=1, keep_rate=0.3, min_tok=128, max_keep=0),         # M <= eff_min
+    dict(M=8, chunk=3, keep_rate=0.4, min_tok=128, max_keep=3),
+    dict(M=1000, chunk=24, keep_rate=1.0, min_tok=128, max_keep=333),   # everything, capped
+    dict(M=131072, chunk=32, keep_rate=0.2, min_tok=128, max_keep=5000),  # nc = 4096
+    dict(M=1 << 20, chunk=256, keep_rate=0.5, min_tok=128, max_keep=100000),
+    dict(M=50000, chunk=20000, keep_rate=0.5, min_tok=64, max_keep=0),  # three chunks
+]
+
+
+def _threshold_case(x, pos_base=0, **kw):
+    params = sp.select_params(mode="threshold", pool_k=1, **kw)
+    t = torch.from_numpy(x.astype(np.float32)).cuda()
+    kept, pos, n = sp.sp_select(t, params, pos_base=pos_base)
+    torch.cuda.synchronize()
+    k_ref, p_ref = oracle.select_threshold(x.astype(np.float32), kw["chunk"], kw["keep_rate"],
+                                           min_tok=kw["min_tok"], max_keep=kw["max_keep"],
+                                           pos_base=pos_base)
+    nk = int(n.cpu()[0])
+    assert nk == len(k_ref), (kw, nk, len(k_ref))
+    assert np.array_equal(kept[:nk].cpu().numpy(), k_ref), kw
+    assert np.array_equal(pos[:nk].cpu().numpy(), p_ref), kw
+
+
+@pytest.mark.parametrize("dist", ["uniform", "ties", "constant", "spiky"])
+@pytest.mark.parametrize("case", THRESH_CASES,
+                         ids=[f"{c['M']}-{c['chunk']}-{c['keep_rate']}-{c['max_keep']}"
+                              for c in THRESH_CASES])
+def test_select_threshold_matches_oracle(case, dist):
+    kw = dict(case)
+    M = kw.pop("M")
+    rng = np.random.default_rng(M + 7 * len(dist))
+    if dist == "uniform":
+        x = rng.random(M)
+    elif dist == "ties":
+        x = rng.integers(0, 4, M) / 3.0
+    elif dist == "constant":
+        x = np.full(M, 0.25)
+    else:
+        x = rng.random(M) ** 12
+    _threshold_case(x, pos_base=M % 7, **kw)
+
+
+def test_select_threshold_varlen():
+    rng = np.random.default_rng(3)
+    Ms = [5000, 3, 777, 32768, 64, 12000]
+    cu = np.concatenate([[0], np.cumsum(Ms)]).astype(np.int64)
+    x = (rng.random(int(cu[-1])) ** 4).astype(np.float32)
+    kw = dict(chunk=32, keep_rate=0.3, min_tok=128, max_keep=700)
+    params = sp.select_params(mode="threshold", pool_k=1, **kw)
+    t = torch.from_numpy(x).cuda()
+    pos_base = [(11 * r) % 5 for r in range(len(Ms))]
+    kept, pos, n = sp.sp_select_varlen(t, cu, params, pos_base=pos_base)
+    torch.cuda.synchronize()
+    kept_h, pos_h, n_h = kept.cpu().numpy(), pos.cpu().numpy(), n.cpu().numpy()
+    for r in range(len(Ms)):
+        k_ref, p_ref = oracle.select_threshold(x[cu[r]:cu[r + 1]], pos_base=pos_base[r],
+                                               base_index=int(cu[r]), **kw)
+        off = int(cu[r])
+        assert n_h[r] == len(k_ref), r
+        assert np.array_equal(kept_h[off:off + n_h[r]], k_ref), r
+        assert np.array_equal(pos_h[off:off + n_h[r]], p_ref), r
