@@ -7,7 +7,8 @@ device memory and the current stream. There is no CPU fallback: if the
 library is missing, or a call fails, an exception says so.
 
 The call names follow the C ABI in ``include/specprefill.h``:
-``sp_score``, ``sp_score_varlen``, ``sp_select``, ``sp_select_varlen``,
+``sp_score``, ``sp_score_varlen``, ``sp_score_windows``, ``sp_window_layout``,
+``sp_select``, ``sp_select_varlen``,
 ``sp_score_workspace_bytes``, ``sp_select_workspace_bytes``,
 ``sp_score_plan`` and ``sp_status_string``.
 """
@@ -29,7 +30,8 @@ SP_LAUNCH_RESIDENT, SP_LAUNCH_COOPERATIVE = 0, 1
 
 EXPORTED = ("sp_score", "sp_score_varlen", "sp_select", "sp_select_varlen",
             "sp_score_workspace_bytes", "sp_select_workspace_bytes", "sp_score_plan",
-            "sp_status_string", "sp_profile_score_kernel", "sp_score_status")
+            "sp_status_string", "sp_profile_score_kernel", "sp_score_status",
+            "sp_score_windows", "sp_window_layout")
 
 
 class SpError(RuntimeError):
@@ -80,8 +82,13 @@ def load_library():
                                      P(SelectParams), vp, vp, vp, vp, sz, vp]
     lib.sp_profile_score_kernel.argtypes = [vp, vp]
     lib.sp_score_status.argtypes = [vp, vp, P(ctypes.c_int32)]
+    lib.sp_score_windows.argtypes = [P(ScoreDesc), i32, vp, vp, P(ctypes.c_int64),
+                                     P(ctypes.c_int64), vp, vp, sz, vp]
+    lib.sp_window_layout.argtypes = [i64, i32, i32, P(ctypes.c_int32), P(ctypes.c_int64),
+                                     P(ctypes.c_int64), P(ctypes.c_int64), i32]
     for name in ("sp_score_plan", "sp_score", "sp_score_varlen", "sp_select", "sp_select_varlen",
-                 "sp_profile_score_kernel", "sp_score_status"):
+                 "sp_profile_score_kernel", "sp_score_status", "sp_score_windows",
+                 "sp_window_layout"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -229,6 +236,50 @@ def sp_score_varlen(Q, K, cu_prompt: Sequence[int], scale: float = 0.0, out=None
         cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), out.data_ptr(), ws.data_ptr(),
         ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "sp_score_varlen")
+    return out
+
+
+def sp_window_layout(M: int, window: int, stride: int):
+    """(starts, lens, keeps) int64 arrays of the sliding windows over M tokens."""
+    lib = load_library()
+    n = ctypes.c_int32(0)
+    _check(lib.sp_window_layout(int(M), int(window), int(stride), ctypes.byref(n), None, None,
+                                None, 0), "sp_window_layout")
+    R = n.value
+    starts, lens, keeps = (np.zeros(R, np.int64) for _ in range(3))
+    p64 = ctypes.POINTER(ctypes.c_int64)
+    _check(lib.sp_window_layout(int(M), int(window), int(stride), ctypes.byref(n),
+                                starts.ctypes.data_as(p64), lens.ctypes.data_as(p64),
+                                keeps.ctypes.data_as(p64), R), "sp_window_layout")
+    return starts, lens, keeps
+
+
+def sp_score_windows(Q, K, cu_window: Sequence[int], keeps: Sequence[int], scale: float = 0.0,
+                     out=None, workspace=None, stream=None, launch: int = SP_LAUNCH_RESIDENT):
+    """importance [sum keeps] float32 of R windows: Q [R,L,H,N,d], K [L,Hkv,T,d]
+    laid out as for sp_score_varlen (cu_window: host offsets [R+1] of the
+    windows' prompt keys); window r contributes its first keeps[r] scores."""
+    torch = _torch()
+    _require_cuda(Q, K)
+    R, L, H, N, d = Q.shape
+    Hkv = K.shape[1]
+    cu = np.ascontiguousarray(np.asarray(cu_window, dtype=np.int64))
+    kp = np.ascontiguousarray(np.asarray(keeps, dtype=np.int64))
+    if cu.shape != (R + 1,) or kp.shape != (R,):
+        raise ValueError("cu_window must hold R+1 offsets and keeps R counts")
+    desc = score_desc(L, H, Hkv, d, N, _dtype_code(Q), scale, launch)
+    if K.shape[2] != int(cu[-1]) + R * N:
+        raise ValueError("K must hold sum(M_r + N) key rows")
+    if out is None:
+        out = torch.empty(int(kp.sum()), dtype=torch.float32, device=Q.device)
+    maxM = int(np.max(np.diff(cu)))
+    ws = _workspace(sp_score_workspace_bytes(desc, maxM), Q.device, workspace)
+    p64 = ctypes.POINTER(ctypes.c_int64)
+    st = load_library().sp_score_windows(
+        ctypes.byref(desc), int(R), Q.data_ptr(), K.data_ptr(), cu.ctypes.data_as(p64),
+        kp.ctypes.data_as(p64), out.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(),
+        _stream(stream))
+    _check(st, "sp_score_windows")
     return out
 
 

@@ -10,7 +10,7 @@
 namespace sp {
 
 hipError_t launch_score(const ScorePlan& p, const sp_score_desc& d, const void* Q, const void* K,
-                        long long plane_stride, int M, float* importance, void* ws,
+                        long long plane_stride, int M, int M_out, float* importance, void* ws,
                         hipStream_t stream);
 hipError_t launch_select(const SelectParamsDev& p, const int64_t* cu, const int32_t* pos_base,
                          int R, const float* importance, int32_t* kept_idx, int32_t* pos_ids,
@@ -311,19 +311,26 @@ sp_status sp_score(const sp_score_desc* desc, const void* Q, const void* K, int3
     if (s != SP_OK) return s;
     if (!ws || !aligned(ws, 256) || ws_bytes < p.ws_total) return SP_EWORKSPACE;
     const long long plane = (long long)(M + desc->N) * desc->d;
-    return to_status(launch_score(p, *desc, Q, K, plane, M, importance, ws, (hipStream_t)stream));
+    return to_status(launch_score(p, *desc, Q, K, plane, M, M, importance, ws, (hipStream_t)stream));
 }
 
-sp_status sp_score_varlen(const sp_score_desc* desc, int32_t R, const void* Q, const void* K,
-                          const int64_t* cu, float* importance, void* ws, size_t ws_bytes,
-                          void* stream) {
+namespace {
+
+// Requests r in [0, R) of a ragged batch, each scored alone; with keep, only the
+// first keep[r] scores of request r are written, packed one request after the
+// other (else all M_r scores at offset cu[r]).
+sp_status score_batch(const sp_score_desc* desc, int32_t R, const void* Q, const void* K,
+                      const int64_t* cu, const int64_t* keep, float* importance, void* ws,
+                      size_t ws_bytes, void* stream) {
     sp_status s = check_desc(desc);
     if (s != SP_OK) return s;
     if (R < 1 || !Q || !K || !cu || !importance) return SP_EINVAL;
     if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(importance, 4)) return SP_EINVAL;
     if (cu[0] != 0) return SP_EINVAL;
-    for (int r = 0; r < R; ++r)
+    for (int r = 0; r < R; ++r) {
         if (cu[r + 1] - cu[r] < 1) return SP_EINVAL;
+        if (keep && (keep[r] < 1 || keep[r] > cu[r + 1] - cu[r])) return SP_EINVAL;
+    }
     if (cu[R] + (long long)R * desc->N > (1ll << 40)) return SP_EUNSUPPORTED;
     const int cus = device_cus();
     if (cus < 1) return SP_EDEVICE;
@@ -338,16 +345,58 @@ sp_status sp_score_varlen(const sp_score_desc* desc, int32_t R, const void* Q, c
     const int es = esize(desc->dtype);
     const long long T = cu[R] + (long long)R * desc->N;
     const long long qsz = (long long)desc->L * desc->H * desc->N * desc->d * es;
+    long long out = 0;
     for (int r = 0; r < R; ++r) {
         const long long M = cu[r + 1] - cu[r];
         ScorePlan p;
         make_plan(*desc, M, cus, &p);
         const char* Qr = (const char*)Q + r * qsz;
         const char* Kr = (const char*)K + (cu[r] + (long long)r * desc->N) * desc->d * es;
-        s = to_status(launch_score(p, *desc, Qr, Kr, T * desc->d, (int)M, importance + cu[r], ws,
+        const long long M_out = keep ? keep[r] : M;
+        float* imp = importance + (keep ? out : cu[r]);
+        s = to_status(launch_score(p, *desc, Qr, Kr, T * desc->d, (int)M, (int)M_out, imp, ws,
                                    (hipStream_t)stream));
         if (s != SP_OK) return s;
+        out += M_out;
     }
+    return SP_OK;
+}
+
+}  // namespace
+
+sp_status sp_score_varlen(const sp_score_desc* desc, int32_t R, const void* Q, const void* K,
+                          const int64_t* cu, float* importance, void* ws, size_t ws_bytes,
+                          void* stream) {
+    return score_batch(desc, R, Q, K, cu, nullptr, importance, ws, ws_bytes, stream);
+}
+
+sp_status sp_score_windows(const sp_score_desc* desc, int32_t R, const void* Q, const void* K,
+                           const int64_t* cu_window_host, const int64_t* keep_host,
+                           float* importance, void* ws, size_t ws_bytes, void* stream) {
+    if (!keep_host) return SP_EINVAL;
+    return score_batch(desc, R, Q, K, cu_window_host, keep_host, importance, ws, ws_bytes, stream);
+}
+
+sp_status sp_window_layout(int64_t M, int32_t window, int32_t stride, int32_t* n_windows,
+                           int64_t* starts, int64_t* lens, int64_t* keeps, int32_t capacity) {
+    if (!n_windows || M < 1 || window < 1 || stride < 1 || stride > window || capacity < 0)
+        return SP_EINVAL;
+    // windows at 0, stride, 2 stride, ...; each keeps its first stride scores,
+    // the one that reaches the prompt's end keeps all of its own and is last
+    int32_t R = 0;
+    for (int64_t pos = 0;; pos += stride) {
+        const int64_t end = pos + window < M ? pos + window : M;
+        const bool last = end >= M;
+        if (starts && R < capacity) {
+            starts[R] = pos;
+            lens[R] = end - pos;
+            keeps[R] = last ? end - pos : stride;
+        }
+        ++R;
+        if (last) break;
+    }
+    *n_windows = R;
+    if (starts && (!lens || !keeps || capacity < R)) return SP_EINVAL;
     return SP_OK;
 }
 

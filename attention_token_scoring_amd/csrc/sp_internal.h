@@ -77,6 +77,7 @@ struct ScoreArgs {
     int* err;                  // [1]: set when a wait times out
     unsigned* done;            // [g]: groups done with each key slice (0 at launch)
     float* importance;         // [M]: the output
+    int M_out;                 // only importance[0..M_out) is written (M_out <= M)
     int L, H, Hkv, G, N, M, d;
     int g;                     // workgroups cooperating on one unit
     int ngroups;               // groups working in parallel

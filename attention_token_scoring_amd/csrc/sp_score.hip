@@ -96,7 +96,7 @@ void set_profile_events(hipEvent_t before, hipEvent_t after) {
 // launch (every workgroup resident on an otherwise idle device) or, if the
 // descriptor asks for it, a cooperative one.
 hipError_t launch_score(const ScorePlan& p, const sp_score_desc& d, const void* Q, const void* K,
-                        long long plane_stride, int M, float* importance, void* ws,
+                        long long plane_stride, int M, int M_out, float* importance, void* ws,
                         hipStream_t stream) {
     char* base = (char*)ws;
     ScoreArgs a;
@@ -106,6 +106,7 @@ hipError_t launch_score(const ScorePlan& p, const sp_score_desc& d, const void* 
     a.err = (int*)(base + p.ws_err);
     a.done = (unsigned*)(base + p.ws_err + 128);
     a.importance = importance;
+    a.M_out = M_out;
     a.part = (float2*)(base + p.ws_part);
     a.tail = (float2*)(base + p.ws_tail);
     a.lse = (float*)(base + p.ws_lse);

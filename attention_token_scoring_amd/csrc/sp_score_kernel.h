@@ -835,7 +835,7 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
         }
         __syncthreads();
     }
-    for (int k = tid; k < nkeys; k += kThreads) {
+    for (int k = tid; k < nkeys && r0 + k < a.M_out; k += kThreads) {
         float sum = 0.f;
         for (int jj = 0; jj < a.N; ++jj) sum += exp2_hw((float)Trun[jj * KRP + k] * kStep);
         a.importance[r0 + k] = sum / (float)a.N;

@@ -3,12 +3,16 @@
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
                [--copy-probe-mib MIB] [--cooperative] [--select workload|threshold]
+               [--window W [--stride S]]
 
 --workload takes any workload of synth (default: the 8B shape at M = 32K); the
 ragged batch is timed through sp_score_varlen + sp_select_varlen.
 --select threshold times the threshold selection (SP_SELECT_THRESHOLD, the
 Implementation Guide program's chunk selection with its 128-token fill and
 2000-token cap) instead of the workload's selection.
+--window W [--stride S] scores the workload's prompt in sliding windows
+(sp_window_layout, sp_score_windows; stride W/2 by default), each window with
+its own synthetic queries and keys.
 --cooperative launches the scoring kernel cooperatively (SP_LAUNCH_COOPERATIVE)
 instead of with the default ordinary launch.
 
@@ -61,6 +65,10 @@ def parse():
     ap.add_argument("--select", choices=("workload", "threshold"), default="workload",
                     help="the workload's selection, or the Implementation Guide program's "
                          "threshold selection (min_tok 128, max_keep 2000)")
+    ap.add_argument("--window", type=int, default=0,
+                    help="score the prompt in sliding windows of this many tokens")
+    ap.add_argument("--stride", type=int, default=0,
+                    help="window stride (default: half the window)")
     ap.add_argument("--cooperative", action="store_true",
                     help="launch the scoring kernel cooperatively (SP_LAUNCH_COOPERATIVE)")
     ap.add_argument("--cpu-layers", type=int, default=1 << 30,
@@ -69,7 +77,10 @@ def parse():
                     help="also run one device copy of this size (counter calibration)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                     help="write the traffic summary from two rocprofv3 --pmc databases and exit")
-    return ap.parse_args()
+    args = ap.parse_args()
+    if args.window and not args.stride:
+        args.stride = max(1, args.window // 2)
+    return args
 
 
 SCORE_KERNEL = "sp::score_kernel<"
@@ -240,6 +251,12 @@ def main():
                                   mass=0.0, boost_first_n=0, boost_last_n=0)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.window:
+        if w.R != 1:
+            print("bench.py: --window takes a single-prompt workload", file=sys.stderr)
+            sys.exit(2)
+        windowed(args, w, sel, sp, torch, dev)
+        return
     if w.R != 1:
         ragged(args, w, sel, sp, torch, dev)
         return
@@ -353,6 +370,84 @@ def main():
 
 def launch_name(args) -> str:
     return "cooperative" if args.cooperative else "resident"
+
+
+def windowed(args, w, sel, sp, torch, dev):
+    """One prompt of the workload scored in sliding windows (each window with
+    its own synthetic queries and keys, as a speculator run per window gives):
+    one step is sp_score_windows + sp_select over the prompt's M tokens. The
+    roofline figure uses the sp_score_windows call's duration (one scoring
+    kernel per window plus its prep kernel)."""
+    import synth
+
+    starts, lens, keeps = sp.sp_window_layout(w.M, args.window, args.stride)
+    ww = dataclasses.replace(w, R=len(lens), M=0, len_range=())
+    Qh, Kh, cu = synth.make_ragged(ww, lens)
+    R = len(lens)
+
+    def to_dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    Q = to_dev(Qh)
+    K = to_dev(Kh)
+    del Qh, Kh
+    launch = sp.SP_LAUNCH_COOPERATIVE if args.cooperative else sp.SP_LAUNCH_RESIDENT
+    desc = sp.score_desc(w.L, w.H, w.Hkv, w.d, w.N, sp.SP_BF16 if w.dtype else sp.SP_F32, 0.0, launch)
+    ws = torch.empty(sp.sp_score_workspace_bytes(desc, int(lens.max())), dtype=torch.uint8,
+                     device=dev)
+    imp = torch.empty(w.M, dtype=torch.float32, device=dev)
+    kept = torch.empty(w.M, dtype=torch.int32, device=dev)
+    pos = torch.empty(w.M, dtype=torch.int32, device=dev)
+    nk = torch.empty(1, dtype=torch.int32, device=dev)
+    params = select_params(sp, sel)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        sp.sp_score_windows(Q, K, cu, keeps, out=imp, workspace=ws, launch=launch)
+        if ev is not None:
+            ev[1].record()
+        sp.sp_select(imp, params, kept_idx=kept, pos_ids=pos, n_kept=nk)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    w0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - w0) * 1e3 / args.steps
+    score_s = float(np.mean([a.elapsed_time(b) for a, b in evs])) / 1e3
+    alg_bytes = int(sum(w.L * w.Hkv * (int(m) + w.N) * w.d + w.L * w.H * w.N * w.d
+                        for m in lens)) * (2 if w.dtype else 4)
+    achieved = alg_bytes / score_s / 1e9
+    out = {
+        "metric": METRIC,
+        "value": w.M / (ms_per_step / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype else "f32",
+        "data": "synthetic",
+        "config": dict(workload_desc(w, sel), launch=launch_name(args),
+                       workload=f"{w.name} in sliding windows of {args.window} tokens, stride "
+                                f"{args.stride}: {R} windows",
+                       window=args.window, stride=args.stride),
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+        "detail": {"sp_score_windows_ms_avg": score_s * 1e3, "alg_bytes_per_step": alg_bytes,
+                   "windows": R, "n_kept": int(nk.cpu()[0])},
+    }
+    print(json.dumps(out), flush=True)
 
 
 def ragged(args, w, sel, sp, torch, dev):

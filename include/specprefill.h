@@ -145,6 +145,39 @@ sp_status sp_score_varlen(const sp_score_desc* desc, int32_t R, const void* Q, c
                           const int64_t* cu_prompt_host, float* importance, void* ws,
                           size_t ws_bytes, void* stream);
 
+/*
+ * Sliding-window scoring ([SP-G] Sliding Window, "Sliding Window Solution";
+ * Implementation Details, "Sliding Window Loop (v3.1)"): a prompt too long for
+ * the speculator is scored in overlapping windows, each prefilled and decoded
+ * by the speculator on its own (its cache cleared in between), so each window
+ * brings its own look-ahead queries and keys.
+ *
+ * sp_window_layout: windows start at 0, stride, 2*stride, ...; window w covers
+ * tokens [start_w, min(start_w + window, M)); the first window that reaches M
+ * is the last and keeps the scores of all its tokens, every other window
+ * keeps its first stride scores. With 1 <= stride <= window this covers every
+ * token exactly once (the Guide's per-token count of scores is then 1).
+ *   n_windows           host, [1] (written: the number of windows R)
+ *   starts, lens, keeps host, [capacity] int64 each (written), or all NULL to
+ *                       count only
+ * Returns SP_EINVAL for M < 1, window < 1, stride < 1, stride > window, or
+ * capacity < R with arrays given. Host only; no device work.
+ *
+ * sp_score_windows: sp_score_varlen over R windows (window r's prompt keys are
+ * its cu_window_host[r+1] - cu_window_host[r] tokens, laid out as for
+ * sp_score_varlen), writing only the first keep_host[r] scores of window r
+ * (1 <= keep_host[r] <= its length), packed in window order. With the
+ * layout above (cu from lens, keep from keeps), importance[i] is token i's
+ * score from the window that keeps it, i < M.
+ *   importance  device, [sum_r keep_host[r]] float32
+ *   ws          as for sp_score_varlen
+ */
+sp_status sp_window_layout(int64_t M, int32_t window, int32_t stride, int32_t* n_windows,
+                           int64_t* starts, int64_t* lens, int64_t* keeps, int32_t capacity);
+sp_status sp_score_windows(const sp_score_desc* desc, int32_t R, const void* Q, const void* K,
+                           const int64_t* cu_window_host, const int64_t* keep_host,
+                           float* importance, void* ws, size_t ws_bytes, void* stream);
+
 /* Bytes of device workspace sp_select / sp_select_varlen need (currently 0 for
  * every valid argument set; (size_t)-1 if the arguments are invalid). */
 size_t sp_select_workspace_bytes(int32_t R, int64_t total_prompt_len,

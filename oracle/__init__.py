@@ -160,6 +160,33 @@ def select_threshold(importance, chunk, keep_rate, min_tok=128, max_keep=0, pos_
     return kept[:k].copy(), pos[:k].copy()
 
 
+def window_layout(M, window, stride):
+    """Sliding windows over M tokens ("SpecPrefill - Implementation Guide",
+    Sliding Window: Sliding Window Solution, and Implementation Details:
+    Sliding Window Loop (v3.1)): a window starts every stride tokens and spans
+    up to window tokens; one that reaches the end of the prompt is the last
+    and keeps all its tokens' scores, the others their first stride.
+    Returns [(start, length, kept), ...]."""
+    if M < 1 or window < 1 or stride < 1 or stride > window:
+        raise ValueError("need M, window, stride >= 1 and stride <= window")
+    out, pos = [], 0
+    while True:
+        end = min(pos + window, M)
+        if end >= M:
+            out.append((pos, end - pos, end - pos))
+            return out
+        out.append((pos, end - pos, stride))
+        pos += stride
+
+
+def score_windows(Qs, Ks, keeps, scale=0.0, nthreads=0):
+    """Importance of a prompt scored window by window: window r's own scores
+    (its queries Qs[r] over its keys Ks[r]), of which the first keeps[r] are
+    kept, concatenated in window order (each token scored by one window)."""
+    parts = [score(Q, K, scale=scale, nthreads=nthreads)[:k] for Q, K, k in zip(Qs, Ks, keeps)]
+    return np.concatenate(parts)
+
+
 def select_params(sel) -> dict:
     """Keyword arguments of select() from a synth.Select."""
     return dict(chunk=sel.chunk, pool_k=sel.pool_k, mode=sel.mode, keep_rate=sel.keep_rate,

@@ -203,11 +203,12 @@ def make_request(w: Workload, r: int = 0):
     return make_q(w, r), make_k(w, r, M), M
 
 
-def make_ragged(w: Workload):
+def make_ragged(w: Workload, lens=None):
     """Packed ragged batch: Q [R][L][H][N][d], K [L][Hkv][T][d] with request r's
     M_r + N key rows at cu_keys[r] (look-ahead keys at the tail of each
-    segment), cu_prompt [R+1] offsets of the prompts."""
-    Ms = prompt_lengths(w)
+    segment), cu_prompt [R+1] offsets of the prompts. lens, if given, are the
+    prompt lengths (else those of the workload)."""
+    Ms = prompt_lengths(w) if lens is None else np.asarray(lens, np.int64)
     R = len(Ms)
     cu_prompt = np.zeros(R + 1, np.int64)
     cu_prompt[1:] = np.cumsum(Ms)

@@ -189,3 +189,14 @@ def test_plan_longest_prompt(lib, dtype, d, longest):
         sp.sp_score_plan(dd, longest + 1)
     assert e.value.status == sp.SP_EUNSUPPORTED
     assert sp.sp_score_workspace_bytes(dd, longest + 1) == 0
+
+
+def test_score_windows_rejects_keeps(lib):
+    d = desc()
+    cu = (ctypes.c_int64 * 3)(0, 100, 150)
+    for keep in ([0, 50], [101, 50], [100, 51], [-1, 1]):
+        kp = (ctypes.c_int64 * 2)(*keep)
+        assert lib.sp_score_windows(ctypes.byref(d), 2, FAKE, FAKE, cu, kp, FAKE, FAKE, 1 << 30,
+                                    None) == sp.SP_EINVAL, keep
+    assert lib.sp_score_windows(ctypes.byref(d), 2, FAKE, FAKE, cu, None, FAKE, FAKE, 1 << 30,
+                                None) == sp.SP_EINVAL

@@ -420,3 +420,42 @@ def test_select_threshold_varlen():
         assert n_h[r] == len(k_ref), r
         assert np.array_equal(kept_h[off:off + n_h[r]], k_ref), r
         assert np.array_equal(pos_h[off:off + n_h[r]], p_ref), r
+
+
+# ----------------------------------------------------------------------------------------
+# sliding-window scoring
+# ----------------------------------------------------------------------------------------
+WINDOW_CASES = [
+    # id, L, H, Hkv, d, N, M, window, stride, dtype
+    ("win-example-4471", 2, 8, 2, 128, 8, 4471, 2000, 1000, BF),
+    ("win-one-window", 2, 4, 2, 64, 8, 700, 2000, 1000, BF),
+    ("win-f32-nonoverlap", 1, 8, 2, 64, 8, 3000, 1024, 1024, F32),
+    ("win-0.8b-shape", 24, 16, 8, 64, 8, 4608, 2000, 1000, BF),
+]
+
+
+@pytest.mark.parametrize("case", WINDOW_CASES, ids=[c[0] for c in WINDOW_CASES])
+def test_score_windows_matches_oracle(case):
+    name, L, H, Hkv, d, N, M, window, stride, dt = case
+    print(f"case {name}", flush=True)
+    starts, lens, keeps = sp.sp_window_layout(M, window, stride)
+    assert [tuple(x) for x in zip(starts, lens, keeps)] == oracle.window_layout(M, window, stride)
+    w = synth.Workload(name, L=L, H=H, Hkv=Hkv, d=d, N=N, dtype=dt, seed=31, R=len(lens),
+                       plant_frac=0.05, plant_chunk=32)
+    Qh, Kh, cu = synth.make_ragged(w, lens)
+    Q, K = to_dev(Qh), to_dev(Kh)
+    imp = sp.sp_score_windows(Q, K, cu, keeps)
+    full = sp.sp_score_varlen(Q, K, cu)
+    torch.cuda.synchronize()
+    imp_h, full_h = imp.cpu().numpy(), full.cpu().numpy()
+    assert imp_h.shape == (M,)
+    # window r's kept scores are the first keeps[r] of its own scores
+    got = np.concatenate([full_h[cu[r]:cu[r] + keeps[r]] for r in range(len(lens))])
+    assert np.array_equal(imp_h, got), name
+    # the oracle scores each window from its own arrays
+    Qs, Ks = [], []
+    cu_keys = np.concatenate([[0], np.cumsum(np.asarray(lens) + N)])
+    for r in range(len(lens)):
+        Qs.append(Qh[r])
+        Ks.append(np.ascontiguousarray(Kh[:, :, cu_keys[r]:cu_keys[r + 1], :]))
+    check_importance(imp_h, oracle.score_windows(Qs, Ks, keeps), name)
