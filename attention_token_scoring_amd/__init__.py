@@ -31,7 +31,7 @@ SP_LAUNCH_RESIDENT, SP_LAUNCH_COOPERATIVE = 0, 1
 EXPORTED = ("sp_score", "sp_score_varlen", "sp_select", "sp_select_varlen",
             "sp_score_workspace_bytes", "sp_select_workspace_bytes", "sp_score_plan",
             "sp_status_string", "sp_profile_score_kernel", "sp_score_status",
-            "sp_score_windows", "sp_window_layout")
+            "sp_score_windows", "sp_window_layout", "sp_gather_rows", "sp_break_even")
 
 
 class SpError(RuntimeError):
@@ -86,9 +86,12 @@ def load_library():
                                      P(ctypes.c_int64), vp, vp, sz, vp]
     lib.sp_window_layout.argtypes = [i64, i32, i32, P(ctypes.c_int32), P(ctypes.c_int64),
                                      P(ctypes.c_int64), P(ctypes.c_int64), i32]
+    lib.sp_gather_rows.argtypes = [vp, i64, vp, vp, i32, P(ctypes.c_int64), vp, vp]
+    f32 = ctypes.c_float
+    lib.sp_break_even.argtypes = [i64, f32, f32, f32, f32, P(ctypes.c_int32)]
     for name in ("sp_score_plan", "sp_score", "sp_score_varlen", "sp_select", "sp_select_varlen",
                  "sp_profile_score_kernel", "sp_score_status", "sp_score_windows",
-                 "sp_window_layout"):
+                 "sp_window_layout", "sp_gather_rows", "sp_break_even"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -281,6 +284,39 @@ def sp_score_windows(Q, K, cu_window: Sequence[int], keeps: Sequence[int], scale
         _stream(stream))
     _check(st, "sp_score_windows")
     return out
+
+
+def sp_gather_rows(src, kept_idx, n_kept, cu_prompt: Optional[Sequence[int]] = None, dst=None,
+                   stream=None):
+    """Rows of the kept tokens in kept order: src [T, ...] (any dtype, rows of a
+    multiple of 4 bytes), kept_idx / n_kept as sp_select(_varlen) returns them,
+    cu_prompt the request offsets (default: one request over all of src)."""
+    torch = _torch()
+    _require_cuda(src, kept_idx, n_kept)
+    T = src.shape[0]
+    cu = np.ascontiguousarray(np.asarray([0, T] if cu_prompt is None else cu_prompt,
+                                         dtype=np.int64))
+    R = cu.shape[0] - 1
+    if dst is None:
+        dst = torch.zeros((int(cu[-1]),) + tuple(src.shape[1:]), dtype=src.dtype, device=src.device)
+    row_bytes = src[0].numel() * src.element_size() if T else 0
+    st = load_library().sp_gather_rows(src.data_ptr(), int(row_bytes), kept_idx.data_ptr(),
+                                       n_kept.data_ptr(), int(R),
+                                       cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                       dst.data_ptr(), _stream(stream))
+    _check(st, "sp_gather_rows")
+    return dst
+
+
+def sp_break_even(M: int, keep_fraction: float, spec_tps: float = 600.0,
+                  target_tps: float = 270.0, safety: float = 1.2) -> bool:
+    """Whether sparse prefill is estimated to save more than safety times the
+    scoring time (the Implementation Guide's break-even detection)."""
+    run = ctypes.c_int32(0)
+    _check(load_library().sp_break_even(int(M), float(keep_fraction), float(spec_tps),
+                                        float(target_tps), float(safety), ctypes.byref(run)),
+           "sp_break_even")
+    return bool(run.value)
 
 
 def sp_select(importance, params: SelectParams, pos_base: int = 0, kept_idx=None, pos_ids=None,

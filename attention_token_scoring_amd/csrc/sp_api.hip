@@ -12,6 +12,9 @@ namespace sp {
 hipError_t launch_score(const ScorePlan& p, const sp_score_desc& d, const void* Q, const void* K,
                         long long plane_stride, int M, int M_out, float* importance, void* ws,
                         hipStream_t stream);
+hipError_t launch_gather(const void* src, long long row_bytes, const int32_t* kept,
+                         const int32_t* n_kept, int R, const int64_t* cu, long long max_rows,
+                         void* dst, hipStream_t stream);
 hipError_t launch_select(const SelectParamsDev& p, const int64_t* cu, const int32_t* pos_base,
                          int R, const float* importance, int32_t* kept_idx, int32_t* pos_ids,
                          int32_t* n_kept, hipStream_t stream);
@@ -397,6 +400,36 @@ sp_status sp_window_layout(int64_t M, int32_t window, int32_t stride, int32_t* n
     }
     *n_windows = R;
     if (starts && (!lens || !keeps || capacity < R)) return SP_EINVAL;
+    return SP_OK;
+}
+
+sp_status sp_gather_rows(const void* src, int64_t row_bytes, const int32_t* kept_idx,
+                         const int32_t* n_kept, int32_t R, const int64_t* cu_host, void* dst,
+                         void* stream) {
+    if (!src || !kept_idx || !n_kept || !cu_host || !dst || R < 1) return SP_EINVAL;
+    if (row_bytes < 4 || row_bytes % 4 != 0) return SP_EUNSUPPORTED;
+    if (!aligned(src, 4) || !aligned(dst, 4) || !aligned(kept_idx, 4) || !aligned(n_kept, 4))
+        return SP_EINVAL;
+    if (cu_host[0] != 0) return SP_EINVAL;
+    long long max_rows = 0;
+    for (int r = 0; r < R; ++r) {
+        const long long m = cu_host[r + 1] - cu_host[r];
+        if (m < 1) return SP_EINVAL;
+        if (m > max_rows) max_rows = m;
+    }
+    if (device_cus() < 1) return SP_EDEVICE;
+    return to_status(launch_gather(src, row_bytes, kept_idx, n_kept, R, cu_host, max_rows, dst,
+                                   (hipStream_t)stream));
+}
+
+sp_status sp_break_even(int64_t M, float keep_fraction, float spec_tps, float target_tps,
+                        float safety, int32_t* run) {
+    if (!run || M < 1 || !(keep_fraction >= 0.f && keep_fraction <= 1.f) || !(spec_tps > 0.f) ||
+        !(target_tps > 0.f) || !(safety > 0.f))
+        return SP_EINVAL;
+    const double scoring = (double)M / spec_tps;
+    const double saved = ((double)M - (double)keep_fraction * (double)M) / target_tps;
+    *run = saved >= scoring * safety ? 1 : 0;
     return SP_OK;
 }
 

@@ -249,6 +249,37 @@ sp_status sp_select_varlen(const float* importance, int32_t R, const int64_t* cu
                            int32_t* kept_idx, int32_t* pos_ids, int32_t* n_kept, void* ws,
                            size_t ws_bytes, void* stream);
 
+/*
+ * Sparse-prefill batch ([SP-G] Full Source Code: the target's batch holds,
+ * for each kept index, the input token at that index and position): copies
+ * the rows of the kept tokens in kept order. For request r (offsets
+ * cu_host[r], as for sp_select_varlen; R = 1 and cu_host = {0, M} for
+ * sp_select's output):
+ *   dst row cu_host[r] + o = src row kept_idx[cu_host[r] + o], o < n_kept[r].
+ *   src       device, rows of row_bytes (a multiple of 4), indexed by kept_idx
+ *             (e.g. int32 token ids: row_bytes = 4; hidden states: d x 2 for bf16)
+ *   kept_idx  device int32, n_kept device int32 [R]: as sp_select / sp_select_varlen
+ *             write them (the counts are read on the device: no host synchronisation)
+ *   dst       device, at least cu_host[R] rows; rows past each request's count
+ *             are left as they are
+ * Positions come with the selection (pos_ids). SP_EUNSUPPORTED for a row size
+ * that is not a positive multiple of 4.
+ */
+sp_status sp_gather_rows(const void* src, int64_t row_bytes, const int32_t* kept_idx,
+                         const int32_t* n_kept, int32_t R, const int64_t* cu_host, void* dst,
+                         void* stream);
+
+/*
+ * Break-even gate ([SP-G] v3 Improvements, "Break-Even Detection";
+ * Configuration Reference, SP_BREAK_EVEN, SP_SPEC_THROUGHPUT,
+ * SP_BREAK_EVEN_SAFETY): scoring takes about M / spec_tps seconds, sparse
+ * prefill saves about (M - keep_fraction * M) / target_tps; *run = 1 when the
+ * saving is at least safety times the scoring time (the Guide's defaults:
+ * 600 and 270 tokens/s, safety 1.2). Host only, in double precision.
+ */
+sp_status sp_break_even(int64_t M, float keep_fraction, float spec_tps, float target_tps,
+                        float safety, int32_t* run);
+
 /* Static, human-readable name of a status code. */
 const char* sp_status_string(sp_status status);
 

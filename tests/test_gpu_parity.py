@@ -459,3 +459,41 @@ def test_score_windows_matches_oracle(case):
         Qs.append(Qh[r])
         Ks.append(np.ascontiguousarray(Kh[:, :, cu_keys[r]:cu_keys[r + 1], :]))
     check_importance(imp_h, oracle.score_windows(Qs, Ks, keeps), name)
+
+
+# ----------------------------------------------------------------------------------------
+# sparse-prefill batch: rows of the kept tokens
+# ----------------------------------------------------------------------------------------
+def test_gather_token_ids_after_select():
+    rng = np.random.default_rng(12)
+    M = 32768
+    x = torch.from_numpy((rng.random(M) ** 6).astype(np.float32)).cuda()
+    tokens = torch.from_numpy(rng.integers(0, 151936, M).astype(np.int32)).cuda()
+    params = sp.select_params(chunk=32, pool_k=13, mode="topk", keep_rate=0.1)
+    kept, pos, n = sp.sp_select(x, params)
+    dst = torch.full((M,), -7, dtype=torch.int32, device="cuda")
+    sp.sp_gather_rows(tokens, kept, n, dst=dst)
+    torch.cuda.synchronize()
+    nk = int(n.cpu()[0])
+    k = kept[:nk].cpu().numpy()
+    assert np.array_equal(dst[:nk].cpu().numpy(), tokens.cpu().numpy()[k])
+    assert np.all(dst[nk:].cpu().numpy() == -7)  # rows past the count untouched
+
+
+def test_gather_hidden_rows_varlen():
+    rng = np.random.default_rng(13)
+    Ms = [5000, 3, 777, 12000]
+    cu = np.concatenate([[0], np.cumsum(Ms)]).astype(np.int64)
+    T = int(cu[-1])
+    x = torch.from_numpy((rng.random(T) ** 3).astype(np.float32)).cuda()
+    rows = torch.from_numpy(rng.standard_normal((T, 64)).astype(np.float32)).cuda().to(torch.bfloat16)
+    params = sp.select_params(chunk=32, pool_k=3, mode="mass", mass=0.6)
+    kept, pos, n = sp.sp_select_varlen(x, cu, params)
+    dst = sp.sp_gather_rows(rows, kept, n, cu_prompt=cu)
+    torch.cuda.synchronize()
+    n_h, kept_h = n.cpu().numpy(), kept.cpu().numpy()
+    rows_h = rows.view(torch.int16).cpu().numpy()
+    dst_h = dst.view(torch.int16).cpu().numpy()
+    for r in range(len(Ms)):
+        off, nk = int(cu[r]), int(n_h[r])
+        assert np.array_equal(dst_h[off:off + nk], rows_h[kept_h[off:off + nk]]), r
