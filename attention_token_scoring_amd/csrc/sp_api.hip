@@ -22,10 +22,8 @@ hipError_t launch_select(const SelectParamsDev& p, const int64_t* cu, const int3
 namespace {
 
 constexpr int kMaxDevices = 64;
-constexpr int kDefaultCUs = 256;  // MI355X; used when no device can be queried
 constexpr int kMaxSelectChunks = 4096;
 constexpr int kMaxSelectRequests = 1024;
-constexpr int kMaxCombiners = 4;
 
 int g_cus[kMaxDevices];
 std::once_flag g_once[kMaxDevices];
@@ -42,8 +40,6 @@ int device_cus() {
     });
     return g_cus[dev];
 }
-
-size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -62,122 +58,6 @@ sp_status check_desc(const sp_score_desc* d) {
     if ((G & (G - 1)) != 0 || G * d->N > 32) return SP_EUNSUPPORTED;
     if ((long long)d->L * d->Hkv > (1 << 20)) return SP_EUNSUPPORTED;
     return SP_OK;
-}
-
-// Launch plan for one prompt of M keys: choose the number g of workgroups that
-// share a (layer, kv-head) unit so that each slice fits what one workgroup can
-// keep in flight and park (registers and LDS), the groups fill the device with
-// at least one CU left for combining, and the per-unit exchanges stay few;
-// then lay out LDS and the workspace.
-sp_status make_plan(const sp_score_desc& d, long long M, int cus, ScorePlan* out) {
-    ScorePlan p;
-    const int G = d.H / d.Hkv;
-    const bool bf = d.dtype == SP_BF16;
-    p.rows = G * d.N <= 16 ? 16 : 32;
-    const int tk = kTileKeys;
-    const int row_bytes = d.d * esize(d.dtype);
-    p.units = d.L * d.Hkv;
-    if (M < 1) return SP_EINVAL;
-    if ((unsigned long long)(M + d.N) * d.d * esize(d.dtype) >= (1ull << 31)) return SP_EUNSUPPORTED;
-    if (cus < 1) cus = kDefaultCUs;
-    if (cus < 2) return SP_EUNSUPPORTED;
-    const double bytes_per_key = (double)row_bytes;
-    // A step takes the longer of (a) the busiest streaming wave's work on its
-    // tiles (measured on the MI355X: ~4.1 us for 4 tiles, ~5.7 us for 5 tiles
-    // without the registers for the guard-free statistics), and (b) the
-    // step's bytes at the HBM rate the kernel sustains (~6.2 TB/s).
-    const double bw_total = 6.2e12;
-    const double wave_base = 1.0e-6, wave_per_tile = 0.77e-6, wave_tight = 0.85e-6,
-                 wave_partial = 0.1e-6;
-    double best = 1e300;
-    int bg = 0, bkr = 0, bng = 0, bdef = 0, btpw = 0;
-    const int tpw0 = tiles_per_wave(bf, d.d);
-    // (one head per step over two halves: the base tile count only)
-    const int tpw1 = (G == 1 && p.rows == 32) ? tpw0 : tpw0 + 1;
-    for (int tpw = tpw0; tpw <= tpw1; ++tpw) {
-        const int cap = kStreamWaves * tpw * kTileKeys;
-        const long long gmin = (M + cap - 1) / cap;
-        const bool roomy = score_roomy(row_bytes, tpw, p.rows / 16);
-        for (long long cand = 0; cand < 2 * (cus - gmin + 1); ++cand) {
-            // each g with the smallest slice that covers M, then with a full one
-            // (cap keys; the last workgroup takes the rest)
-            const long long g = gmin + cand / 2;
-            if (g > cus - 1 || g > kMaxRanks) break;
-            long long kr = (M + g - 1) / g;
-            kr = (kr + tk - 1) / tk * tk;
-            if (cand % 2 == 1) {
-                if (kr == cap) continue;  // (already planned)
-                kr = cap;
-            }
-            if (kr > cap) continue;
-            const long long geff = (M + kr - 1) / kr;
-            if (geff != g) continue;  // the same slice with fewer workgroups is planned at geff
-            int defer = 0;
-            for (int D = kMaxDefer; D >= 1; --D)
-                if (score_lds_layout(D + 1, tpw, p.rows, row_bytes, d.N, (int)kr).total <= kLdsBytes) {
-                    defer = D;
-                    break;
-                }
-            if (defer == 0) continue;
-            long long ng = (cus - 1) / g;
-            if (ng > p.units) ng = p.units;
-            if (ng < 1) continue;
-            const long long iters = (p.units + ng - 1) / ng;
-            // where the kernel has a guard-free copy of the statistics for
-            // waves whose tiles all lie inside the slice, a slice that leaves
-            // some wave short puts the slower copy on every step's critical
-            // path; a shallower deferral exposes more of each exchange's latency
-            const long long busiest = (kr / tk + kStreamWaves - 1) / kStreamWaves;  // tiles of the busiest wave
-            const double wave = wave_base + wave_per_tile * busiest + (roomy ? 0.0 : wave_tight) +
-                                (roomy && kr < cap ? wave_partial : 0.0);
-            const double hbm = (double)(g * ng) * kr * bytes_per_key / bw_total;
-            const double sync = (kMaxDefer - defer) * 1.0e-6;
-            const double cost = iters * ((wave > hbm ? wave : hbm) + sync);
-            if (cost < best * 0.999) {
-                best = cost;
-                bg = (int)g;
-                bkr = (int)kr;
-                bng = (int)ng;
-                bdef = defer;
-                btpw = tpw;
-            }
-        }
-    }
-    if (bg == 0) return SP_EUNSUPPORTED;
-    p.tpw = btpw;
-    p.cap = kStreamWaves * btpw * kTileKeys;
-    p.g = bg;
-    p.KR = bkr;
-    p.ngroups = bng;
-    p.defer = bdef;
-    p.ncomb = cus - bg * bng;
-    if (p.ncomb > kMaxCombiners) p.ncomb = kMaxCombiners;
-    p.grid = bg * bng + p.ncomb;
-    p.cus = cus;
-    p.lds = score_lds_layout(bdef + 1, btpw, p.rows, row_bytes, d.N, bkr);
-    p.ws_err = 0;      // error word; then at +128 one slice counter per rank (g <= kMaxRanks)
-    p.ws_part = 2048;
-    p.ws_tail = p.ws_part + round_up((size_t)p.units * p.g * p.rows * 8, 256);
-    p.ws_lse = p.ws_tail + round_up((size_t)p.units * p.rows * 8, 256);
-    p.ws_tg = p.ws_lse + round_up((size_t)p.units * p.rows * 4, 256);
-    p.ws_total = p.ws_tg + round_up((size_t)p.ngroups * d.N * M * 4, 256);
-    *out = p;
-    return SP_OK;
-}
-
-// Workspace for any prompt of at most max_M keys (bounds that hold for every
-// plan make_plan can choose for M <= max_M).
-size_t workspace_bound(const sp_score_desc& d, long long max_M, int cus) {
-    if (cus < 1) cus = kDefaultCUs;
-    const int G = d.H / d.Hkv;
-    const int rows = G * d.N <= 16 ? 16 : 32;
-    const long long cap = (long long)kStreamWaves * (tiles_per_wave(d.dtype == SP_BF16, d.d) + 1) * kTileKeys;
-    const long long units = (long long)d.L * d.Hkv;
-    long long tg_elems = (long long)(units < cus ? units : cus) * max_M;
-    if (tg_elems > (long long)cus * cap) tg_elems = (long long)cus * cap;
-    tg_elems *= d.N;
-    return 2048 + round_up((size_t)units * cus * rows * 8, 256) + round_up((size_t)units * rows * 8, 256) +
-           round_up((size_t)units * rows * 4, 256) + round_up((size_t)tg_elems * 4, 256);
 }
 
 sp_status to_status(hipError_t e) { return e == hipSuccess ? SP_OK : SP_EDEVICE; }
@@ -237,6 +117,52 @@ SelectParamsDev to_dev(const sp_select_params* p) {
     q.min_tok = p->min_tok;
     q.max_keep = p->max_keep;
     return q;
+}
+
+// Requests r in [0, R) of a ragged batch, each scored alone; with keep, only the
+// first keep[r] scores of request r are written, packed one request after the
+// other (else all M_r scores at offset cu[r]).
+sp_status score_batch(const sp_score_desc* desc, int32_t R, const void* Q, const void* K,
+                      const int64_t* cu, const int64_t* keep, float* importance, void* ws,
+                      size_t ws_bytes, void* stream) {
+    sp_status s = check_desc(desc);
+    if (s != SP_OK) return s;
+    if (R < 1 || !Q || !K || !cu || !importance) return SP_EINVAL;
+    if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(importance, 4)) return SP_EINVAL;
+    if (cu[0] != 0) return SP_EINVAL;
+    for (int r = 0; r < R; ++r) {
+        if (cu[r + 1] - cu[r] < 1) return SP_EINVAL;
+        if (keep && (keep[r] < 1 || keep[r] > cu[r + 1] - cu[r])) return SP_EINVAL;
+    }
+    if (cu[R] + (long long)R * desc->N > (1ll << 40)) return SP_EUNSUPPORTED;
+    const int cus = device_cus();
+    if (cus < 1) return SP_EDEVICE;
+    if (!ws || !aligned(ws, 256)) return SP_EWORKSPACE;
+    // validate every request's plan before enqueueing anything
+    for (int r = 0; r < R; ++r) {
+        ScorePlan p;
+        s = make_plan(*desc, cu[r + 1] - cu[r], cus, &p);
+        if (s != SP_OK) return s;
+        if (ws_bytes < p.ws_total) return SP_EWORKSPACE;
+    }
+    const int es = esize(desc->dtype);
+    const long long T = cu[R] + (long long)R * desc->N;
+    const long long qsz = (long long)desc->L * desc->H * desc->N * desc->d * es;
+    long long out = 0;
+    for (int r = 0; r < R; ++r) {
+        const long long M = cu[r + 1] - cu[r];
+        ScorePlan p;
+        make_plan(*desc, M, cus, &p);
+        const char* Qr = (const char*)Q + r * qsz;
+        const char* Kr = (const char*)K + (cu[r] + (long long)r * desc->N) * desc->d * es;
+        const long long M_out = keep ? keep[r] : M;
+        float* imp = importance + (keep ? out : cu[r]);
+        s = to_status(launch_score(p, *desc, Qr, Kr, T * desc->d, (int)M, (int)M_out, imp, ws,
+                                   (hipStream_t)stream));
+        if (s != SP_OK) return s;
+        out += M_out;
+    }
+    return SP_OK;
 }
 
 }  // namespace
@@ -316,56 +242,6 @@ sp_status sp_score(const sp_score_desc* desc, const void* Q, const void* K, int3
     const long long plane = (long long)(M + desc->N) * desc->d;
     return to_status(launch_score(p, *desc, Q, K, plane, M, M, importance, ws, (hipStream_t)stream));
 }
-
-namespace {
-
-// Requests r in [0, R) of a ragged batch, each scored alone; with keep, only the
-// first keep[r] scores of request r are written, packed one request after the
-// other (else all M_r scores at offset cu[r]).
-sp_status score_batch(const sp_score_desc* desc, int32_t R, const void* Q, const void* K,
-                      const int64_t* cu, const int64_t* keep, float* importance, void* ws,
-                      size_t ws_bytes, void* stream) {
-    sp_status s = check_desc(desc);
-    if (s != SP_OK) return s;
-    if (R < 1 || !Q || !K || !cu || !importance) return SP_EINVAL;
-    if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(importance, 4)) return SP_EINVAL;
-    if (cu[0] != 0) return SP_EINVAL;
-    for (int r = 0; r < R; ++r) {
-        if (cu[r + 1] - cu[r] < 1) return SP_EINVAL;
-        if (keep && (keep[r] < 1 || keep[r] > cu[r + 1] - cu[r])) return SP_EINVAL;
-    }
-    if (cu[R] + (long long)R * desc->N > (1ll << 40)) return SP_EUNSUPPORTED;
-    const int cus = device_cus();
-    if (cus < 1) return SP_EDEVICE;
-    if (!ws || !aligned(ws, 256)) return SP_EWORKSPACE;
-    // validate every request's plan before enqueueing anything
-    for (int r = 0; r < R; ++r) {
-        ScorePlan p;
-        s = make_plan(*desc, cu[r + 1] - cu[r], cus, &p);
-        if (s != SP_OK) return s;
-        if (ws_bytes < p.ws_total) return SP_EWORKSPACE;
-    }
-    const int es = esize(desc->dtype);
-    const long long T = cu[R] + (long long)R * desc->N;
-    const long long qsz = (long long)desc->L * desc->H * desc->N * desc->d * es;
-    long long out = 0;
-    for (int r = 0; r < R; ++r) {
-        const long long M = cu[r + 1] - cu[r];
-        ScorePlan p;
-        make_plan(*desc, M, cus, &p);
-        const char* Qr = (const char*)Q + r * qsz;
-        const char* Kr = (const char*)K + (cu[r] + (long long)r * desc->N) * desc->d * es;
-        const long long M_out = keep ? keep[r] : M;
-        float* imp = importance + (keep ? out : cu[r]);
-        s = to_status(launch_score(p, *desc, Qr, Kr, T * desc->d, (int)M, (int)M_out, imp, ws,
-                                   (hipStream_t)stream));
-        if (s != SP_OK) return s;
-        out += M_out;
-    }
-    return SP_OK;
-}
-
-}  // namespace
 
 sp_status sp_score_varlen(const sp_score_desc* desc, int32_t R, const void* Q, const void* K,
                           const int64_t* cu, float* importance, void* ws, size_t ws_bytes,

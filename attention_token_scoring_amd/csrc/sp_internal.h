@@ -22,6 +22,7 @@ constexpr int kTileKeys = 16;
 constexpr int kMaxRanks = 480;
 constexpr int kMaxDefer = 3;          // units between streaming and finishing a unit
 constexpr int kLdsBytes = 160 * 1024;  // LDS of one CU
+constexpr int kDefaultCUs = 256;       // MI355X; used when no device can be queried
 // Tiles per streaming wave and unit: the base value, or one more for long
 // prompts (a deeper slice per workgroup).
 constexpr int tiles_per_wave(bool bf16, int d) { return (!bf16 && d == 128) ? 2 : 4; }
@@ -122,6 +123,13 @@ struct SelectParamsDev {
     float last_mult;
     int min_tok, max_keep;  // (threshold mode)
 };
+
+// Launch plan for one prompt of M keys on a device with cus compute units
+// (SP_EINVAL for M < 1, SP_EUNSUPPORTED where no split fits).
+sp_status make_plan(const sp_score_desc& d, long long M, int cus, ScorePlan* out);
+
+// Workspace bytes that cover every plan make_plan can choose for M <= max_M.
+size_t workspace_bound(const sp_score_desc& d, long long max_M, int cus);
 
 // Events the calling thread wants recorded around each scoring kernel launch
 // (profiling aid; both null when unset).

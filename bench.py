@@ -104,10 +104,10 @@ def _code_only(text: str) -> str:
 
 def kernel_source_sha() -> str:
     """Fingerprint of the code of every source the scoring kernels and their
-    plan come from."""
+    plan come from (sp_score*: the kernels, their launch and the planner)."""
     csrc = os.path.join(ROOT, "attention_token_scoring_amd", "csrc")
     names = sorted(n for n in os.listdir(csrc)
-                   if n.startswith("sp_score") or n in ("sp_internal.h", "sp_api.hip"))
+                   if n.startswith("sp_score") or n == "sp_internal.h")
     h = hashlib.sha256()
     for name in names:
         with open(os.path.join(csrc, name), encoding="utf-8") as f:
