@@ -1,5 +1,7 @@
 // Launch planning for the scoring kernel: the split of each (layer, kv-head)
 // unit over workgroups, the LDS layout and the workspace.
+#include <mutex>
+
 #include "sp_internal.h"
 
 namespace sp {
@@ -19,7 +21,7 @@ int esize(sp_dtype t) { return t == SP_BF16 ? 2 : 4; }
 // keep in flight and park (registers and LDS), the groups fill the device with
 // at least one CU left for combining, and the per-unit exchanges stay few;
 // then lay out LDS and the workspace.
-sp_status make_plan(const sp_score_desc& d, long long M, int cus, ScorePlan* out) {
+static sp_status plan_uncached(const sp_score_desc& d, long long M, int cus, ScorePlan* out) {
     ScorePlan p;
     const int G = d.H / d.Hkv;
     const bool bf = d.dtype == SP_BF16;
@@ -111,6 +113,62 @@ sp_status make_plan(const sp_score_desc& d, long long M, int cus, ScorePlan* out
     p.ws_lse = p.ws_tail + round_up((size_t)p.units * p.rows * 8, 256);
     p.ws_tg = p.ws_lse + round_up((size_t)p.units * p.rows * 4, 256);
     p.ws_total = p.ws_tg + round_up((size_t)p.ngroups * d.N * M * 4, 256);
+    *out = p;
+    return SP_OK;
+}
+
+// The search above costs microseconds of host time per call, as much as a
+// small prompt's whole scoring kernel; a serving loop asks for the same few
+// shapes over and over, so plans are kept in a small direct-mapped table
+// keyed by everything the search reads.
+namespace {
+
+struct PlanKey {
+    int L, H, Hkv, d, N, dtype, cus;
+    long long M;
+    bool operator==(const PlanKey& o) const {
+        return L == o.L && H == o.H && Hkv == o.Hkv && d == o.d && N == o.N && dtype == o.dtype &&
+               cus == o.cus && M == o.M;
+    }
+};
+
+constexpr int kPlanSlots = 256;
+struct PlanSlot {
+    bool used = false;
+    PlanKey key;
+    ScorePlan plan;
+};
+PlanSlot g_plans[kPlanSlots];
+std::mutex g_plans_mu;
+
+unsigned plan_slot(const PlanKey& k) {
+    unsigned long long h = 1469598103934665603ull;
+    const long long f[8] = {k.L, k.H, k.Hkv, k.d, k.N, k.dtype, k.cus, k.M};
+    for (long long v : f) h = (h ^ (unsigned long long)v) * 1099511628211ull;
+    return (unsigned)(h ^ (h >> 29)) % kPlanSlots;
+}
+
+}  // namespace
+
+sp_status make_plan(const sp_score_desc& d, long long M, int cus, ScorePlan* out) {
+    const PlanKey k{d.L, d.H, d.Hkv, d.d, d.N, (int)d.dtype, cus, M};
+    const unsigned slot = plan_slot(k);
+    {
+        std::lock_guard<std::mutex> lk(g_plans_mu);
+        if (g_plans[slot].used && g_plans[slot].key == k) {
+            *out = g_plans[slot].plan;
+            return SP_OK;
+        }
+    }
+    ScorePlan p;
+    const sp_status s = plan_uncached(d, M, cus, &p);
+    if (s != SP_OK) return s;
+    {
+        std::lock_guard<std::mutex> lk(g_plans_mu);
+        g_plans[slot].used = true;
+        g_plans[slot].key = k;
+        g_plans[slot].plan = p;
+    }
     *out = p;
     return SP_OK;
 }
