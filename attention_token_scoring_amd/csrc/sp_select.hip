@@ -32,7 +32,8 @@ constexpr int kSeg = 16;        // contiguous elements a thread quantises per ti
 constexpr int kTile = kSelThreads * kSeg;  // elements per staged tile
 constexpr int kDigit = 11;                 // radix select: key bits per round
 constexpr int kBins = 1 << kDigit;
-constexpr int kFinal = 64;                 // candidates ranked exactly by one wave
+constexpr int kFinal = 64;                 // candidates ranked exactly, one per thread
+constexpr int kRankBatch = 8;              // candidates read at a time while ranking
 
 struct SelectBatch {
     int cu[kSelBatch + 1];      // prompt offsets of the requests in this launch
@@ -347,27 +348,33 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectBatch b, Sele
         thr = (double)p.mass * (double)total;
         keep_all = !((double)total >= thr);  // no rank reaches the threshold
     }
-    kand = wave_bitwise64<true>(kand);
-    kor = wave_bitwise64<false>(kor);
-    if (lane == 0) {
-        sh.rand_[w] = kand;
-        sh.ror_[w] = kor;
-    }
-    __syncthreads();
-    kand = ~0ull;
-    kor = 0ull;
-    for (int x2 = 0; x2 < kSelWaves; ++x2) {
-        kand &= sh.rand_[x2];
-        kor |= sh.ror_[x2];
-    }
-    const unsigned long long diff = kand ^ kor;  // bits where the keys differ
     // Rounds fix kDigit bits at a time from the highest bit where keys
     // differ, keeping the candidates (keys matching prefix on the bits of
     // fmask) that contain the last kept rank, until at most kFinal are left or
     // all bits are fixed. Keys above the candidates rank before all of them.
-    int hi = diff == 0ull ? -1 : 63 - __builtin_clzll(diff);
-    unsigned long long fmask = hi >= 63 ? 0ull : ~0ull << (hi + 1);
-    unsigned long long prefix = kand & fmask;
+    // With at most kFinal chunks there are no rounds: every chunk is a
+    // candidate (fmask and prefix 0).
+    int hi = -1;
+    unsigned long long fmask = 0ull, prefix = 0ull;
+    if (nc > kFinal && !keep_all) {
+        kand = wave_bitwise64<true>(kand);
+        kor = wave_bitwise64<false>(kor);
+        if (lane == 0) {
+            sh.rand_[w] = kand;
+            sh.ror_[w] = kor;
+        }
+        __syncthreads();
+        kand = ~0ull;
+        kor = 0ull;
+        for (int x2 = 0; x2 < kSelWaves; ++x2) {
+            kand &= sh.rand_[x2];
+            kor |= sh.ror_[x2];
+        }
+        const unsigned long long diff = kand ^ kor;  // bits where the keys differ
+        hi = diff == 0ull ? -1 : 63 - __builtin_clzll(diff);
+        fmask = hi >= 63 ? 0ull : ~0ull << (hi + 1);
+        prefix = kand & fmask;
+    }
     unsigned long long above_mass = 0ull;
     unsigned int above_count = 0u;
     unsigned int ncand = (unsigned)nc;
@@ -454,7 +461,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectBatch b, Sele
     }
     __syncthreads();  // the histograms alias S
 
-    // The last candidates: at most kFinal are ranked exactly by one wave;
+    // The last candidates: at most kFinal are ranked exactly, one per thread;
     // more can only remain when all their bits are fixed, i.e. they are equal
     // keys, and then their index order decides (a scan).
     bool keep[kPer];
@@ -477,20 +484,40 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectBatch b, Sele
             }
         }
         __syncthreads();
-        if (w == 0) {
-            const int n = sh.ncand < kFinal ? sh.ncand : kFinal;
-            if (lane < n) {
-                const unsigned long long mk = sh.ck[lane];
-                const unsigned int mi = sh.ci[lane];
+        // slots up to the next multiple of kRankBatch: entries that rank
+        // before none (key 0 with an index past every chunk)
+        const int n = sh.ncand < kFinal ? sh.ncand : kFinal;
+        const int npad = (n + kRankBatch - 1) / kRankBatch * kRankBatch;
+        if (tid >= n && tid < npad) {
+            sh.ck[tid] = 0ull;
+            sh.ci[tid] = ~0u;
+            sh.cmass[tid] = 0ull;
+        }
+        __syncthreads();
+        {
+            if (tid < n) {
+                const unsigned long long mk = sh.ck[tid];
+                const unsigned int mi = sh.ci[tid];
                 unsigned int rank = 0u;
                 unsigned long long before = 0ull;
-                for (int j = 0; j < n; ++j) {
-                    if (ranks_before(sh.ck[j], sh.ci[j], mk, mi)) {
-                        ++rank;
-                        before += sh.cmass[j];
+                // kRankBatch candidates' loads in flight at a time
+                for (int j0 = 0; j0 < npad; j0 += kRankBatch) {
+                    unsigned long long kk[kRankBatch], mm[kRankBatch];
+                    unsigned int ii[kRankBatch];
+#pragma unroll
+                    for (int u = 0; u < kRankBatch; ++u) {
+                        kk[u] = sh.ck[j0 + u];
+                        ii[u] = sh.ci[j0 + u];
+                        mm[u] = sh.cmass[j0 + u];
+                    }
+#pragma unroll
+                    for (int u = 0; u < kRankBatch; ++u) {
+                        const bool b = ranks_before(kk[u], ii[u], mk, mi);
+                        rank += b ? 1u : 0u;
+                        before += mm[u] & (0ull - (unsigned long long)b);  // (every load used)
                     }
                 }
-                sh.ckeep[lane] = topk ? (long long)(above_count + rank) < kc_topk
+                sh.ckeep[tid] = topk ? (long long)(above_count + rank) < kc_topk
                                       : (double)(above_mass + before) < thr;
             }
         }
