@@ -30,7 +30,7 @@ __device__ __forceinline__ float dot16(uint4 q, uint4 k, float acc) {
     return acc;
 }
 
-template <bool BF16>
+template <bool BF16, int D>
 __global__ __launch_bounds__(256) void score_prep_kernel(ScoreArgs a, int rows) {
     __shared__ float logit[32][33];  // [row][look-ahead key]
     const int u = blockIdx.x, tid = threadIdx.x;
@@ -45,16 +45,23 @@ __global__ __launch_bounds__(256) void score_prep_kernel(ScoreArgs a, int rows) 
     const int l = u / a.Hkv, kvh = u % a.Hkv;
     constexpr int esz = BF16 ? 2 : 4;
     const char* kp = (const char*)a.K + ((long long)u * a.plane_stride + (long long)a.M * a.d) * esz;
-    const int n16 = a.d * esz / 16;
+    constexpr int n16 = D * esz / 16;  // (all of a row's loads in flight at once)
     for (int x = tid; x < rows * a.N; x += 256) {
         const int row = x / a.N, t = x % a.N;
         const int j = row / a.G, hl = row % a.G;
         if (j < a.N && t <= j) {
             const long long qrow = ((long long)l * a.H + (long long)kvh * a.G + hl) * a.N + j;
-            const uint4* q = (const uint4*)((const char*)a.Q + qrow * a.d * esz);
-            const uint4* k = (const uint4*)(kp + (long long)t * a.d * esz);
+            const uint4* q = (const uint4*)((const char*)a.Q + qrow * D * esz);
+            const uint4* k = (const uint4*)(kp + (long long)t * D * esz);
+            uint4 qv[n16], kv[n16];
+#pragma unroll
+            for (int e = 0; e < n16; ++e) {
+                qv[e] = q[e];
+                kv[e] = k[e];
+            }
             float acc = 0.f;
-            for (int e = 0; e < n16; ++e) acc = dot16<BF16>(q[e], k[e], acc);
+#pragma unroll
+            for (int e = 0; e < n16; ++e) acc = dot16<BF16>(qv[e], kv[e], acc);
             logit[row][t] = acc;
         }
     }
@@ -133,10 +140,17 @@ hipError_t launch_score(const ScorePlan& p, const sp_score_desc& d, const void* 
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, p.lds.total);
     if (e != hipSuccess) return e;
 
-    if (d.dtype == SP_BF16)
-        hipLaunchKernelGGL(score_prep_kernel<true>, dim3(p.units), dim3(256), 0, stream, a, p.rows);
-    else
-        hipLaunchKernelGGL(score_prep_kernel<false>, dim3(p.units), dim3(256), 0, stream, a, p.rows);
+    if (d.dtype == SP_BF16) {
+        if (d.d == 128)
+            hipLaunchKernelGGL((score_prep_kernel<true, 128>), dim3(p.units), dim3(256), 0, stream, a, p.rows);
+        else
+            hipLaunchKernelGGL((score_prep_kernel<true, 64>), dim3(p.units), dim3(256), 0, stream, a, p.rows);
+    } else {
+        if (d.d == 128)
+            hipLaunchKernelGGL((score_prep_kernel<false, 128>), dim3(p.units), dim3(256), 0, stream, a, p.rows);
+        else
+            hipLaunchKernelGGL((score_prep_kernel<false, 64>), dim3(p.units), dim3(256), 0, stream, a, p.rows);
+    }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     void* args[] = {&a};
