@@ -241,7 +241,8 @@ def main():
                       args.copy_probe_mib or 1024)
         return
     if args.gpus != 1:
-        print("bench.py: this build runs on one GPU only; --gpus must be 1", file=sys.stderr)
+        print("bench.py: the scoring path runs on one GPU (no multi-GPU sharding); --gpus must be 1",
+              file=sys.stderr)
         sys.exit(2)
     import torch
 
