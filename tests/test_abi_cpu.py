@@ -200,3 +200,26 @@ def test_score_windows_rejects_keeps(lib):
                                     None) == sp.SP_EINVAL, keep
     assert lib.sp_score_windows(ctypes.byref(d), 2, FAKE, FAKE, cu, None, FAKE, FAKE, 1 << 30,
                                 None) == sp.SP_EINVAL
+
+
+def test_plan_cache_returns_each_shapes_own_plan(lib):
+    # plans are cached per (shape, M, compute units) in a table of a few
+    # hundred slots: more distinct keys than slots, asked for in shuffled
+    # order, must each get back the plan their first (uncached) call computed
+    import numpy as np
+    rng = np.random.default_rng(11)
+    shapes = [dict(L=32, H=32, Hkv=8, d=128), dict(L=24, H=16, Hkv=8, d=64),
+              dict(L=2, H=4, Hkv=2, d=64, dtype=sp.SP_F32), dict(L=28, H=16, Hkv=4, d=128),
+              dict(L=16, H=8, Hkv=8, d=64, N=4)]
+    keys = [(i, int(M)) for i in range(len(shapes)) for M in rng.integers(1, 80000, 120)]
+    first = {}
+    for i, M in keys:
+        first[(i, M)] = sp.sp_score_plan(desc(**shapes[i]), M)
+    for _ in range(2):
+        for x in rng.permutation(len(keys)):
+            i, M = keys[x]
+            assert sp.sp_score_plan(desc(**shapes[i]), M) == first[(i, M)], (shapes[i], M)
+    # and the cached plan of a shape is not served for another at the same M
+    a = sp.sp_score_plan(desc(**shapes[0]), 32768)
+    b = sp.sp_score_plan(desc(**shapes[3]), 32768)
+    assert a != b
