@@ -18,8 +18,11 @@
  * Conventions for every call:
  *  - Pointers marked "device" are HIP device memory (hipMalloc / torch CUDA
  *    tensors); "host" pointers are ordinary CPU memory read during the call.
- *    The caller owns every buffer; the library allocates nothing and keeps no
- *    state between calls. Tensors are dense, row-major, innermost index last.
+ *    The caller owns every buffer; the library allocates nothing. Between
+ *    calls it keeps only host-side caches that do not change any result: each
+ *    device's compute-unit count and the launch plans of recent (shape, M)
+ *    pairs, guarded for concurrent callers. Tensors are dense, row-major,
+ *    innermost index last.
  *  - `stream` is a hipStream_t (NULL = the default stream). Calls are
  *    asynchronous and stream-ordered: they enqueue kernels and return. No call
  *    synchronises the device.
