@@ -1,0 +1,65 @@
+"""Parity on seeded random shapes and selection settings, beyond the listed
+cases: head-group size, look-ahead steps, head dimension, operand type,
+layer and kv-head counts and prompt length drawn at random within what the
+kernels implement (G a power of two, G * N <= 32, d in {64, 128}); each
+case's importance is compared with the oracle's (the same bounds as the
+listed cases) and then selected with random chunking, pooling, mode and
+boosts (bit-exact against the oracle on the GPU's importance)."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+import attention_token_scoring_amd as sp  # noqa: E402
+from test_gpu_parity import check_importance, to_dev  # noqa: E402
+
+
+def _cases(n=16, seed=2024):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        G = int(rng.choice([1, 2, 4, 8, 16]))
+        N = int(rng.integers(1, 32 // G + 1)) if G < 32 else 1
+        N = min(N, 16)
+        d = int(rng.choice([64, 128]))
+        dt = synth.BF16 if rng.random() < 0.7 else synth.F32
+        L = int(rng.integers(1, 4))
+        Hkv = int(rng.integers(1, 4))
+        M = int(np.exp(rng.uniform(0, np.log(4000))))
+        sel = dict(chunk=int(rng.choice([8, 16, 32, 64])), pool_k=int(rng.choice([1, 3, 5, 13])),
+                   mode=str(rng.choice(["topk", "mass"])), keep_rate=float(rng.uniform(0.05, 0.5)),
+                   mass=float(rng.uniform(0.5, 0.95)))
+        if rng.random() < 0.5:
+            sel.update(boost_first_n=int(rng.integers(0, 80)), boost_first_mult=float(rng.uniform(1, 2)),
+                       boost_last_n=int(rng.integers(0, 80)), boost_last_mult=float(rng.uniform(1, 2)))
+        out.append((f"r{i}-{'bf16' if dt == synth.BF16 else 'f32'}-d{d}-G{G}-N{N}-L{L}-Hkv{Hkv}-M{M}",
+                    L, G * Hkv, Hkv, d, N, M, dt, i, sel))
+    return out
+
+
+CASES = _cases()
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_random_shape_score_and_select(case):
+    name, L, H, Hkv, d, N, M, dt, seed, sel = case
+    print(f"case {name} {sel}", flush=True)
+    w = synth.Workload("case", L=L, H=H, Hkv=Hkv, d=d, N=N, dtype=dt, seed=100 + seed, M=M,
+                       plant_frac=0.05, plant_chunk=32)
+    Qh, Kh, _ = synth.make_request(w)
+    imp = sp.sp_score(to_dev(Qh), to_dev(Kh))
+    torch.cuda.synchronize()
+    check_importance(imp.cpu().numpy(), oracle.score(Qh, Kh), name)
+    params = sp.select_params(**sel)
+    kept, pos, n = sp.sp_select(imp, params, pos_base=7)
+    torch.cuda.synchronize()
+    k_ref, p_ref = oracle.select(imp.cpu().numpy(), pos_base=7, **sel)
+    nk = int(n.cpu()[0])
+    assert nk == len(k_ref), name
+    assert np.array_equal(kept[:nk].cpu().numpy(), k_ref), name
+    assert np.array_equal(pos[:nk].cpu().numpy(), p_ref), name
