@@ -63,3 +63,47 @@ def test_random_shape_score_and_select(case):
     assert nk == len(k_ref), name
     assert np.array_equal(kept[:nk].cpu().numpy(), k_ref), name
     assert np.array_equal(pos[:nk].cpu().numpy(), p_ref), name
+
+
+def _ragged_cases(n=6, seed=77):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i, (name, L, H, Hkv, d, N, M, dt, s, sel) in enumerate(_cases(n, seed)):
+        R = int(rng.integers(2, 7))
+        lens = [int(np.exp(rng.uniform(0, np.log(3000)))) for _ in range(R)]
+        out.append((f"ragged{i}-R{R}-" + name.split("-", 1)[1].rsplit("-M", 1)[0], L, H, Hkv, d, N, lens,
+                    dt, s, sel))
+    return out
+
+
+RAGGED = _ragged_cases()
+
+
+@pytest.mark.parametrize("case", RAGGED, ids=[c[0] for c in RAGGED])
+def test_random_ragged_batch(case):
+    """Every request of a random ragged batch (sp_score_varlen, then
+    sp_select_varlen with per-request position bases) against the oracle on
+    that request's own slices of the packed arrays."""
+    name, L, H, Hkv, d, N, lens, dt, seed, sel = case
+    print(f"case {name} lens {lens} {sel}", flush=True)
+    w = synth.Workload("case", L=L, H=H, Hkv=Hkv, d=d, N=N, dtype=dt, seed=200 + seed, M=max(lens),
+                       plant_frac=0.05, plant_chunk=32)
+    Qh, Kh, cu = synth.make_ragged(w, lens)
+    imp = sp.sp_score_varlen(to_dev(Qh), to_dev(Kh), cu)
+    torch.cuda.synchronize()
+    imp_h = imp.cpu().numpy()
+    ck = np.concatenate([[0], np.cumsum(np.asarray(lens) + N)])
+    for r in range(len(lens)):
+        ref = oracle.score(Qh[r], np.ascontiguousarray(Kh[:, :, ck[r]:ck[r + 1], :]))
+        check_importance(imp_h[cu[r]:cu[r + 1]], ref, f"{name} r={r}")
+    pos_base = [(5 * r + 3) % 11 for r in range(len(lens))]
+    kept, pos, n = sp.sp_select_varlen(imp, cu, sp.select_params(**sel), pos_base=pos_base)
+    torch.cuda.synchronize()
+    kept_h, pos_h, n_h = kept.cpu().numpy(), pos.cpu().numpy(), n.cpu().numpy()
+    for r in range(len(lens)):
+        k_ref, p_ref = oracle.select(imp_h[cu[r]:cu[r + 1]], pos_base=pos_base[r], base_index=int(cu[r]),
+                                     **sel)
+        off = int(cu[r])
+        assert n_h[r] == len(k_ref), (name, r)
+        assert np.array_equal(kept_h[off:off + n_h[r]], k_ref), (name, r)
+        assert np.array_equal(pos_h[off:off + n_h[r]], p_ref), (name, r)
