@@ -107,3 +107,43 @@ def test_random_ragged_batch(case):
         assert n_h[r] == len(k_ref), (name, r)
         assert np.array_equal(kept_h[off:off + n_h[r]], k_ref), (name, r)
         assert np.array_equal(pos_h[off:off + n_h[r]], p_ref), (name, r)
+
+
+def _window_cases(n=6, seed=91):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i, (name, L, H, Hkv, d, N, M, dt, s, sel) in enumerate(_cases(n, seed)):
+        M = int(rng.integers(1, 6000))
+        window = int(rng.integers(1, 2500))
+        stride = int(rng.integers(1, window + 1))
+        if M // stride > 60:  # (keep the window count, and so the oracle's work, small)
+            stride = max(stride, -(-M // 60))
+            window = max(window, stride)
+        out.append((f"win{i}-M{M}-w{window}-s{stride}-" + name.split("-", 1)[1].rsplit("-M", 1)[0],
+                    L, H, Hkv, d, N, M, window, stride, dt, s))
+    return out
+
+
+WINDOWS = _window_cases()
+
+
+@pytest.mark.parametrize("case", WINDOWS, ids=[c[0] for c in WINDOWS])
+def test_random_sliding_windows(case):
+    """Random window layouts: the library's layout equals the oracle's, and
+    sp_score_windows equals the oracle scoring each window from its own
+    arrays and keeping its first keeps[r] scores."""
+    name, L, H, Hkv, d, N, M, window, stride, dt, seed = case
+    print(f"case {name}", flush=True)
+    starts, lens, keeps = sp.sp_window_layout(M, window, stride)
+    assert [tuple(x) for x in zip(starts, lens, keeps)] == oracle.window_layout(M, window, stride)
+    w = synth.Workload("case", L=L, H=H, Hkv=Hkv, d=d, N=N, dtype=dt, seed=300 + seed, R=len(lens),
+                       plant_frac=0.05, plant_chunk=32)
+    Qh, Kh, cu = synth.make_ragged(w, lens)
+    imp = sp.sp_score_windows(to_dev(Qh), to_dev(Kh), cu, keeps)
+    torch.cuda.synchronize()
+    ck = np.concatenate([[0], np.cumsum(np.asarray(lens) + N)])
+    Qs = [Qh[r] for r in range(len(lens))]
+    Ks = [np.ascontiguousarray(Kh[:, :, ck[r]:ck[r + 1], :]) for r in range(len(lens))]
+    imp_h = imp.cpu().numpy()
+    assert imp_h.shape == (M,)
+    check_importance(imp_h, oracle.score_windows(Qs, Ks, keeps), name)
