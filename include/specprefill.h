@@ -32,7 +32,10 @@
  *    small). SP_EDEVICE reports a failed kernel launch; faults during
  *    execution surface at the caller's next synchronisation, as usual in HIP.
  *  - Inputs containing NaN or Inf give unspecified (but memory-safe) results.
- *  - Two calls may run concurrently only with distinct workspaces and outputs.
+ *  - Two calls may run concurrently only with distinct workspaces and outputs;
+ *    concurrent scoring calls also compete for compute units, which an
+ *    ordinary (SP_LAUNCH_RESIDENT) scoring launch needs all at once: see
+ *    sp_launch below.
  */
 #ifndef SPECPREFILL_H
 #define SPECPREFILL_H
