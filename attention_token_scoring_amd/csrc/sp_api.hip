@@ -11,7 +11,7 @@ namespace sp {
 
 hipError_t launch_score(const ScorePlan& p, const sp_score_desc& d, const void* Q, const void* K,
                         long long plane_stride, int M, int M_out, float* importance, void* ws,
-                        hipStream_t stream);
+                        bool first, hipStream_t stream);
 hipError_t launch_gather(const void* src, long long row_bytes, const int32_t* kept,
                          const int32_t* n_kept, int R, const int64_t* cu, long long max_rows,
                          void* dst, hipStream_t stream);
@@ -158,7 +158,7 @@ sp_status score_batch(const sp_score_desc* desc, int32_t R, const void* Q, const
         const long long M_out = keep ? keep[r] : M;
         float* imp = importance + (keep ? out : cu[r]);
         s = to_status(launch_score(p, *desc, Qr, Kr, T * desc->d, (int)M, (int)M_out, imp, ws,
-                                   (hipStream_t)stream));
+                                   r == 0, (hipStream_t)stream));
         if (s != SP_OK) return s;
         out += M_out;
     }
@@ -194,6 +194,11 @@ size_t sp_score_workspace_bytes(const sp_score_desc* desc, int64_t max_prompt_le
 sp_status sp_profile_score_kernel(void* before, void* after) {
     if ((before == nullptr) != (after == nullptr)) return SP_EINVAL;
     sp::set_profile_events((hipEvent_t)before, (hipEvent_t)after);
+    return SP_OK;
+}
+
+sp_status sp_set_wait_limit(uint64_t ticks) {
+    sp::set_wait_limit((unsigned long long)ticks);
     return SP_OK;
 }
 
@@ -240,7 +245,8 @@ sp_status sp_score(const sp_score_desc* desc, const void* Q, const void* K, int3
     if (s != SP_OK) return s;
     if (!ws || !aligned(ws, 256) || ws_bytes < p.ws_total) return SP_EWORKSPACE;
     const long long plane = (long long)(M + desc->N) * desc->d;
-    return to_status(launch_score(p, *desc, Q, K, plane, M, M, importance, ws, (hipStream_t)stream));
+    return to_status(launch_score(p, *desc, Q, K, plane, M, M, importance, ws, true,
+                                  (hipStream_t)stream));
 }
 
 sp_status sp_score_varlen(const sp_score_desc* desc, int32_t R, const void* Q, const void* K,

@@ -88,6 +88,8 @@ struct ScoreArgs {
     int nbk;                   // D + 1 banks of parked logits
     ScoreLds lds;
     float c;                   // scale * log2(e)
+    int reset_err;             // 1: the prep kernel clears the error word (first request of a call)
+    unsigned long long spin_ticks;  // limit of a bounded wait, in ticks of the 100 MHz clock
 };
 
 struct ScorePlan {
@@ -134,6 +136,10 @@ size_t workspace_bound(const sp_score_desc& d, long long max_M, int cus);
 // Events the calling thread wants recorded around each scoring kernel launch
 // (profiling aid; both null when unset).
 void set_profile_events(hipEvent_t before, hipEvent_t after);
+
+// Limit of the scoring kernel's bounded waits for the calling thread's later
+// calls (0: the default of 2 s); a testing aid.
+void set_wait_limit(unsigned long long ticks);
 
 // Scoring kernels, one translation unit per operand type and head
 // dimension: the instantiation for (rows, G, tiles per wave), or nullptr.

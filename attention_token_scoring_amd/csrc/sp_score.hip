@@ -34,7 +34,7 @@ template <bool BF16, int D>
 __global__ __launch_bounds__(256) void score_prep_kernel(ScoreArgs a, int rows) {
     __shared__ float logit[32][33];  // [row][look-ahead key]
     const int u = blockIdx.x, tid = threadIdx.x;
-    if (u == 0 && tid == 0) *a.err = 0;
+    if (u == 0 && tid == 0 && a.reset_err) *a.err = 0;
     if (u == 0)
         for (int x = tid; x < a.g; x += 256) a.done[x] = 0u;
     // this unit's g * rows partial slots, two per 16-byte store
@@ -92,19 +92,24 @@ static const void* pick_kernel(int dtype, int d, int rows, int G, int tpw) {
 }
 
 static thread_local hipEvent_t t_ev_before = nullptr, t_ev_after = nullptr;
+static thread_local unsigned long long t_wait_limit = 0;
 
 void set_profile_events(hipEvent_t before, hipEvent_t after) {
     t_ev_before = before;
     t_ev_after = after;
 }
 
-// One request: prep (reset synchronisation state, look-ahead statistics),
+void set_wait_limit(unsigned long long ticks) { t_wait_limit = ticks; }
+
+// One request: prep (reset synchronisation state, look-ahead statistics; the
+// error word only for the first request of a call, so that it reports a time-out
+// in any request of the call),
 // then the scoring kernel, which also writes the importance: an ordinary
 // launch (every workgroup resident on an otherwise idle device) or, if the
 // descriptor asks for it, a cooperative one.
 hipError_t launch_score(const ScorePlan& p, const sp_score_desc& d, const void* Q, const void* K,
                         long long plane_stride, int M, int M_out, float* importance, void* ws,
-                        hipStream_t stream) {
+                        bool first, hipStream_t stream) {
     char* base = (char*)ws;
     ScoreArgs a;
     a.Q = Q;
@@ -134,6 +139,8 @@ hipError_t launch_score(const ScorePlan& p, const sp_score_desc& d, const void* 
     a.lds = p.lds;
     const float scale = d.scale > 0.f ? d.scale : 1.0f / sqrtf((float)d.d);
     a.c = scale * 1.4426950408889634f;
+    a.reset_err = first ? 1 : 0;
+    a.spin_ticks = t_wait_limit > 0 ? t_wait_limit : kSpinTicks;
 
     const void* fn = pick_kernel(d.dtype, d.d, p.rows, a.G, p.tpw);
     if (!fn) return hipErrorInvalidValue;

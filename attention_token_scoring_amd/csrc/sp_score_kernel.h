@@ -57,9 +57,10 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-// 2 s of the 100 MHz constant clock: a wait longer than this means a
-// workgroup it waits for is not running (not resident, or a bug); the kernel
-// records it in the error word and moves on instead of hanging.
+// 2 s of the 100 MHz constant clock (the default limit of a bounded wait): a
+// wait longer than this means a workgroup it waits for is not running (not
+// resident, or a bug); the kernel records it in the error word and moves on
+// instead of hanging. The host may lower the limit (a testing aid).
 constexpr unsigned long long kSpinTicks = 200000000ull;
 // After 100 us a wait also looks at the error word, so that once one wait of
 // the launch has timed out the others end too and the launch drains in about
@@ -71,6 +72,8 @@ constexpr uint32_t kOob = 0x7ffffff0u;
 // published yet (a NaN pattern no published value has).
 constexpr unsigned long long kSentinel = ~0ull;
 constexpr unsigned kSentinel32 = ~0u;
+// Bits of the quiet NaN written in place of the scores of a call that timed out.
+constexpr unsigned kNaNBits = 0x7fc00000u;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
@@ -147,9 +150,9 @@ __device__ __forceinline__ unsigned ld32(const void* p) {
 }
 
 // Whether a bounded wait that started at t0 should give up.
-__device__ __forceinline__ bool wait_expired(unsigned long long t0, const int* err) {
+__device__ __forceinline__ bool wait_expired(unsigned long long t0, const ScoreArgs& a) {
     const unsigned long long dt = wall_clock64() - t0;
-    return dt > kSpinTicks || (dt > kAbortTicks && ld32(err) != 0u);
+    return dt > a.spin_ticks || (dt > kAbortTicks && ld32(a.err) != 0u);
 }
 
 // Parked logits: y = (log2-domain logit) - (row reference) <= 0 as a 16-bit
@@ -302,7 +305,7 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
                 const unsigned long long* gate = (const unsigned long long*)(a.part + ((size_t)u * a.g + k_hi - 1) * ROWS);
                 while (ld64(gate) == kSentinel) {
                     __builtin_amdgcn_s_sleep(8);
-                    if (wait_expired(t0, a.err)) {
+                    if (wait_expired(t0, a)) {
                         if (lane == 0) __hip_atomic_store(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                         break;
                     }
@@ -326,7 +329,7 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
                     pend = np;
                     if (__ballot(pend != 0) == 0) break;
                     __builtin_amdgcn_s_sleep(2);
-                    if (wait_expired(t0, a.err)) {
+                    if (wait_expired(t0, a)) {
                         if (lane == 0) __hip_atomic_store(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                         break;
                     }
@@ -720,7 +723,7 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
                     if (miss) lse_v[S] = ld32(a.lse + (size_t)u * ROWS + lane);
                     miss = lane < ROWS && lse_v[S] == kSentinel32;
                     if (__ballot(miss) == 0) break;
-                    if (wait_expired(t0, a.err)) {
+                    if (wait_expired(t0, a)) {
                         if (lane == 0) __hip_atomic_store(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                         break;
                     }
@@ -835,10 +838,17 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
         }
         __syncthreads();
     }
+    // A call in which some bounded wait gave up (here or in any workgroup
+    // that got to it first) has scores built on missing statistics: they are
+    // replaced by NaN bit patterns (stored as bits, no arithmetic on them), so
+    // that the selection rejects them instead of returning a plausible set.
+    const bool poisoned = ld32(a.err) != 0u;
     for (int k = tid; k < nkeys && r0 + k < a.M_out; k += kThreads) {
         float sum = 0.f;
         for (int jj = 0; jj < a.N; ++jj) sum += exp2_hw((float)Trun[jj * KRP + k] * kStep);
-        a.importance[r0 + k] = sum / (float)a.N;
+        const float v = sum / (float)a.N;
+        __hip_atomic_store((unsigned*)a.importance + r0 + k, poisoned ? kNaNBits : __float_as_uint(v),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 

@@ -177,16 +177,24 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectBatch b, Sele
 
     // 1. min and max (exact in any order); kLd loads in flight per thread,
     // indices past the end re-read the last element
+    // (a NaN or infinite score, which a scoring call that timed out leaves,
+    // makes the request's count -1 and leaves its outputs untouched)
     float mn = INFINITY, mx = -INFINITY;
+    int nonfinite = 0;
     for (int t0 = 0; t0 < M; t0 += kSelThreads * kLd) {
         float v[kLd];
 #pragma unroll
         for (int k = 0; k < kLd; ++k) v[k] = x[min(t0 + k * kSelThreads + tid, M - 1)];
 #pragma unroll
         for (int k = 0; k < kLd; ++k) {
+            nonfinite |= (__float_as_uint(v[k]) & 0x7f800000u) == 0x7f800000u;
             mn = fminf(mn, v[k]);
             mx = fmaxf(mx, v[k]);
         }
+    }
+    if (__syncthreads_or(nonfinite)) {
+        if (tid == 0) nkept_all[b.first + r] = -1;
+        return;
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
@@ -633,6 +641,14 @@ __global__ __launch_bounds__(kSelThreads) void select_threshold_kernel(
     int32_t* kept = kept_all + base;
     int32_t* pos = pos_all + base;
     const int eff_min = min(p.min_tok, max(4, M / 10));
+    // non-finite scores: count -1, outputs untouched (as in select_kernel)
+    int nonfinite = 0;
+    for (int i = tid; i < M; i += kSelThreads)
+        nonfinite |= (__float_as_uint(x[i]) & 0x7f800000u) == 0x7f800000u;
+    if (__syncthreads_or(nonfinite)) {
+        if (tid == 0) nkept_all[b.first + r] = -1;
+        return;
+    }
     int n;
     if (p.keep_rate >= 1.0f || M <= eff_min) {
         for (int o = tid; o < M; o += kSelThreads) {
