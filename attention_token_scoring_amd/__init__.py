@@ -31,7 +31,8 @@ SP_LAUNCH_RESIDENT, SP_LAUNCH_COOPERATIVE = 0, 1
 EXPORTED = ("sp_score", "sp_score_varlen", "sp_select", "sp_select_varlen",
             "sp_score_workspace_bytes", "sp_select_workspace_bytes", "sp_score_plan",
             "sp_status_string", "sp_profile_score_kernel", "sp_score_status",
-            "sp_score_windows", "sp_window_layout", "sp_gather_rows", "sp_break_even")
+            "sp_score_windows", "sp_window_layout", "sp_gather_rows", "sp_break_even",
+            "sp_read_probe", "sp_set_wait_limit")
 
 
 class SpError(RuntimeError):
@@ -89,9 +90,11 @@ def load_library():
     lib.sp_gather_rows.argtypes = [vp, i64, vp, vp, i32, P(ctypes.c_int64), vp, vp]
     f32 = ctypes.c_float
     lib.sp_break_even.argtypes = [i64, f32, f32, f32, f32, P(ctypes.c_int32)]
+    lib.sp_read_probe.argtypes = [vp, sz, i32, i32, vp, vp]
+    lib.sp_set_wait_limit.argtypes = [ctypes.c_uint64]
     for name in ("sp_score_plan", "sp_score", "sp_score_varlen", "sp_select", "sp_select_varlen",
                  "sp_profile_score_kernel", "sp_score_status", "sp_score_windows",
-                 "sp_window_layout", "sp_gather_rows", "sp_break_even"):
+                 "sp_window_layout", "sp_gather_rows", "sp_break_even", "sp_read_probe", "sp_set_wait_limit"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -126,6 +129,20 @@ def _require_cuda(*ts):
             raise ValueError("tensors must live on the GPU")
         if not t.is_contiguous():
             raise ValueError("tensors must be contiguous")
+
+
+def _check_out(t, dtype, min_numel: int, name: str):
+    """A caller-supplied output (or input) tensor the kernels index up to
+    min_numel elements: it must be a contiguous CUDA tensor of `dtype` with at
+    least that many elements (a smaller one would be written out of bounds)."""
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() < min_numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs at least {min_numel}")
 
 
 def _stream(stream):
@@ -184,6 +201,12 @@ def sp_score_status(workspace, stream=None) -> bool:
     return bool(out.value)
 
 
+def sp_set_wait_limit(ticks: int = 0):
+    """Testing aid: limit of the scoring kernel's bounded waits for this
+    thread's later calls, in 100 MHz clock ticks (0: the default, 2 s)."""
+    _check(load_library().sp_set_wait_limit(int(ticks)), "sp_set_wait_limit")
+
+
 def _workspace(nbytes: int, device, workspace=None):
     torch = _torch()
     if workspace is not None:
@@ -208,6 +231,7 @@ def sp_score(Q, K, M: Optional[int] = None, scale: float = 0.0, out=None, worksp
         raise ValueError("K must be [L, Hkv, M+N, d] with Q's dtype")
     if out is None:
         out = torch.empty(M, dtype=torch.float32, device=Q.device)
+    _check_out(out, torch.float32, M, "out")
     ws = _workspace(sp_score_workspace_bytes(desc, M), Q.device, workspace)
     st = load_library().sp_score(ctypes.byref(desc), Q.data_ptr(), K.data_ptr(), int(M),
                                  out.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(),
@@ -232,6 +256,7 @@ def sp_score_varlen(Q, K, cu_prompt: Sequence[int], scale: float = 0.0, out=None
         raise ValueError("K must hold sum(M_r + N) key rows")
     if out is None:
         out = torch.empty(int(cu[-1]), dtype=torch.float32, device=Q.device)
+    _check_out(out, torch.float32, int(cu[-1]), "out")
     maxM = int(np.max(np.diff(cu))) if R else 1
     ws = _workspace(sp_score_workspace_bytes(desc, maxM), Q.device, workspace)
     st = load_library().sp_score_varlen(
@@ -275,6 +300,7 @@ def sp_score_windows(Q, K, cu_window: Sequence[int], keeps: Sequence[int], scale
         raise ValueError("K must hold sum(M_r + N) key rows")
     if out is None:
         out = torch.empty(int(kp.sum()), dtype=torch.float32, device=Q.device)
+    _check_out(out, torch.float32, int(kp.sum()), "out")
     maxM = int(np.max(np.diff(cu)))
     ws = _workspace(sp_score_workspace_bytes(desc, maxM), Q.device, workspace)
     p64 = ctypes.POINTER(ctypes.c_int64)
@@ -300,6 +326,11 @@ def sp_gather_rows(src, kept_idx, n_kept, cu_prompt: Optional[Sequence[int]] = N
     if dst is None:
         dst = torch.zeros((int(cu[-1]),) + tuple(src.shape[1:]), dtype=src.dtype, device=src.device)
     row_bytes = src[0].numel() * src.element_size() if T else 0
+    _require_cuda(dst)
+    if dst.numel() * dst.element_size() < int(cu[-1]) * row_bytes:
+        raise ValueError(f"dst must hold at least {int(cu[-1])} rows of {row_bytes} bytes")
+    _check_out(kept_idx, torch.int32, int(cu[-1]), "kept_idx")
+    _check_out(n_kept, torch.int32, R, "n_kept")
     st = load_library().sp_gather_rows(src.data_ptr(), int(row_bytes), kept_idx.data_ptr(),
                                        n_kept.data_ptr(), int(R),
                                        cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
@@ -330,6 +361,10 @@ def sp_select(importance, params: SelectParams, pos_base: int = 0, kept_idx=None
     kept_idx = torch.empty(M, dtype=torch.int32, device=dev) if kept_idx is None else kept_idx
     pos_ids = torch.empty(M, dtype=torch.int32, device=dev) if pos_ids is None else pos_ids
     n_kept = torch.empty(1, dtype=torch.int32, device=dev) if n_kept is None else n_kept
+    _check_out(importance, torch.float32, M, "importance")
+    _check_out(kept_idx, torch.int32, M, "kept_idx")
+    _check_out(pos_ids, torch.int32, M, "pos_ids")
+    _check_out(n_kept, torch.int32, 1, "n_kept")
     st = load_library().sp_select(importance.data_ptr(), int(M), ctypes.byref(params),
                                   int(pos_base), kept_idx.data_ptr(), pos_ids.data_ptr(),
                                   n_kept.data_ptr(), None, 0, _stream(stream))
@@ -351,6 +386,10 @@ def sp_select_varlen(importance, cu_prompt: Sequence[int], params: SelectParams,
     kept_idx = torch.empty(total, dtype=torch.int32, device=dev) if kept_idx is None else kept_idx
     pos_ids = torch.empty(total, dtype=torch.int32, device=dev) if pos_ids is None else pos_ids
     n_kept = torch.empty(R, dtype=torch.int32, device=dev) if n_kept is None else n_kept
+    _check_out(importance, torch.float32, total, "importance")
+    _check_out(kept_idx, torch.int32, total, "kept_idx")
+    _check_out(pos_ids, torch.int32, total, "pos_ids")
+    _check_out(n_kept, torch.int32, R, "n_kept")
     pb = None
     if pos_base is not None:
         pb_arr = np.ascontiguousarray(np.asarray(pos_base, dtype=np.int32))
@@ -361,3 +400,17 @@ def sp_select_varlen(importance, cu_prompt: Sequence[int], params: SelectParams,
         0, _stream(stream))
     _check(st, "sp_select_varlen")
     return kept_idx, pos_ids, n_kept
+
+
+def sp_read_probe(buf, grid: int, depth: int = 8, flag=None, stream=None):
+    """Measurement aid: one streaming read of the whole of `buf` (a contiguous
+    CUDA tensor) by `grid` workgroups (see the C header). Returns `flag`."""
+    torch = _torch()
+    _require_cuda(buf)
+    if flag is None:
+        flag = torch.zeros(1, dtype=torch.int32, device=buf.device)
+    _check_out(flag, torch.int32, 1, "flag")
+    nbytes = buf.numel() * buf.element_size()
+    _check(load_library().sp_read_probe(buf.data_ptr(), int(nbytes), int(grid), int(depth),
+                                        flag.data_ptr(), _stream(stream)), "sp_read_probe")
+    return flag

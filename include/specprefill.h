@@ -31,7 +31,8 @@
  *    what the kernels implement), SP_EWORKSPACE (workspace missing or too
  *    small). SP_EDEVICE reports a failed kernel launch; faults during
  *    execution surface at the caller's next synchronisation, as usual in HIP.
- *  - Inputs containing NaN or Inf give unspecified (but memory-safe) results.
+ *  - Q or K containing NaN or Inf give unspecified (but memory-safe) scores;
+ *    scores containing NaN or Inf make the selection report n_kept = -1.
  *  - Two calls may run concurrently only with distinct workspaces and outputs;
  *    concurrent scoring calls also compete for compute units, which an
  *    ordinary (SP_LAUNCH_RESIDENT) scoring launch needs all at once: see
@@ -228,7 +229,9 @@ size_t sp_select_workspace_bytes(int32_t R, int64_t total_prompt_len,
  * identical outputs on every run.
  *   importance  device, [M] float32
  *   kept_idx, pos_ids  device, [M] int32 each (first *n_kept entries written)
- *   n_kept      device, [1] int32 (written)
+ *   n_kept      device, [1] int32 (written): the kept count, or -1 if some score
+ *               is NaN or infinite (kept_idx and pos_ids are then not written;
+ *               a scoring call whose bounded waits timed out leaves NaN scores)
  * Supported: M <= 2^24, nc = ceil(M/chunk) <= 4096, and boost multipliers
  * with max(1, first_mult, last_mult, first_mult*last_mult) * 2^32 * pool_k *
  * chunk < 2^53 (so the pooled sums stay exact in double).
@@ -248,7 +251,7 @@ sp_status sp_select(const float* importance, int32_t M, const sp_select_params* 
  *                   kept tokens as packed indices cu_prompt_host[r] + i, from
  *                   offset cu_prompt_host[r]
  *   pos_ids         device, [cu_prompt_host[R]] int32: pos_base_r + i, same offsets
- *   n_kept          device, [R] int32
+ *   n_kept          device, [R] int32 (-1 for a request with a non-finite score)
  */
 sp_status sp_select_varlen(const float* importance, int32_t R, const int64_t* cu_prompt_host,
                            const int32_t* pos_base_host, const sp_select_params* params,
@@ -314,11 +317,13 @@ sp_status sp_score_plan(const sp_score_desc* desc, int32_t M, int32_t info[8]);
 sp_status sp_profile_score_kernel(void* before, void* after);
 
 /*
- * Whether the last sp_score / sp_score_varlen that used workspace ws ran to
- * completion without any of its bounded cross-workgroup waits running out.
- * The scoring kernel never hangs: a wait that sees no progress for 2 s (which
- * would take a workgroup that never runs) gives up and marks the workspace,
- * and that call's importance is then not valid.
+ * Whether the last sp_score / sp_score_varlen / sp_score_windows call that
+ * used workspace ws ran to completion without any of its bounded
+ * cross-workgroup waits running out (in any of its requests). The scoring
+ * kernel never hangs: a wait that sees no progress for 2 s (which would take a
+ * workgroup that never runs) gives up and marks the workspace; the
+ * workgroups that finish after that write NaN in place of their scores (so
+ * that sp_select reports n_kept = -1), and the call's importance is not valid.
  *   ws         device workspace passed to that call
  *   stream     the stream that call was enqueued on
  *   timed_out  host, written: 0 (complete) or 1 (a wait timed out)
@@ -326,6 +331,31 @@ sp_status sp_profile_score_kernel(void* before, void* after);
  * SP_EINVAL for null pointers; SP_EDEVICE if the copy fails.
  */
 sp_status sp_score_status(const void* ws, void* stream, int32_t* timed_out);
+
+/*
+ * Testing aid: the limit, in ticks of the device's 100 MHz constant clock, of
+ * every bounded wait in the scoring calls the calling thread makes from now on
+ * (0 restores the default, 2 s). A tiny limit makes those waits give up at
+ * once, so that the time-out path (error word, NaN scores, n_kept = -1) can be
+ * exercised with every kernel still ending normally. Always SP_OK.
+ */
+sp_status sp_set_wait_limit(uint64_t ticks);
+
+/*
+ * Measurement aid, not part of the scoring computation: enqueues one plain
+ * streaming read of `bytes` bytes of device memory at buf by `grid`
+ * workgroups of 512 threads, each thread keeping `depth` (4, 8 or 16) 16-byte
+ * loads in flight (workgroup b reads the chunks b, b + grid, ... of
+ * 512 x depth x 16 bytes). bytes divided by the launch's duration is the HBM
+ * read rate the device sustains for that launch shape: the practical ceiling
+ * of a kernel that reads its input once.
+ *   buf     device, 16-byte aligned; bytes a positive multiple of 16
+ *   flag    device, [1] int32: written (1) only if the XOR of all words read
+ *           equals 0x5a17c0de (this keeps the loads; normally untouched)
+ * SP_EINVAL for null pointers or bad sizes, SP_EUNSUPPORTED for another depth.
+ */
+sp_status sp_read_probe(const void* buf, size_t bytes, int32_t grid, int32_t depth, int32_t* flag,
+                        void* stream);
 
 #ifdef __cplusplus
 }
