@@ -4,6 +4,7 @@ Sliding Window, Sliding Window Solution: 4471 tokens, window 2000, stride
 1000) and the coverage property the v3.1 fix states (every token scored by
 exactly one window)."""
 import json
+import math
 import os
 
 import numpy as np
@@ -58,3 +59,71 @@ def test_layout_rejects(M, window, stride):
         sp.sp_window_layout(M, window, stride)
     with pytest.raises(ValueError):
         oracle.window_layout(M, window, stride)
+
+
+# ---------------------------------------------------------------------------------------
+# oracle.score_windows against closed forms on the same worked example
+# ---------------------------------------------------------------------------------------
+def _window_inputs(length, N, planted, a):
+    """One window's Q [1,1,N,4] and K [1,1,length+N,4] (float32): every query
+    is e_0, every key 0 except the planted local positions, whose first
+    coordinate is a (so with scale 1 their logit is a and every other logit 0)."""
+    Q = np.zeros((1, 1, N, 4), np.float32)
+    Q[..., 0] = 1.0
+    K = np.zeros((1, 1, length + N, 4), np.float32)
+    for i in planted:
+        K[0, 0, i, 0] = a
+    return Q, K
+
+
+def test_oracle_score_windows_closed_form():
+    """The Guide's 4471-token example (window 2000, stride 1000), each window
+    with its own keys: window w plants a strong key in the part it keeps
+    (local 10 (w + 1)) and, unless it is the last, one in the part it drops
+    (local stride + 5). In window w (n keys, k planted) look-ahead row j sees
+    n + j + 1 keys with denominator Z_j = k e^a + (n + j + 1 - k), so a kept
+    token's score is (1/N) sum_j e^{a [planted]} / Z_j. This fixes which
+    window supplies each token, which part of it is kept, that each window's
+    softmax runs over its own keys, and the order of the stitched scores."""
+    g, layout = expected()
+    N, a = 4, 3.0
+    Qs, Ks, keeps, want = [], [], [], []
+    for w, (start, length, keep) in enumerate(layout):
+        last = w == len(layout) - 1
+        planted = [10 * (w + 1)] + ([] if last else [g["stride"] + 5])
+        Q, K = _window_inputs(length, N, planted, a)
+        Qs.append(Q)
+        Ks.append(K)
+        keeps.append(keep)
+        k = len(planted)
+        Z = [k * math.exp(a) + (length + j + 1 - k) for j in range(N)]
+        for i in range(keep):
+            num = math.exp(a) if i in planted else 1.0
+            want.append(sum(num / z for z in Z) / N)
+    got = oracle.score_windows(Qs, Ks, keeps, scale=1.0)
+    want = np.array(want)
+    assert got.shape == (g["M"],)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=0)
+    # the kept strong keys sit at global positions start + 10 (w + 1); the
+    # dropped ones (local stride + 5) leave no peak at start + stride + 5
+    peaks = np.flatnonzero(got > 2 * np.median(got))
+    assert peaks.tolist() == [s + 10 * (w + 1) for w, (s, _, _) in enumerate(layout)]
+
+
+def test_oracle_score_windows_uniform_keys():
+    """All of a window's keys equal: every kept token of a window of n keys
+    scores (1/N) sum_j 1/(n + j + 1): tokens 0-2999 from the 2000-key windows,
+    tokens 3000-4470 from the last window of 1471 keys."""
+    g, layout = expected()
+    N = 8
+    rng = np.random.default_rng(3)
+    Qs, Ks, keeps = [], [], []
+    for start, length, keep in layout:
+        Qs.append(rng.standard_normal((2, 4, N, 16)).astype(np.float32))
+        row = rng.standard_normal(16).astype(np.float32)
+        Ks.append(np.broadcast_to(row, (2, 2, length + N, 16)).copy())
+        keeps.append(keep)
+    got = oracle.score_windows(Qs, Ks, keeps)
+    u = lambda n: sum(1.0 / (n + j + 1) for j in range(N)) / N  # noqa: E731
+    np.testing.assert_allclose(got[:3000], u(2000), rtol=1e-12)
+    np.testing.assert_allclose(got[3000:], u(1471), rtol=1e-12)
