@@ -26,6 +26,7 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 
 F32, BF16 = 0, 1
 TOPK, MASS = 0, 1
+NORMS = {"minmax": 0, "percentile": 1, "zscore": 2}
 
 
 def build(force: bool = True) -> str:
@@ -53,8 +54,8 @@ def _load():
         lib.oracle_softmax_row.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32, dbl, i32,
                                            i32, i32, vp]
         lib.oracle_score.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32, dbl, i32, vp]
-        lib.oracle_select.argtypes = [vp, i32, i32, i32, i32, flt, flt, i32, flt, i32, flt, lng,
-                                      lng, vp, vp, vp, vp, vp, vp, vp, vp]
+        lib.oracle_select.argtypes = [vp, i32, i32, i32, i32, flt, flt, i32, flt, i32, flt, i32,
+                                      flt, flt, lng, lng, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.oracle_select_threshold.argtypes = [vp, i32, i32, flt, i32, i32, lng, lng, vp, vp, vp]
         for f in (lib.oracle_softmax_row, lib.oracle_score, lib.oracle_select,
                   lib.oracle_select_threshold):
@@ -109,9 +110,11 @@ def score(Q, K, scale=0.0, nthreads=0) -> np.ndarray:
 
 
 def select(importance, chunk, pool_k, mode, keep_rate=0.0, mass=0.0, boost_first_n=0,
-           boost_first_mult=1.0, boost_last_n=0, boost_last_mult=1.0, pos_base=0, base_index=0,
-           debug=False):
-    """Selection of one prompt from a float32 importance array.
+           boost_first_mult=1.0, boost_last_n=0, boost_last_mult=1.0, norm="minmax",
+           norm_lo=0.0, norm_hi=0.0, pos_base=0, base_index=0, debug=False):
+    """Selection of one prompt from a float32 importance array. norm:
+    "minmax", "percentile" (norm_lo, norm_hi: the two quantiles) or "zscore"
+    (norm_hi: the clip c in standard deviations).
 
     Returns (kept_idx int32, pos_ids int32) or, with debug, also a dict of the
     intermediate arrays (v, q, C, key, kept_chunk)."""
@@ -129,6 +132,7 @@ def select(importance, chunk, pool_k, mode, keep_rate=0.0, mass=0.0, boost_first
     kc = np.empty(max(nc, 1), np.uint8)
     rc = _load().oracle_select(x.ctypes.data, M, chunk, pool_k, mode_i, keep_rate, mass,
                                boost_first_n, boost_first_mult, boost_last_n, boost_last_mult,
+                               NORMS.get(norm, norm), norm_lo, norm_hi,
                                pos_base, base_index, kept.ctypes.data, pos.ctypes.data,
                                n.ctypes.data, v.ctypes.data, q.ctypes.data, C.ctypes.data,
                                key.ctypes.data, kc.ctypes.data)
@@ -192,4 +196,5 @@ def select_params(sel) -> dict:
     return dict(chunk=sel.chunk, pool_k=sel.pool_k, mode=sel.mode, keep_rate=sel.keep_rate,
                 mass=sel.mass, boost_first_n=sel.boost_first_n,
                 boost_first_mult=sel.boost_first_mult, boost_last_n=sel.boost_last_n,
-                boost_last_mult=sel.boost_last_mult)
+                boost_last_mult=sel.boost_last_mult, norm=sel.norm, norm_lo=sel.norm_lo,
+                norm_hi=sel.norm_hi)

@@ -32,6 +32,7 @@
  *  - query head h reads kv-head floor(h / (H/Hkv));
  *  - importance_i = (1/N) sum_j max_{l,h} a_{l,h,j,i} (the review's formula
  *    sums over the look-ahead index, written with a mismatched letter);
+ *  - robust normalisation (percentile clip, clipped z-score): see normalise;
  *  - selection: min-max normalise (all 1 when max == min), boost first then
  *    last, fixed point 2^32, chunk sums, average pool over chunks with the
  *    window clipped at the edges (mean over the tokens actually in the
@@ -178,6 +179,109 @@ int oracle_score(const void* Q, const void* K, int dtype, int L, int H, int Hkv,
 /* selection                                                                              */
 /* ------------------------------------------------------------------------------------- */
 
+enum { ORC_NORM_MINMAX = 0, ORC_NORM_PERCENTILE = 1, ORC_NORM_ZSCORE = 2 };
+
+static int cmp_f32_asc(const void* a, const void* b) {
+    const float x = *(const float*)a, y = *(const float*)b;
+    return (x < y) ? -1 : (x > y);
+}
+
+/* v = (x - lo) / (hi - lo) in fp32 (a subtraction and one IEEE division), or
+ * 1 everywhere when hi == lo; with clamp, values outside [0, 1] are clamped
+ * and a degenerate range gives 1 for x >= hi and 0 below. */
+static void scale_to_unit(const float* x, int M, float lo, float hi, int clamp, float* v) {
+    const float range = hi - lo;
+    for (int i = 0; i < M; ++i) {
+        if (range > 0.0f) {
+            float num = x[i] - lo;
+            v[i] = num / range;
+            if (clamp) {
+                if (v[i] < 0.0f) v[i] = 0.0f;
+                if (v[i] > 1.0f) v[i] = 1.0f;
+            }
+        } else {
+            v[i] = (clamp && x[i] < hi) ? 0.0f : 1.0f;
+        }
+    }
+}
+
+/*
+ * Normalisation of the scores to [0, 1] before boosting.
+ *  - min-max ([SP-G] v3.1 item 5): v = (x - min) / (max - min), all 1 when
+ *    max == min.
+ *  - percentile clip ([SP-G] Limitations item 5 names percentile-based
+ *    normalisation as the remedy for outliers; the reading: clip to two order
+ *    statistics, then min-max between them): with s the scores sorted
+ *    ascending, lo = s[floor(p_lo (M-1))], hi = s[ceil(p_hi (M-1))] (indices
+ *    evaluated in double from the float parameters, 0 <= p_lo < p_hi <= 1);
+ *    v = clamp((x - lo) / (hi - lo), 0, 1), or (x >= hi ? 1 : 0) when hi == lo.
+ *    p_lo = 0, p_hi = 1 is min-max exactly.
+ *  - clipped z-score (same passage names z-score normalisation; the reading:
+ *    standardise, clip at +-c standard deviations, map [-c, c] onto [0, 1]).
+ *    Statistics are taken exactly on a 16-bit grid of the min-max values u
+ *    (a z-score is unchanged by the positive affine map to u):
+ *    y = rint(u * 2^16) (integers in [0, 65536]), S1 = sum y, S2 = sum y^2,
+ *    D = M S2 - S1^2 (exact; M^2 times the variance of y). D == 0: v = 1
+ *    everywhere. Otherwise z = (double)(M y - S1) / sqrt((double) D) (the
+ *    integer M y - S1 is exact in double; (double) D rounds once), clipped to
+ *    [-c, c], and v = (float)((z + c) / (2 c)), every step one IEEE double
+ *    operation. c = p_hi > 0; p_lo must be 0.
+ * Returns 0, or -1 on invalid parameters.
+ */
+static int normalise(const float* x, int M, int norm, float p_lo, float p_hi, float* v) {
+    float mn = x[0], mx = x[0];
+    for (int i = 1; i < M; ++i) {
+        if (x[i] < mn) mn = x[i];
+        if (x[i] > mx) mx = x[i];
+    }
+    if (norm == ORC_NORM_MINMAX) {
+        scale_to_unit(x, M, mn, mx, 0, v);
+        return 0;
+    }
+    if (norm == ORC_NORM_PERCENTILE) {
+        if (!(p_lo >= 0.0f && p_lo < p_hi && p_hi <= 1.0f)) return -1;
+        float* s = (float*)malloc(sizeof(float) * (size_t)M);
+        if (!s) return -2;
+        memcpy(s, x, sizeof(float) * (size_t)M);
+        qsort(s, (size_t)M, sizeof(float), cmp_f32_asc);
+        const long i_lo = (long)floor((double)p_lo * (double)(M - 1));
+        const long i_hi = (long)ceil((double)p_hi * (double)(M - 1));
+        const float lo = s[i_lo], hi = s[i_hi];
+        free(s);
+        scale_to_unit(x, M, lo, hi, 1, v);
+        return 0;
+    }
+    if (norm == ORC_NORM_ZSCORE) {
+        if (!(p_lo == 0.0f && p_hi > 0.0f) || !isfinite(p_hi)) return -1;
+        scale_to_unit(x, M, mn, mx, 0, v); /* u: the min-max values */
+        uint64_t S1 = 0, S2 = 0;
+        int64_t* y = (int64_t*)malloc(sizeof(int64_t) * (size_t)M);
+        if (!y) return -2;
+        for (int i = 0; i < M; ++i) {
+            y[i] = (int64_t)llrint((double)(v[i] * 65536.0f));
+            S1 += (uint64_t)y[i];
+            S2 += (uint64_t)(y[i] * y[i]);
+        }
+        const unsigned __int128 D =
+            (unsigned __int128)M * S2 - (unsigned __int128)S1 * S1;
+        if (D == 0) {
+            for (int i = 0; i < M; ++i) v[i] = 1.0f;
+        } else {
+            const double sd = sqrt((double)D);
+            const double c = (double)p_hi;
+            for (int i = 0; i < M; ++i) {
+                double z = (double)((int64_t)M * y[i] - (int64_t)S1) / sd;
+                if (z < -c) z = -c;
+                if (z > c) z = c;
+                v[i] = (float)((z + c) / (2.0 * c));
+            }
+        }
+        free(y);
+        return 0;
+    }
+    return -1;
+}
+
 typedef struct {
     double key;
     long idx;
@@ -199,6 +303,8 @@ static int rank_cmp(const void* a, const void* b) {
  *                top-K; [SP-G] Chunk Selection), 1 = cumulative mass
  *                ([SP-G] v3 Improvements 1)
  *   boosts     : [SP-G] v3 Improvements 2; normalisation: [SP-G] v3.1 item 5
+ *                (min-max) or [SP-G] Limitations item 5 (percentile clip,
+ *                clipped z-score; see normalise)
  *   pooling    : [SP-R] Core algorithm, chunk selection and pooling
  *   outputs    : kept_idx[n] = base_index + i, pos_ids[n] = pos_base + i for
  *                every token i of every kept chunk, ascending ([SP-R] Core
@@ -210,9 +316,10 @@ static int rank_cmp(const void* a, const void* b) {
  */
 int oracle_select(const float* importance, int M, int chunk, int pool_k, int mode,
                   float keep_rate, float mass, int first_n, float first_mult, int last_n,
-                  float last_mult, long pos_base, long base_index, int32_t* kept_idx,
-                  int32_t* pos_ids, int32_t* n_kept, float* v_out, uint64_t* q_out,
-                  uint64_t* C_out, double* key_out, uint8_t* kept_chunk_out) {
+                  float last_mult, int norm, float norm_lo, float norm_hi, long pos_base,
+                  long base_index, int32_t* kept_idx, int32_t* pos_ids, int32_t* n_kept,
+                  float* v_out, uint64_t* q_out, uint64_t* C_out, double* key_out,
+                  uint8_t* kept_chunk_out) {
     if (M < 1 || chunk < 1 || pool_k < 1 || (pool_k % 2) == 0) return -1;
     if (mode == ORC_TOPK && !(keep_rate > 0.0f && keep_rate <= 1.0f)) return -1;
     if (mode == ORC_MASS && !(mass > 0.0f && mass <= 1.0f)) return -1;
@@ -231,20 +338,13 @@ int oracle_select(const float* importance, int M, int chunk, int pool_k, int mod
         return -2;
     }
 
-    /* min-max normalisation, fp32 */
-    float mn = importance[0], mx = importance[0];
-    for (int i = 1; i < M; ++i) {
-        if (importance[i] < mn) mn = importance[i];
-        if (importance[i] > mx) mx = importance[i];
+    /* normalisation to [0, 1] (min-max, percentile clip or clipped z-score) */
+    const int nrc = normalise(importance, M, norm, norm_lo, norm_hi, v);
+    if (nrc) {
+        free(v); free(C); free(len); free(key); free(rk); free(keep);
+        return nrc;
     }
-    const float range = mx - mn;
     for (int i = 0; i < M; ++i) {
-        if (range > 0.0f) {
-            float num = importance[i] - mn;
-            v[i] = num / range;
-        } else {
-            v[i] = 1.0f;
-        }
         /* structural boosts: first, then last (both apply where they overlap) */
         if (i < first_n) v[i] = v[i] * first_mult;
         if (i >= M - last_n) v[i] = v[i] * last_mult;

@@ -74,6 +74,9 @@ class Select:
     boost_first_mult: float = 1.0
     boost_last_n: int = 0
     boost_last_mult: float = 1.0
+    norm: str = "minmax"  # "minmax" | "percentile" | "zscore"
+    norm_lo: float = 0.0
+    norm_hi: float = 0.0
 
 
 @dataclass(frozen=True)
