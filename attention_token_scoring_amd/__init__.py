@@ -27,6 +27,7 @@ SP_OK, SP_EINVAL, SP_EUNSUPPORTED, SP_EWORKSPACE, SP_EDEVICE = range(5)
 SP_F32, SP_BF16 = 0, 1
 SP_SELECT_TOPK, SP_SELECT_MASS, SP_SELECT_THRESHOLD = 0, 1, 2
 SP_LAUNCH_RESIDENT, SP_LAUNCH_COOPERATIVE = 0, 1
+SP_NORM_MINMAX, SP_NORM_PERCENTILE, SP_NORM_ZSCORE = 0, 1, 2
 
 EXPORTED = ("sp_score", "sp_score_varlen", "sp_select", "sp_select_varlen",
             "sp_score_workspace_bytes", "sp_select_workspace_bytes", "sp_score_plan",
@@ -52,7 +53,8 @@ class SelectParams(ctypes.Structure):
                 ("keep_rate", ctypes.c_float), ("mass", ctypes.c_float),
                 ("boost_first_n", ctypes.c_int32), ("boost_first_mult", ctypes.c_float),
                 ("boost_last_n", ctypes.c_int32), ("boost_last_mult", ctypes.c_float),
-                ("min_tok", ctypes.c_int32), ("max_keep", ctypes.c_int32)]
+                ("min_tok", ctypes.c_int32), ("max_keep", ctypes.c_int32),
+                ("norm", ctypes.c_int), ("norm_lo", ctypes.c_float), ("norm_hi", ctypes.c_float)]
 
 
 _lib = None
@@ -157,12 +159,15 @@ def score_desc(L, H, Hkv, d, N, dtype=SP_BF16, scale=0.0, launch=SP_LAUNCH_RESID
 
 def select_params(chunk=32, pool_k=1, mode="topk", keep_rate=0.0, mass=0.0, boost_first_n=0,
                   boost_first_mult=1.0, boost_last_n=0, boost_last_mult=1.0, min_tok=0,
-                  max_keep=0) -> SelectParams:
+                  max_keep=0, norm="minmax", norm_lo=0.0, norm_hi=0.0) -> SelectParams:
     m = {"topk": SP_SELECT_TOPK, "mass": SP_SELECT_MASS,
          "threshold": SP_SELECT_THRESHOLD}.get(mode, mode)
+    nm = {"minmax": SP_NORM_MINMAX, "percentile": SP_NORM_PERCENTILE,
+          "zscore": SP_NORM_ZSCORE}.get(norm, norm)
     return SelectParams(int(chunk), int(pool_k), int(m), float(keep_rate), float(mass),
                         int(boost_first_n), float(boost_first_mult), int(boost_last_n),
-                        float(boost_last_mult), int(min_tok), int(max_keep))
+                        float(boost_last_mult), int(min_tok), int(max_keep), int(nm),
+                        float(norm_lo), float(norm_hi))
 
 
 def sp_score_workspace_bytes(desc: ScoreDesc, max_prompt_len: int) -> int:

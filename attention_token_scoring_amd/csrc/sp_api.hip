@@ -78,6 +78,16 @@ sp_status check_select_params(const sp_select_params* p) {
         return SP_EINVAL;
     }
     if (p->mode != SP_SELECT_THRESHOLD && (p->min_tok != 0 || p->max_keep != 0)) return SP_EINVAL;
+    if (p->norm == SP_NORM_MINMAX) {
+        if (p->norm_lo != 0.f || p->norm_hi != 0.f) return SP_EINVAL;
+    } else if (p->norm == SP_NORM_PERCENTILE) {
+        if (!(p->norm_lo >= 0.f && p->norm_lo < p->norm_hi && p->norm_hi <= 1.f)) return SP_EINVAL;
+    } else if (p->norm == SP_NORM_ZSCORE) {
+        if (p->norm_lo != 0.f || !(p->norm_hi > 0.f) || !isfinite(p->norm_hi)) return SP_EINVAL;
+    } else {
+        return SP_EINVAL;
+    }
+    if (p->mode == SP_SELECT_THRESHOLD && p->norm != SP_NORM_MINMAX) return SP_EINVAL;
     if (p->boost_first_n < 0 || p->boost_last_n < 0) return SP_EINVAL;
     if (!(p->boost_first_mult >= 0.f) || !(p->boost_last_mult >= 0.f) ||
         !isfinite(p->boost_first_mult) || !isfinite(p->boost_last_mult))
@@ -116,6 +126,9 @@ SelectParamsDev to_dev(const sp_select_params* p) {
     q.last_mult = p->boost_last_mult;
     q.min_tok = p->min_tok;
     q.max_keep = p->max_keep;
+    q.norm = p->norm;
+    q.norm_lo = p->norm_lo;
+    q.norm_hi = p->norm_hi;
     return q;
 }
 

@@ -124,6 +124,8 @@ struct SelectParamsDev {
     int last_n;
     float last_mult;
     int min_tok, max_keep;  // (threshold mode)
+    int norm;               // SP_NORM_MINMAX / SP_NORM_PERCENTILE / SP_NORM_ZSCORE
+    float norm_lo, norm_hi; // (percentile: the two quantiles; z-score: 0 and the clip c)
 };
 
 // Launch plan for one prompt of M keys on a device with cus compute units

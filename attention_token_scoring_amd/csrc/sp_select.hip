@@ -66,6 +66,8 @@ struct SelectShared {
     unsigned long long bc_prefix, bc_mass; // broadcast of a round's result
     unsigned int bc_count, bc_ties;
     float fmin[kSelWaves], fmax[kSelWaves];
+    unsigned long long zs[2];             // (z-score) sums of y and y^2
+    float pct[2];                         // (percentile) the two order statistics
     unsigned long long rand_[kSelWaves], ror_[kSelWaves];  // AND / OR of the keys per wave
     int kc;                               // number of kept chunks
 };
@@ -160,6 +162,76 @@ __device__ T block_excl_scan(T* data, int n, unsigned long long* wtmp) {
     return total;
 }
 
+// Order-preserving map of float bits to unsigned keys (and back): negative
+// values have all bits flipped, others only the sign bit.
+__device__ __forceinline__ unsigned f32_key(float f) {
+    const unsigned b = __float_as_uint(f);
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float key_f32(unsigned k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// The k-th smallest (0-based) of x[0..M): a radix select over the keys'
+// bits (digits of 11, 11 and 10 bits from the top; a histogram of the
+// candidates' digit in LDS, one pad word per 32 bins so that wave 0's lanes
+// read their 32-bin groups without bank conflicts). hist holds 2112 words.
+__device__ float order_stat(const float* __restrict__ x, int M, int k, unsigned* hist,
+                            unsigned long long* bc_prefix, unsigned* bc_count) {
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    unsigned prefix = 0u, pmask = 0u;
+    const int shifts[3] = {21, 10, 0}, widths[3] = {11, 11, 10};
+    for (int rnd = 0; rnd < 3; ++rnd) {
+        const int sh = shifts[rnd];
+        const unsigned dmask = (1u << widths[rnd]) - 1u;
+        for (int d = tid; d < 2048 + 64; d += kSelThreads) hist[d] = 0u;
+        __syncthreads();
+        for (int i = tid; i < M; i += kSelThreads) {
+            const unsigned key = f32_key(x[i]);
+            if ((key & pmask) == prefix) {
+                const unsigned d = (key >> sh) & dmask;
+                atomicAdd(&hist[d + (d >> 5)], 1u);
+            }
+        }
+        __syncthreads();
+        if (w == 0) {
+            // lane L sums bins 32 L .. 32 L + 31; the first lane whose
+            // inclusive count exceeds k holds the digit, then one lane per bin
+            unsigned c = 0u;
+            for (int j = 0; j < 32; ++j) c += hist[lane * 33 + j];
+            const unsigned incl = wave_scan_u32(c);
+            const unsigned long long bal = __ballot(incl > (unsigned)k);
+            const int F = bal ? __builtin_ctzll(bal) : 63;
+            const unsigned before = __shfl(incl - c, F);
+            const unsigned cb = lane < 32 ? hist[F * 33 + lane] : 0u;
+            const unsigned incl2 = wave_scan_u32(cb);
+            const unsigned long long bal2 = __ballot(lane < 32 && before + incl2 > (unsigned)k);
+            const int J = bal2 ? __builtin_ctzll(bal2) : 0;
+            if (lane == J) {
+                *bc_prefix = (unsigned long long)(F * 32 + J);
+                *bc_count = before + incl2 - cb;
+            }
+        }
+        __syncthreads();
+        prefix |= (unsigned)*bc_prefix << sh;
+        pmask |= dmask << sh;
+        k -= (int)*bc_count;
+        __syncthreads();
+    }
+    return key_f32(prefix);
+}
+
+// A non-negative 128-bit integer rounded to the nearest double (ties to even):
+// the top 64 bits with the rest folded into a sticky bit, converted, scaled.
+__device__ __forceinline__ double u128_to_f64(unsigned __int128 v) {
+    const unsigned long long hi = (unsigned long long)(v >> 64);
+    if (hi == 0ull) return (double)(unsigned long long)v;
+    const int sh = 64 - __builtin_clzll(hi);
+    unsigned long long m = (unsigned long long)(v >> sh);
+    if ((unsigned long long)v & ((1ull << sh) - 1ull)) m |= 1ull;
+    return ldexp((double)m, sh);
+}
+
 __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectBatch b, SelectParamsDev p,
                                                              const float* __restrict__ x_all,
                                                              int32_t* __restrict__ kept_all,
@@ -222,6 +294,73 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectBatch b, Sele
     const float drange = range * dscale;
     const float dnms = -mn * dscale;
     const float drcp = __fdiv_rn(1.0f, drange);
+    // The min-max value u of one score: the correctly rounded quotient
+    // (x - mn) / range by a reciprocal and one correction (Markstein): with
+    // both operands scaled by a power of two taking range into [1, 2)
+    // (a2 = (x - mn) * scale in one rounding), y = 1/range rounded,
+    // q0 = a2 * y and the exact residual a2 - q0 * range, q0 + residual * y
+    // rounds to the IEEE quotient (a quotient too small for that is too
+    // small to survive the fixed point); a plain division when the range is
+    // subnormal or near the top of the range; 1 when max == min.
+    auto minmax_value = [&](float xv) __attribute__((always_inline)) {
+        if (dfast) {
+            const float a2 = fmaf(xv, dscale, dnms);
+            const float q0 = a2 * drcp;
+            return fmaf(fmaf(-q0, drange, a2), drcp, q0);
+        }
+        return range > 0.f ? __fdiv_rn(xv - mn, range) : 1.0f;
+    };
+
+    // Robust normalisations ("SpecPrefill - Implementation Guide",
+    // Limitations item 5). Percentile clip: v = clamp((x - lo) / (hi - lo), 0, 1)
+    // between two order statistics of the scores (v = x >= hi ? 1 : 0 when
+    // they are equal). Clipped z-score: from the exact integer sums of the
+    // min-max values on a 2^-16 grid, y = rint(u 2^16), S1 = sum y,
+    // S2 = sum y^2, D = M S2 - S1^2; z = (M y - S1) / sqrt(D) clipped to
+    // [-c, c] and v = (z + c) / (2c) in double, then rounded to float (1
+    // everywhere when D = 0). Every step is exact or one IEEE operation.
+    float plo = 0.f, phi = 0.f;
+    long long zS1 = 0;
+    double zsd = 0.0, zc = 0.0;
+    bool zflat = true;
+    if (p.norm == SP_NORM_PERCENTILE) {
+        const int i_lo = (int)floor((double)p.norm_lo * (double)(M - 1));
+        const int i_hi = (int)ceil((double)p.norm_hi * (double)(M - 1));
+        unsigned* hist = (unsigned*)sh.hcount[0];
+        plo = order_stat(x, M, i_lo, hist, &sh.bc_prefix, &sh.bc_count);
+        phi = order_stat(x, M, i_hi, hist, &sh.bc_prefix, &sh.bc_count);
+    } else if (p.norm == SP_NORM_ZSCORE) {
+        unsigned long long s1 = 0ull, s2 = 0ull;
+        for (int i = tid; i < M; i += kSelThreads) {
+            const unsigned long long y = (unsigned long long)rintf(minmax_value(x[i]) * 65536.0f);
+            s1 += y;
+            s2 += y * y;
+        }
+        if (tid < 2) sh.zs[tid] = 0ull;
+        __syncthreads();
+        atomicAdd(&sh.zs[0], s1);
+        atomicAdd(&sh.zs[1], s2);
+        __syncthreads();
+        const unsigned long long S1 = sh.zs[0], S2 = sh.zs[1];
+        const unsigned __int128 D = (unsigned __int128)(unsigned)M * S2 - (unsigned __int128)S1 * S1;
+        zflat = D == 0;
+        zsd = sqrt(u128_to_f64(D));
+        zS1 = (long long)S1;
+        zc = (double)p.norm_hi;
+    }
+    const float prange = phi - plo;
+    auto robust_value = [&](float xv) __attribute__((always_inline)) {
+        if (p.norm == SP_NORM_PERCENTILE) {
+            if (!(prange > 0.f)) return xv < phi ? 0.0f : 1.0f;
+            const float v = __fdiv_rn(xv - plo, prange);
+            return v < 0.f ? 0.0f : (v > 1.f ? 1.0f : v);
+        }
+        if (zflat) return 1.0f;
+        const long long y = (long long)rintf(minmax_value(xv) * 65536.0f);
+        double z = (double)((long long)M * y - zS1) / zsd;
+        z = z < -zc ? -zc : (z > zc ? zc : z);
+        return (float)((z + zc) / (2.0 * zc));
+    };
 
     // 2-3. normalise, boost, fixed point, chunk sums. Tiles of kTile elements
     // are staged in LDS with coalesced loads; each thread then takes kSeg
@@ -247,14 +386,9 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectBatch b, Sele
 #pragma unroll
             for (int e = 0; e < kSeg; ++e) xv[e] = sh.stage[tid * (kSeg + 1) + e];
             float vq[kSeg];
-            if (dfast) {
-                // the correctly rounded quotient (x - mn) / range by a
-                // reciprocal and one correction (Markstein): with both
-                // operands scaled by a power of two taking range into [1, 2)
-                // (a2 = (x - mn) * scale in one rounding), y = 1/range rounded,
-                // q0 = a2 * y and the exact residual a2 - q0 * range,
-                // q0 + residual * y rounds to the IEEE quotient (a quotient too
-                // small for that is too small to survive the fixed point)
+            if (p.norm != SP_NORM_MINMAX) {
+                for (int e = 0; e < kSeg; ++e) vq[e] = robust_value(xv[e]);
+            } else if (dfast) {
 #pragma unroll
                 for (int e = 0; e < kSeg; ++e) {
                     const float a2 = fmaf(xv[e], dscale, dnms);

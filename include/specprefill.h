@@ -60,6 +60,9 @@ typedef enum { SP_F32 = 0, SP_BF16 = 1 } sp_dtype;
 
 typedef enum { SP_SELECT_TOPK = 0, SP_SELECT_MASS = 1, SP_SELECT_THRESHOLD = 2 } sp_select_mode;
 
+/* How sp_select maps the scores to [0, 1] before boosting (step 1 of sp_select). */
+typedef enum { SP_NORM_MINMAX = 0, SP_NORM_PERCENTILE = 1, SP_NORM_ZSCORE = 2 } sp_norm;
+
 /* How sp_score launches its scoring kernel, whose workgroups wait on each
  * other and so must all be resident on the device at once.
  *   SP_LAUNCH_RESIDENT     (0, the default) an ordinary launch of no more
@@ -100,7 +103,11 @@ typedef struct {
  *   boost_*    multipliers >= 0 for the first / last n tokens (1.0 = off)
  *   min_tok    (threshold mode) >= 0; the fill target is min(min_tok, max(4, M/10))
  *              tokens (the Guide's program passes 128); 0 in the other modes
- *   max_keep   (threshold mode) >= 0; cap on kept tokens, 0 = none; 0 in the other modes */
+ *   max_keep   (threshold mode) >= 0; cap on kept tokens, 0 = none; 0 in the other modes
+ *   norm       an sp_norm (0 = SP_NORM_MINMAX, the only one threshold mode takes);
+ *              SP_NORM_PERCENTILE uses the quantiles 0 <= norm_lo < norm_hi <= 1;
+ *              SP_NORM_ZSCORE uses norm_lo = 0 and the clip c = norm_hi > 0
+ *              (in standard deviations); both 0 for SP_NORM_MINMAX */
 typedef struct {
     int32_t chunk, pool_k;
     sp_select_mode mode;
@@ -110,6 +117,8 @@ typedef struct {
     int32_t boost_last_n;
     float boost_last_mult;
     int32_t min_tok, max_keep;
+    sp_norm norm;
+    float norm_lo, norm_hi;
 } sp_select_params;
 
 /* Bytes of device workspace sp_score / sp_score_varlen need for prompts of at
@@ -195,6 +204,15 @@ size_t sp_select_workspace_bytes(int32_t R, int64_t total_prompt_len,
  * Improvements; [SP-R] Core algorithm: chunk selection, pooling, position-ID
  * recovery). With x = importance:
  *  1. v_i = (x_i - min x) / (max x - min x) in float32 (all 1 if max == min);
+ *     or, for the robust normalisations ([SP-G] Limitations item 5 names
+ *     percentile-based and z-score normalisation as remedies for outliers):
+ *     SP_NORM_PERCENTILE: lo = s[floor(norm_lo (M-1))], hi = s[ceil(norm_hi (M-1))]
+ *       for s = x sorted ascending (indices in double); v_i = (x_i - lo) / (hi - lo)
+ *       in float32 clamped to [0, 1] (x_i >= hi ? 1 : 0 when hi == lo);
+ *     SP_NORM_ZSCORE: u_i the min-max values above, y_i = rint(u_i 2^16),
+ *       S1 = sum y, S2 = sum y^2, D = M S2 - S1^2 (exact integers); v_i = 1 if
+ *       D == 0, else z_i = (double)(M y_i - S1) / sqrt((double) D) clipped to
+ *       [-c, c] (c = norm_hi) and v_i = (float)((z_i + c) / (2c)) in double;
  *  2. v_i *= first_mult for i < first_n, then v_i *= last_mult for i >= M - last_n;
  *  3. q_i = round_half_even(v_i * 2^32) as uint64;
  *  4. chunk c holds tokens [c*chunk, min((c+1)*chunk, M)); C_c = sum q_i;

@@ -132,6 +132,15 @@ def test_plan_for_the_8b_shape(lib):
     (dict(mode="threshold", pool_k=1, max_keep=-1), sp.SP_EINVAL),
     (dict(mode="threshold", pool_k=1, keep_rate=0.0), sp.SP_EINVAL),
     (dict(mode="threshold", pool_k=1, chunk=1), sp.SP_EUNSUPPORTED),  # nc = 10000 > 4096
+    (dict(norm=3), sp.SP_EINVAL),
+    (dict(norm="minmax", norm_hi=0.5), sp.SP_EINVAL),
+    (dict(norm="percentile", norm_lo=0.5, norm_hi=0.5), sp.SP_EINVAL),
+    (dict(norm="percentile", norm_lo=-0.1, norm_hi=0.9), sp.SP_EINVAL),
+    (dict(norm="percentile", norm_lo=0.1, norm_hi=1.1), sp.SP_EINVAL),
+    (dict(norm="zscore", norm_hi=0.0), sp.SP_EINVAL),
+    (dict(norm="zscore", norm_lo=0.1, norm_hi=3.0), sp.SP_EINVAL),
+    (dict(norm="zscore", norm_hi=float("inf")), sp.SP_EINVAL),
+    (dict(mode="threshold", pool_k=1, norm="percentile", norm_lo=0.1, norm_hi=0.9), sp.SP_EINVAL),
 ])
 def test_select_rejects(lib, kw, status):
     base = dict(chunk=32, pool_k=3, mode="topk", keep_rate=0.3)

@@ -353,6 +353,74 @@ def test_select_matches_oracle(case, dist):
 
 
 # ----------------------------------------------------------------------------------------
+# robust normalisations (percentile clip, clipped z-score): bit-exact against the oracle
+# ----------------------------------------------------------------------------------------
+NORM_CASES = [
+    dict(M=32768, chunk=32, pool_k=13, mode="topk", keep_rate=0.1),
+    dict(M=32768, chunk=32, pool_k=13, mode="mass", mass=0.85),
+    dict(M=4608, chunk=32, pool_k=5, mode="mass", mass=0.85, boost_first_n=64,
+         boost_first_mult=1.5, boost_last_n=128, boost_last_mult=1.3),
+    dict(M=1000, chunk=24, pool_k=3, mode="topk", keep_rate=0.3),
+    dict(M=1, chunk=32, pool_k=3, mode="topk", keep_rate=0.1),
+    dict(M=77, chunk=4, pool_k=1, mode="mass", mass=0.6),
+    dict(M=200000, chunk=512, pool_k=3, mode="mass", mass=0.9),
+    dict(M=1 << 22, chunk=2048, pool_k=5, mode="topk", keep_rate=0.3),
+]
+NORMS = [("percentile", 0.01, 0.99), ("percentile", 0.0, 1.0), ("percentile", 0.25, 0.5),
+         ("zscore", 0.0, 3.0), ("zscore", 0.0, 0.5)]
+
+
+@pytest.mark.parametrize("dist", ["uniform", "ties", "constant", "outliers", "signed"])
+@pytest.mark.parametrize("norm", NORMS, ids=[f"{n}-{lo}-{hi}" for n, lo, hi in NORMS])
+@pytest.mark.parametrize("case", NORM_CASES,
+                         ids=[f"{c['M']}-{c['chunk']}-{c['mode']}" for c in NORM_CASES])
+def test_select_robust_norms_match_oracle(case, norm, dist):
+    kw = dict(case)
+    M = kw.pop("M")
+    rng = np.random.default_rng(M + 7 * len(dist))
+    if dist == "uniform":
+        x = rng.random(M)
+    elif dist == "ties":
+        x = rng.integers(0, 4, M) / 3.0
+    elif dist == "constant":
+        x = np.full(M, 0.125)
+    elif dist == "outliers":
+        x = 0.01 + 0.01 * rng.random(M)
+        x[rng.integers(0, M, max(1, M // 500))] = rng.random(max(1, M // 500)) * 50.0
+    else:  # signed scores spanning many binades (not importance arrays, but valid input)
+        x = rng.standard_normal(M) * np.exp2(rng.integers(-30, 30, M))
+    n, lo, hi = norm
+    _select_case(x, pos_base=5, norm=n, norm_lo=lo, norm_hi=hi, **kw)
+
+
+def test_select_robust_norms_on_scored_workload():
+    """The 0.8B workload's GPU importance under each robust normalisation, in
+    both selection modes, and a ragged batch of its slices (per-request
+    statistics)."""
+    w = synth.WORKLOADS["spec0.8b_m4608"]
+    Qh, Kh, M = synth.make_request(w)
+    imp = sp.sp_score(to_dev(Qh), to_dev(Kh))
+    torch.cuda.synchronize()
+    x = imp.cpu().numpy()
+    for n, lo, hi in NORMS:
+        for kw in (dict(mode="mass", mass=0.85), dict(mode="topk", keep_rate=0.2)):
+            _select_case(x, chunk=32, pool_k=5, norm=n, norm_lo=lo, norm_hi=hi,
+                         boost_first_n=64, boost_first_mult=1.5, boost_last_n=128,
+                         boost_last_mult=1.3, **kw)
+    cu = [0, 1000, 1001, 3000, M]
+    for n, lo, hi in NORMS:
+        sel = dict(chunk=16, pool_k=3, mode="mass", mass=0.8, norm=n, norm_lo=lo, norm_hi=hi)
+        kept, pos, nk = sp.sp_select_varlen(imp, cu, sp.select_params(**sel), pos_base=[0, 1, 2, 3])
+        torch.cuda.synchronize()
+        kh, ph, nh = kept.cpu().numpy(), pos.cpu().numpy(), nk.cpu().numpy()
+        for r in range(4):
+            k_ref, p_ref = oracle.select(x[cu[r]:cu[r + 1]], pos_base=r, base_index=cu[r], **sel)
+            assert nh[r] == len(k_ref), (n, r)
+            assert np.array_equal(kh[cu[r]:cu[r] + nh[r]], k_ref), (n, r)
+            assert np.array_equal(ph[cu[r]:cu[r] + nh[r]], p_ref), (n, r)
+
+
+# ----------------------------------------------------------------------------------------
 # threshold selection (the Implementation Guide program's chunk selection and cap)
 # ----------------------------------------------------------------------------------------
 THRESH_CASES = [
