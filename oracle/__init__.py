@@ -54,11 +54,13 @@ def _load():
         lib.oracle_softmax_row.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32, dbl, i32,
                                            i32, i32, vp]
         lib.oracle_score.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32, dbl, i32, vp]
+        lib.oracle_score_lastrow.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, dbl,
+                                             i32, vp]
         lib.oracle_select.argtypes = [vp, i32, i32, i32, i32, flt, flt, i32, flt, i32, flt, i32,
                                       flt, flt, lng, lng, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.oracle_select_threshold.argtypes = [vp, i32, i32, flt, i32, i32, lng, lng, vp, vp, vp]
-        for f in (lib.oracle_softmax_row, lib.oracle_score, lib.oracle_select,
-                  lib.oracle_select_threshold):
+        for f in (lib.oracle_softmax_row, lib.oracle_score, lib.oracle_score_lastrow,
+                  lib.oracle_select, lib.oracle_select_threshold):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -106,6 +108,26 @@ def score(Q, K, scale=0.0, nthreads=0) -> np.ndarray:
                               float(scale), int(nthreads), out.ctypes.data)
     if rc:
         raise ValueError(f"oracle_score failed ({rc})")
+    return out
+
+
+def score_lastrow(Q, Q_last, K, scale=0.0, nthreads=0) -> np.ndarray:
+    """importance[M] (float64) with the last prompt token's query row Q_last
+    [L,H,d] as one more step (see oracle_score_lastrow)."""
+    Q = np.ascontiguousarray(Q)
+    Q_last = np.ascontiguousarray(Q_last)
+    K = np.ascontiguousarray(K)
+    if not (_dtype_of(Q) == _dtype_of(K) == _dtype_of(Q_last)):
+        raise TypeError("Q, Q_last and K dtypes differ")
+    L, H, Hkv, d, N, M = _dims(Q, K)
+    if Q_last.shape != (L, H, d):
+        raise ValueError("Q_last must be [L, H, d]")
+    out = np.empty(M, np.float64)
+    rc = _load().oracle_score_lastrow(Q.ctypes.data, Q_last.ctypes.data, K.ctypes.data,
+                                      _dtype_of(Q), L, H, Hkv, d, N, M, float(scale),
+                                      int(nthreads), out.ctypes.data)
+    if rc:
+        raise ValueError(f"oracle_score_lastrow failed ({rc})")
     return out
 
 

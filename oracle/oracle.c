@@ -175,6 +175,84 @@ int oracle_score(const void* Q, const void* K, int dtype, int L, int H, int Hkv,
     return fail ? -2 : 0;
 }
 
+/*
+ * Importance with the query row of the last prompt token as one more step
+ * ([SP-G] How It Works, Attention Capture (cb_eval): the attention row of
+ * the last query position is captured during the prefill, like each
+ * look-ahead step's, and the importance averages over all captured steps).
+ * That row, at position M-1, sees the M prompt keys 0..M-1:
+ *   importance_i = (sum_{j<N} S_j[i] + X[i]) / (N + 1),
+ *   S_j[i] = max_{l,h} a_{l,h,j,i} (as in oracle_score),
+ *   X[i]   = max_{l,h} softmax_{i'<M}(scale <Q_last[l][h], K[l][h/G][i']>)_i.
+ *   Q_last: [L][H][d]; importance: out, M doubles.
+ */
+int oracle_score_lastrow(const void* Q, const void* Q_last, const void* K, int dtype, int L,
+                         int H, int Hkv, int d, int N, int M, double scale, int nthreads,
+                         double* importance) {
+    if (check_dims(dtype, L, H, Hkv, d, N, M)) return -1;
+    int rc = oracle_score(Q, K, dtype, L, H, Hkv, d, N, M, scale, nthreads, importance);
+    if (rc) return rc;
+    if (!(scale > 0.0)) scale = 1.0 / sqrt((double)d);
+    const int G = H / Hkv;
+    double* X = (double*)calloc((size_t)M, sizeof(double));
+    if (!X) return -2;
+    int fail = 0;
+    /* rows (l, h) in parallel, each thread with its own running max */
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel num_threads(nthreads)
+#endif
+    {
+        double* Xp = (double*)calloc((size_t)M, sizeof(double));
+        double* p = (double*)malloc(sizeof(double) * (size_t)M);
+        if (!Xp || !p) {
+#ifdef _OPENMP
+#pragma omp atomic write
+#endif
+            fail = 1;
+        }
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+        for (long r = 0; r < (long)L * H; ++r) {
+            if (!Xp || !p) continue;
+            const int l = (int)(r / H), h = (int)(r % H);
+            const size_t qoff = ((size_t)l * H + h) * (size_t)d;
+            const size_t kbase = ((size_t)l * Hkv + h / G) * (size_t)(M + N) * (size_t)d;
+            double m = -INFINITY;
+            for (int i = 0; i < M; ++i) {
+                double s = 0.0;
+                for (int t = 0; t < d; ++t)
+                    s += elem(Q_last, dtype, qoff + t) * elem(K, dtype, kbase + (size_t)i * d + t);
+                p[i] = scale * s;
+                if (p[i] > m) m = p[i];
+            }
+            double Z = 0.0;
+            for (int i = 0; i < M; ++i) {
+                p[i] = exp(p[i] - m);
+                Z += p[i];
+            }
+            for (int i = 0; i < M; ++i)
+                if (p[i] / Z > Xp[i]) Xp[i] = p[i] / Z;
+        }
+#ifdef _OPENMP
+#pragma omp critical
+#endif
+        {
+            if (Xp)
+                for (int i = 0; i < M; ++i)
+                    if (Xp[i] > X[i]) X[i] = Xp[i];
+        }
+        free(Xp);
+        free(p);
+    }
+    /* importance currently holds (1/N) sum_j S_j */
+    if (!fail)
+        for (int i = 0; i < M; ++i) importance[i] = (importance[i] * N + X[i]) / (N + 1);
+    free(X);
+    return fail ? -2 : 0;
+}
+
 /* ------------------------------------------------------------------------------------- */
 /* selection                                                                              */
 /* ------------------------------------------------------------------------------------- */
