@@ -33,7 +33,7 @@ EXPORTED = ("sp_score", "sp_score_varlen", "sp_select", "sp_select_varlen",
             "sp_score_workspace_bytes", "sp_select_workspace_bytes", "sp_score_plan",
             "sp_status_string", "sp_profile_score_kernel", "sp_score_status",
             "sp_score_windows", "sp_window_layout", "sp_gather_rows", "sp_break_even",
-            "sp_read_probe", "sp_set_wait_limit")
+            "sp_read_probe", "sp_set_wait_limit", "sp_score_lastrow")
 
 
 class SpError(RuntimeError):
@@ -94,9 +94,11 @@ def load_library():
     lib.sp_break_even.argtypes = [i64, f32, f32, f32, f32, P(ctypes.c_int32)]
     lib.sp_read_probe.argtypes = [vp, sz, i32, i32, vp, vp]
     lib.sp_set_wait_limit.argtypes = [ctypes.c_uint64]
+    lib.sp_score_lastrow.argtypes = [P(ScoreDesc), vp, vp, vp, i32, vp, vp, sz, vp]
     for name in ("sp_score_plan", "sp_score", "sp_score_varlen", "sp_select", "sp_select_varlen",
                  "sp_profile_score_kernel", "sp_score_status", "sp_score_windows",
-                 "sp_window_layout", "sp_gather_rows", "sp_break_even", "sp_read_probe", "sp_set_wait_limit"):
+                 "sp_window_layout", "sp_gather_rows", "sp_break_even", "sp_read_probe", "sp_set_wait_limit",
+                 "sp_score_lastrow"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -242,6 +244,32 @@ def sp_score(Q, K, M: Optional[int] = None, scale: float = 0.0, out=None, worksp
                                  out.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(),
                                  _stream(stream))
     _check(st, "sp_score")
+    return out
+
+
+def sp_score_lastrow(Q, Q_last, K, M: Optional[int] = None, scale: float = 0.0, out=None,
+                     workspace=None, stream=None, launch: int = SP_LAUNCH_RESIDENT):
+    """importance [M] float32 with the last prompt token's query row as one
+    more step: Q [L,H,N,d], Q_last [L,H,d], K [L,Hkv,M+N,d]."""
+    torch = _torch()
+    _require_cuda(Q, Q_last, K)
+    L, H, N, d = Q.shape
+    Hkv = K.shape[1]
+    if M is None:
+        M = K.shape[2] - N
+    desc = score_desc(L, H, Hkv, d, N, _dtype_code(Q), scale, launch)
+    if _dtype_code(K) != desc.dtype or K.shape[0] != L or K.shape[3] != d or K.shape[2] != M + N:
+        raise ValueError("K must be [L, Hkv, M+N, d] with Q's dtype")
+    if _dtype_code(Q_last) != desc.dtype or tuple(Q_last.shape) != (L, H, d):
+        raise ValueError("Q_last must be [L, H, d] with Q's dtype")
+    if out is None:
+        out = torch.empty(M, dtype=torch.float32, device=Q.device)
+    _check_out(out, torch.float32, M, "out")
+    ws = _workspace(sp_score_workspace_bytes(desc, M), Q.device, workspace)
+    st = load_library().sp_score_lastrow(ctypes.byref(desc), Q.data_ptr(), Q_last.data_ptr(),
+                                         K.data_ptr(), int(M), out.data_ptr(), ws.data_ptr(),
+                                         ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "sp_score_lastrow")
     return out
 
 

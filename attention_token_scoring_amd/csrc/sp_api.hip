@@ -11,7 +11,7 @@ namespace sp {
 
 hipError_t launch_score(const ScorePlan& p, const sp_score_desc& d, const void* Q, const void* K,
                         long long plane_stride, int M, int M_out, float* importance, void* ws,
-                        bool first, hipStream_t stream);
+                        bool first, int tail_n, int blend_n, hipStream_t stream);
 hipError_t launch_gather(const void* src, long long row_bytes, const int32_t* kept,
                          const int32_t* n_kept, int R, const int64_t* cu, long long max_rows,
                          void* dst, hipStream_t stream);
@@ -171,7 +171,7 @@ sp_status score_batch(const sp_score_desc* desc, int32_t R, const void* Q, const
         const long long M_out = keep ? keep[r] : M;
         float* imp = importance + (keep ? out : cu[r]);
         s = to_status(launch_score(p, *desc, Qr, Kr, T * desc->d, (int)M, (int)M_out, imp, ws,
-                                   r == 0, (hipStream_t)stream));
+                                   r == 0, desc->N, 0, (hipStream_t)stream));
         if (s != SP_OK) return s;
         out += M_out;
     }
@@ -198,10 +198,15 @@ const char* sp_status_string(sp_status s) {
 
 size_t sp_score_workspace_bytes(const sp_score_desc* desc, int64_t max_prompt_len) {
     if (check_desc(desc) != SP_OK || max_prompt_len < 1) return 0;
-    // (plans get harder as prompts grow: if the longest has none, 0)
+    // (plans get harder as prompts grow: if the longest has none, 0). The
+    // bound also covers the one-step plans of sp_score_lastrow's second pass.
     ScorePlan p;
     if (make_plan(*desc, max_prompt_len, device_cus(), &p) != SP_OK) return 0;
-    return workspace_bound(*desc, max_prompt_len, device_cus());
+    sp_score_desc d1 = *desc;
+    d1.N = 1;
+    const size_t a = workspace_bound(*desc, max_prompt_len, device_cus());
+    const size_t b = workspace_bound(d1, max_prompt_len, device_cus());
+    return a > b ? a : b;
 }
 
 sp_status sp_profile_score_kernel(void* before, void* after) {
@@ -258,8 +263,37 @@ sp_status sp_score(const sp_score_desc* desc, const void* Q, const void* K, int3
     if (s != SP_OK) return s;
     if (!ws || !aligned(ws, 256) || ws_bytes < p.ws_total) return SP_EWORKSPACE;
     const long long plane = (long long)(M + desc->N) * desc->d;
-    return to_status(launch_score(p, *desc, Q, K, plane, M, M, importance, ws, true,
+    return to_status(launch_score(p, *desc, Q, K, plane, M, M, importance, ws, true, desc->N, 0,
                                   (hipStream_t)stream));
+}
+
+sp_status sp_score_lastrow(const sp_score_desc* desc, const void* Q, const void* Q_last,
+                           const void* K, int32_t M, float* importance, void* ws,
+                           size_t ws_bytes, void* stream) {
+    sp_status s = check_desc(desc);
+    if (s != SP_OK) return s;
+    if (!Q || !Q_last || !K || !importance || M < 1) return SP_EINVAL;
+    if (!aligned(Q, 16) || !aligned(Q_last, 16) || !aligned(K, 16) || !aligned(importance, 4))
+        return SP_EINVAL;
+    const int cus = device_cus();
+    if (cus < 1) return SP_EDEVICE;
+    // pass 1: the N look-ahead rows; pass 2: the last prompt token's row (one
+    // step, keys 0..M-1, no look-ahead keys), blended in as step N + 1
+    sp_score_desc d1 = *desc;
+    d1.N = 1;
+    ScorePlan p, p1;
+    s = make_plan(*desc, M, cus, &p);
+    if (s != SP_OK) return s;
+    s = make_plan(d1, M, cus, &p1);
+    if (s != SP_OK) return s;
+    if (!ws || !aligned(ws, 256) || ws_bytes < p.ws_total || ws_bytes < p1.ws_total)
+        return SP_EWORKSPACE;
+    const long long plane = (long long)(M + desc->N) * desc->d;
+    s = to_status(launch_score(p, *desc, Q, K, plane, M, M, importance, ws, true, desc->N, 0,
+                               (hipStream_t)stream));
+    if (s != SP_OK) return s;
+    return to_status(launch_score(p1, d1, Q_last, K, plane, M, M, importance, ws, false, 0,
+                                  desc->N, (hipStream_t)stream));
 }
 
 sp_status sp_score_varlen(const sp_score_desc* desc, int32_t R, const void* Q, const void* K,

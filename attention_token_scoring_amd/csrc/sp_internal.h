@@ -89,6 +89,8 @@ struct ScoreArgs {
     ScoreLds lds;
     float c;                   // scale * log2(e)
     int reset_err;             // 1: the prep kernel clears the error word (first request of a call)
+    int tail_n;                // look-ahead keys after the prompt that the rows see causally (N, or 0)
+    int blend_n;               // 0: write the scores; n > 0: importance = (n importance + score) / (n + 1)
     unsigned long long spin_ticks;  // limit of a bounded wait, in ticks of the 100 MHz clock
 };
 

@@ -49,7 +49,7 @@ __global__ __launch_bounds__(256) void score_prep_kernel(ScoreArgs a, int rows) 
     for (int x = tid; x < rows * a.N; x += 256) {
         const int row = x / a.N, t = x % a.N;
         const int j = row / a.G, hl = row % a.G;
-        if (j < a.N && t <= j) {
+        if (j < a.N && t <= j && t < a.tail_n) {
             const long long qrow = ((long long)l * a.H + (long long)kvh * a.G + hl) * a.N + j;
             const uint4* q = (const uint4*)((const char*)a.Q + qrow * D * esz);
             const uint4* k = (const uint4*)(kp + (long long)t * D * esz);
@@ -69,9 +69,10 @@ __global__ __launch_bounds__(256) void score_prep_kernel(ScoreArgs a, int rows) 
     if (tid < rows) {
         const int j = tid / a.G;
         float m = -INFINITY, s = 0.f;
+        const int nt = min(j + 1, a.tail_n);  // look-ahead keys row j sees
         if (j < a.N) {
-            for (int t = 0; t <= j; ++t) m = fmaxf(m, logit[tid][t]);
-            for (int t = 0; t <= j; ++t) s += exp2_hw(fmaf(logit[tid][t], a.c, -m * a.c));
+            for (int t = 0; t < nt; ++t) m = fmaxf(m, logit[tid][t]);
+            for (int t = 0; t < nt; ++t) s += exp2_hw(fmaf(logit[tid][t], a.c, -m * a.c));
         }
         a.tail[(size_t)u * rows + tid] = make_float2(m, s);
     }
@@ -109,7 +110,7 @@ void set_wait_limit(unsigned long long ticks) { t_wait_limit = ticks; }
 // descriptor asks for it, a cooperative one.
 hipError_t launch_score(const ScorePlan& p, const sp_score_desc& d, const void* Q, const void* K,
                         long long plane_stride, int M, int M_out, float* importance, void* ws,
-                        bool first, hipStream_t stream) {
+                        bool first, int tail_n, int blend_n, hipStream_t stream) {
     char* base = (char*)ws;
     ScoreArgs a;
     a.Q = Q;
@@ -140,6 +141,8 @@ hipError_t launch_score(const ScorePlan& p, const sp_score_desc& d, const void* 
     const float scale = d.scale > 0.f ? d.scale : 1.0f / sqrtf((float)d.d);
     a.c = scale * 1.4426950408889634f;
     a.reset_err = first ? 1 : 0;
+    a.tail_n = tail_n;
+    a.blend_n = blend_n;
     a.spin_ticks = t_wait_limit > 0 ? t_wait_limit : kSpinTicks;
 
     const void* fn = pick_kernel(d.dtype, d.d, p.rows, a.G, p.tpw);

@@ -842,11 +842,14 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
     // that got to it first) has scores built on missing statistics: they are
     // replaced by NaN bit patterns (stored as bits, no arithmetic on them), so
     // that the selection rejects them instead of returning a plausible set.
+    // (With blend_n = n > 0 this call adds one more step to scores already
+    // averaged over n steps: (n * importance + this step's score) / (n + 1).)
     const bool poisoned = ld32(a.err) != 0u;
     for (int k = tid; k < nkeys && r0 + k < a.M_out; k += kThreads) {
         float sum = 0.f;
         for (int jj = 0; jj < a.N; ++jj) sum += exp2_hw((float)Trun[jj * KRP + k] * kStep);
-        const float v = sum / (float)a.N;
+        float v = sum / (float)a.N;
+        if (a.blend_n > 0) v = (a.importance[r0 + k] * (float)a.blend_n + v) / (float)(a.blend_n + 1);
         __hip_atomic_store((unsigned*)a.importance + r0 + k, poisoned ? kNaNBits : __float_as_uint(v),
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }

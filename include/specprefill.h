@@ -121,8 +121,9 @@ typedef struct {
     float norm_lo, norm_hi;
 } sp_select_params;
 
-/* Bytes of device workspace sp_score / sp_score_varlen need for prompts of at
- * most max_prompt_len tokens; 0 if the shape is invalid or unsupported. */
+/* Bytes of device workspace sp_score / sp_score_lastrow / sp_score_varlen /
+ * sp_score_windows need for prompts of at most max_prompt_len tokens; 0 if the
+ * shape is invalid or unsupported. */
 size_t sp_score_workspace_bytes(const sp_score_desc* desc, int64_t max_prompt_len);
 
 /*
@@ -143,6 +144,24 @@ size_t sp_score_workspace_bytes(const sp_score_desc* desc, int64_t max_prompt_le
  */
 sp_status sp_score(const sp_score_desc* desc, const void* Q, const void* K, int32_t M,
                    float* importance, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * sp_score with the query row of the last prompt token as one more step
+ * ([SP-G] How It Works, Attention Capture (cb_eval): the attention of the last
+ * query position is captured during the speculator's prefill, like each
+ * look-ahead step's, and the importance averages over all captured steps).
+ * That row, at position M-1, sees the M prompt keys 0..M-1 (none of the
+ * look-ahead keys):
+ *   importance[i] = (1/(N+1)) * (sum_{j<N} max_{l,h} a_{l,h,j,i} + max_{l,h} b_{l,h,i}),
+ *   b_{l,h,.} = softmax over i < M of scale * <Q_last[l][h][:], K[l][h/G][i][:]>,
+ * with a as for sp_score. Two passes over K: the look-ahead rows as sp_score
+ * computes them, then the last row, whose finishing blends it in.
+ *   Q_last  device, [L][H][d] of desc->dtype; the other arguments as for sp_score
+ *           (the workspace bound of sp_score_workspace_bytes covers both passes)
+ */
+sp_status sp_score_lastrow(const sp_score_desc* desc, const void* Q, const void* Q_last,
+                           const void* K, int32_t M, float* importance, void* ws,
+                           size_t ws_bytes, void* stream);
 
 /*
  * sp_score for a ragged batch of R requests (R >= 1), each scored exactly as
@@ -335,7 +354,7 @@ sp_status sp_score_plan(const sp_score_desc* desc, int32_t M, int32_t info[8]);
 sp_status sp_profile_score_kernel(void* before, void* after);
 
 /*
- * Whether the last sp_score / sp_score_varlen / sp_score_windows call that
+ * Whether the last sp_score / sp_score_lastrow / sp_score_varlen / sp_score_windows call that
  * used workspace ws ran to completion without any of its bounded
  * cross-workgroup waits running out (in any of its requests). The scoring
  * kernel never hangs: a wait that sees no progress for 2 s (which would take a

@@ -353,6 +353,53 @@ def test_select_matches_oracle(case, dist):
 
 
 # ----------------------------------------------------------------------------------------
+# the last prompt token's query row as one more step (sp_score_lastrow)
+# ----------------------------------------------------------------------------------------
+def _lastrow_inputs(L, H, Hkv, d, N, M, dt, seed):
+    """Q [L,H,N,d], Q_last [L,H,d] (the same generator with one more query row)
+    and K [L,Hkv,M+N,d]."""
+    wq = workload(L, H, Hkv, d, N + 1, M, dt, seed=seed)
+    Qa = synth.make_q(wq)
+    w = workload(L, H, Hkv, d, N, M, dt, seed=seed)
+    Kh = synth.make_k(w, 0, M)
+    return np.ascontiguousarray(Qa[:, :, :N]), np.ascontiguousarray(Qa[:, :, N]), Kh
+
+
+LASTROW_CASES = [
+    ("bf16-d128-G4-N8-M1000", 2, 8, 2, 128, 8, 1000, BF),
+    ("bf16-d128-G4-N8-M1", 2, 8, 2, 128, 8, 1, BF),
+    ("bf16-d64-G2-N8-M777", 3, 4, 2, 64, 8, 777, BF),
+    ("f32-d64-G2-N8-M1024", 2, 4, 2, 64, 8, 1024, F32),
+    ("f32-d128-G4-N8-M300", 2, 8, 2, 128, 8, 300, F32),
+    ("bf16-d128-G8-N4-M2000", 1, 16, 2, 128, 4, 2000, BF),
+    ("bf16-d128-G32-N1-M700", 1, 32, 1, 128, 1, 700, BF),
+    ("multi-bf16-d128-rows32", 32, 32, 8, 128, 8, 4100, BF),
+    ("multi-bf16-d64-rows16", 24, 16, 8, 64, 8, 4608, BF),
+]
+
+
+@pytest.mark.parametrize("case", LASTROW_CASES, ids=[c[0] for c in LASTROW_CASES])
+def test_score_lastrow_matches_oracle(case):
+    name, L, H, Hkv, d, N, M, dt = case
+    print(f"case lastrow {name}", flush=True)
+    Qh, Ql, Kh = _lastrow_inputs(L, H, Hkv, d, N, M, dt, seed=41)
+    imp = sp.sp_score_lastrow(to_dev(Qh), to_dev(Ql), to_dev(Kh))
+    torch.cuda.synchronize()
+    check_importance(imp.cpu().numpy(), oracle.score_lastrow(Qh, Ql, Kh), f"lastrow {name}")
+
+
+def test_score_lastrow_workload_8b_32k():
+    """The 8B shape at M = 32768 with a last-row query: full comparison."""
+    w = synth.WORKLOADS["spec8b_m32k"]
+    print("lastrow spec8b_m32k: generating", flush=True)
+    Qh, Ql, Kh = _lastrow_inputs(w.L, w.H, w.Hkv, w.d, w.N, w.M, w.dtype, seed=w.seed)
+    imp = sp.sp_score_lastrow(to_dev(Qh), to_dev(Ql), to_dev(Kh))
+    torch.cuda.synchronize()
+    print("lastrow spec8b_m32k: oracle", flush=True)
+    check_importance(imp.cpu().numpy(), oracle.score_lastrow(Qh, Ql, Kh), "lastrow 8b/32k")
+
+
+# ----------------------------------------------------------------------------------------
 # robust normalisations (percentile clip, clipped z-score): bit-exact against the oracle
 # ----------------------------------------------------------------------------------------
 NORM_CASES = [
