@@ -33,7 +33,7 @@ EXPORTED = ("sp_score", "sp_score_varlen", "sp_select", "sp_select_varlen",
             "sp_score_workspace_bytes", "sp_select_workspace_bytes", "sp_score_plan",
             "sp_status_string", "sp_profile_score_kernel", "sp_score_status",
             "sp_score_windows", "sp_window_layout", "sp_gather_rows", "sp_break_even",
-            "sp_read_probe", "sp_set_wait_limit", "sp_score_lastrow")
+            "sp_read_probe", "sp_set_wait_limit", "sp_score_lastrow", "sp_score_noalloc")
 
 
 class SpError(RuntimeError):
@@ -95,10 +95,11 @@ def load_library():
     lib.sp_read_probe.argtypes = [vp, sz, i32, i32, vp, vp]
     lib.sp_set_wait_limit.argtypes = [ctypes.c_uint64]
     lib.sp_score_lastrow.argtypes = [P(ScoreDesc), vp, vp, vp, i32, vp, vp, sz, vp]
+    lib.sp_score_noalloc.argtypes = [P(ScoreDesc), vp, vp, i32, vp, vp]
     for name in ("sp_score_plan", "sp_score", "sp_score_varlen", "sp_select", "sp_select_varlen",
                  "sp_profile_score_kernel", "sp_score_status", "sp_score_windows",
                  "sp_window_layout", "sp_gather_rows", "sp_break_even", "sp_read_probe", "sp_set_wait_limit",
-                 "sp_score_lastrow"):
+                 "sp_score_lastrow", "sp_score_noalloc"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib

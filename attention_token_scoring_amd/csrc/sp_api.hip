@@ -7,6 +7,11 @@
 
 #include "sp_internal.h"
 
+// Workspace of sp_score_noalloc: one copy per device, held until the process
+// ends. In host code this name only stands for the array; kernels get the
+// device address that hipGetSymbolAddress reports for the current device.
+static __device__ __align__(256) unsigned char scratch[SP_NOALLOC_SCRATCH_BYTES];
+
 namespace sp {
 
 hipError_t launch_score(const ScorePlan& p, const sp_score_desc& d, const void* Q, const void* K,
@@ -27,6 +32,12 @@ constexpr int kMaxSelectRequests = 1024;
 
 int g_cus[kMaxDevices];
 std::once_flag g_once[kMaxDevices];
+
+// Device address of each device's copy of the scratch array of
+// sp_score_noalloc (looked up once per device, that device current).
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+std::once_flag g_scratch_once[kMaxDevices];
 
 // Compute units of the current device (0 if there is no usable device).
 int device_cus() {
@@ -265,6 +276,31 @@ sp_status sp_score(const sp_score_desc* desc, const void* Q, const void* K, int3
     const long long plane = (long long)(M + desc->N) * desc->d;
     return to_status(launch_score(p, *desc, Q, K, plane, M, M, importance, ws, true, desc->N, 0,
                                   (hipStream_t)stream));
+}
+
+sp_status sp_score_noalloc(const sp_score_desc* desc, const void* Q, const void* K, int32_t M,
+                           float* importance, void* stream) {
+    sp_status s = check_desc(desc);
+    if (s != SP_OK) return s;
+    if (!Q || !K || !importance || M < 1) return SP_EINVAL;
+    if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(importance, 4)) return SP_EINVAL;
+    const int cus = device_cus();
+    if (cus < 1) return SP_EDEVICE;
+    ScorePlan p;
+    s = make_plan(*desc, M, cus, &p);
+    if (s != SP_OK) return s;
+    if (p.ws_total > SP_NOALLOC_SCRATCH_BYTES) return SP_EWORKSPACE;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SP_EDEVICE;
+    std::call_once(g_scratch_once[dev], [dev] {
+        void* ptr = nullptr;
+        g_scratch_err[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        g_scratch_ptr[dev] = ptr;
+    });
+    if (g_scratch_err[dev] != hipSuccess || !g_scratch_ptr[dev]) return SP_EDEVICE;
+    const long long plane = (long long)(M + desc->N) * desc->d;
+    return to_status(launch_score(p, *desc, Q, K, plane, M, M, importance, g_scratch_ptr[dev],
+                                  true, desc->N, 0, (hipStream_t)stream));
 }
 
 sp_status sp_score_lastrow(const sp_score_desc* desc, const void* Q, const void* Q_last,

@@ -146,6 +146,26 @@ sp_status sp_score(const sp_score_desc* desc, const void* Q, const void* K, int3
                    float* importance, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * sp_score for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation and kernels as sp_score, with the workspace in a static
+ * device array of SP_NOALLOC_SCRATCH_BYTES that the library holds on every
+ * device it runs on until the process ends (its address is looked up on the
+ * first call on each device). The call allocates nothing. Every call on a
+ * device shares that device's array: calls that overlap on one device (other
+ * streams, other threads) race and must not be made; the kernels reset what
+ * they need on every call, so consecutive calls need nothing in between.
+ * A time-out of its bounded waits shows as NaN scores (sp_select then reports
+ * n_kept = -1); sp_score_status does not apply.
+ *   Arguments as for sp_score, without the workspace. SP_EWORKSPACE when the
+ *   plan for (desc, M) needs more than SP_NOALLOC_SCRATCH_BYTES of workspace
+ *   (the 8B shape at 128K keys needs about 20 MiB).
+ */
+#define SP_NOALLOC_SCRATCH_BYTES (32u << 20)
+sp_status sp_score_noalloc(const sp_score_desc* desc, const void* Q, const void* K, int32_t M,
+                           float* importance, void* stream);
+
+/*
  * sp_score with the query row of the last prompt token as one more step
  * ([SP-G] How It Works, Attention Capture (cb_eval): the attention of the last
  * query position is captured during the speculator's prefill, like each
