@@ -39,6 +39,13 @@ constexpr bool score_roomy(int row_bytes, int tpw, int nh) {
 constexpr int row_stride(int kr) { return (kr + 63) / 64 * 64 + 16; }
 
 // Byte offsets of the scoring kernel's LDS regions (all 16-byte aligned).
+// LDS bytes of the DMA kernel's static region (Q, statistics, references,
+// log-sum-exps), besides its dynamic K slots.
+constexpr int dma_static_lds(int rows, int row_bytes, int N_unused = 0) {
+    return 2 * rows * (row_bytes + 16) + 2 * kStreamWaves * rows * 8 + (kMaxDefer + 1) * kStreamWaves * rows * 4 +
+           2 * rows * 4 + N_unused * 0;
+}
+
 struct ScoreLds {
     int bank;   // [nbk][SW][TPW][64 lanes][NH][4]: parked logits, 16-bit codes
     int ref;    // [nbk][SW][rows] float: reference (log2 domain) of the parked logits
@@ -49,14 +56,26 @@ struct ScoreLds {
     int total;
 };
 
-inline ScoreLds score_lds_layout(int nbk, int tpw, int rows, int row_bytes, int N, int KR) {
+// With dma, the first region holds the K tiles (one slot per tile of each
+// streaming wave) instead of parked logits, which stay in registers.
+inline ScoreLds score_lds_layout(int nbk, int tpw, int rows, int row_bytes, int N, int KR,
+                                 bool dma = false) {
     auto up = [](int x) { return (x + 15) / 16 * 16; };
     const int nh = rows / 16;
     ScoreLds l;
     l.bank = 0;
     // the running maxima are written once, at the end, over the banks
     l.trun = 0;
-    const int banks = nbk * kStreamWaves * tpw * 64 * nh * 8;
+    const int banks = dma ? kStreamWaves * tpw * kTileKeys * row_bytes
+                          : nbk * kStreamWaves * tpw * 64 * nh * 8;
+    if (dma) {
+        // only the K slots (and, at the end, the running maxima over them) are
+        // dynamic; the kernel's other regions are a static array of misc bytes
+        const int trun = N * row_stride(KR) * 4;
+        l.ref = l.q = l.red = l.lse = 0;
+        l.total = up(banks > trun ? banks : trun);
+        return l;
+    }
     const int trun = N * row_stride(KR) * 4;
     l.ref = l.bank + up(banks > trun ? banks : trun);
     l.q = l.ref + up(nbk * kStreamWaves * rows * 4);
@@ -97,6 +116,7 @@ struct ScoreArgs {
 struct ScorePlan {
     int rows;      // 16 or 32
     int tpw;       // tiles per streaming wave and unit
+    bool dma;      // K tiles by DMA into LDS (parked logits in registers)
     int cap;       // prompt keys one workgroup can hold
     int g, ngroups, KR, units;
     int ncomb;     // combiner workgroups (on CUs no group uses)
@@ -146,10 +166,10 @@ void set_profile_events(hipEvent_t before, hipEvent_t after);
 void set_wait_limit(unsigned long long ticks);
 
 // Scoring kernels, one translation unit per operand type and head
-// dimension: the instantiation for (rows, G, tiles per wave), or nullptr.
-const void* score_kernel_bf16_d128(int rows, int G, int tpw);
-const void* score_kernel_bf16_d64(int rows, int G, int tpw);
-const void* score_kernel_f32_d128(int rows, int G, int tpw);
-const void* score_kernel_f32_d64(int rows, int G, int tpw);
+// dimension: the instantiation for (rows, G, tiles per wave, K path), or nullptr.
+const void* score_kernel_bf16_d128(int rows, int G, int tpw, bool dma);
+const void* score_kernel_bf16_d64(int rows, int G, int tpw, bool dma);
+const void* score_kernel_f32_d128(int rows, int G, int tpw, bool dma);
+const void* score_kernel_f32_d64(int rows, int G, int tpw, bool dma);
 
 }  // namespace sp

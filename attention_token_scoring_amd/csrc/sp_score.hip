@@ -81,13 +81,13 @@ __global__ __launch_bounds__(256) void score_prep_kernel(ScoreArgs a, int rows) 
 // ---------------------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------------------
-static const void* pick_kernel(int dtype, int d, int rows, int G, int tpw) {
+static const void* pick_kernel(int dtype, int d, int rows, int G, int tpw, bool dma) {
     if (dtype == SP_BF16) {
-        if (d == 128) return score_kernel_bf16_d128(rows, G, tpw);
-        if (d == 64) return score_kernel_bf16_d64(rows, G, tpw);
+        if (d == 128) return score_kernel_bf16_d128(rows, G, tpw, dma);
+        if (d == 64) return score_kernel_bf16_d64(rows, G, tpw, dma);
     } else {
-        if (d == 128) return score_kernel_f32_d128(rows, G, tpw);
-        if (d == 64) return score_kernel_f32_d64(rows, G, tpw);
+        if (d == 128) return score_kernel_f32_d128(rows, G, tpw, dma);
+        if (d == 64) return score_kernel_f32_d64(rows, G, tpw, dma);
     }
     return nullptr;
 }
@@ -145,7 +145,7 @@ hipError_t launch_score(const ScorePlan& p, const sp_score_desc& d, const void* 
     a.blend_n = blend_n;
     a.spin_ticks = t_wait_limit > 0 ? t_wait_limit : kSpinTicks;
 
-    const void* fn = pick_kernel(d.dtype, d.d, p.rows, a.G, p.tpw);
+    const void* fn = pick_kernel(d.dtype, d.d, p.rows, a.G, p.tpw, p.dma);
     if (!fn) return hipErrorInvalidValue;
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, p.lds.total);
     if (e != hipSuccess) return e;

@@ -3,8 +3,8 @@
 
 namespace sp {
 
-const void* score_kernel_bf16_d64(int rows, int G, int tpw) {
-    return pick_kernel_for<64, true>(rows, G, tpw);
+const void* score_kernel_bf16_d64(int rows, int G, int tpw, bool dma) {
+    return pick_kernel_for<64, true>(rows, G, tpw, dma);
 }
 
 }  // namespace sp

@@ -3,8 +3,8 @@
 
 namespace sp {
 
-const void* score_kernel_f32_d128(int rows, int G, int tpw) {
-    return pick_kernel_for<128, false>(rows, G, tpw);
+const void* score_kernel_f32_d128(int rows, int G, int tpw, bool dma) {
+    return pick_kernel_for<128, false>(rows, G, tpw, dma);
 }
 
 }  // namespace sp

@@ -197,10 +197,11 @@ __device__ __forceinline__ void unpack_v2(int word, int off, int& lo, int& hi) {
 // four 4-deep k-steps (d = 16 s + 4 g + e). Both operands use the same mapping.
 // C layout: lane L holds rows L % 16 of keys 4 (L / 16) + r, r = 0..3.
 // ---------------------------------------------------------------------------------------
-template <int D_, bool BF16_, int NH_, int G_, int TPW_>
+template <int D_, bool BF16_, int NH_, int G_, int TPW_, bool DMA_ = false>
 struct Cfg {
     static constexpr int D = D_, NH = NH_, G = G_;
     static constexpr bool BF16 = BF16_;
+    static constexpr bool DMA = DMA_;  // K tiles by DMA into LDS (else a register ring)
     static constexpr int ESZ = BF16 ? 2 : 4;
     static constexpr int KB = D * ESZ;    // bytes per key (and query) row
     static constexpr int QS = KB + 16;    // LDS bytes per staged query row
@@ -215,6 +216,51 @@ struct Cfg {
     static_assert(G <= 16 || (G == 32 && NH == 2), "unsupported head grouping");
     static constexpr int GL = G == 32 ? 16 : G;  // heads of a step within one half
 };
+
+// s_waitcnt operands (gfx9 encoding): vector memory count n, nothing else
+// waited for; LDS / scalar count 0, nothing else waited for.
+constexpr unsigned vm_wait(int n) { return (unsigned)((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8)); }
+constexpr unsigned kLgkmWait0 = (15u) | (3u << 14) | (7u << 4);
+// cache policy of the DMA loads: non-temporal (streamed once)
+constexpr int kNonTemporal = 2;
+
+// LDS stores the compiler does not order against the DMA writes in flight
+// (it cannot tell that they go to other addresses, and would wait for every
+// load before each store). LDS operations complete in issue order, so the
+// waits the compiler computes for its own LDS accesses stay correct.
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+    return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+__device__ __forceinline__ void lds_store_f2(void* p, float2 v) {
+    asm volatile("ds_write_b64 %0, %1" : : "v"(lds_addr(p)), "v"(v) : "memory");
+}
+__device__ __forceinline__ void lds_store_f1(void* p, float v) {
+    asm volatile("ds_write_b32 %0, %1" : : "v"(lds_addr(p)), "v"(v) : "memory");
+}
+
+// One DMA load: 16 bytes per lane from the buffer at voffset + soffset into
+// LDS at lds + 16 * lane (non-temporal). (A device function: the builtin
+// cannot appear in a lambda, which is also compiled for the host.)
+__device__ __forceinline__ void dma_load16(__amdgpu_buffer_rsrc_t rs, char* lds, uint32_t voffset,
+                                           uint32_t soffset) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, voffset,
+                                             soffset, 0, kNonTemporal);
+}
+
+// The per-step workgroup barrier. With K in flight by DMA it waits for the
+// wave's LDS operations only (a full barrier would also wait for every load in
+// flight); the compiler fences keep LDS accesses on their side of it.
+template <class C>
+__device__ __forceinline__ void step_barrier() {
+    if constexpr (C::DMA) {
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_waitcnt(kLgkmWait0);
+        __builtin_amdgcn_s_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    } else {
+        __syncthreads();
+    }
+}
 
 template <class C>
 struct Frag {
@@ -373,11 +419,20 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
     // ---------------------------------------------------------------------------
     const int group = (int)blockIdx.x / a.g, rank = (int)blockIdx.x % a.g;
     const int KRP = row_stride(a.KR);
+    // With K by DMA, the regions other than the K slots live in an array of
+    // their own, so that the compiler can tell the waves' LDS stores there from
+    // the DMA writes in flight (it would otherwise wait for every load before
+    // each store).
+    constexpr int kMiscQ = 0, kMiscRed = kMiscQ + 2 * ROWS * C::QS,
+                  kMiscRef = kMiscRed + 2 * SW * ROWS * 8,
+                  kMiscLse = kMiscRef + (kMaxDefer + 1) * SW * ROWS * 4,
+                  kMiscBytes = kMiscLse + 2 * ROWS * 4;
+    __shared__ __attribute__((aligned(16))) char misc_lds[C::DMA ? kMiscBytes : 16];
     int* Trun = (int*)(smem + a.lds.trun);  // running maxima at the end (over the parked banks)
-    float2* red = (float2*)(smem + a.lds.red);      // [2][SW][ROWS]
-    float* lse_s = (float*)(smem + a.lds.lse);      // [2][ROWS]
-    float* refs = (float*)(smem + a.lds.ref);       // [nbk][SW][ROWS]
-    char* qlds = smem + a.lds.q;                    // [2][ROWS][QS]
+    float2* red = (float2*)(C::DMA ? misc_lds + kMiscRed : smem + a.lds.red);   // [2][SW][ROWS]
+    float* lse_s = (float*)(C::DMA ? misc_lds + kMiscLse : smem + a.lds.lse);   // [2][ROWS]
+    float* refs = (float*)(C::DMA ? misc_lds + kMiscRef : smem + a.lds.ref);    // [nbk][SW][ROWS]
+    char* qlds = C::DMA ? misc_lds + kMiscQ : smem + a.lds.q;                  // [2][ROWS][QS]
     char* banks = smem + a.lds.bank;                // [nbk][SW][TPW][64][NH][8 B]
 
     const int r0 = rank * a.KR;
@@ -387,7 +442,8 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
     const uint32_t plane_bytes = (uint32_t)(a.M + a.N) * (uint32_t)C::KB;
     const int D = a.defer, nbk = a.nbk;
     const int n_units = group < a.units ? (a.units - group + a.ngroups - 1) / a.ngroups : 0;
-    const int n_steps = (n_units + D + 1) & ~1;  // even: the streaming loop is unrolled by 2
+    // even: the register-ring loop is unrolled by 2; the DMA loop by its banks (4)
+    const int n_steps = C::DMA ? (n_units + D + 3) & ~3 : (n_units + D + 1) & ~1;
     auto unit_of = [&](int it) __attribute__((always_inline)) { return it >= 0 && it < n_units ? group + it * a.ngroups : -1; };
 
     // Per-lane query rows of the halves: the look-ahead step of each
@@ -396,6 +452,255 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
     for (int hf = 0; hf < NH; ++hf) jrow[hf] = (hf * 16 + (lane & 15)) / G;
 
     if (w < SW) {
+        if constexpr (C::DMA) {
+        // ============= streaming waves: K tiles by DMA into LDS =============
+        // The tiles of the next unit travel HBM -> LDS (buffer loads with the
+        // lds modifier: no registers, non-temporal), each load instruction
+        // covering whole 128-byte lines of consecutive key rows; a tile is
+        // stored with its 16-byte chunks XOR-swizzled by row, so that the
+        // MFMA-layout reads (16 rows x one chunk column) hit every bank once.
+        // Each wave owns one LDS slot per tile of its slice; the slot of tile t
+        // is refilled with tile t of the next unit as soon as its reads are
+        // done, so a unit is always in flight (the outstanding load count,
+        // TPW - 1 tiles, is the same before every tile). Parked logits stay in
+        // registers (NB banks, the step loop unrolled by NB), and the per-step
+        // barrier waits for LDS only, never for the loads in flight.
+        constexpr int TB = kTileKeys * C::KB;  // bytes of one 16-key tile
+        constexpr int CPR = C::KB / 16;         // 16-byte chunks per key row
+        constexpr int RPI = 64 / CPR;           // key rows one load instruction covers
+        constexpr int SWZ = 16 / CPR;           // rows sharing one 64-bank line
+        constexpr int NB = kMaxDefer + 1;       // register banks of parked logits
+        constexpr int VM_AHEAD = (TPW - 1) * NLD;  // loads issued after a tile's own
+        static_assert(RPI * NLD == kTileKeys, "tile load shape");
+        char* ring = smem + a.lds.bank + (size_t)w * TPW * TB;
+        const int ntv = min(max((ntiles - w + SW - 1) / SW, 0), TPW);
+        const int tpart = (nkeys % kTileKeys != 0 && ntv > 0 && w + SW * (ntv - 1) == ntiles - 1) ? ntv - 1 : -1;
+        const int rem = nkeys - (w + SW * max(tpart, 0)) * kTileKeys - 4 * g4;
+        const bool full = tpart < 0 && ntv == TPW;
+        // DMA side: the lane's byte offset in a tile for load s (row RPI s + lane / CPR,
+        // the chunk that lands in LDS column lane % CPR); read side: the LDS offset
+        // of row lane % 16, k-step s (chunk 4 s + lane / 16)
+        uint32_t loff[NLD];
+        int roff[NLD];
+#pragma unroll
+        for (int s = 0; s < NLD; ++s) {
+            const int row = RPI * s + lane / CPR, col = lane % CPR;
+            loff[s] = (uint32_t)(row * C::KB + ((col ^ ((row / SWZ) % CPR)) * 16));
+            const int r2 = lane & 15, ch = 4 * s + g4;
+            roff[s] = r2 * C::KB + ((ch ^ ((r2 / SWZ) % CPR)) * 16);
+        }
+        uint32_t tbo[TPW];  // byte offset of tile t in the plane (past the slice: out of range, zeros)
+#pragma unroll
+        for (int t = 0; t < TPW; ++t)
+            tbo[t] = t < ntv ? (uint32_t)(r0 + (w + SW * t) * kTileKeys) * (uint32_t)C::KB : kOob;
+        auto issue_tile = [&](__amdgpu_buffer_rsrc_t rs, int t) __attribute__((always_inline)) {
+#pragma unroll
+            for (int s = 0; s < NLD; ++s) dma_load16(rs, ring + t * TB + s * 1024, loff[s], tbo[t]);
+        };
+
+        constexpr int NHF = G == 32 ? 1 : NH;
+        constexpr bool kRoomy = NB * TPW * NH * 2 + NH * NLD * 4 + NLD * 4 + TPW * NH * 4 <= 176;
+        constexpr int SGL = C::GL >= 2 && !kRoomy ? 2 : 1;
+        constexpr int KEEP = 4 / SGL;
+        int trun[TPW][NHF][KEEP];
+#pragma unroll
+        for (int t = 0; t < TPW; ++t)
+#pragma unroll
+            for (int hf = 0; hf < NHF; ++hf)
+#pragma unroll
+                for (int kk = 0; kk < KEEP; ++kk) trun[t][hf][kk] = kNegInf;
+        const bool lb0 = (lane & 1) != 0;
+
+        int park[NB][TPW][2 * NH];  // parked logits of the last NB units (16-bit codes, 2 per word)
+        f32x4 acc[TPW][NH];
+        {
+            const auto rs = plane_rsrc(a, unit_of(0), plane_bytes, C::ESZ);
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) issue_tile(rs, t);
+        }
+        step_barrier<C>();  // Q of unit 0 is staged
+
+        auto stream = [&](auto Pc, auto Bc, int it) __attribute__((always_inline)) {
+            constexpr int P = decltype(Pc)::value, B = decltype(Bc)::value;
+            i32x4 qf[NH][NLD];
+#pragma unroll
+            for (int hf = 0; hf < NH; ++hf)
+#pragma unroll
+                for (int s = 0; s < NLD; ++s)
+                    qf[hf][s] = *(const i32x4*)(qlds + (P * ROWS + hf * 16 + (lane & 15)) * C::QS + 16 * g4 + 64 * s);
+            const auto rs1 = plane_rsrc(a, unit_of(it + 1), plane_bytes, C::ESZ);
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) {
+                __builtin_amdgcn_s_waitcnt(vm_wait(VM_AHEAD));  // this tile's loads have landed
+                i32x4 kf[NLD];
+#pragma unroll
+                for (int s = 0; s < NLD; ++s) kf[s] = *(const i32x4*)(ring + t * TB + roff[s]);
+#pragma unroll
+                for (int hf = 0; hf < NH; ++hf) acc[t][hf] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < NLD; ++s)
+#pragma unroll
+                    for (int hf = 0; hf < NH; ++hf) mma<C>(acc[t][hf], qf[hf][s], kf[s]);
+                // the slot's reads are done: refill it with the same tile of the next unit
+                __builtin_amdgcn_s_waitcnt(kLgkmWait0);
+                __atomic_signal_fence(__ATOMIC_SEQ_CST);
+                issue_tile(rs1, t);
+            }
+            // per wave-row statistics over this wave's keys of the slice (as in
+            // the register-ring variant) and the shifted log2 logits in acc
+            auto stats = [&](auto FullC) __attribute__((always_inline)) {
+                constexpr bool FULL = decltype(FullC)::value;
+#pragma unroll
+                for (int hf = 0; hf < NH; ++hf) {
+                    float m = -INFINITY;
+#pragma unroll
+                    for (int t = 0; t < TPW; ++t) {
+                        float mt = fmaxf(fmaxf(acc[t][hf][0], acc[t][hf][1]), fmaxf(acc[t][hf][2], acc[t][hf][3]));
+                        if constexpr (FULL) {
+                            m = fmaxf(m, mt);
+                        } else {
+                            if (t == tpart) {
+                                int lim = rem;
+                                asm volatile("" : "+v"(lim));
+                                mt = -INFINITY;
+#pragma unroll
+                                for (int r = 0; r < 4; ++r)
+                                    if (r < lim) mt = fmaxf(mt, acc[t][hf][r]);
+                            }
+                            if (t < ntv) m = fmaxf(m, mt);
+                        }
+                    }
+                    m = xor16_max(m);
+                    m = xor32_max(m);
+                    const float cm = m == -INFINITY ? 0.f : m * c;
+                    float s = 0.f;
+#pragma unroll
+                    for (int t = 0; t < TPW; ++t) {
+                        float e[4];
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const float y = fmaf(acc[t][hf][r], c, -cm);
+                            acc[t][hf][r] = y;
+                            e[r] = exp2_hw(y);
+                        }
+                        float st = (e[0] + e[1]) + (e[2] + e[3]);
+                        if constexpr (FULL) {
+                            s += st;
+                        } else {
+                            if (t == tpart) {
+                                int lim = rem;
+                                asm volatile("" : "+v"(lim));
+                                st = 0.f;
+#pragma unroll
+                                for (int r = 0; r < 4; ++r)
+                                    if (r < lim) st += e[r];
+                            }
+                            if (t < ntv) s += st;
+                        }
+                    }
+                    s = xor16_sum(s);
+                    s = xor32_sum(s);
+                    if (g4 == 0) {
+                        lds_store_f2(&red[(P * SW + w) * ROWS + hf * 16 + lane], make_float2(m, s));
+                        lds_store_f1(&refs[(B * SW + w) * ROWS + hf * 16 + lane], cm);
+                    }
+                }
+            };
+            if (full) stats(std::true_type{});
+            else stats(std::false_type{});
+#pragma unroll
+            for (int t = 0; t < TPW; ++t)
+#pragma unroll
+                for (int hf = 0; hf < NH; ++hf) {
+                    constexpr float k = -1.f / kCodeRange;
+                    park[B][t][2 * hf] = pack_u2(acc[t][hf][0] * k, acc[t][hf][1] * k);
+                    park[B][t][2 * hf + 1] = pack_u2(acc[t][hf][2] * k, acc[t][hf][3] * k);
+                }
+        };
+
+        // finish the unit parked in register bank BF (log-sum-exps in lse_s[pb])
+        auto finish = [&](auto BFc, int pb) __attribute__((always_inline)) {
+            constexpr int BF = decltype(BFc)::value;
+            int off[NH];
+#pragma unroll
+            for (int hf = 0; hf < NH; ++hf) {
+                const int row = hf * 16 + (lane & 15);
+                off[hf] = offset_steps(refs[(BF * SW + w) * ROWS + row] - lse_s[pb * ROWS + row]);
+            }
+#pragma unroll
+            for (int hf = 0; hf < NHF; ++hf) {
+#pragma unroll
+                for (int t = 0; t < TPW; ++t) {
+                    int y[4], y1[4];
+                    unpack_v2(park[BF][t][2 * hf], off[hf], y[0], y[1]);
+                    unpack_v2(park[BF][t][2 * hf + 1], off[hf], y[2], y[3]);
+                    if constexpr (G == 32) {
+                        unpack_v2(park[BF][t][2], off[1], y1[0], y1[1]);
+                        unpack_v2(park[BF][t][3], off[1], y1[2], y1[3]);
+                    }
+                    int v[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        int x = y[r];
+                        if constexpr (G == 32) x = max(x, y1[r]);
+                        v[r] = group_max16<SGL>(x);
+                    }
+                    if constexpr (KEEP == 2) {
+                        trun[t][hf][0] = max(trun[t][hf][0], lb0 ? v[2] : v[0]);
+                        trun[t][hf][1] = max(trun[t][hf][1], lb0 ? v[3] : v[1]);
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) trun[t][hf][r] = max(trun[t][hf][r], v[r]);
+                    }
+                }
+            }
+        };
+
+        // step it: stream unit it into bank it % NB, then (after the barrier,
+        // when the control wave has put unit it - 3's log-sum-exps in LDS)
+        // finish unit it - 3, parked in bank (it + 1) % NB
+        auto step = [&](auto Pc, auto Bc, int it) __attribute__((always_inline)) {
+            constexpr int B = decltype(Bc)::value;
+            if (it < n_units) stream(Pc, Bc, it);
+            step_barrier<C>();
+            const int fu = it - kMaxDefer;
+            if (fu >= 0 && fu < n_units) finish(std::integral_constant<int, (B + 1) % NB>{}, it & 1);
+        };
+        for (int it = 0; it < n_steps; it += NB) {
+            step(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, it);
+            step(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{}, it + 1);
+            step(std::integral_constant<int, 0>{}, std::integral_constant<int, 2>{}, it + 2);
+            step(std::integral_constant<int, 1>{}, std::integral_constant<int, 3>{}, it + 3);
+        }
+        __builtin_amdgcn_s_waitcnt(vm_wait(0));  // the last (empty) refills have landed
+        __syncthreads();  // every wave is done with its slots, which Trun overlays
+#pragma unroll
+        for (int m = SGL; m < C::GL; m <<= 1)
+#pragma unroll
+            for (int t = 0; t < TPW; ++t)
+#pragma unroll
+                for (int hf = 0; hf < NHF; ++hf)
+#pragma unroll
+                    for (int kk = 0; kk < KEEP; ++kk)
+                        trun[t][hf][kk] = max(trun[t][hf][kk], __shfl_xor(trun[t][hf][kk], m));
+        const int kg = (lane & 15) % C::GL;
+#pragma unroll
+        for (int hf = 0; hf < NHF; ++hf)
+            if (jrow[hf] < a.N && kg < SGL) {
+#pragma unroll
+                for (int t = 0; t < TPW; ++t) {
+                    if (t >= ntv) break;
+                    int* rowp = Trun + jrow[hf] * KRP + (w + SW * t) * kTileKeys + 4 * g4;
+                    if constexpr (KEEP == 2) {
+                        rowp[2 * (lane & 1)] = trun[t][hf][0];
+                        rowp[2 * (lane & 1) + 1] = trun[t][hf][1];
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) rowp[r] = trun[t][hf][r];
+                    }
+                }
+            }
+        } else {
         // ======================= streaming waves =======================
         // This wave's tiles w, w + SW, ...: the first ntv hold keys of the
         // slice (the rest are read as zeros and masked); when the slice ends
@@ -667,6 +972,7 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
                     }
                 }
             }
+        }
     } else {
         // ======================= control wave =======================
         // Its memory instructions are few and latency-critical: they are
@@ -756,7 +1062,7 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
             __builtin_amdgcn_s_setprio(3);
             q_issue(so, unit_of(it + 3));
             __builtin_amdgcn_s_setprio(0);
-            __syncthreads();
+            step_barrier<C>();
             __builtin_amdgcn_s_setprio(3);
             if (it < n_units) publish(unit_of(it), P);
             lse_issue(sl, unit_of(it + kLseAhead - D));
@@ -769,7 +1075,7 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
         q_issue(std::integral_constant<int, 0>{}, unit_of(2));
         lse_issue(std::integral_constant<int, 0>{}, unit_of(-D));
         if constexpr (kLseAhead == 2) lse_issue(std::integral_constant<int, 1>{}, unit_of(1 - D));
-        __syncthreads();
+        step_barrier<C>();
         for (int it = 0; it < n_steps; it += 2) {
             ctrl_step(std::integral_constant<int, 0>{}, it);
             ctrl_step(std::integral_constant<int, 1>{}, it + 1);
@@ -861,32 +1167,40 @@ const void* kernel_ptr() {
 }
 
 // The instantiation for head-group size G (nullptr when unsupported).
-template <int D, bool BF, int NH, int TPW>
+template <int D, bool BF, int NH, int TPW, bool DMA>
 const void* pick_g(int G) {
     switch (G) {
         case 1:
             // (one head per step and two halves keep 32 running maxima per
             // lane: only the base tile count fits the registers)
             if constexpr (NH == 2 && TPW > tiles_per_wave(BF, D)) return nullptr;
-            else return kernel_ptr<Cfg<D, BF, NH, 1, TPW>>();
-        case 2: return kernel_ptr<Cfg<D, BF, NH, 2, TPW>>();
-        case 4: return kernel_ptr<Cfg<D, BF, NH, 4, TPW>>();
-        case 8: return kernel_ptr<Cfg<D, BF, NH, 8, TPW>>();
-        case 16: return kernel_ptr<Cfg<D, BF, NH, 16, TPW>>();
+            else return kernel_ptr<Cfg<D, BF, NH, 1, TPW, DMA>>();
+        case 2: return kernel_ptr<Cfg<D, BF, NH, 2, TPW, DMA>>();
+        case 4: return kernel_ptr<Cfg<D, BF, NH, 4, TPW, DMA>>();
+        case 8: return kernel_ptr<Cfg<D, BF, NH, 8, TPW, DMA>>();
+        case 16: return kernel_ptr<Cfg<D, BF, NH, 16, TPW, DMA>>();
         case 32:
-            if constexpr (NH == 2) return kernel_ptr<Cfg<D, BF, 2, 32, TPW>>();
+            if constexpr (NH == 2) return kernel_ptr<Cfg<D, BF, 2, 32, TPW, DMA>>();
             return nullptr;
         default: return nullptr;
     }
 }
 
-// The instantiation for (rows, G, tiles per wave) of one operand type and
-// head dimension; TPW is tiles_per_wave(BF, D) or one more.
+// The instantiation for (rows, G, tiles per wave, K path) of one operand type
+// and head dimension; TPW is tiles_per_wave(BF, D) or one more; the DMA path
+// exists for bf16 at the base tile count.
 template <int D, bool BF>
-const void* pick_kernel_for(int rows, int G, int tpw) {
+const void* pick_kernel_for(int rows, int G, int tpw, bool dma) {
     constexpr int T0 = tiles_per_wave(BF, D);
-    if (tpw == T0) return rows == 32 ? pick_g<D, BF, 2, T0>(G) : pick_g<D, BF, 1, T0>(G);
-    if (tpw == T0 + 1) return rows == 32 ? pick_g<D, BF, 2, T0 + 1>(G) : pick_g<D, BF, 1, T0 + 1>(G);
+    if (dma) {
+        if constexpr (BF) {
+            if (tpw == T0) return rows == 32 ? pick_g<D, BF, 2, T0, true>(G) : pick_g<D, BF, 1, T0, true>(G);
+        }
+        return nullptr;
+    }
+    if (tpw == T0) return rows == 32 ? pick_g<D, BF, 2, T0, false>(G) : pick_g<D, BF, 1, T0, false>(G);
+    if (tpw == T0 + 1)
+        return rows == 32 ? pick_g<D, BF, 2, T0 + 1, false>(G) : pick_g<D, BF, 1, T0 + 1, false>(G);
     return nullptr;
 }
 

@@ -96,6 +96,12 @@ static sp_status plan_uncached(const sp_score_desc& d, long long M, int cus, Sco
         }
     }
     if (bg == 0) return SP_EUNSUPPORTED;
+    // bf16 at the base tile count streams K by DMA into LDS when its slots,
+    // with the full deferral, fit
+    p.dma = bf && btpw == tpw0 &&
+            score_lds_layout(kMaxDefer + 1, btpw, p.rows, row_bytes, d.N, bkr, true).total +
+                    dma_static_lds(p.rows, row_bytes) <= kLdsBytes;
+    if (p.dma) bdef = kMaxDefer;
     p.tpw = btpw;
     p.cap = kStreamWaves * btpw * kTileKeys;
     p.g = bg;
@@ -106,7 +112,7 @@ static sp_status plan_uncached(const sp_score_desc& d, long long M, int cus, Sco
     if (p.ncomb > kMaxCombiners) p.ncomb = kMaxCombiners;
     p.grid = bg * bng + p.ncomb;
     p.cus = cus;
-    p.lds = score_lds_layout(bdef + 1, btpw, p.rows, row_bytes, d.N, bkr);
+    p.lds = score_lds_layout(bdef + 1, btpw, p.rows, row_bytes, d.N, bkr, p.dma);
     p.ws_err = 0;      // error word; then at +128 one slice counter per rank (g <= kMaxRanks)
     p.ws_part = 2048;
     p.ws_tail = p.ws_part + round_up((size_t)p.units * p.g * p.rows * 8, 256);
