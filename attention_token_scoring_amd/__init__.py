@@ -183,9 +183,9 @@ def sp_select_workspace_bytes(R: int, total_prompt_len: int, params: SelectParam
 
 
 def sp_score_plan(desc: ScoreDesc, M: int) -> dict:
-    info = (ctypes.c_int32 * 8)()
+    info = (ctypes.c_int32 * 9)()
     _check(load_library().sp_score_plan(ctypes.byref(desc), int(M), info), "sp_score_plan")
-    keys = ("grid", "g", "ngroups", "keys_per_wg", "rows", "units", "cus", "defer")
+    keys = ("grid", "g", "ngroups", "keys_per_wg", "rows", "units", "cus", "defer", "dma")
     return {k: int(info[i]) for i, k in enumerate(keys)}
 
 

@@ -242,7 +242,7 @@ sp_status sp_score_status(const void* ws, void* stream, int32_t* timed_out) {
     return SP_OK;
 }
 
-sp_status sp_score_plan(const sp_score_desc* desc, int32_t M, int32_t info[8]) {
+sp_status sp_score_plan(const sp_score_desc* desc, int32_t M, int32_t info[9]) {
     sp_status s = check_desc(desc);
     if (s != SP_OK) return s;
     if (!info) return SP_EINVAL;
@@ -258,6 +258,7 @@ sp_status sp_score_plan(const sp_score_desc* desc, int32_t M, int32_t info[8]) {
     info[5] = p.units;
     info[6] = cus > 0 ? cus : kDefaultCUs;
     info[7] = p.defer;
+    info[8] = p.dma ? 1 : 0;
     return SP_OK;
 }
 

@@ -66,7 +66,9 @@ inline ScoreLds score_lds_layout(int nbk, int tpw, int rows, int row_bytes, int 
     l.bank = 0;
     // the running maxima are written once, at the end, over the banks
     l.trun = 0;
-    const int banks = dma ? kStreamWaves * tpw * kTileKeys * row_bytes
+    // (DMA slots per wave: one per tile, at most 4 for 256-byte rows)
+    const int slots = (row_bytes >= 256 && tpw > 4) ? 4 : tpw;
+    const int banks = dma ? kStreamWaves * slots * kTileKeys * row_bytes
                           : nbk * kStreamWaves * tpw * 64 * nh * 8;
     if (dma) {
         // only the K slots (and, at the end, the running maxima over them) are

@@ -215,6 +215,9 @@ struct Cfg {
     // sit in G adjacent lanes of one half
     static_assert(G <= 16 || (G == 32 && NH == 2), "unsupported head grouping");
     static constexpr int GL = G == 32 ? 16 : G;  // heads of a step within one half
+    // DMA slots per streaming wave: one per tile of the slice, at most 4 for
+    // 256-byte key rows (the LDS holds 7 x 4 tiles of 4 KB besides the rest)
+    static constexpr int S = !DMA ? 0 : (KB >= 256 && TPW > 4 ? 4 : TPW);
 };
 
 // s_waitcnt operands (gfx9 encoding): vector memory count n, nothing else
@@ -459,20 +462,24 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
         // covering whole 128-byte lines of consecutive key rows; a tile is
         // stored with its 16-byte chunks XOR-swizzled by row, so that the
         // MFMA-layout reads (16 rows x one chunk column) hit every bank once.
-        // Each wave owns one LDS slot per tile of its slice; the slot of tile t
-        // is refilled with tile t of the next unit as soon as its reads are
-        // done, so a unit is always in flight (the outstanding load count,
-        // TPW - 1 tiles, is the same before every tile). Parked logits stay in
-        // registers (NB banks, the step loop unrolled by NB), and the per-step
-        // barrier waits for LDS only, never for the loads in flight.
+        // Each wave streams its tiles q = it * TPW + t through S LDS slots
+        // (tile q in slot q % S); a slot is refilled with tile q + S as soon
+        // as tile q's reads are done, so S - 1 tiles are always in flight and
+        // the outstanding load count before every tile is the same. With the
+        // step loop unrolled by NB (a multiple of S), slots and refills are
+        // compile-time constants. Parked logits stay in registers (NB banks),
+        // and the per-step barrier waits for LDS only, never for the loads in
+        // flight.
         constexpr int TB = kTileKeys * C::KB;  // bytes of one 16-key tile
         constexpr int CPR = C::KB / 16;         // 16-byte chunks per key row
         constexpr int RPI = 64 / CPR;           // key rows one load instruction covers
         constexpr int SWZ = 16 / CPR;           // rows sharing one 64-bank line
         constexpr int NB = kMaxDefer + 1;       // register banks of parked logits
-        constexpr int VM_AHEAD = (TPW - 1) * NLD;  // loads issued after a tile's own
+        constexpr int S = C::S;                 // LDS slots of this wave
+        constexpr int VM_AHEAD = (S - 1) * NLD; // loads issued after a tile's own
         static_assert(RPI * NLD == kTileKeys, "tile load shape");
-        char* ring = smem + a.lds.bank + (size_t)w * TPW * TB;
+        static_assert(S <= TPW && NB % S == 0 || S == TPW, "slots must be static in the unrolled loop");
+        char* ring = smem + a.lds.bank + (size_t)w * S * TB;
         const int ntv = min(max((ntiles - w + SW - 1) / SW, 0), TPW);
         const int tpart = (nkeys % kTileKeys != 0 && ntv > 0 && w + SW * (ntv - 1) == ntiles - 1) ? ntv - 1 : -1;
         const int rem = nkeys - (w + SW * max(tpart, 0)) * kTileKeys - 4 * g4;
@@ -493,9 +500,10 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
 #pragma unroll
         for (int t = 0; t < TPW; ++t)
             tbo[t] = t < ntv ? (uint32_t)(r0 + (w + SW * t) * kTileKeys) * (uint32_t)C::KB : kOob;
-        auto issue_tile = [&](__amdgpu_buffer_rsrc_t rs, int t) __attribute__((always_inline)) {
+        // tile t of a unit (plane rs) into LDS slot sl
+        auto issue_tile = [&](__amdgpu_buffer_rsrc_t rs, int t, int sl) __attribute__((always_inline)) {
 #pragma unroll
-            for (int s = 0; s < NLD; ++s) dma_load16(rs, ring + t * TB + s * 1024, loff[s], tbo[t]);
+            for (int s = 0; s < NLD; ++s) dma_load16(rs, ring + sl * TB + s * 1024, loff[s], tbo[t]);
         };
 
         constexpr int NHF = G == 32 ? 1 : NH;
@@ -514,9 +522,10 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
         int park[NB][TPW][2 * NH];  // parked logits of the last NB units (16-bit codes, 2 per word)
         f32x4 acc[TPW][NH];
         {
+            // tiles 0..S-1 (of unit 0) into slots 0..S-1
             const auto rs = plane_rsrc(a, unit_of(0), plane_bytes, C::ESZ);
 #pragma unroll
-            for (int t = 0; t < TPW; ++t) issue_tile(rs, t);
+            for (int t = 0; t < S; ++t) issue_tile(rs, t, t);
         }
         step_barrier<C>();  // Q of unit 0 is staged
 
@@ -528,23 +537,27 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
 #pragma unroll
                 for (int s = 0; s < NLD; ++s)
                     qf[hf][s] = *(const i32x4*)(qlds + (P * ROWS + hf * 16 + (lane & 15)) * C::QS + 16 * g4 + 64 * s);
+            const auto rs0 = plane_rsrc(a, unit_of(it), plane_bytes, C::ESZ);
             const auto rs1 = plane_rsrc(a, unit_of(it + 1), plane_bytes, C::ESZ);
 #pragma unroll
             for (int t = 0; t < TPW; ++t) {
+                // tile q = it TPW + t sits in slot q % S; (it % NB = B is static)
+                const int sl = (B * TPW + t) % S;
                 __builtin_amdgcn_s_waitcnt(vm_wait(VM_AHEAD));  // this tile's loads have landed
                 i32x4 kf[NLD];
 #pragma unroll
-                for (int s = 0; s < NLD; ++s) kf[s] = *(const i32x4*)(ring + t * TB + roff[s]);
+                for (int s = 0; s < NLD; ++s) kf[s] = *(const i32x4*)(ring + sl * TB + roff[s]);
 #pragma unroll
                 for (int hf = 0; hf < NH; ++hf) acc[t][hf] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int s = 0; s < NLD; ++s)
 #pragma unroll
                     for (int hf = 0; hf < NH; ++hf) mma<C>(acc[t][hf], qf[hf][s], kf[s]);
-                // the slot's reads are done: refill it with the same tile of the next unit
+                // the slot's reads are done: refill it with tile q + S (tile
+                // (t + S) % TPW of this unit or the next)
                 __builtin_amdgcn_s_waitcnt(kLgkmWait0);
                 __atomic_signal_fence(__ATOMIC_SEQ_CST);
-                issue_tile(rs1, t);
+                issue_tile(t + S < TPW ? rs0 : rs1, (t + S) % TPW, sl);
             }
             // per wave-row statistics over this wave's keys of the slice (as in
             // the register-ring variant) and the shifted log2 logits in acc
@@ -1195,6 +1208,8 @@ const void* pick_kernel_for(int rows, int G, int tpw, bool dma) {
     if (dma) {
         if constexpr (BF) {
             if (tpw == T0) return rows == 32 ? pick_g<D, BF, 2, T0, true>(G) : pick_g<D, BF, 1, T0, true>(G);
+            if (tpw == T0 + 1)
+                return rows == 32 ? pick_g<D, BF, 2, T0 + 1, true>(G) : pick_g<D, BF, 1, T0 + 1, true>(G);
         }
         return nullptr;
     }

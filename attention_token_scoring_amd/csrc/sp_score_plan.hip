@@ -96,9 +96,9 @@ static sp_status plan_uncached(const sp_score_desc& d, long long M, int cus, Sco
         }
     }
     if (bg == 0) return SP_EUNSUPPORTED;
-    // bf16 at the base tile count streams K by DMA into LDS when its slots,
-    // with the full deferral, fit
-    p.dma = bf && btpw == tpw0 &&
+    // bf16 streams K by DMA into LDS when its slots, with the full deferral,
+    // fit
+    p.dma = bf &&
             score_lds_layout(kMaxDefer + 1, btpw, p.rows, row_bytes, d.N, bkr, true).total +
                     dma_static_lds(p.rows, row_bytes) <= kLdsBytes;
     if (p.dma) bdef = kMaxDefer;

@@ -354,11 +354,12 @@ const char* sp_status_string(sp_status status);
  * tests): info[0] workgroups, info[1] workgroups per (layer, kv-head) unit,
  * info[2] groups working in parallel, info[3] prompt keys per workgroup,
  * info[4] query rows per tile (16 or 32), info[5] units, info[6] device
- * compute units, info[7] units between streaming a unit and finishing it.
+ * compute units, info[7] units between streaming a unit and finishing it,
+ * info[8] 1 if K tiles travel by DMA into LDS (else a register ring).
  * Workgroups beyond info[1] * info[2] combine the per-unit statistics. No
  * device work is enqueued.
  */
-sp_status sp_score_plan(const sp_score_desc* desc, int32_t M, int32_t info[8]);
+sp_status sp_score_plan(const sp_score_desc* desc, int32_t M, int32_t info[9]);
 
 /*
  * Profiling aid, not part of the scoring computation. While set, every
