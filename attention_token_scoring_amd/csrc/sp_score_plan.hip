@@ -84,7 +84,18 @@ static sp_status plan_uncached(const sp_score_desc& d, long long M, int cus, Sco
                                 (roomy && kr < cap ? wave_partial : 0.0);
             const double hbm = (double)(g * ng) * kr * bytes_per_key / bw_total;
             const double sync = (kMaxDefer - defer) * 1.0e-6;
-            const double cost = iters * ((wave > hbm ? wave : hbm) + sync);
+            double cost = iters * ((wave > hbm ? wave : hbm) + sync);
+            if (bf && score_lds_layout(kMaxDefer + 1, tpw, p.rows, row_bytes, d.N, (int)kr, true).total +
+                              dma_static_lds(p.rows, row_bytes) <= kLdsBytes) {
+                // K by DMA (measured on the MI355X at the 8B shape): a step
+                // streams at the full read rate (~7.1 TB/s once ~200 CUs
+                // stream) plus ~0.28 us of per-step work that does not
+                // overlap; waves with fewer tiles than the others (a slice
+                // that is not a whole number of tiles per wave) add ~0.12 us
+                const double bw = 7.1e12 * ((double)(g * ng) < 200.0 ? (double)(g * ng) / 200.0 : 1.0);
+                const bool whole = kr % (kStreamWaves * kTileKeys) == 0 || g == 1;
+                cost = iters * ((double)(g * ng) * kr * bytes_per_key / bw + 0.28e-6 + (whole ? 0.0 : 0.12e-6));
+            }
             if (cost < best * 0.999) {
                 best = cost;
                 bg = (int)g;
