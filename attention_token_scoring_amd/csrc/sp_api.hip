@@ -16,7 +16,8 @@ namespace sp {
 
 hipError_t launch_score(const ScorePlan& p, const sp_score_desc& d, const void* Q, const void* K,
                         long long plane_stride, int M, int M_out, float* importance, void* ws,
-                        bool first, int tail_n, int blend_n, hipStream_t stream);
+                        unsigned call_epoch, bool first, int tail_n, int blend_n, hipStream_t stream);
+unsigned next_epoch();
 hipError_t launch_gather(const void* src, long long row_bytes, const int32_t* kept,
                          const int32_t* n_kept, int R, const int64_t* cu, long long max_rows,
                          void* dst, hipStream_t stream);
@@ -173,6 +174,7 @@ sp_status score_batch(const sp_score_desc* desc, int32_t R, const void* Q, const
     const long long T = cu[R] + (long long)R * desc->N;
     const long long qsz = (long long)desc->L * desc->H * desc->N * desc->d * es;
     long long out = 0;
+    const unsigned call = next_epoch();
     for (int r = 0; r < R; ++r) {
         const long long M = cu[r + 1] - cu[r];
         ScorePlan p;
@@ -181,7 +183,7 @@ sp_status score_batch(const sp_score_desc* desc, int32_t R, const void* Q, const
         const char* Kr = (const char*)K + (cu[r] + (long long)r * desc->N) * desc->d * es;
         const long long M_out = keep ? keep[r] : M;
         float* imp = importance + (keep ? out : cu[r]);
-        s = to_status(launch_score(p, *desc, Qr, Kr, T * desc->d, (int)M, (int)M_out, imp, ws,
+        s = to_status(launch_score(p, *desc, Qr, Kr, T * desc->d, (int)M, (int)M_out, imp, ws, call,
                                    r == 0, desc->N, 0, (hipStream_t)stream));
         if (s != SP_OK) return s;
         out += M_out;
@@ -233,12 +235,13 @@ sp_status sp_set_wait_limit(uint64_t ticks) {
 
 sp_status sp_score_status(const void* ws, void* stream, int32_t* timed_out) {
     if (!ws || !timed_out) return SP_EINVAL;
-    int32_t v = 0;
-    // (the error word sits at the start of the workspace, see make_plan)
-    if (hipMemcpyAsync(&v, ws, sizeof(v), hipMemcpyDeviceToHost, (hipStream_t)stream) != hipSuccess)
+    // The workspace starts with the error word ((call epoch << 32) | 1 once a
+    // wait timed out) and, at byte 8, the epoch of the last call.
+    unsigned long long v[2] = {0ull, 0ull};
+    if (hipMemcpyAsync(v, ws, sizeof(v), hipMemcpyDeviceToHost, (hipStream_t)stream) != hipSuccess)
         return SP_EDEVICE;
     if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return SP_EDEVICE;
-    *timed_out = v != 0 ? 1 : 0;
+    *timed_out = (v[0] & 1ull) != 0ull && (unsigned)(v[0] >> 32) == (unsigned)v[1] ? 1 : 0;
     return SP_OK;
 }
 
@@ -275,8 +278,8 @@ sp_status sp_score(const sp_score_desc* desc, const void* Q, const void* K, int3
     if (s != SP_OK) return s;
     if (!ws || !aligned(ws, 256) || ws_bytes < p.ws_total) return SP_EWORKSPACE;
     const long long plane = (long long)(M + desc->N) * desc->d;
-    return to_status(launch_score(p, *desc, Q, K, plane, M, M, importance, ws, true, desc->N, 0,
-                                  (hipStream_t)stream));
+    return to_status(launch_score(p, *desc, Q, K, plane, M, M, importance, ws, next_epoch(), true,
+                                  desc->N, 0, (hipStream_t)stream));
 }
 
 sp_status sp_score_noalloc(const sp_score_desc* desc, const void* Q, const void* K, int32_t M,
@@ -301,7 +304,7 @@ sp_status sp_score_noalloc(const sp_score_desc* desc, const void* Q, const void*
     if (g_scratch_err[dev] != hipSuccess || !g_scratch_ptr[dev]) return SP_EDEVICE;
     const long long plane = (long long)(M + desc->N) * desc->d;
     return to_status(launch_score(p, *desc, Q, K, plane, M, M, importance, g_scratch_ptr[dev],
-                                  true, desc->N, 0, (hipStream_t)stream));
+                                  next_epoch(), true, desc->N, 0, (hipStream_t)stream));
 }
 
 sp_status sp_score_lastrow(const sp_score_desc* desc, const void* Q, const void* Q_last,
@@ -326,10 +329,11 @@ sp_status sp_score_lastrow(const sp_score_desc* desc, const void* Q, const void*
     if (!ws || !aligned(ws, 256) || ws_bytes < p.ws_total || ws_bytes < p1.ws_total)
         return SP_EWORKSPACE;
     const long long plane = (long long)(M + desc->N) * desc->d;
-    s = to_status(launch_score(p, *desc, Q, K, plane, M, M, importance, ws, true, desc->N, 0,
+    const unsigned call = next_epoch();
+    s = to_status(launch_score(p, *desc, Q, K, plane, M, M, importance, ws, call, true, desc->N, 0,
                                (hipStream_t)stream));
     if (s != SP_OK) return s;
-    return to_status(launch_score(p1, d1, Q_last, K, plane, M, M, importance, ws, false, 0,
+    return to_status(launch_score(p1, d1, Q_last, K, plane, M, M, importance, ws, call, false, 0,
                                   desc->N, (hipStream_t)stream));
 }
 

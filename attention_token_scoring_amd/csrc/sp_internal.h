@@ -17,9 +17,15 @@ constexpr int kWaves = 8;
 constexpr int kStreamWaves = 7;
 constexpr int kThreads = kWaves * 64;
 constexpr int kTileKeys = 16;
-// Workgroups sharing a unit: at most this many (the combiner gathers 8 waves x
-// 2 lane groups x 32 ranks; the workspace header holds one counter per slice).
-constexpr int kMaxRanks = 480;
+// Ranks (partials) one combiner lane polls at once, and the workgroups that can
+// share a unit: at most what a combiner workgroup gathers in one batch
+// (8 waves x 2 lane groups x kCombinerBatch ranks at 32 query rows).
+constexpr int kCombinerBatch = 16;
+constexpr int kMaxRanks = kWaves * 2 * kCombinerBatch;
+// The workspace header: the error word at byte 0, the last call's epoch at 8,
+// and from byte 128 one 8-byte flag per streaming workgroup (rank x group).
+constexpr int kHeaderBytes = 4096;
+constexpr int kMaxFlags = (kHeaderBytes - 128) / 8;
 constexpr int kMaxDefer = 3;          // units between streaming and finishing a unit
 constexpr int kLdsBytes = 160 * 1024;  // LDS of one CU
 constexpr int kDefaultCUs = 256;       // MI355X; used when no device can be queried
@@ -93,11 +99,19 @@ struct ScoreArgs {
     const void* K;             // key row 0 of (layer 0, kv-head 0) of this request
     long long plane_stride;    // elements between consecutive (layer, kv-head) key planes
     int* Tg;                   // [ngroups][N][M]: per-group running max of log2 probabilities, in code steps
-    float2* part;              // [units][g][rows]: per-workgroup (row max, row sum); sentinel until published
-    float2* tail;              // [units][rows]: the look-ahead keys' (row max, row sum)
-    float* lse;                // [units][rows]: each row's log2-sum-exp2; sentinel until published
-    int* err;                  // [1]: set when a wait times out
-    unsigned* done;            // [g]: groups done with each key slice (0 at launch)
+    // Synchronisation slots carry the epoch of the launch that wrote them in
+    // the high 32 bits of each 8-byte word, so a slot left by an earlier
+    // launch is never taken for this one's and nothing is reset in between
+    // (epochs are distinct, non-zero and scattered over 32 bits; a slot counts
+    // as written only when both of its words carry the epoch, so leftover
+    // bytes pass for one with odds of about 2^-64).
+    unsigned long long* part;  // [units][g][rows][2]: per-workgroup (row max | epoch), (row sum | epoch)
+    unsigned long long* lse;   // [units][rows][2]: each row's (log2-sum-exp2 | epoch), twice
+    unsigned long long* err;   // [1]: (call epoch << 32) | 1 once a wait of the call has timed out
+    unsigned* hdr;             // [1]: the epoch of the last call (for sp_score_status)
+    unsigned long long* flags; // [g][ngroups]: (epoch << 32) | epoch once a group's running maxima are in Tg
+    unsigned epoch;            // this launch's tag
+    unsigned call_epoch;       // the call's tag (shared by its launches: the error word spans the call)
     float* importance;         // [M]: the output
     int M_out;                 // only importance[0..M_out) is written (M_out <= M)
     int L, H, Hkv, G, N, M, d;
@@ -109,8 +123,7 @@ struct ScoreArgs {
     int nbk;                   // D + 1 banks of parked logits
     ScoreLds lds;
     float c;                   // scale * log2(e)
-    int reset_err;             // 1: the prep kernel clears the error word (first request of a call)
-    int tail_n;                // look-ahead keys after the prompt that the rows see causally (N, or 0)
+    int tail_n;                // look-ahead keys after the prompt, seen causally (N; 0: none)
     int blend_n;               // 0: write the scores; n > 0: importance = (n importance + score) / (n + 1)
     unsigned long long spin_ticks;  // limit of a bounded wait, in ticks of the 100 MHz clock
 };
@@ -126,7 +139,7 @@ struct ScorePlan {
     int defer;
     int cus;       // compute units of the device planned for
     ScoreLds lds;
-    size_t ws_err, ws_part, ws_tail, ws_lse, ws_tg, ws_total;  // byte offsets / sizes in the workspace
+    size_t ws_err, ws_part, ws_lse, ws_tg, ws_total;  // byte offsets / sizes in the workspace
 };
 
 // Selection of one request (one workgroup).

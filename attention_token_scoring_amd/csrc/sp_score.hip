@@ -1,81 +1,19 @@
-// Scoring: the small kernel before the scoring kernel (prep: per-unit
-// synchronisation state and the look-ahead keys' statistics) and the launch
-// sequence. The method and the scoring kernel are described in
-// sp_score_kernel.h.
+// Scoring: the launch sequence (the method and the scoring kernel are
+// described in sp_score_kernel.h).
+#include <atomic>
+
 #include "sp_score_kernel.h"
 
 namespace sp {
 
-// Before the scoring kernel: reset its synchronisation state (every
-// partial and log-sum-exp slot to the sentinel, the error word), and compute
-// for every unit and query row the share of the look-ahead keys M..M+N-1 in the
-// row's softmax denominator (row j sees look-ahead key t iff t <= j), as a raw
-// max and a sum of exp2((x - max) * c). One 256-thread block per unit: one
-// thread per (row, look-ahead key) dot product, 16-byte loads.
-template <bool BF16>
-__device__ __forceinline__ float dot16(uint4 q, uint4 k, float acc) {
-    if constexpr (BF16) {
-        const unsigned qa[4] = {q.x, q.y, q.z, q.w}, ka[4] = {k.x, k.y, k.z, k.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            acc = fmaf(__uint_as_float(qa[i] << 16), __uint_as_float(ka[i] << 16), acc);
-            acc = fmaf(__uint_as_float(qa[i] & 0xffff0000u), __uint_as_float(ka[i] & 0xffff0000u), acc);
-        }
-    } else {
-        acc = fmaf(__uint_as_float(q.x), __uint_as_float(k.x), acc);
-        acc = fmaf(__uint_as_float(q.y), __uint_as_float(k.y), acc);
-        acc = fmaf(__uint_as_float(q.z), __uint_as_float(k.z), acc);
-        acc = fmaf(__uint_as_float(q.w), __uint_as_float(k.w), acc);
-    }
-    return acc;
-}
-
-template <bool BF16, int D>
-__global__ __launch_bounds__(256) void score_prep_kernel(ScoreArgs a, int rows) {
-    __shared__ float logit[32][33];  // [row][look-ahead key]
-    const int u = blockIdx.x, tid = threadIdx.x;
-    if (u == 0 && tid == 0 && a.reset_err) *a.err = 0;
-    if (u == 0)
-        for (int x = tid; x < a.g; x += 256) a.done[x] = 0u;
-    // this unit's g * rows partial slots, two per 16-byte store
-    uint4* slots = (uint4*)(a.part + (size_t)u * a.g * rows);
-    for (int x = tid; x < a.g * rows / 2; x += 256) slots[x] = make_uint4(~0u, ~0u, ~0u, ~0u);
-    if (tid < rows) ((unsigned*)a.lse)[(size_t)u * rows + tid] = kSentinel32;
-
-    const int l = u / a.Hkv, kvh = u % a.Hkv;
-    constexpr int esz = BF16 ? 2 : 4;
-    const char* kp = (const char*)a.K + ((long long)u * a.plane_stride + (long long)a.M * a.d) * esz;
-    constexpr int n16 = D * esz / 16;  // (all of a row's loads in flight at once)
-    for (int x = tid; x < rows * a.N; x += 256) {
-        const int row = x / a.N, t = x % a.N;
-        const int j = row / a.G, hl = row % a.G;
-        if (j < a.N && t <= j && t < a.tail_n) {
-            const long long qrow = ((long long)l * a.H + (long long)kvh * a.G + hl) * a.N + j;
-            const uint4* q = (const uint4*)((const char*)a.Q + qrow * D * esz);
-            const uint4* k = (const uint4*)(kp + (long long)t * D * esz);
-            uint4 qv[n16], kv[n16];
-#pragma unroll
-            for (int e = 0; e < n16; ++e) {
-                qv[e] = q[e];
-                kv[e] = k[e];
-            }
-            float acc = 0.f;
-#pragma unroll
-            for (int e = 0; e < n16; ++e) acc = dot16<BF16>(qv[e], kv[e], acc);
-            logit[row][t] = acc;
-        }
-    }
-    __syncthreads();
-    if (tid < rows) {
-        const int j = tid / a.G;
-        float m = -INFINITY, s = 0.f;
-        const int nt = min(j + 1, a.tail_n);  // look-ahead keys row j sees
-        if (j < a.N) {
-            for (int t = 0; t < nt; ++t) m = fmaxf(m, logit[tid][t]);
-            for (int t = 0; t < nt; ++t) s += exp2_hw(fmaf(logit[tid][t], a.c, -m * a.c));
-        }
-        a.tail[(size_t)u * rows + tid] = make_float2(m, s);
-    }
+// Under stream capture a launch's epoch is fixed into the graph, and every
+// replay would reuse it: a small kernel captured before the scoring kernel
+// clears the tagged words (counters, partial and log-sum-exp slots; the
+// error word only before a call's first launch), so that each replay starts
+// from slots that no epoch matches.
+__global__ __launch_bounds__(256) void clear_tags_kernel(uint4* p, size_t n16) {
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256)
+        p[i] = make_uint4(0u, 0u, 0u, 0u);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -102,28 +40,48 @@ void set_profile_events(hipEvent_t before, hipEvent_t after) {
 
 void set_wait_limit(unsigned long long ticks) { t_wait_limit = ticks; }
 
-// One request: prep (reset synchronisation state, look-ahead statistics; the
-// error word only for the first request of a call, so that it reports a time-out
-// in any request of the call),
-// then the scoring kernel, which also writes the importance: an ordinary
-// launch (every workgroup resident on an otherwise idle device) or, if the
-// descriptor asks for it, a cooperative one.
+// Epochs: a process-wide launch count passed through a bijective 32-bit
+// integer mix (the "lowbias32" function of Wellons' hash-prospector), so that
+// no two launches of the process share one, and leftover data in a workspace
+// (small integers, a constant fill, earlier epochs) does not pass for the
+// current one. 0 and ~0 are skipped.
+static std::atomic<unsigned> g_launches{0};
+
+unsigned next_epoch() {
+    for (;;) {
+        unsigned x = g_launches.fetch_add(1u, std::memory_order_relaxed) + 1u;
+        x ^= x >> 16;
+        x *= 0x7feb352du;
+        x ^= x >> 15;
+        x *= 0x846ca68bu;
+        x ^= x >> 16;
+        if (x != 0u && x != ~0u) return x;
+    }
+}
+
+// One launch of the scoring kernel (which also writes the importance): an
+// ordinary launch (every workgroup resident on an otherwise idle device) or,
+// if the descriptor asks for it, a cooperative one. call_epoch tags the
+// call's error word (shared by all its launches); first: the call's first
+// launch.
 hipError_t launch_score(const ScorePlan& p, const sp_score_desc& d, const void* Q, const void* K,
                         long long plane_stride, int M, int M_out, float* importance, void* ws,
-                        bool first, int tail_n, int blend_n, hipStream_t stream) {
+                        unsigned call_epoch, bool first, int tail_n, int blend_n, hipStream_t stream) {
     char* base = (char*)ws;
     ScoreArgs a;
     a.Q = Q;
     a.K = K;
     a.plane_stride = plane_stride;
-    a.err = (int*)(base + p.ws_err);
-    a.done = (unsigned*)(base + p.ws_err + 128);
+    a.err = (unsigned long long*)(base + p.ws_err);
+    a.hdr = (unsigned*)(base + p.ws_err + 8);
+    a.flags = (unsigned long long*)(base + p.ws_err + 128);
     a.importance = importance;
     a.M_out = M_out;
-    a.part = (float2*)(base + p.ws_part);
-    a.tail = (float2*)(base + p.ws_tail);
-    a.lse = (float*)(base + p.ws_lse);
+    a.part = (unsigned long long*)(base + p.ws_part);
+    a.lse = (unsigned long long*)(base + p.ws_lse);
     a.Tg = (int*)(base + p.ws_tg);
+    a.epoch = next_epoch();
+    a.call_epoch = call_epoch;
     a.L = d.L;
     a.H = d.H;
     a.Hkv = d.Hkv;
@@ -140,7 +98,6 @@ hipError_t launch_score(const ScorePlan& p, const sp_score_desc& d, const void* 
     a.lds = p.lds;
     const float scale = d.scale > 0.f ? d.scale : 1.0f / sqrtf((float)d.d);
     a.c = scale * 1.4426950408889634f;
-    a.reset_err = first ? 1 : 0;
     a.tail_n = tail_n;
     a.blend_n = blend_n;
     a.spin_ticks = t_wait_limit > 0 ? t_wait_limit : kSpinTicks;
@@ -150,19 +107,17 @@ hipError_t launch_score(const ScorePlan& p, const sp_score_desc& d, const void* 
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, p.lds.total);
     if (e != hipSuccess) return e;
 
-    if (d.dtype == SP_BF16) {
-        if (d.d == 128)
-            hipLaunchKernelGGL((score_prep_kernel<true, 128>), dim3(p.units), dim3(256), 0, stream, a, p.rows);
-        else
-            hipLaunchKernelGGL((score_prep_kernel<true, 64>), dim3(p.units), dim3(256), 0, stream, a, p.rows);
-    } else {
-        if (d.d == 128)
-            hipLaunchKernelGGL((score_prep_kernel<false, 128>), dim3(p.units), dim3(256), 0, stream, a, p.rows);
-        else
-            hipLaunchKernelGGL((score_prep_kernel<false, 64>), dim3(p.units), dim3(256), 0, stream, a, p.rows);
-    }
-    e = hipGetLastError();
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    e = hipStreamIsCapturing(stream, &cap);
     if (e != hipSuccess) return e;
+    if (cap != hipStreamCaptureStatusNone) {
+        const size_t lo = first ? 0 : 16;  // (keep the call's error word)
+        const size_t n16 = (p.ws_tg - lo) / 16;
+        hipLaunchKernelGGL(clear_tags_kernel, dim3((unsigned)((n16 + 255) / 256 < 1024 ? (n16 + 255) / 256 : 1024)),
+                           dim3(256), 0, stream, (uint4*)(base + lo), n16);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     void* args[] = {&a};
     if (t_ev_before) {
         e = hipEventRecord(t_ev_before, stream);

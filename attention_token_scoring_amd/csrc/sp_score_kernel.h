@@ -68,10 +68,7 @@ constexpr unsigned long long kSpinTicks = 200000000ull;
 constexpr unsigned long long kAbortTicks = 10000ull;
 // Buffer offset that is always out of range: loads there return zeros.
 constexpr uint32_t kOob = 0x7ffffff0u;
-// Content of a partial-statistics or log-sum-exp slot that has not been
-// published yet (a NaN pattern no published value has).
-constexpr unsigned long long kSentinel = ~0ull;
-constexpr unsigned kSentinel32 = ~0u;
+
 // Bits of the quiet NaN written in place of the scores of a call that timed out.
 constexpr unsigned kNaNBits = 0x7fc00000u;
 
@@ -149,10 +146,50 @@ __device__ __forceinline__ unsigned ld32(const void* p) {
     return __hip_atomic_load((unsigned*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// A 32-bit value in the low half of a slot, the epoch of its launch in the high half.
+__device__ __forceinline__ unsigned long long tagged(float v, unsigned epoch) {
+    return (unsigned long long)__float_as_uint(v) | ((unsigned long long)epoch << 32);
+}
+__device__ __forceinline__ bool tag_is(unsigned long long v, unsigned epoch) {
+    return (unsigned)(v >> 32) == epoch;
+}
+__device__ __forceinline__ float tag_value(unsigned long long v) { return __uint_as_float((unsigned)v); }
+__device__ __forceinline__ void st64u(void* p, unsigned long long v) {
+    __hip_atomic_store((unsigned long long*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The call's error word: set once a bounded wait of any of its launches has
+// timed out.
+template <class A>
+__device__ __forceinline__ bool err_set(const A& a) {
+    const unsigned long long v = ld64(a.err);
+    return tag_is(v, a.call_epoch) && (v & 1ull) != 0ull;
+}
+template <class A>
+__device__ __forceinline__ void set_err(const A& a) {
+    st64u(a.err, ((unsigned long long)a.call_epoch << 32) | 1ull);
+}
+
+// A streaming wave's tiles are w, w + SW, ... (ntv of them in the slice).
+// masked_tile: the one that needs per-key masks (its last, when that reaches
+// past the nall keys every row sees), else -1. The keys past nall (at most
+// N - 1 look-ahead keys and the slice's ragged end) span at most three
+// consecutive tiles, so no wave has two of them.
+__device__ __forceinline__ int masked_tile(int ntv, int w, int nall) {
+    return ntv > 0 && (w + kStreamWaves * (ntv - 1) + 1) * kTileKeys > nall ? ntv - 1 : -1;
+}
+// Keys of tile `tile` (of the slice [r0, r1)) that step j sees, counted from
+// this lane's first key in it (4 (lane / 16)); step j sees keys < M + j + 1.
+__device__ __forceinline__ int visible_keys(const ScoreArgs& a, int r0, int r1, int j, int tile) {
+    const int lane = (int)(threadIdx.x & 63);
+    return min(r1, a.M + j + 1) - r0 - tile * kTileKeys - 4 * (lane >> 4);
+}
+
 // Whether a bounded wait that started at t0 should give up.
-__device__ __forceinline__ bool wait_expired(unsigned long long t0, const ScoreArgs& a) {
+template <class A>
+__device__ __forceinline__ bool wait_expired(unsigned long long t0, const A& a) {
     const unsigned long long dt = wall_clock64() - t0;
-    return dt > a.spin_ticks || (dt > kAbortTicks && ld32(a.err) != 0u);
+    return dt > a.spin_ticks || (dt > kAbortTicks && err_set(a));
 }
 
 // Parked logits: y = (log2-domain logit) - (row reference) <= 0 as a 16-bit
@@ -318,18 +355,24 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
     const int g4 = lane >> 4;  // lane group
     const float c = a.c;
     const int nstream = a.g * a.ngroups;
+    // (the workspace remembers the last call's epoch, for the status query)
+    if (blockIdx.x == 0 && tid == 0)
+        __hip_atomic_store(a.hdr, a.call_epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
     // ---------------------------------------------------------------------------
     // Combiner workgroups: for units cw, cw + ncw, ... wait until the g
-    // partials are published, combine them with the look-ahead keys' share and
-    // publish each row's log-sum-exp. Lane L handles row L % ROWS for ranks
-    // L / ROWS, L / ROWS + SUBS, ... in batches of B.
+    // partials of this launch are published (both words of a slot carry its
+    // epoch), combine them (the last slice's partial includes the look-ahead
+    // keys) and publish each row's log-sum-exp. Lane L handles row L % ROWS
+    // for ranks L / ROWS, L / ROWS + SUBS, ... in batches of B.
     // ---------------------------------------------------------------------------
     if ((int)blockIdx.x >= nstream) {
-        constexpr int SUBS = 64 / ROWS;
-        constexpr int B = 32;  // ranks polled per lane at once
         const int cg = (int)blockIdx.x - nstream, ncg = (int)gridDim.x - nstream;
+        float2* cred = (float2*)smem;  // [kWaves][ROWS]
+        constexpr int SUBS = 64 / ROWS;
+        constexpr int B = kCombinerBatch;  // ranks polled per lane at once
         const int row = lane % ROWS, sub = lane / ROWS;
+        const unsigned E = a.epoch;
         // Teams of wpu waves share a unit: each wave gathers at most SUBS * B
         // ranks [k_lo, k_hi) in one batch, and the team's first wave combines
         // the team's results through LDS. wpu grows while enough units can
@@ -340,61 +383,62 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
         const int teams = kWaves / wpu, team = w / wpu, wt = w % wpu;
         const int per = (a.g + wpu - 1) / wpu;
         const int k_lo = min(wt * per, a.g), k_hi = min(k_lo + per, a.g);
-        float2* cred = (float2*)smem;  // [kWaves][ROWS]
         for (int ub = cg * teams; ub < a.units; ub += ncg * teams) {
             const int u = ub + team;  // (past the last unit: barriers only)
             float m = -INFINITY, s = 0.f;
-            const unsigned long long* slot =
-                (const unsigned long long*)(a.part + (size_t)u * a.g * ROWS) + row;
+            // (row max, row sum) words of rank k at slot + 2 k ROWS, + 1
+            const unsigned long long* slot = a.part + ((size_t)u * a.g * ROWS + row) * 2;
             const unsigned long long t0 = wall_clock64();
             if (u < a.units && k_lo < k_hi) {
                 // Until this wave's partials start to appear, watch one slot
-                // (its last rank's first row) instead of re-polling all of
-                // them: the combiner CUs' memory queues stay short.
-                const unsigned long long* gate = (const unsigned long long*)(a.part + ((size_t)u * a.g + k_hi - 1) * ROWS);
-                while (ld64(gate) == kSentinel) {
+                // (the sum word of its last rank's first row) instead of
+                // re-polling all of them: the combiner CUs' memory queues stay short.
+                const unsigned long long* gate = a.part + (((size_t)u * a.g + k_hi - 1) * ROWS) * 2 + 1;
+                while (!tag_is(ld64(gate), E)) {
                     __builtin_amdgcn_s_sleep(8);
                     if (wait_expired(t0, a)) {
-                        if (lane == 0) __hip_atomic_store(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        if (lane == 0) set_err(a);
                         break;
                     }
                 }
                 const int k0 = k_lo + sub;
-                unsigned long long v[B];
+                unsigned long long vm[B], vs[B];
                 unsigned long long pend = 0;  // bit x: rank k0 + SUBS x not seen yet
-#pragma unroll
+    #pragma unroll
                 for (int x = 0; x < B; ++x) {
-                    v[x] = kSentinel;
+                    vm[x] = vs[x] = 0ull;
                     if (k0 + SUBS * x < k_hi) pend |= 1ull << x;
                 }
                 while (true) {
-#pragma unroll
+    #pragma unroll
                     for (int x = 0; x < B; ++x)
-                        if ((pend >> x) & 1) v[x] = ld64(slot + (size_t)(k0 + SUBS * x) * ROWS);
+                        if ((pend >> x) & 1) {
+                            const unsigned long long* sl = slot + (size_t)(k0 + SUBS * x) * ROWS * 2;
+                            vm[x] = ld64(sl);
+                            vs[x] = ld64(sl + 1);
+                        }
                     unsigned long long np = 0;
-#pragma unroll
+    #pragma unroll
                     for (int x = 0; x < B; ++x)
-                        if (((pend >> x) & 1) && v[x] == kSentinel) np |= 1ull << x;
+                        if (((pend >> x) & 1) && !(tag_is(vm[x], E) && tag_is(vs[x], E))) np |= 1ull << x;
                     pend = np;
                     if (__ballot(pend != 0) == 0) break;
                     __builtin_amdgcn_s_sleep(2);
                     if (wait_expired(t0, a)) {
-                        if (lane == 0) __hip_atomic_store(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        if (lane == 0) set_err(a);
                         break;
                     }
                 }
                 float mx = -INFINITY;
-#pragma unroll
+    #pragma unroll
                 for (int x = 0; x < B; ++x)
-                    if (k0 + SUBS * x < k_hi && v[x] != kSentinel)
-                        mx = fmaxf(mx, __uint_as_float((unsigned)v[x]));
+                    if (k0 + SUBS * x < k_hi && !((pend >> x) & 1)) mx = fmaxf(mx, tag_value(vm[x]));
                 if (mx != -INFINITY) {
                     float acc = 0.f;
-#pragma unroll
+    #pragma unroll
                     for (int x = 0; x < B; ++x)
-                        if (k0 + SUBS * x < k_hi && v[x] != kSentinel)
-                            acc = fmaf(__uint_as_float((unsigned)(v[x] >> 32)),
-                                       exp2_hw((__uint_as_float((unsigned)v[x]) - mx) * c), acc);
+                        if (k0 + SUBS * x < k_hi && !((pend >> x) & 1))
+                            acc = fmaf(tag_value(vs[x]), exp2_hw((tag_value(vm[x]) - mx) * c), acc);
                     m = mx;
                     s = acc;
                 }
@@ -404,13 +448,13 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
             if (sub == 0) cred[w * ROWS + row] = make_float2(m, s);
             __syncthreads();
             if (u < a.units && wt == 0 && lane < ROWS) {
-                const float2 t = a.tail[(size_t)u * ROWS + lane];
-                float mm = t.x, ss = t.y;
+                float mm = -INFINITY, ss = 0.f;
                 for (int x = 0; x < wpu; ++x)
                     combine(mm, ss, cred[(team * wpu + x) * ROWS + lane].x, cred[(team * wpu + x) * ROWS + lane].y, c);
-                __hip_atomic_store((unsigned*)a.lse + (size_t)u * ROWS + lane,
-                                   __float_as_uint(mm * c + log2_hw(ss)), __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+                // (two tagged copies: a slot is taken only when both words carry the epoch)
+                const unsigned long long v = tagged(mm * c + log2_hw(ss), E);
+                st64u(a.lse + ((size_t)u * ROWS + lane) * 2, v);
+                st64u(a.lse + ((size_t)u * ROWS + lane) * 2 + 1, v);
             }
             __syncthreads();  // (cred is rewritten for the next unit)
         }
@@ -438,9 +482,15 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
     char* qlds = C::DMA ? misc_lds + kMiscQ : smem + a.lds.q;                  // [2][ROWS][QS]
     char* banks = smem + a.lds.bank;                // [nbk][SW][TPW][64][NH][8 B]
 
+    // The slices cover the prompt keys and then the tail_n look-ahead keys
+    // (the last slice holds these): look-ahead key M + i counts in the
+    // softmax of steps j >= i only. nall: keys of the slice every step sees;
+    // nout: prompt keys of the slice (the ones that get scores).
     const int r0 = rank * a.KR;
-    const int r1 = min(r0 + a.KR, a.M);
+    const int r1 = min(r0 + a.KR, a.M + a.tail_n);
     const int nkeys = max(r1 - r0, 0);
+    const int nall = max(min(r1, a.M + 1) - r0, 0);
+    const int nout = max(min(r1, a.M) - r0, 0);
     const int ntiles = (nkeys + kTileKeys - 1) / kTileKeys;
     const uint32_t plane_bytes = (uint32_t)(a.M + a.N) * (uint32_t)C::KB;
     const int D = a.defer, nbk = a.nbk;
@@ -481,8 +531,8 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
         static_assert(S <= TPW && NB % S == 0 || S == TPW, "slots must be static in the unrolled loop");
         char* ring = smem + a.lds.bank + (size_t)w * S * TB;
         const int ntv = min(max((ntiles - w + SW - 1) / SW, 0), TPW);
-        const int tpart = (nkeys % kTileKeys != 0 && ntv > 0 && w + SW * (ntv - 1) == ntiles - 1) ? ntv - 1 : -1;
-        const int rem = nkeys - (w + SW * max(tpart, 0)) * kTileKeys - 4 * g4;
+        const int tpart = masked_tile(ntv, w, nall);
+        const int tile_p = w + SW * max(tpart, 0);  // (its index in the slice)
         const bool full = tpart < 0 && ntv == TPW;
         // DMA side: the lane's byte offset in a tile for load s (row RPI s + lane / CPR,
         // the chunk that lands in LDS column lane % CPR); read side: the LDS offset
@@ -573,7 +623,8 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
                             m = fmaxf(m, mt);
                         } else {
                             if (t == tpart) {
-                                int lim = rem;
+                                // keys of the tile this lane's rows see (4 g4 + r < lim)
+                                int lim = visible_keys(a, r0, r1, (hf * 16 + (lane & 15)) / G, tile_p);
                                 asm volatile("" : "+v"(lim));
                                 mt = -INFINITY;
 #pragma unroll
@@ -601,7 +652,8 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
                             s += st;
                         } else {
                             if (t == tpart) {
-                                int lim = rem;
+                                // keys of the tile this lane's rows see (4 g4 + r < lim)
+                                int lim = visible_keys(a, r0, r1, (hf * 16 + (lane & 15)) / G, tile_p);
                                 asm volatile("" : "+v"(lim));
                                 st = 0.f;
 #pragma unroll
@@ -719,9 +771,8 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
         // slice (the rest are read as zeros and masked); when the slice ends
         // inside tile tpart, that tile's keys past the end are masked too.
         const int ntv = min(max((ntiles - w + SW - 1) / SW, 0), TPW);
-        const int tpart = (nkeys % kTileKeys != 0 && ntv > 0 && w + SW * (ntv - 1) == ntiles - 1) ? ntv - 1 : -1;
-        // keys of tile tpart this lane's C rows may hold (4 g4 + r < rem)
-        const int rem = nkeys - (w + SW * max(tpart, 0)) * kTileKeys - 4 * g4;
+        const int tpart = masked_tile(ntv, w, nall);
+        const int tile_p = w + SW * max(tpart, 0);  // (its index in the slice)
         const bool full = tpart < 0 && ntv == TPW;  // every tile of this wave inside the slice
         uint32_t koff[TPW];  // buffer offset of this lane's first load of tile t
 #pragma unroll
@@ -812,7 +863,8 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
                             m = fmaxf(m, mt);
                         } else {
                             if (t == tpart) {
-                                int lim = rem;
+                                // keys of the tile this lane's rows see (4 g4 + r < lim)
+                                int lim = visible_keys(a, r0, r1, (hf * 16 + (lane & 15)) / G, tile_p);
                                 asm volatile("" : "+v"(lim));  // keep the per-lane compares in this branch
                                 mt = -INFINITY;
 #pragma unroll
@@ -840,7 +892,8 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
                             s += st;
                         } else {
                             if (t == tpart) {
-                                int lim = rem;
+                                // keys of the tile this lane's rows see (4 g4 + r < lim)
+                                int lim = visible_keys(a, r0, r1, (hf * 16 + (lane & 15)) / G, tile_p);
                                 asm volatile("" : "+v"(lim));
                                 st = 0.f;
 #pragma unroll
@@ -1027,36 +1080,47 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
         // (a unit's log-sum-exps appear a few microseconds after the last of
         // its g workgroups has published; one step later they are there)
         constexpr int kLseAhead = 1;
-        unsigned lse_v[2] = {kSentinel32, kSentinel32};
-        auto lse_issue = [&](auto Sc, int u) __attribute__((always_inline)) {
+        unsigned long long lse_v[2][2] = {{0ull, 0ull}, {0ull, 0ull}};
+        auto lse_load = [&](auto Sc, int u) __attribute__((always_inline)) {
             constexpr int S = decltype(Sc)::value;
-            if (u >= 0 && lane < ROWS) lse_v[S] = ld32(a.lse + (size_t)u * ROWS + lane);
+            const unsigned long long* sl = a.lse + ((size_t)u * ROWS + lane) * 2;
+            lse_v[S][0] = ld64(sl);
+            lse_v[S][1] = ld64(sl + 1);
+        };
+        auto lse_issue = [&](auto Sc, int u) __attribute__((always_inline)) {
+            if (u >= 0 && lane < ROWS) lse_load(Sc, u);
         };
         auto lse_take = [&](auto Sc, int u, int pb) __attribute__((always_inline)) {
             constexpr int S = decltype(Sc)::value;
-            bool miss = lane < ROWS && lse_v[S] == kSentinel32;
+            auto absent = [&]() __attribute__((always_inline)) {
+                return lane < ROWS && !(tag_is(lse_v[S][0], a.epoch) && tag_is(lse_v[S][1], a.epoch));
+            };
+            bool miss = absent();
             if (__ballot(miss) != 0) {
                 const unsigned long long t0 = wall_clock64();
                 while (true) {
                     __builtin_amdgcn_s_sleep(2);
-                    if (miss) lse_v[S] = ld32(a.lse + (size_t)u * ROWS + lane);
-                    miss = lane < ROWS && lse_v[S] == kSentinel32;
+                    if (miss) lse_load(Sc, u);
+                    miss = absent();
                     if (__ballot(miss) == 0) break;
                     if (wait_expired(t0, a)) {
-                        if (lane == 0) __hip_atomic_store(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        if (lane == 0) set_err(a);
                         break;
                     }
                 }
             }
-            if (lane < ROWS) lse_s[pb * ROWS + lane] = __uint_as_float(lse_v[S]);
+            if (lane < ROWS) lse_s[pb * ROWS + lane] = tag_value(lse_v[S][0]);
         };
         // the workgroup's partial of unit u: combine the streaming waves' rows
+        // and publish (row max, row sum), each word tagged with the epoch
         auto publish = [&](int u, int pb) __attribute__((always_inline)) {
             if (lane < ROWS) {
                 float mm = red[(pb * SW + 0) * ROWS + lane].x, ss = red[(pb * SW + 0) * ROWS + lane].y;
                 for (int x = 1; x < SW; ++x)
                     combine(mm, ss, red[(pb * SW + x) * ROWS + lane].x, red[(pb * SW + x) * ROWS + lane].y, c);
-                st64(a.part + ((size_t)u * a.g + rank) * ROWS + lane, mm, ss);
+                unsigned long long* sl = a.part + (((size_t)u * a.g + rank) * ROWS + lane) * 2;
+                st64u(sl, tagged(mm, a.epoch));
+                st64u(sl + 1, tagged(ss, a.epoch));
             }
         };
         // Step it (parity P): take unit it-D's log-sum-exps (loaded kLseAhead
@@ -1097,41 +1161,59 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
     }
     __syncthreads();
     // The ngroups workgroups of this rank (one per group) hold the running
-    // maxima of the same key slice. Each but the last to finish leaves its
-    // values for the last one (agent-scope stores, complete before the
-    // count); the last takes the max over groups, exponentiates and averages
-    // over the steps: importance_i = (1/N) sum_j exp2(kStep * max v).
-    int& last_s = *(int*)lse_s;  // (the log-sum-exp slots are free by now)
+    // maxima of the same key slice. All but the last group's leave theirs in
+    // Tg (agent-scope stores, complete before the flag) and raise a flag
+    // tagged with the epoch; the last group's workgroup (the one with the
+    // fewest units, so usually the first to get here) waits for the flags,
+    // takes the max over groups, exponentiates and averages over the steps:
+    // importance_i = (1/N) sum_j exp2(kStep * max v). (No shared counter: a
+    // read-modify-write that dozens of workgroups retry at once costs tens of
+    // microseconds.)
     if (a.ngroups > 1) {
-        for (int x = tid; x < a.N * nkeys; x += kThreads) {
-            const int jj = x / nkeys, k = x - jj * nkeys;
-            __hip_atomic_store(&a.Tg[((size_t)group * a.N + jj) * a.M + r0 + k], Trun[jj * KRP + k],
-                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int merger = a.ngroups - 1;
+        unsigned long long* flags = a.flags + (size_t)rank * a.ngroups;
+        const unsigned long long mark = ((unsigned long long)a.epoch << 32) | a.epoch;
+        if (group != merger) {
+            for (int x = tid; x < a.N * nout; x += kThreads) {
+                const int jj = x / nout, k = x - jj * nout;
+                __hip_atomic_store(&a.Tg[((size_t)group * a.N + jj) * a.M + r0 + k], Trun[jj * KRP + k],
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            if (tid == 0) st64u(flags + group, mark);
+            return;
         }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if (w == 0) {
+            // lane x watches groups x, x + 64, ...
+            const unsigned long long t0 = wall_clock64();
+            while (true) {
+                bool miss = false;
+                for (int x = lane; x < merger; x += 64) miss |= ld64(flags + x) != mark;
+                if (__ballot(miss) == 0) break;
+                __builtin_amdgcn_s_sleep(2);
+                if (wait_expired(t0, a)) {
+                    if (lane == 0) set_err(a);
+                    break;
+                }
+            }
+        }
         __syncthreads();
-        if (tid == 0)
-            last_s = __hip_atomic_fetch_add(a.done + rank, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                     (unsigned)(a.ngroups - 1);
-        __syncthreads();
-        if (!last_s) return;
     }
     if (a.ngroups > 1) {
         // XB values per thread (one pass covers N x 560 keys at N = 8), the
         // other groups' copies GB groups at a time: XB * GB = 63 independent
         // loads in flight (the most a wave can have) instead of one round
-        // trip each (waiting workgroups would learn of the last arrival only
-        // by polling the counter, microseconds later than the last one learns
-        // it from its own increment, so one workgroup does the whole slice)
+        // trip each
         constexpr int XB = 9, GB = 7;
-        const int total = a.N * nkeys;
+        const int total = a.N * nout;
         const size_t gstride = (size_t)a.N * a.M;
         for (int x0 = 0; x0 < total; x0 += kThreads * XB) {
             int v[XB], li[XB], go[XB];
 #pragma unroll
             for (int i = 0; i < XB; ++i) {
                 const int x = x0 + i * kThreads + tid;
-                const int jj = x / nkeys, k = x - jj * nkeys;
+                const int jj = x / nout, k = x - jj * nout;
                 li[i] = x < total ? jj * KRP + k : -1;
                 go[i] = jj * a.M + r0 + k;
                 v[i] = x < total ? Trun[li[i]] : kNegInf;
@@ -1163,8 +1245,8 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
     // that the selection rejects them instead of returning a plausible set.
     // (With blend_n = n > 0 this call adds one more step to scores already
     // averaged over n steps: (n * importance + this step's score) / (n + 1).)
-    const bool poisoned = ld32(a.err) != 0u;
-    for (int k = tid; k < nkeys && r0 + k < a.M_out; k += kThreads) {
+    const bool poisoned = err_set(a);
+    for (int k = tid; k < nout && r0 + k < a.M_out; k += kThreads) {
         float sum = 0.f;
         for (int jj = 0; jj < a.N; ++jj) sum += exp2_hw((float)Trun[jj * KRP + k] * kStep);
         float v = sum / (float)a.N;

@@ -34,6 +34,9 @@ static sp_status plan_uncached(const sp_score_desc& d, long long M, int cus, Sco
     if (cus < 1) cus = kDefaultCUs;
     if (cus < 2) return SP_EUNSUPPORTED;
     const double bytes_per_key = (double)row_bytes;
+    // the slices cover the prompt and the look-ahead keys (the last slice
+    // holds the latter too: they count in the rows' softmax denominators)
+    const long long MK = M + d.N;
     // A step takes the longer of (a) the busiest streaming wave's work on its
     // tiles (measured on the MI355X: ~4.1 us for 4 tiles, ~5.7 us for 5 tiles
     // without the registers for the guard-free statistics), and (b) the
@@ -48,21 +51,21 @@ static sp_status plan_uncached(const sp_score_desc& d, long long M, int cus, Sco
     const int tpw1 = (G == 1 && p.rows == 32) ? tpw0 : tpw0 + 1;
     for (int tpw = tpw0; tpw <= tpw1; ++tpw) {
         const int cap = kStreamWaves * tpw * kTileKeys;
-        const long long gmin = (M + cap - 1) / cap;
+        const long long gmin = (MK + cap - 1) / cap;
         const bool roomy = score_roomy(row_bytes, tpw, p.rows / 16);
         for (long long cand = 0; cand < 2 * (cus - gmin + 1); ++cand) {
             // each g with the smallest slice that covers M, then with a full one
             // (cap keys; the last workgroup takes the rest)
             const long long g = gmin + cand / 2;
             if (g > cus - 1 || g > kMaxRanks) break;
-            long long kr = (M + g - 1) / g;
+            long long kr = (MK + g - 1) / g;
             kr = (kr + tk - 1) / tk * tk;
             if (cand % 2 == 1) {
                 if (kr == cap) continue;  // (already planned)
                 kr = cap;
             }
             if (kr > cap) continue;
-            const long long geff = (M + kr - 1) / kr;
+            const long long geff = (MK + kr - 1) / kr;
             if (geff != g) continue;  // the same slice with fewer workgroups is planned at geff
             int defer = 0;
             for (int D = kMaxDefer; D >= 1; --D)
@@ -73,6 +76,7 @@ static sp_status plan_uncached(const sp_score_desc& d, long long M, int cus, Sco
             if (defer == 0) continue;
             long long ng = (cus - 1) / g;
             if (ng > p.units) ng = p.units;
+            if (ng > kMaxFlags / g) ng = kMaxFlags / g;
             if (ng < 1) continue;
             const long long iters = (p.units + ng - 1) / ng;
             // where the kernel has a guard-free copy of the statistics for
@@ -124,11 +128,11 @@ static sp_status plan_uncached(const sp_score_desc& d, long long M, int cus, Sco
     p.grid = bg * bng + p.ncomb;
     p.cus = cus;
     p.lds = score_lds_layout(bdef + 1, btpw, p.rows, row_bytes, d.N, bkr, p.dma);
-    p.ws_err = 0;      // error word; then at +128 one slice counter per rank (g <= kMaxRanks)
-    p.ws_part = 2048;
-    p.ws_tail = p.ws_part + round_up((size_t)p.units * p.g * p.rows * 8, 256);
-    p.ws_lse = p.ws_tail + round_up((size_t)p.units * p.rows * 8, 256);
-    p.ws_tg = p.ws_lse + round_up((size_t)p.units * p.rows * 4, 256);
+    // the header (error word, last epoch, one flag per streaming workgroup)
+    p.ws_err = 0;
+    p.ws_part = kHeaderBytes;
+    p.ws_lse = p.ws_part + round_up((size_t)p.units * p.g * p.rows * 16, 256);
+    p.ws_tg = p.ws_lse + round_up((size_t)p.units * p.rows * 16, 256);
     p.ws_total = p.ws_tg + round_up((size_t)p.ngroups * d.N * M * 4, 256);
     *out = p;
     return SP_OK;
@@ -201,8 +205,8 @@ size_t workspace_bound(const sp_score_desc& d, long long max_M, int cus) {
     long long tg_elems = (long long)(units < cus ? units : cus) * max_M;
     if (tg_elems > (long long)cus * cap) tg_elems = (long long)cus * cap;
     tg_elems *= d.N;
-    return 2048 + round_up((size_t)units * cus * rows * 8, 256) + round_up((size_t)units * rows * 8, 256) +
-           round_up((size_t)units * rows * 4, 256) + round_up((size_t)tg_elems * 4, 256);
+    return kHeaderBytes + round_up((size_t)units * cus * rows * 16, 256) + round_up((size_t)units * rows * 16, 256) +
+           round_up((size_t)tg_elems * 4, 256);
 }
 
 }  // namespace sp

@@ -82,10 +82,11 @@ typedef enum { SP_LAUNCH_RESIDENT = 0, SP_LAUNCH_COOPERATIVE = 1 } sp_launch;
  * Hkv key/value heads (H % Hkv == 0; query head h reads kv-head h / (H/Hkv)),
  * head dimension d, N look-ahead steps. scale multiplies the logits; 0 selects
  * 1/sqrt(d). launch is an sp_launch (0 = SP_LAUNCH_RESIDENT). Supported:
- * d in {64, 128}; G = H/Hkv a power of two; G*N <= 32; and prompts of at most
- * (compute units - 1) x 560 keys (x 336 for f32 at d = 128; fewer for G = 1
- * with 32 query rows): 142,800 keys on a 256-CU MI355X, 85,680 for f32 at
- * d = 128. sp_score_plan reports SP_EUNSUPPORTED beyond. */
+ * d in {64, 128}; G = H/Hkv a power of two; G*N <= 32; and prompts whose
+ * M + N keys are at most (compute units - 1) x 560 (x 336 for f32 at d = 128;
+ * fewer for G = 1 with 32 query rows): M <= 142,792 at N = 8 on a 256-CU
+ * MI355X, 85,672 for f32 at d = 128. sp_score_plan reports SP_EUNSUPPORTED
+ * beyond. */
 typedef struct {
     int32_t L, H, Hkv, d, N;
     sp_dtype dtype;
@@ -140,7 +141,12 @@ size_t sp_score_workspace_bytes(const sp_score_desc* desc, int64_t max_prompt_le
  *   M           prompt length, >= 1
  *   importance  device, [M] float32 (written)
  *   ws          device workspace of ws_bytes >= sp_score_workspace_bytes(desc, M);
- *               contents need no initialisation and are clobbered
+ *               contents need no initialisation and are clobbered. Calls that
+ *               overlap on one workspace (other streams or threads) race.
+ * The call may be captured into a HIP graph (a small clearing kernel is then
+ * captured before the scoring kernel, so that replays start afresh); eager
+ * calls need nothing between them (what the kernel leaves in the workspace is
+ * tagged with a per-launch number).
  */
 sp_status sp_score(const sp_score_desc* desc, const void* Q, const void* K, int32_t M,
                    float* importance, void* ws, size_t ws_bytes, void* stream);
@@ -153,8 +159,8 @@ sp_status sp_score(const sp_score_desc* desc, const void* Q, const void* K, int3
  * device it runs on until the process ends (its address is looked up on the
  * first call on each device). The call allocates nothing. Every call on a
  * device shares that device's array: calls that overlap on one device (other
- * streams, other threads) race and must not be made; the kernels reset what
- * they need on every call, so consecutive calls need nothing in between.
+ * streams, other threads) race and must not be made; consecutive calls need
+ * nothing in between.
  * A time-out of its bounded waits shows as NaN scores (sp_select then reports
  * n_kept = -1); sp_score_status does not apply.
  *   Arguments as for sp_score, without the workspace. SP_EWORKSPACE when the
@@ -385,7 +391,7 @@ sp_status sp_profile_score_kernel(void* before, void* after);
  *   ws         device workspace passed to that call
  *   stream     the stream that call was enqueued on
  *   timed_out  host, written: 0 (complete) or 1 (a wait timed out)
- * This call waits for the stream (it copies one word back to the host).
+ * This call waits for the stream (it copies 16 bytes back to the host).
  * SP_EINVAL for null pointers; SP_EDEVICE if the copy fails.
  */
 sp_status sp_score_status(const void* ws, void* stream, int32_t* timed_out);

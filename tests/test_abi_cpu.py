@@ -184,16 +184,17 @@ def test_plan_does_not_depend_on_the_launch_mode(lib):
         assert a == b
 
 
-@pytest.mark.parametrize("dtype,d,longest", [(sp.SP_BF16, 128, 142800), (sp.SP_BF16, 64, 142800),
-                                             (sp.SP_F32, 64, 142800), (sp.SP_F32, 128, 85680)])
+@pytest.mark.parametrize("dtype,d,longest", [(sp.SP_BF16, 128, 142792), (sp.SP_BF16, 64, 142792),
+                                             (sp.SP_F32, 64, 142792), (sp.SP_F32, 128, 85672)])
 def test_plan_longest_prompt(lib, dtype, d, longest):
     """On 256 CUs: 255 workgroups of at most 560 keys (336 for f32 at d = 128)
-    and one combiner; one key more is rejected."""
-    dd = desc(L=1, H=4, Hkv=1, d=d, dtype=dtype)
+    hold the M prompt keys and the N = 8 look-ahead keys, and one combiner;
+    one key more is rejected."""
+    dd = desc(L=1, H=4, Hkv=1, d=d, N=8, dtype=dtype)
     p = sp.sp_score_plan(dd, longest)
     if p["cus"] != 256:
         pytest.skip("the limits below are those of a 256-CU device")
-    assert p["g"] == 255 and p["grid"] == 256 and p["g"] * p["keys_per_wg"] >= longest
+    assert p["g"] == 255 and p["grid"] == 256 and p["g"] * p["keys_per_wg"] >= longest + 8
     with pytest.raises(sp.SpError) as e:
         sp.sp_score_plan(dd, longest + 1)
     assert e.value.status == sp.SP_EUNSUPPORTED

@@ -173,11 +173,54 @@ def test_score_cooperative_launch_matches(case):
     check_importance(a.cpu().numpy(), oracle.score(Qh, Kh), name)
 
 
+# The look-ahead keys M..M+N-1 are streamed by the last key slices, with a
+# per-row causal mask (step j sees look-ahead keys up to M + j). Prompt
+# lengths picked from each shape's plan put them at the slice boundaries:
+# a last slice that holds only look-ahead keys, look-ahead keys split over
+# two slices, and a slice that ends right after key M.
+BOUNDARY_SHAPES = [
+    ("bf16-d128-G4-N8", 2, 32, 8, 128, 8, BF),
+    ("bf16-d128-G1-N16", 1, 4, 4, 128, 16, BF),
+    ("f32-d64-G4-N8", 1, 8, 2, 64, 8, F32),
+]
+
+
+def _boundary_prompts(desc, N):
+    """(M, kind) for the three placements, from the plans of M in 600..30000."""
+    found = {}
+    for M in range(600, 30000):
+        p = sp.sp_score_plan(desc, M)
+        kr = p["keys_per_wg"]
+        for kind, hit in (("tail-only slice", M % kr == 0), ("tail split", M % kr == kr - 3),
+                          ("slice ends after key M", (M + 1) % kr == 0)):
+            if hit and kind not in found and (M + N + kr - 1) // kr == p["g"]:
+                found[kind] = M
+        if len(found) == 3:
+            break
+    return sorted((m, k) for k, m in found.items())
+
+
+@pytest.mark.parametrize("shape", BOUNDARY_SHAPES, ids=[c[0] for c in BOUNDARY_SHAPES])
+def test_score_lookahead_keys_at_slice_boundaries(shape):
+    name, L, H, Hkv, d, N, dt = shape
+    desc = sp.score_desc(L, H, Hkv, d, N, sp.SP_BF16 if dt else sp.SP_F32)
+    cases = _boundary_prompts(desc, N)
+    assert len(cases) == 3, cases
+    for M, kind in cases:
+        label = f"{name}-M{M} ({kind})"
+        print(f"case {label}", flush=True)
+        w = workload(L, H, Hkv, d, N, M, dt, seed=37)
+        Qh, Kh, _ = synth.make_request(w)
+        imp = sp.sp_score(to_dev(Qh), to_dev(Kh))
+        torch.cuda.synchronize()
+        check_importance(imp.cpu().numpy(), oracle.score(Qh, Kh), label)
+
+
 # The longest prompts the planner accepts: one workgroup per CU but one (the
 # combiner's), each holding as many keys as its registers and LDS allow.
 LONGEST_CASES = [
-    ("longest-bf16-d128", 1, 4, 1, 128, 8, 142800, BF),
-    ("longest-f32-d128", 1, 4, 1, 128, 8, 85680, F32),
+    ("longest-bf16-d128", 1, 4, 1, 128, 8, 142792, BF),
+    ("longest-f32-d128", 1, 4, 1, 128, 8, 85672, F32),
 ]
 
 

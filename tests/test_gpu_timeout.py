@@ -62,7 +62,7 @@ def test_timed_out_call_is_reported_and_poisoned(restore_limit):
 
 def test_timed_out_ragged_call_is_reported(restore_limit):
     """A time-out in any request of a ragged call is reported: the error word is
-    cleared only by the call's first request."""
+    tagged with the call's number, which all its requests share."""
     lens = np.array([3000, 2000], np.int64)
     w = synth.Workload("timeout", L=8, H=32, Hkv=8, d=128, N=8, dtype=synth.BF16, seed=33,
                        R=2, len_range=(2000, 3000, 1000), plant_frac=0.05)
