@@ -1146,13 +1146,16 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
             __builtin_amdgcn_s_setprio(0);
         };
 
+        // (Q of unit 1 is in flight while unit 0's lands; unit 2's loads are
+        // issued after the first barrier, so that the streaming waves, whose
+        // first K tiles are already on their way, do not wait for their issue)
         q_issue(std::integral_constant<int, 0>{}, unit_of(0));
-        q_store(std::integral_constant<int, 0>{}, 0);
         q_issue(std::integral_constant<int, 1>{}, unit_of(1));
-        q_issue(std::integral_constant<int, 0>{}, unit_of(2));
+        q_store(std::integral_constant<int, 0>{}, 0);
         lse_issue(std::integral_constant<int, 0>{}, unit_of(-D));
         if constexpr (kLseAhead == 2) lse_issue(std::integral_constant<int, 1>{}, unit_of(1 - D));
         step_barrier<C>();
+        q_issue(std::integral_constant<int, 0>{}, unit_of(2));
         for (int it = 0; it < n_steps; it += 2) {
             ctrl_step(std::integral_constant<int, 0>{}, it);
             ctrl_step(std::integral_constant<int, 1>{}, it + 1);
@@ -1202,12 +1205,16 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
     }
     if (a.ngroups > 1) {
         // XB values per thread (one pass covers N x 560 keys at N = 8), the
-        // other groups' copies GB groups at a time: XB * GB = 63 independent
-        // loads in flight (the most a wave can have) instead of one round
-        // trip each
+        // other groups' copies (groups 0 .. ngroups - 2: this workgroup is the
+        // last group's) GB groups at a time: XB * GB = 63 independent loads in
+        // flight (the most a wave can have) instead of one round trip each.
+        // Every load is issued unconditionally from an address in bounds
+        // (lanes past the end read element 0, batches past the last group
+        // re-read it; neither changes a max), so that none waits for another.
         constexpr int XB = 9, GB = 7;
         const int total = a.N * nout;
         const size_t gstride = (size_t)a.N * a.M;
+        const int last_other = a.ngroups - 2;
         for (int x0 = 0; x0 < total; x0 += kThreads * XB) {
             int v[XB], li[XB], go[XB];
 #pragma unroll
@@ -1215,18 +1222,16 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
                 const int x = x0 + i * kThreads + tid;
                 const int jj = x / nout, k = x - jj * nout;
                 li[i] = x < total ? jj * KRP + k : -1;
-                go[i] = jj * a.M + r0 + k;
+                go[i] = x < total ? jj * a.M + r0 + k : 0;
                 v[i] = x < total ? Trun[li[i]] : kNegInf;
             }
-            for (int gb = 0; gb < a.ngroups; gb += GB) {
+            for (int gb = 0; gb <= last_other; gb += GB) {
                 int t[GB][XB];
 #pragma unroll
                 for (int y = 0; y < GB; ++y) {
-                    const int gr = gb + y;
-                    const bool use = gr < a.ngroups && gr != group;
+                    const int* tg = a.Tg + (size_t)min(gb + y, last_other) * gstride;
 #pragma unroll
-                    for (int i = 0; i < XB; ++i)
-                        t[y][i] = use && li[i] >= 0 ? (int)ld32(a.Tg + gr * gstride + go[i]) : kNegInf;
+                    for (int i = 0; i < XB; ++i) t[y][i] = (int)ld32(tg + go[i]);
                 }
 #pragma unroll
                 for (int y = 0; y < GB; ++y)
