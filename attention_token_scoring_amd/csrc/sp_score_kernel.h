@@ -1164,35 +1164,33 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
     }
     __syncthreads();
     // The ngroups workgroups of this rank (one per group) hold the running
-    // maxima of the same key slice. All but the last group's leave theirs in
-    // Tg (agent-scope stores, complete before the flag) and raise a flag
-    // tagged with the epoch; the last group's workgroup (the one with the
-    // fewest units, so usually the first to get here) waits for the flags,
-    // takes the max over groups, exponentiates and averages over the steps:
-    // importance_i = (1/N) sum_j exp2(kStep * max v). (No shared counter: a
-    // read-modify-write that dozens of workgroups retry at once costs tens of
-    // microseconds.)
+    // maxima of the same key slice. Each leaves its copy in Tg (agent-scope
+    // stores, complete before its flag) and raises a flag tagged with the
+    // epoch; once the slice's flags are all up, the workgroup of group q takes
+    // the max over groups of its share of the slice's keys (keys [q s, q s + s),
+    // s = ceil(nout / ngroups)), exponentiates and averages over the steps:
+    // importance_i = (1/N) sum_j exp2(kStep * max v). (A shared counter would
+    // let the last group to arrive do it alone, but a read-modify-write that
+    // dozens of workgroups retry at once costs tens of microseconds, and one
+    // workgroup merging all keys of 28 groups waits for four batches of loads.)
+    int k_lo = 0, k_hi = nout;
     if (a.ngroups > 1) {
-        const int merger = a.ngroups - 1;
         unsigned long long* flags = a.flags + (size_t)rank * a.ngroups;
         const unsigned long long mark = ((unsigned long long)a.epoch << 32) | a.epoch;
-        if (group != merger) {
-            for (int x = tid; x < a.N * nout; x += kThreads) {
-                const int jj = x / nout, k = x - jj * nout;
-                __hip_atomic_store(&a.Tg[((size_t)group * a.N + jj) * a.M + r0 + k], Trun[jj * KRP + k],
-                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            __syncthreads();
-            if (tid == 0) st64u(flags + group, mark);
-            return;
+        for (int x = tid; x < a.N * nout; x += kThreads) {
+            const int jj = x / nout, k = x - jj * nout;
+            __hip_atomic_store(&a.Tg[((size_t)group * a.N + jj) * a.M + r0 + k], Trun[jj * KRP + k],
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (tid == 0) st64u(flags + group, mark);
         if (w == 0) {
             // lane x watches groups x, x + 64, ...
             const unsigned long long t0 = wall_clock64();
             while (true) {
                 bool miss = false;
-                for (int x = lane; x < merger; x += 64) miss |= ld64(flags + x) != mark;
+                for (int x = lane; x < a.ngroups; x += 64) miss |= x != group && ld64(flags + x) != mark;
                 if (__ballot(miss) == 0) break;
                 __builtin_amdgcn_s_sleep(2);
                 if (wait_expired(t0, a)) {
@@ -1202,25 +1200,26 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
             }
         }
         __syncthreads();
-    }
-    if (a.ngroups > 1) {
-        // XB values per thread (one pass covers N x 560 keys at N = 8), the
-        // other groups' copies (groups 0 .. ngroups - 2: this workgroup is the
-        // last group's) GB groups at a time: XB * GB = 63 independent loads in
-        // flight (the most a wave can have) instead of one round trip each.
-        // Every load is issued unconditionally from an address in bounds
-        // (lanes past the end read element 0, batches past the last group
-        // re-read it; neither changes a max), so that none waits for another.
-        constexpr int XB = 9, GB = 7;
-        const int total = a.N * nout;
+        const int share = (nout + a.ngroups - 1) / a.ngroups;
+        k_lo = min(group * share, nout);
+        k_hi = min(k_lo + share, nout);
+        // XB values per thread, the other groups' copies GB at a time: XB * GB
+        // = 60 independent loads in flight (a wave can have 63) instead of one
+        // round trip each. Every load is issued unconditionally from an
+        // address in bounds (lanes past the end read element 0, batches past
+        // the last group re-read it; neither changes a max), so that none
+        // waits for another.
+        constexpr int XB = 4, GB = 15;
+        const int cnt = k_hi - k_lo;
+        const int total = a.N * cnt;
         const size_t gstride = (size_t)a.N * a.M;
-        const int last_other = a.ngroups - 2;
+        const int last_other = a.ngroups - 2;  // the others, as 0 .. ngroups - 2
         for (int x0 = 0; x0 < total; x0 += kThreads * XB) {
             int v[XB], li[XB], go[XB];
 #pragma unroll
             for (int i = 0; i < XB; ++i) {
                 const int x = x0 + i * kThreads + tid;
-                const int jj = x / nout, k = x - jj * nout;
+                const int jj = x / cnt, k = k_lo + x - jj * cnt;
                 li[i] = x < total ? jj * KRP + k : -1;
                 go[i] = x < total ? jj * a.M + r0 + k : 0;
                 v[i] = x < total ? Trun[li[i]] : kNegInf;
@@ -1229,7 +1228,8 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
                 int t[GB][XB];
 #pragma unroll
                 for (int y = 0; y < GB; ++y) {
-                    const int* tg = a.Tg + (size_t)min(gb + y, last_other) * gstride;
+                    const int o = min(gb + y, last_other);
+                    const int* tg = a.Tg + (size_t)(o + (o >= group ? 1 : 0)) * gstride;
 #pragma unroll
                     for (int i = 0; i < XB; ++i) t[y][i] = (int)ld32(tg + go[i]);
                 }
@@ -1251,7 +1251,7 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
     // (With blend_n = n > 0 this call adds one more step to scores already
     // averaged over n steps: (n * importance + this step's score) / (n + 1).)
     const bool poisoned = err_set(a);
-    for (int k = tid; k < nout && r0 + k < a.M_out; k += kThreads) {
+    for (int k = k_lo + tid; k < k_hi && r0 + k < a.M_out; k += kThreads) {
         float sum = 0.f;
         for (int jj = 0; jj < a.N; ++jj) sum += exp2_hw((float)Trun[jj * KRP + k] * kStep);
         float v = sum / (float)a.N;
