@@ -710,5 +710,19 @@ def headline_line(args, w, value, ms_per_step, config, roof):
     }
 
 
+def release_device_memory():
+    """Return torch's cached device memory while the runtime is whole: under
+    a profiler, whose finalisation runs at exit, teardown work left to the
+    interpreter's exit would run after it."""
+    if "torch" in sys.modules:
+        torch = sys.modules["torch"]
+        if torch.cuda.is_initialized():
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+
+
 if __name__ == "__main__":
-    main()
+    try:
+        main()
+    finally:
+        release_device_memory()
