@@ -28,7 +28,8 @@ hipError_t launch_select(const SelectParamsDev& p, const int64_t* cu, const int3
 namespace {
 
 constexpr int kMaxDevices = 64;
-constexpr int kMaxSelectChunks = 4096;
+constexpr int kMaxSelectChunks = 5120;   // top-K and mass modes
+constexpr int kMaxThresholdChunks = 4096;
 constexpr int kMaxSelectRequests = 1024;
 
 int g_cus[kMaxDevices];
@@ -113,7 +114,7 @@ sp_status check_select_prompt(const sp_select_params* p, long long M) {
     if (M > (1ll << 24)) return SP_EUNSUPPORTED;
     const long long nc = (M + p->chunk - 1) / p->chunk;
     if (nc > kMaxSelectChunks) return SP_EUNSUPPORTED;
-    if (p->mode == SP_SELECT_THRESHOLD) return SP_OK;  // (no fixed-point sums)
+    if (p->mode == SP_SELECT_THRESHOLD) return nc > kMaxThresholdChunks ? SP_EUNSUPPORTED : SP_OK;
     double vmax = 1.0;
     const double a = p->boost_first_mult, b = p->boost_last_mult;
     if (a > vmax) vmax = a;

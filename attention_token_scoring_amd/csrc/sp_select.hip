@@ -25,7 +25,12 @@ namespace sp {
 
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
-constexpr int kMaxChunks = 4096;
+// Chunks per prompt: 5 per thread (5120 covers the longest prompt the scoring
+// kernel takes, 142,792 tokens, at chunk 28 or more); the threshold mode's
+// bitonic sort keeps 4096.
+constexpr int kScanPer = 5;
+constexpr int kMaxChunks = kScanPer * kSelThreads;
+constexpr int kMaxThreshChunks = 4096;
 constexpr int kSelBatch = 256;  // requests per launch (offsets travel in the kernel arguments)
 constexpr int kLd = 16;         // importance loads in flight per thread
 constexpr int kSeg = 16;        // contiguous elements a thread quantises per tile
@@ -129,15 +134,15 @@ __device__ __forceinline__ bool ranks_before(unsigned long long ka, unsigned int
     return ka > kb || (ka == kb && ia < ib);
 }
 
-// In-place exclusive scan of data[0..n) (n <= 4 * kSelThreads); returns the total.
+// In-place exclusive scan of data[0..n) (n <= kScanPer * kSelThreads); returns the total.
 template <typename T>
 __device__ T block_excl_scan(T* data, int n, unsigned long long* wtmp) {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int i0 = tid * 4;
-    T loc[4];
+    const int i0 = tid * kScanPer;
+    T loc[kScanPer];
     T run = 0;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
+    for (int e = 0; e < kScanPer; ++e) {
         loc[e] = (i0 + e < n) ? data[i0 + e] : (T)0;
         run += loc[e];
     }
@@ -154,7 +159,7 @@ __device__ T block_excl_scan(T* data, int n, unsigned long long* wtmp) {
     }
     T ex = wbase + incl - run;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
+    for (int e = 0; e < kScanPer; ++e) {
         if (i0 + e < n) data[i0 + e] = ex;
         ex += loc[e];
     }
@@ -739,10 +744,10 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectBatch b, Sele
 // so the result does not depend on how the work is split.
 // ---------------------------------------------------------------------------------------
 struct ThreshShared {
-    float a[kMaxChunks];     // chunk means
-    float srt[kMaxChunks];   // the means sorted descending (padded with -inf)
-    int cnt[kMaxChunks];     // free tokens of dropped chunks, then their exclusive scan
-    int off[kMaxChunks];     // kept tokens per chunk, then their exclusive scan
+    float a[kMaxThreshChunks];     // chunk means
+    float srt[kMaxThreshChunks];   // the means sorted descending (padded with -inf)
+    int cnt[kMaxThreshChunks];     // free tokens of dropped chunks, then their exclusive scan
+    int off[kMaxThreshChunks];     // kept tokens per chunk, then their exclusive scan
     unsigned long long wtmp[kSelWaves];
     float thr;
     int total;

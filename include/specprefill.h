@@ -295,7 +295,9 @@ size_t sp_select_workspace_bytes(int32_t R, int64_t total_prompt_len,
  *   n_kept      device, [1] int32 (written): the kept count, or -1 if some score
  *               is NaN or infinite (kept_idx and pos_ids are then not written;
  *               a scoring call whose bounded waits timed out leaves NaN scores)
- * Supported: M <= 2^24, nc = ceil(M/chunk) <= 4096, and boost multipliers
+ * Supported: M <= 2^24, nc = ceil(M/chunk) <= 5120 (4096 in threshold mode:
+ * with chunk 32 that is 163,840 tokens, more than the longest prompt sp_score
+ * takes, and 131,072 in threshold mode), and boost multipliers
  * with max(1, first_mult, last_mult, first_mult*last_mult) * 2^32 * pool_k *
  * chunk < 2^53 (so the pooled sums stay exact in double).
  */

@@ -122,7 +122,7 @@ def test_plan_for_the_8b_shape(lib):
     (dict(mode=5), sp.SP_EINVAL),
     (dict(boost_first_mult=-1.0), sp.SP_EINVAL),
     (dict(boost_last_n=-3), sp.SP_EINVAL),
-    (dict(chunk=1), sp.SP_EUNSUPPORTED),            # nc = 10000 > 4096
+    (dict(chunk=1), sp.SP_EUNSUPPORTED),            # nc = 10000 > 5120
     (dict(boost_first_mult=3e6), sp.SP_EUNSUPPORTED),  # pooled sums would exceed 2^53
     (dict(min_tok=128), sp.SP_EINVAL),              # threshold-mode fields in top-K mode
     (dict(mode="mass", mass=0.5, max_keep=10), sp.SP_EINVAL),
@@ -132,6 +132,7 @@ def test_plan_for_the_8b_shape(lib):
     (dict(mode="threshold", pool_k=1, max_keep=-1), sp.SP_EINVAL),
     (dict(mode="threshold", pool_k=1, keep_rate=0.0), sp.SP_EINVAL),
     (dict(mode="threshold", pool_k=1, chunk=1), sp.SP_EUNSUPPORTED),  # nc = 10000 > 4096
+    (dict(mode="threshold", pool_k=1, chunk=2), sp.SP_EUNSUPPORTED),  # nc = 5000 > 4096
     (dict(norm=3), sp.SP_EINVAL),
     (dict(norm="minmax", norm_hi=0.5), sp.SP_EINVAL),
     (dict(norm="percentile", norm_lo=0.5, norm_hi=0.5), sp.SP_EINVAL),
@@ -148,6 +149,19 @@ def test_select_rejects(lib, kw, status):
     p = sp.select_params(**base)
     st = lib.sp_select(FAKE, 10000, ctypes.byref(p), 0, FAKE, FAKE, FAKE, None, 0, None)
     assert st == status
+
+
+@pytest.mark.parametrize("mode,limit", [("topk", 5120), ("mass", 5120), ("threshold", 4096)])
+def test_select_chunk_count_limit(lib, mode, limit):
+    """One chunk more than the kernels hold is refused before anything runs
+    (the largest accepted count is exercised on the GPU)."""
+    kw = dict(chunk=32, pool_k=1 if mode == "threshold" else 3, mode=mode, keep_rate=0.3)
+    if mode == "mass":
+        kw.update(mass=0.85)
+    p = sp.select_params(**kw)
+    M = limit * 32 + 1
+    assert lib.sp_select(FAKE, M, ctypes.byref(p), 0, FAKE, FAKE, FAKE, None, 0, None) \
+        == sp.SP_EUNSUPPORTED
 
 
 def test_select_rejects_null_and_sizes(lib):

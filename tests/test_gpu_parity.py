@@ -358,7 +358,11 @@ def test_select_position_id_example():
 
 SELECT_CASES = [
     dict(M=32768, chunk=32, pool_k=13, mode="topk", keep_rate=0.1),
-    dict(M=32768, chunk=8, pool_k=5, mode="mass", mass=0.85),       # nc = 4096 (maximum)
+    dict(M=32768, chunk=8, pool_k=5, mode="mass", mass=0.85),       # nc = 4096
+    dict(M=163840, chunk=32, pool_k=13, mode="topk", keep_rate=0.1),  # nc = 5120 (maximum)
+    dict(M=163835, chunk=32, pool_k=5, mode="mass", mass=0.85),     # nc = 5120, ragged last chunk
+    dict(M=142792, chunk=32, pool_k=13, mode="mass", mass=0.85, boost_first_n=64,
+         boost_first_mult=1.5, boost_last_n=128, boost_last_mult=1.3),  # the longest scored prompt
     dict(M=4608, chunk=32, pool_k=5, mode="mass", mass=0.85, boost_first_n=64,
          boost_first_mult=1.5, boost_last_n=128, boost_last_mult=1.3),
     dict(M=1000, chunk=24, pool_k=3, mode="topk", keep_rate=0.3),     # chunk not a power of 2
