@@ -165,9 +165,9 @@ sp_status sp_score(const sp_score_desc* desc, const void* Q, const void* K, int3
  * n_kept = -1); sp_score_status does not apply.
  *   Arguments as for sp_score, without the workspace. SP_EWORKSPACE when the
  *   plan for (desc, M) needs more than SP_NOALLOC_SCRATCH_BYTES of workspace
- *   (the 8B shape at 128K keys needs about 20 MiB).
+ *   (the 8B shape needs about 12 MiB at 32K keys, 34 MiB at 128K keys).
  */
-#define SP_NOALLOC_SCRATCH_BYTES (32u << 20)
+#define SP_NOALLOC_SCRATCH_BYTES (64u << 20)
 sp_status sp_score_noalloc(const sp_score_desc* desc, const void* Q, const void* K, int32_t M,
                            float* importance, void* stream);
 

@@ -57,7 +57,7 @@ def test_noalloc_matches_sp_score_on_consecutive_calls():
 
 def test_noalloc_refuses_a_plan_larger_than_its_array():
     # 4096 (layer, kv-head) units at 32K keys: the partial statistics alone
-    # need more than the array's 32 MiB; refused before any launch (the
+    # need more than the array's 64 MiB; refused before any launch (the
     # pointers are never dereferenced)
     desc = sp.score_desc(512, 32, 8, 128, 8, sp.SP_BF16)
     fake = ctypes.c_void_p(0x100000)
