@@ -2,8 +2,9 @@
 (torch.cuda.CUDAGraph on the capture stream) and replayed several times,
 with eager work that overwrites the outputs between replays; every replay
 must reproduce the eager call bit for bit (the scoring kernel is
-deterministic, and its prep kernel resets the workspace's synchronisation
-state on every replay, with no memset nodes in the graph)."""
+deterministic; a launch's epoch is fixed into the graph, so a clearing kernel
+captured before it resets the workspace's tagged words on every replay, with
+no memset nodes in the graph)."""
 import numpy as np
 import pytest
 
