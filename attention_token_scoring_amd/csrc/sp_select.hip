@@ -256,9 +256,21 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectBatch b, Sele
     // indices past the end re-read the last element
     // (a NaN or infinite score, which a scoring call that timed out leaves,
     // makes the request's count -1 and leaves its outputs untouched)
+    // (the first kLd loads are the first tile of step 2 in the same layout:
+    // they stay in registers for it)
+    static_assert(kSelThreads * kLd == kTile && kLd == kSeg, "step 1's first loads are step 2's first tile");
     float mn = INFINITY, mx = -INFINITY;
     int nonfinite = 0;
-    for (int t0 = 0; t0 < M; t0 += kSelThreads * kLd) {
+    float tile0[kLd];
+#pragma unroll
+    for (int k = 0; k < kLd; ++k) tile0[k] = x[min(k * kSelThreads + tid, M - 1)];
+#pragma unroll
+    for (int k = 0; k < kLd; ++k) {
+        nonfinite |= (__float_as_uint(tile0[k]) & 0x7f800000u) == 0x7f800000u;
+        mn = fminf(mn, tile0[k]);
+        mx = fmaxf(mx, tile0[k]);
+    }
+    for (int t0 = kSelThreads * kLd; t0 < M; t0 += kSelThreads * kLd) {
         float v[kLd];
 #pragma unroll
         for (int k = 0; k < kLd; ++k) v[k] = x[min(t0 + k * kSelThreads + tid, M - 1)];
@@ -373,7 +385,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectBatch b, Sele
     // (the next tile's loads are issued before this tile is processed)
     float v[kSeg];
 #pragma unroll
-    for (int k = 0; k < kSeg; ++k) v[k] = x[min(k * kSelThreads + tid, M - 1)];
+    for (int k = 0; k < kSeg; ++k) v[k] = tile0[k];
     for (int t0 = 0; t0 < M; t0 += kTile) {
 #pragma unroll
         for (int k = 0; k < kSeg; ++k) {
