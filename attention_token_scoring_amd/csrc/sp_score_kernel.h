@@ -16,11 +16,16 @@
 //    each load instruction reads 64 contiguous bytes of 16 key rows.
 //  * g workgroups (one per CU, all resident at once: an ordinary launch no
 //    larger than what the device holds at a time, or a cooperative launch)
-//    share a unit, each owning a key slice. Seven waves stream K, each keeping
-//    two units of its tiles in flight, so HBM never waits for the rest of the
-//    pipeline. A streamed unit's logits are parked in LDS as 16-bit fixed-point
-//    log2 values relative to each wave-row's maximum, together with the
-//    wave's (max, sum) per row.
+//    share a unit, each owning a key slice; the slices cover the M prompt keys
+//    and then the N look-ahead keys (look-ahead key M+i counts in the softmax
+//    of steps j >= i only, a per-lane mask on the one tile per wave that
+//    reaches past key M). Seven waves stream K: bf16 tiles travel HBM -> LDS
+//    by DMA (buffer loads with the lds modifier) through a few slots per wave,
+//    f32 tiles through a register ring two units deep, so HBM never waits for
+//    the rest of the pipeline. A streamed unit's logits are parked as 16-bit
+//    fixed-point log2 values relative to each wave-row's maximum (in
+//    registers on the DMA path, in LDS otherwise), together with the wave's
+//    (max, sum) per row.
 //  * The eighth wave of each workgroup does the cross-workgroup exchange, off
 //    the streaming waves' instruction stream (a wave's vector-memory counter is
 //    in order on gfx950, so a poll issued by a streaming wave would wait for
@@ -29,9 +34,9 @@
 //    step before they are needed.
 //  * Combiner workgroups on CUs no group uses gather the g partials of each unit
 //    (their loads do not queue behind any K stream; the eight waves of a
-//    combiner split the ranks), add the look-ahead keys' share, and publish
-//    each row's log-sum-exp. Partial and log-sum-exp slots
-//    hold a sentinel until written, so no counters or flags are needed.
+//    combiner split the ranks) and publish each row's log-sum-exp. Every
+//    exchanged word carries the epoch of the launch that wrote it, so nothing
+//    is reset between launches (and no counter is shared).
 //  * D units after streaming a unit, its parked logits become log2
 //    probabilities in whole code steps (integers; a probability p carries a
 //    relative error of at most 3.4e-4); the max over the G heads of a step is
@@ -39,10 +44,9 @@
 //    running max kept in registers (log2 domain: exp2 is monotone, so one
 //    exponential per (step, key) at the end).
 //  * At the end the ngroups workgroups holding the same key slice (one per
-//    group) meet through a counter: the last to finish takes the max over
-//    groups, exponentiates and averages over the steps for its slice.
-//  * The look-ahead keys M..M+N-1 only enter denominators; a small prep kernel
-//    computes their share of each row's statistics.
+//    group) leave their running maxima in memory and raise epoch-tagged
+//    flags; then each takes the max over groups of its share of the slice's
+//    keys, exponentiates and averages over the steps.
 #pragma once
 
 #include <math.h>

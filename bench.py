@@ -335,7 +335,7 @@ def run_steps(torch, sp, step, steps: int, warmup: int, settle_s: float, kernel_
         step(i, kev=ev)
     torch.cuda.synchronize()
     kms = np.array([a.elapsed_time(b) for a, b in kevs])
-    # breakdown pass: the sp_score call (prep included) and the selection
+    # breakdown pass: the sp_score call and the selection
     sev = _events(torch, 50)
     xev = _events(torch, 50)
     for i in range(50):
@@ -449,7 +449,7 @@ def bench_ragged(args, w, sel, sp, torch, dev, steps, warmup, cpu_s):
     + sp_select_varlen over the whole batch. The batch's keys (tens of GB) are
     far larger than the Infinity Cache, so one copy suffices. The roofline
     figure uses the sp_score_varlen call's duration (one scoring kernel per
-    request plus its prep kernel), a lower bound for the kernels' rate."""
+    request), a lower bound for the kernels' rate."""
     import synth
 
     Qh, Kh, cu = synth.make_ragged(w)
@@ -487,7 +487,7 @@ def bench_ragged(args, w, sel, sp, torch, dev, steps, warmup, cpu_s):
     alg = alg_bytes_of(w, Ms)
     out = {"value": total / (res["ms_per_step"] / 1e3), "unit": "tokens/s", "M": total,
            "roofline": roofline(alg, res["kernel_ms_mean"] / 1e3, None),
-           "roofline_basis": "sp_score_varlen call (every request's prep and scoring kernel)",
+           "roofline_basis": "sp_score_varlen call (every request's scoring kernel)",
            "timing": res, "alg_bytes_per_step": alg, "requests": R,
            "config": dict(workload_desc(w, sel), M=total,
                           workload=f"{w.name}: R={R} prompts, M in [{int(Ms.min())}, "
@@ -513,7 +513,7 @@ def bench_windowed(args, w, sel, sp, torch, dev):
     its own synthetic queries and keys, as a speculator run per window gives):
     one step is sp_score_windows + sp_select over the prompt's M tokens. The
     roofline figure uses the sp_score_windows call's duration (one scoring
-    kernel per window plus its prep kernel)."""
+    kernel per window)."""
     import synth
 
     starts, lens, keeps = sp.sp_window_layout(w.M, args.window, args.stride)
@@ -557,7 +557,7 @@ def bench_windowed(args, w, sel, sp, torch, dev):
                                     f"stride {args.stride}: {R} windows",
                            window=args.window, stride=args.stride),
             "detail": {"timing": res, "alg_bytes_per_step": alg, "windows": R,
-                       "roofline_basis": "sp_score_windows call (every window's prep and "
+                       "roofline_basis": "sp_score_windows call (every window's "
                                          "scoring kernel)",
                        "n_kept": int(nk.cpu()[0])}}
 

@@ -248,7 +248,7 @@ def test_score_status_after_a_normal_call():
     Q, K = to_dev(Qh), to_dev(Kh)
     desc = sp.score_desc(w.L, w.H, w.Hkv, w.d, w.N)
     ws = torch.empty(sp.sp_score_workspace_bytes(desc, M), dtype=torch.uint8, device="cuda")
-    ws.fill_(0xff)  # (the prep kernel must clear the error word)
+    ws.fill_(0xff)  # (an error word left in the workspace must not count for this call)
     sp.sp_score(Q, K, workspace=ws)
     assert sp.sp_score_status(ws) is False
 
