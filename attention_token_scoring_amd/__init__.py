@@ -33,7 +33,8 @@ EXPORTED = ("sp_score", "sp_score_varlen", "sp_select", "sp_select_varlen",
             "sp_score_workspace_bytes", "sp_select_workspace_bytes", "sp_score_plan",
             "sp_status_string", "sp_profile_score_kernel", "sp_score_status",
             "sp_score_windows", "sp_window_layout", "sp_gather_rows", "sp_break_even",
-            "sp_read_probe", "sp_set_wait_limit", "sp_score_lastrow", "sp_score_noalloc")
+            "sp_read_probe", "sp_set_wait_limit", "sp_score_lastrow", "sp_score_noalloc",
+            "sp_score_select")
 
 
 class SpError(RuntimeError):
@@ -96,10 +97,12 @@ def load_library():
     lib.sp_set_wait_limit.argtypes = [ctypes.c_uint64]
     lib.sp_score_lastrow.argtypes = [P(ScoreDesc), vp, vp, vp, i32, vp, vp, sz, vp]
     lib.sp_score_noalloc.argtypes = [P(ScoreDesc), vp, vp, i32, vp, vp]
+    lib.sp_score_select.argtypes = [P(ScoreDesc), vp, vp, i32, P(SelectParams), i32, vp, vp, vp, vp,
+                                    vp, sz, vp]
     for name in ("sp_score_plan", "sp_score", "sp_score_varlen", "sp_select", "sp_select_varlen",
                  "sp_profile_score_kernel", "sp_score_status", "sp_score_windows",
                  "sp_window_layout", "sp_gather_rows", "sp_break_even", "sp_read_probe", "sp_set_wait_limit",
-                 "sp_score_lastrow", "sp_score_noalloc"):
+                 "sp_score_lastrow", "sp_score_noalloc", "sp_score_select"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -404,6 +407,39 @@ def sp_select(importance, params: SelectParams, pos_base: int = 0, kept_idx=None
                                   n_kept.data_ptr(), None, 0, _stream(stream))
     _check(st, "sp_select")
     return kept_idx, pos_ids, n_kept
+
+
+def sp_score_select(Q, K, params: SelectParams, pos_base: int = 0, M: Optional[int] = None,
+                    scale: float = 0.0, out=None, kept_idx=None, pos_ids=None, n_kept=None,
+                    workspace=None, stream=None, launch: int = SP_LAUNCH_RESIDENT):
+    """sp_score and sp_select of one prompt in one launch: (importance [M]
+    float32, kept_idx [M] int32, pos_ids [M] int32, n_kept [1] int32)."""
+    torch = _torch()
+    _require_cuda(Q, K)
+    L, H, N, d = Q.shape
+    Hkv = K.shape[1]
+    if M is None:
+        M = K.shape[2] - N
+    desc = score_desc(L, H, Hkv, d, N, _dtype_code(Q), scale, launch)
+    if _dtype_code(K) != desc.dtype or K.shape[0] != L or K.shape[3] != d or K.shape[2] != M + N:
+        raise ValueError("K must be [L, Hkv, M+N, d] with Q's dtype")
+    dev = Q.device
+    out = torch.empty(M, dtype=torch.float32, device=dev) if out is None else out
+    kept_idx = torch.empty(M, dtype=torch.int32, device=dev) if kept_idx is None else kept_idx
+    pos_ids = torch.empty(M, dtype=torch.int32, device=dev) if pos_ids is None else pos_ids
+    n_kept = torch.empty(1, dtype=torch.int32, device=dev) if n_kept is None else n_kept
+    _check_out(out, torch.float32, M, "out")
+    _check_out(kept_idx, torch.int32, M, "kept_idx")
+    _check_out(pos_ids, torch.int32, M, "pos_ids")
+    _check_out(n_kept, torch.int32, 1, "n_kept")
+    ws = _workspace(sp_score_workspace_bytes(desc, M), dev, workspace)
+    st = load_library().sp_score_select(ctypes.byref(desc), Q.data_ptr(), K.data_ptr(), int(M),
+                                        ctypes.byref(params), int(pos_base), out.data_ptr(),
+                                        kept_idx.data_ptr(), pos_ids.data_ptr(), n_kept.data_ptr(),
+                                        ws.data_ptr(), ws.numel() * ws.element_size(),
+                                        _stream(stream))
+    _check(st, "sp_score_select")
+    return out, kept_idx, pos_ids, n_kept
 
 
 def sp_select_varlen(importance, cu_prompt: Sequence[int], params: SelectParams,

@@ -16,7 +16,8 @@ namespace sp {
 
 hipError_t launch_score(const ScorePlan& p, const sp_score_desc& d, const void* Q, const void* K,
                         long long plane_stride, int M, int M_out, float* importance, void* ws,
-                        unsigned call_epoch, bool first, int tail_n, int blend_n, hipStream_t stream);
+                        unsigned call_epoch, bool first, int tail_n, int blend_n, const FusedSelect* fs,
+                        hipStream_t stream);
 unsigned next_epoch();
 hipError_t launch_gather(const void* src, long long row_bytes, const int32_t* kept,
                          const int32_t* n_kept, int R, const int64_t* cu, long long max_rows,
@@ -185,7 +186,7 @@ sp_status score_batch(const sp_score_desc* desc, int32_t R, const void* Q, const
         const long long M_out = keep ? keep[r] : M;
         float* imp = importance + (keep ? out : cu[r]);
         s = to_status(launch_score(p, *desc, Qr, Kr, T * desc->d, (int)M, (int)M_out, imp, ws, call,
-                                   r == 0, desc->N, 0, (hipStream_t)stream));
+                                   r == 0, desc->N, 0, nullptr, (hipStream_t)stream));
         if (s != SP_OK) return s;
         out += M_out;
     }
@@ -280,7 +281,33 @@ sp_status sp_score(const sp_score_desc* desc, const void* Q, const void* K, int3
     if (!ws || !aligned(ws, 256) || ws_bytes < p.ws_total) return SP_EWORKSPACE;
     const long long plane = (long long)(M + desc->N) * desc->d;
     return to_status(launch_score(p, *desc, Q, K, plane, M, M, importance, ws, next_epoch(), true,
-                                  desc->N, 0, (hipStream_t)stream));
+                                  desc->N, 0, nullptr, (hipStream_t)stream));
+}
+
+sp_status sp_score_select(const sp_score_desc* desc, const void* Q, const void* K, int32_t M,
+                          const sp_select_params* params, int32_t pos_base, float* importance,
+                          int32_t* kept_idx, int32_t* pos_ids, int32_t* n_kept, void* ws,
+                          size_t ws_bytes, void* stream) {
+    sp_status s = check_desc(desc);
+    if (s != SP_OK) return s;
+    s = check_select_params(params);
+    if (s != SP_OK) return s;
+    if (params->mode == SP_SELECT_THRESHOLD) return SP_EUNSUPPORTED;
+    if (!Q || !K || !importance || !kept_idx || !pos_ids || !n_kept || M < 1) return SP_EINVAL;
+    if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(importance, 4)) return SP_EINVAL;
+    s = check_select_prompt(params, M);
+    if (s != SP_OK) return s;
+    if ((long long)pos_base + M > 2147483647ll || (long long)pos_base < -2147483647ll) return SP_EINVAL;
+    const int cus = device_cus();
+    if (cus < 1) return SP_EDEVICE;
+    ScorePlan p;
+    s = make_plan(*desc, M, cus, &p);
+    if (s != SP_OK) return s;
+    if (!ws || !aligned(ws, 256) || ws_bytes < p.ws_total) return SP_EWORKSPACE;
+    const FusedSelect fs{to_dev(params), pos_base, kept_idx, pos_ids, n_kept};
+    const long long plane = (long long)(M + desc->N) * desc->d;
+    return to_status(launch_score(p, *desc, Q, K, plane, M, M, importance, ws, next_epoch(), true,
+                                  desc->N, 0, &fs, (hipStream_t)stream));
 }
 
 sp_status sp_score_noalloc(const sp_score_desc* desc, const void* Q, const void* K, int32_t M,
@@ -305,7 +332,7 @@ sp_status sp_score_noalloc(const sp_score_desc* desc, const void* Q, const void*
     if (g_scratch_err[dev] != hipSuccess || !g_scratch_ptr[dev]) return SP_EDEVICE;
     const long long plane = (long long)(M + desc->N) * desc->d;
     return to_status(launch_score(p, *desc, Q, K, plane, M, M, importance, g_scratch_ptr[dev],
-                                  next_epoch(), true, desc->N, 0, (hipStream_t)stream));
+                                  next_epoch(), true, desc->N, 0, nullptr, (hipStream_t)stream));
 }
 
 sp_status sp_score_lastrow(const sp_score_desc* desc, const void* Q, const void* Q_last,
@@ -332,10 +359,10 @@ sp_status sp_score_lastrow(const sp_score_desc* desc, const void* Q, const void*
     const long long plane = (long long)(M + desc->N) * desc->d;
     const unsigned call = next_epoch();
     s = to_status(launch_score(p, *desc, Q, K, plane, M, M, importance, ws, call, true, desc->N, 0,
-                               (hipStream_t)stream));
+                               nullptr, (hipStream_t)stream));
     if (s != SP_OK) return s;
     return to_status(launch_score(p1, d1, Q_last, K, plane, M, M, importance, ws, call, false, 0,
-                                  desc->N, (hipStream_t)stream));
+                                  desc->N, nullptr, (hipStream_t)stream));
 }
 
 sp_status sp_score_varlen(const sp_score_desc* desc, int32_t R, const void* Q, const void* K,

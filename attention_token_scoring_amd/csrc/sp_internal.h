@@ -23,9 +23,12 @@ constexpr int kTileKeys = 16;
 constexpr int kCombinerBatch = 16;
 constexpr int kMaxRanks = kWaves * 2 * kCombinerBatch;
 // The workspace header: the error word at byte 0, the last call's epoch at 8,
-// and from byte 128 one 8-byte flag per streaming workgroup (rank x group).
-constexpr int kHeaderBytes = 4096;
-constexpr int kMaxFlags = (kHeaderBytes - 128) / 8;
+// from byte 128 one 8-byte flag per streaming workgroup (rank x group: its
+// running maxima are in place), and from byte kDoneFlags one per streaming
+// workgroup (its scores are written; the fused selection waits for them).
+constexpr int kHeaderBytes = 8192;
+constexpr int kDoneFlags = 4096;
+constexpr int kMaxFlags = (kDoneFlags - 128) / 8;
 constexpr int kMaxDefer = 3;          // units between streaming and finishing a unit
 constexpr int kLdsBytes = 160 * 1024;  // LDS of one CU
 constexpr int kDefaultCUs = 256;       // MI355X; used when no device can be queried
@@ -93,6 +96,27 @@ inline ScoreLds score_lds_layout(int nbk, int tpw, int rows, int row_bytes, int 
     return l;
 }
 
+struct SelectParamsDev {
+    int chunk, pool_k, mode;
+    float keep_rate, mass;
+    int first_n;
+    float first_mult;
+    int last_n;
+    float last_mult;
+    int min_tok, max_keep;  // (threshold mode)
+    int norm;               // SP_NORM_MINMAX / SP_NORM_PERCENTILE / SP_NORM_ZSCORE
+    float norm_lo, norm_hi; // (percentile: the two quantiles; z-score: 0 and the clip c)
+};
+
+// The selection a fused scoring launch runs after its scores (sp_score_select).
+struct FusedSelect {
+    SelectParamsDev p;
+    int pos_base;
+    int32_t* kept;
+    int32_t* pos;
+    int32_t* n_kept;
+};
+
 // Everything the cooperative scoring kernel needs for one request.
 struct ScoreArgs {
     const void* Q;             // [L][H][N][d] of this request
@@ -126,6 +150,16 @@ struct ScoreArgs {
     int tail_n;                // look-ahead keys after the prompt, seen causally (N; 0: none)
     int blend_n;               // 0: write the scores; n > 0: importance = (n importance + score) / (n + 1)
     unsigned long long spin_ticks;  // limit of a bounded wait, in ticks of the 100 MHz clock
+    // Fused selection (sp_score_select): once every streaming workgroup has
+    // written its scores (flags in done), the last combiner workgroup selects
+    // from importance[0..M).
+    int sel;                   // 1: select after scoring
+    int sel_pos_base;
+    SelectParamsDev selp;
+    int32_t* sel_kept;         // [M]
+    int32_t* sel_pos;          // [M]
+    int32_t* sel_n;            // [1]
+    unsigned long long* done;  // [streaming workgroups]: (epoch << 32) | epoch once its scores are written
 };
 
 struct ScorePlan {
@@ -140,29 +174,6 @@ struct ScorePlan {
     int cus;       // compute units of the device planned for
     ScoreLds lds;
     size_t ws_err, ws_part, ws_lse, ws_tg, ws_total;  // byte offsets / sizes in the workspace
-};
-
-// Selection of one request (one workgroup).
-struct SelectReq {
-    const float* x;       // importance of this request
-    int32_t* kept;        // output region of this request
-    int32_t* pos;
-    int32_t* n_kept;      // one int
-    int M;
-    int pos_base;
-    int base_index;       // added to kept indices (packed offset of the request)
-};
-
-struct SelectParamsDev {
-    int chunk, pool_k, mode;
-    float keep_rate, mass;
-    int first_n;
-    float first_mult;
-    int last_n;
-    float last_mult;
-    int min_tok, max_keep;  // (threshold mode)
-    int norm;               // SP_NORM_MINMAX / SP_NORM_PERCENTILE / SP_NORM_ZSCORE
-    float norm_lo, norm_hi; // (percentile: the two quantiles; z-score: 0 and the clip c)
 };
 
 // Launch plan for one prompt of M keys on a device with cus compute units

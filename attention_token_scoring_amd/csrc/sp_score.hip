@@ -66,7 +66,8 @@ unsigned next_epoch() {
 // launch.
 hipError_t launch_score(const ScorePlan& p, const sp_score_desc& d, const void* Q, const void* K,
                         long long plane_stride, int M, int M_out, float* importance, void* ws,
-                        unsigned call_epoch, bool first, int tail_n, int blend_n, hipStream_t stream) {
+                        unsigned call_epoch, bool first, int tail_n, int blend_n, const FusedSelect* fs,
+                        hipStream_t stream) {
     char* base = (char*)ws;
     ScoreArgs a;
     a.Q = Q;
@@ -101,10 +102,22 @@ hipError_t launch_score(const ScorePlan& p, const sp_score_desc& d, const void* 
     a.tail_n = tail_n;
     a.blend_n = blend_n;
     a.spin_ticks = t_wait_limit > 0 ? t_wait_limit : kSpinTicks;
+    a.sel = fs ? 1 : 0;
+    a.done = (unsigned long long*)(base + p.ws_err + kDoneFlags);
+    if (fs) {
+        a.selp = fs->p;
+        a.sel_pos_base = fs->pos_base;
+        a.sel_kept = fs->kept;
+        a.sel_pos = fs->pos;
+        a.sel_n = fs->n_kept;
+    }
+    // (the fused selection reuses the combiner's LDS)
+    size_t lds = p.lds.total;
+    if (fs && lds < sizeof(SelectShared<kThreads>)) lds = sizeof(SelectShared<kThreads>);
 
     const void* fn = pick_kernel(d.dtype, d.d, p.rows, a.G, p.tpw, p.dma);
     if (!fn) return hipErrorInvalidValue;
-    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, p.lds.total);
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
 
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
@@ -124,15 +137,15 @@ hipError_t launch_score(const ScorePlan& p, const sp_score_desc& d, const void* 
         if (e != hipSuccess) return e;
     }
     if (d.launch == SP_LAUNCH_COOPERATIVE) {
-        e = hipLaunchCooperativeKernel(fn, dim3(p.grid), dim3(kThreads), args, (unsigned)p.lds.total, stream);
+        e = hipLaunchCooperativeKernel(fn, dim3(p.grid), dim3(kThreads), args, (unsigned)lds, stream);
     } else {
         // every workgroup must fit on the device at once (one per unit here)
         int per_cu = 0;
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, p.lds.total);
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, lds);
         if (e != hipSuccess) return e;
         if (per_cu < 1 || (long long)p.grid > (long long)per_cu * p.cus)
             return hipErrorCooperativeLaunchTooLarge;
-        e = hipLaunchKernel(fn, dim3(p.grid), dim3(kThreads), args, (unsigned)p.lds.total, stream);
+        e = hipLaunchKernel(fn, dim3(p.grid), dim3(kThreads), args, (unsigned)lds, stream);
     }
     if (e != hipSuccess) return e;
     if (t_ev_after) {

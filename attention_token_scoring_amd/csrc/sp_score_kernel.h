@@ -54,6 +54,7 @@
 #include <type_traits>
 
 #include "sp_internal.h"
+#include "sp_select_core.h"
 
 namespace sp {
 
@@ -346,6 +347,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t plane_rsrc(const ScoreArgs& a,
     return make_rsrc(plane, u < 0 ? 0u : plane_bytes);
 }
 
+// The fused selection, a function of its own (not inlined: with the
+// scoring kernel's register pressure the inlined selection does not compile),
+// on the launch's dynamic LDS.
+extern __shared__ __attribute__((aligned(16))) unsigned long long fused_lds[];
+__device__ __attribute__((noinline)) inline void fused_select(SelectParamsDev p, const float* x, int M, int pb,
+                                                              int32_t* kept, int32_t* pos, int32_t* n) {
+    select_prompt<kThreads>(*reinterpret_cast<SelectShared<kThreads>*>(fused_lds), p, x, M, 0, pb, kept, pos, n);
+}
+
 template <class C>
 __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
     constexpr int TPW = C::TPW, NH = C::NH, ROWS = C::ROWS, G = C::G, NLD = C::NLD;
@@ -461,6 +471,35 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
                 st64u(a.lse + ((size_t)u * ROWS + lane) * 2 + 1, v);
             }
             __syncthreads();  // (cred is rewritten for the next unit)
+        }
+        if (a.sel && cg == ncg - 1) {
+            // Fused selection: once every streaming workgroup has written its
+            // scores (its done flag carries the epoch; an agent-scope acquire
+            // then makes them visible to this CU's plain loads), the selection
+            // of the prompt runs here, on the LDS the combiner no longer needs.
+            const unsigned long long mark = ((unsigned long long)a.epoch << 32) | a.epoch;
+            bool expired = false;
+            if (w == 0) {
+                const unsigned long long t0 = wall_clock64();
+                while (true) {
+                    bool miss = false;
+                    for (int x = lane; x < nstream; x += 64) miss |= ld64(a.done + x) != mark;
+                    if (__ballot(miss) == 0) break;
+                    __builtin_amdgcn_s_sleep(2);
+                    if (wait_expired(t0, a)) {
+                        if (lane == 0) set_err(a);
+                        expired = true;
+                        break;
+                    }
+                }
+            }
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            if (__syncthreads_or(expired) || err_set(a)) {
+                // (scores missing or poisoned: no selection)
+                if (tid == 0) *a.sel_n = -1;
+                return;
+            }
+            fused_select(a.selp, a.importance, a.M, a.sel_pos_base, a.sel_kept, a.sel_pos, a.sel_n);
         }
         return;
     }
@@ -1262,6 +1301,12 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
         if (a.blend_n > 0) v = (a.importance[r0 + k] * (float)a.blend_n + v) / (float)(a.blend_n + 1);
         __hip_atomic_store((unsigned*)a.importance + r0 + k, poisoned ? kNaNBits : __float_as_uint(v),
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (a.sel) {
+        // this workgroup's scores are written (complete before the flag)
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (tid == 0) st64u(a.done + blockIdx.x, ((unsigned long long)a.epoch << 32) | a.epoch);
     }
 }
 

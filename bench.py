@@ -429,6 +429,29 @@ def bench_single(args, w, sels, sp, torch, dev, steps, warmup, cpu_s):
                                     "select_ms_mean": r["select_ms_mean"],
                                     "n_kept": int(nk.cpu()[0])}
         out["select_modes"] = modes
+    if sels[0].mode != "threshold":
+        # the same step as one launch (sp_score_select: the selection runs in
+        # the scoring launch, after its scores)
+        fparams = select_params(sp, sels[0])
+
+        def fused_step(i, kev=None, sev=None, xev=None):
+            if kev is not None:
+                sp.sp_profile_score_kernel(kev[0], kev[1])
+            if sev is not None:
+                sev[0].record()
+            sp.sp_score_select(Q, Ks[i % copies], fparams, M=M, out=imp, kept_idx=kept, pos_ids=pos,
+                               n_kept=nk, workspace=ws, launch=launch)
+            if sev is not None:
+                sev[1].record()
+            if kev is not None:
+                sp.sp_profile_score_kernel()
+            if xev is not None:
+                xev[0].record()
+                xev[1].record()
+
+        r = run_steps(torch, sp, fused_step, steps, warmup, args.settle_s, 50, ws)
+        out["fused"] = {"value": M / (r["ms_per_step"] / 1e3), "ms_per_step": r["ms_per_step"],
+                        "kernel_ms_mean": r["kernel_ms_mean"], "n_kept": int(nk.cpu()[0])}
     del Q, Ks, K0, ws
     torch.cuda.empty_cache()
     if cpu_s > 0:
@@ -685,7 +708,7 @@ def summary(r):
          "roofline": r["roofline"], "score_kernel_ms_mean": t["kernel_ms_mean"],
          "score_kernel_ms_median": t["kernel_ms_median"], "sp_score_ms_mean": t["sp_score_ms_mean"],
          "select_ms_mean": t["select_ms_mean"]}
-    for k in ("plan", "select_modes", "cpu_baseline", "cpu_baseline_1thread", "roofline_basis"):
+    for k in ("plan", "select_modes", "fused", "cpu_baseline", "cpu_baseline_1thread", "roofline_basis"):
         if k in r:
             s[k] = r[k]
     return s

@@ -383,8 +383,27 @@ sp_status sp_score_plan(const sp_score_desc* desc, int32_t M, int32_t info[9]);
 sp_status sp_profile_score_kernel(void* before, void* after);
 
 /*
- * Whether the last sp_score / sp_score_lastrow / sp_score_varlen / sp_score_windows call that
- * used workspace ws ran to completion without any of its bounded
+ * sp_score and sp_select of one prompt in one launch (the computation of
+ * each as cited there), for short prompts where a launch is a large part of
+ * the time: once every workgroup of the scoring kernel has written its
+ * scores, one of its workgroups (512 threads) runs the selection on them.
+ * The outputs are those of sp_score followed by sp_select with the same
+ * arguments, bit for bit.
+ *   desc, Q, K, M, ws, ws_bytes, stream  as for sp_score (importance is
+ *            written as well)
+ *   params, pos_base, kept_idx, pos_ids, n_kept  as for sp_select; the
+ *            top-K and mass modes only (SP_EUNSUPPORTED for the threshold mode)
+ * A time-out of the scoring kernel's bounded waits leaves n_kept = -1.
+ */
+sp_status sp_score_select(const sp_score_desc* desc, const void* Q, const void* K, int32_t M,
+                          const sp_select_params* params, int32_t pos_base, float* importance,
+                          int32_t* kept_idx, int32_t* pos_ids, int32_t* n_kept, void* ws,
+                          size_t ws_bytes, void* stream);
+
+/*
+ * Whether the last scoring call (sp_score, sp_score_lastrow, sp_score_select,
+ * sp_score_varlen or sp_score_windows) that used workspace ws ran to
+ * completion without any of its bounded
  * cross-workgroup waits running out (in any of its requests). The scoring
  * kernel never hangs: a wait that sees no progress for 2 s (which would take a
  * workgroup that never runs) gives up and marks the workspace; the

@@ -164,6 +164,27 @@ def test_select_chunk_count_limit(lib, mode, limit):
         == sp.SP_EUNSUPPORTED
 
 
+def test_score_select_rejects(lib):
+    """The fused call validates like sp_score and sp_select, and refuses the
+    threshold mode; every case fails before anything runs."""
+    d = desc()
+    ok = sp.select_params(chunk=32, pool_k=3, mode="topk", keep_rate=0.3)
+    thr = sp.select_params(chunk=32, pool_k=1, mode="threshold", keep_rate=0.3, min_tok=128)
+    bad = sp.select_params(chunk=0, pool_k=3, mode="topk", keep_rate=0.3)
+
+    def call(params, M=1000, kept=FAKE, pos_base=0, ws_bytes=1 << 30, dd=d):
+        return lib.sp_score_select(ctypes.byref(dd), FAKE, FAKE, M, ctypes.byref(params), pos_base,
+                                   FAKE, kept, FAKE, FAKE, FAKE, ws_bytes, None)
+
+    assert call(thr) == sp.SP_EUNSUPPORTED
+    assert call(bad) == sp.SP_EINVAL
+    assert call(ok, kept=None) == sp.SP_EINVAL
+    assert call(ok, M=0) == sp.SP_EINVAL
+    assert call(ok, M=5120 * 32 + 1) == sp.SP_EUNSUPPORTED
+    assert call(ok, pos_base=2147483600) == sp.SP_EINVAL
+    assert call(ok, dd=desc(N=0)) == sp.SP_EINVAL
+
+
 def test_select_rejects_null_and_sizes(lib):
     p = sp.select_params(chunk=32, pool_k=3, keep_rate=0.3)
     assert lib.sp_select(None, 100, ctypes.byref(p), 0, FAKE, FAKE, FAKE, None, 0, None) \
