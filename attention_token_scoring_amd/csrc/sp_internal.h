@@ -47,7 +47,11 @@ constexpr bool score_roomy(int row_bytes, int tpw, int nh) {
 // apart.
 constexpr int row_stride(int kr) { return (kr + 63) / 64 * 64 + 16; }
 
-// Byte offsets of the scoring kernel's LDS regions (all 16-byte aligned).
+// K slots per streaming wave when K goes by DMA into LDS: one per tile of a
+// unit, at most 4 for 256-byte key rows (the LDS holds 7 x 4 tiles of 4 KB
+// besides the kernel's other regions). (Two units' worth for 128-byte rows,
+// twice the bytes in flight, measured no faster at the 0.8B shape.)
+constexpr int dma_slots(int row_bytes, int tpw) { return row_bytes >= 256 && tpw > 4 ? 4 : tpw; }
 // LDS bytes of the DMA kernel's static region (Q, statistics, references,
 // log-sum-exps), besides its dynamic K slots.
 constexpr int dma_static_lds(int rows, int row_bytes, int N_unused = 0) {
@@ -55,6 +59,7 @@ constexpr int dma_static_lds(int rows, int row_bytes, int N_unused = 0) {
            2 * rows * 4 + N_unused * 0;
 }
 
+// Byte offsets of the scoring kernel's LDS regions (all 16-byte aligned).
 struct ScoreLds {
     int bank;   // [nbk][SW][TPW][64 lanes][NH][4]: parked logits, 16-bit codes
     int ref;    // [nbk][SW][rows] float: reference (log2 domain) of the parked logits
@@ -75,8 +80,7 @@ inline ScoreLds score_lds_layout(int nbk, int tpw, int rows, int row_bytes, int 
     l.bank = 0;
     // the running maxima are written once, at the end, over the banks
     l.trun = 0;
-    // (DMA slots per wave: one per tile, at most 4 for 256-byte rows)
-    const int slots = (row_bytes >= 256 && tpw > 4) ? 4 : tpw;
+    const int slots = dma_slots(row_bytes, tpw);
     const int banks = dma ? kStreamWaves * slots * kTileKeys * row_bytes
                           : nbk * kStreamWaves * tpw * 64 * nh * 8;
     if (dma) {

@@ -257,9 +257,9 @@ struct Cfg {
     // sit in G adjacent lanes of one half
     static_assert(G <= 16 || (G == 32 && NH == 2), "unsupported head grouping");
     static constexpr int GL = G == 32 ? 16 : G;  // heads of a step within one half
-    // DMA slots per streaming wave: one per tile of the slice, at most 4 for
-    // 256-byte key rows (the LDS holds 7 x 4 tiles of 4 KB besides the rest)
-    static constexpr int S = !DMA ? 0 : (KB >= 256 && TPW > 4 ? 4 : TPW);
+    // DMA slots per streaming wave (one per tile of a unit, at most 4 for
+    // 256-byte key rows)
+    static constexpr int S = !DMA ? 0 : dma_slots(KB, TPW);
 };
 
 // s_waitcnt operands (gfx9 encoding): vector memory count n, nothing else
@@ -1246,45 +1246,59 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
         const int share = (nout + a.ngroups - 1) / a.ngroups;
         k_lo = min(group * share, nout);
         k_hi = min(k_lo + share, nout);
-        // XB values per thread, the other groups' copies GB at a time: XB * GB
-        // = 60 independent loads in flight (a wave can have 63) instead of one
-        // round trip each. Every load is issued unconditionally from an
-        // address in bounds (lanes past the end read element 0, batches past
-        // the last group re-read it; neither changes a max), so that none
-        // waits for another.
-        constexpr int XB = 4, GB = 15;
+        // XB values per thread, the other groups' copies GB at a time: up to
+        // XB * GB = 60 independent loads in flight (a wave can have 63)
+        // instead of one round trip each, shaped to the merge (XB = 1 when
+        // one pass covers the values, GB the smallest that covers the other
+        // groups), since the issue of a wave's loads, not their latency, is
+        // what a small merge waits for. Every load is issued unconditionally
+        // from an address in bounds (lanes past the end read element 0,
+        // batches past the last group re-read it; neither changes a max), so
+        // that none waits for another.
         const int cnt = k_hi - k_lo;
         const int total = a.N * cnt;
         const size_t gstride = (size_t)a.N * a.M;
         const int last_other = a.ngroups - 2;  // the others, as 0 .. ngroups - 2
-        for (int x0 = 0; x0 < total; x0 += kThreads * XB) {
-            int v[XB], li[XB], go[XB];
+        auto merge = [&](auto XBc, auto GBc) __attribute__((always_inline)) {
+            constexpr int XB = decltype(XBc)::value, GB = decltype(GBc)::value;
+            for (int x0 = 0; x0 < total; x0 += kThreads * XB) {
+                int v[XB], li[XB], go[XB];
 #pragma unroll
-            for (int i = 0; i < XB; ++i) {
-                const int x = x0 + i * kThreads + tid;
-                const int jj = x / cnt, k = k_lo + x - jj * cnt;
-                li[i] = x < total ? jj * KRP + k : -1;
-                go[i] = x < total ? jj * a.M + r0 + k : 0;
-                v[i] = x < total ? Trun[li[i]] : kNegInf;
-            }
-            for (int gb = 0; gb <= last_other; gb += GB) {
-                int t[GB][XB];
+                for (int i = 0; i < XB; ++i) {
+                    const int x = x0 + i * kThreads + tid;
+                    const int jj = x / cnt, k = k_lo + x - jj * cnt;
+                    li[i] = x < total ? jj * KRP + k : -1;
+                    go[i] = x < total ? jj * a.M + r0 + k : 0;
+                    v[i] = x < total ? Trun[li[i]] : kNegInf;
+                }
+                for (int gb = 0; gb <= last_other; gb += GB) {
+                    int t[GB][XB];
 #pragma unroll
-                for (int y = 0; y < GB; ++y) {
-                    const int o = min(gb + y, last_other);
-                    const int* tg = a.Tg + (size_t)(o + (o >= group ? 1 : 0)) * gstride;
+                    for (int y = 0; y < GB; ++y) {
+                        const int o = min(gb + y, last_other);
+                        const int* tg = a.Tg + (size_t)(o + (o >= group ? 1 : 0)) * gstride;
 #pragma unroll
-                    for (int i = 0; i < XB; ++i) t[y][i] = (int)ld32(tg + go[i]);
+                        for (int i = 0; i < XB; ++i) t[y][i] = (int)ld32(tg + go[i]);
+                    }
+                    // (every load issued before the first max: the scheduler
+                    // would otherwise interleave them, a wait between each)
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int y = 0; y < GB; ++y)
+#pragma unroll
+                        for (int i = 0; i < XB; ++i) v[i] = max(v[i], t[y][i]);
                 }
 #pragma unroll
-                for (int y = 0; y < GB; ++y)
-#pragma unroll
-                    for (int i = 0; i < XB; ++i) v[i] = max(v[i], t[y][i]);
+                for (int i = 0; i < XB; ++i)
+                    if (li[i] >= 0) Trun[li[i]] = v[i];
             }
-#pragma unroll
-            for (int i = 0; i < XB; ++i)
-                if (li[i] >= 0) Trun[li[i]] = v[i];
-        }
+        };
+        using I = std::integral_constant<int, 1>;
+        if (last_other < 3) merge(std::integral_constant<int, 4>{}, std::integral_constant<int, 3>{});
+        else if (last_other < 7) merge(std::integral_constant<int, 4>{}, std::integral_constant<int, 7>{});
+        else if (total > kThreads) merge(std::integral_constant<int, 4>{}, std::integral_constant<int, 15>{});
+        else if (last_other < 30) merge(I{}, std::integral_constant<int, 30>{});
+        else merge(I{}, std::integral_constant<int, 60>{});
         __syncthreads();
     }
     // A call in which some bounded wait gave up (here or in any workgroup
