@@ -157,7 +157,6 @@ struct ScoreArgs {
     // Fused selection (sp_score_select): once every streaming workgroup has
     // written its scores (flags in done), the last combiner workgroup selects
     // from importance[0..M).
-    int sel;                   // 1: select after scoring
     int sel_pos_base;
     SelectParamsDev selp;
     int32_t* sel_kept;         // [M]
@@ -201,5 +200,9 @@ const void* score_kernel_bf16_d128(int rows, int G, int tpw, bool dma);
 const void* score_kernel_bf16_d64(int rows, int G, int tpw, bool dma);
 const void* score_kernel_f32_d128(int rows, int G, int tpw, bool dma);
 const void* score_kernel_f32_d64(int rows, int G, int tpw, bool dma);
+const void* score_select_kernel_bf16_d128(int rows, int G, int tpw, bool dma);
+const void* score_select_kernel_bf16_d64(int rows, int G, int tpw, bool dma);
+const void* score_select_kernel_f32_d128(int rows, int G, int tpw, bool dma);
+const void* score_select_kernel_f32_d64(int rows, int G, int tpw, bool dma);
 
 }  // namespace sp

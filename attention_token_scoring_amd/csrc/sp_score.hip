@@ -19,13 +19,18 @@ __global__ __launch_bounds__(256) void clear_tags_kernel(uint4* p, size_t n16) {
 // ---------------------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------------------
-static const void* pick_kernel(int dtype, int d, int rows, int G, int tpw, bool dma) {
+// The scoring kernel for a launch plan (sel: the fused launch that also selects).
+static const void* pick_kernel(int dtype, int d, int rows, int G, int tpw, bool dma, bool sel) {
     if (dtype == SP_BF16) {
-        if (d == 128) return score_kernel_bf16_d128(rows, G, tpw, dma);
-        if (d == 64) return score_kernel_bf16_d64(rows, G, tpw, dma);
+        if (d == 128)
+            return sel ? score_select_kernel_bf16_d128(rows, G, tpw, dma) : score_kernel_bf16_d128(rows, G, tpw, dma);
+        if (d == 64)
+            return sel ? score_select_kernel_bf16_d64(rows, G, tpw, dma) : score_kernel_bf16_d64(rows, G, tpw, dma);
     } else {
-        if (d == 128) return score_kernel_f32_d128(rows, G, tpw, dma);
-        if (d == 64) return score_kernel_f32_d64(rows, G, tpw, dma);
+        if (d == 128)
+            return sel ? score_select_kernel_f32_d128(rows, G, tpw, dma) : score_kernel_f32_d128(rows, G, tpw, dma);
+        if (d == 64)
+            return sel ? score_select_kernel_f32_d64(rows, G, tpw, dma) : score_kernel_f32_d64(rows, G, tpw, dma);
     }
     return nullptr;
 }
@@ -102,7 +107,6 @@ hipError_t launch_score(const ScorePlan& p, const sp_score_desc& d, const void* 
     a.tail_n = tail_n;
     a.blend_n = blend_n;
     a.spin_ticks = t_wait_limit > 0 ? t_wait_limit : kSpinTicks;
-    a.sel = fs ? 1 : 0;
     a.done = (unsigned long long*)(base + p.ws_err + kDoneFlags);
     if (fs) {
         a.selp = fs->p;
@@ -115,7 +119,7 @@ hipError_t launch_score(const ScorePlan& p, const sp_score_desc& d, const void* 
     size_t lds = p.lds.total;
     if (fs && lds < sizeof(SelectShared<kThreads>)) lds = sizeof(SelectShared<kThreads>);
 
-    const void* fn = pick_kernel(d.dtype, d.d, p.rows, a.G, p.tpw, p.dma);
+    const void* fn = pick_kernel(d.dtype, d.d, p.rows, a.G, p.tpw, p.dma, fs != nullptr);
     if (!fn) return hipErrorInvalidValue;
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;

@@ -356,7 +356,8 @@ __device__ __attribute__((noinline)) inline void fused_select(SelectParamsDev p,
     select_prompt<kThreads>(*reinterpret_cast<SelectShared<kThreads>*>(fused_lds), p, x, M, 0, pb, kept, pos, n);
 }
 
-template <class C>
+// SEL: the fused launch (sp_score_select), which also selects from the scores.
+template <class C, bool SEL>
 __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
     constexpr int TPW = C::TPW, NH = C::NH, ROWS = C::ROWS, G = C::G, NLD = C::NLD;
     constexpr int SW = kStreamWaves;  // waves 0..SW-1 stream K; wave SW synchronises
@@ -472,7 +473,7 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
             }
             __syncthreads();  // (cred is rewritten for the next unit)
         }
-        if (a.sel && cg == ncg - 1) {
+        if (SEL && cg == ncg - 1) {
             // Fused selection: once every streaming workgroup has written its
             // scores (its done flag carries the epoch; an agent-scope acquire
             // then makes them visible to this CU's plain loads), the selection
@@ -1316,7 +1317,7 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
         __hip_atomic_store((unsigned*)a.importance + r0 + k, poisoned ? kNaNBits : __float_as_uint(v),
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    if (a.sel) {
+    if constexpr (SEL) {
         // this workgroup's scores are written (complete before the flag)
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
@@ -1324,26 +1325,26 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
     }
 }
 
-template <class C>
+template <class C, bool SEL>
 const void* kernel_ptr() {
-    return (const void*)&score_kernel<C>;
+    return (const void*)&score_kernel<C, SEL>;
 }
 
 // The instantiation for head-group size G (nullptr when unsupported).
-template <int D, bool BF, int NH, int TPW, bool DMA>
+template <int D, bool BF, int NH, int TPW, bool DMA, bool SEL>
 const void* pick_g(int G) {
     switch (G) {
         case 1:
             // (one head per step and two halves keep 32 running maxima per
             // lane: only the base tile count fits the registers)
             if constexpr (NH == 2 && TPW > tiles_per_wave(BF, D)) return nullptr;
-            else return kernel_ptr<Cfg<D, BF, NH, 1, TPW, DMA>>();
-        case 2: return kernel_ptr<Cfg<D, BF, NH, 2, TPW, DMA>>();
-        case 4: return kernel_ptr<Cfg<D, BF, NH, 4, TPW, DMA>>();
-        case 8: return kernel_ptr<Cfg<D, BF, NH, 8, TPW, DMA>>();
-        case 16: return kernel_ptr<Cfg<D, BF, NH, 16, TPW, DMA>>();
+            else return kernel_ptr<Cfg<D, BF, NH, 1, TPW, DMA>, SEL>();
+        case 2: return kernel_ptr<Cfg<D, BF, NH, 2, TPW, DMA>, SEL>();
+        case 4: return kernel_ptr<Cfg<D, BF, NH, 4, TPW, DMA>, SEL>();
+        case 8: return kernel_ptr<Cfg<D, BF, NH, 8, TPW, DMA>, SEL>();
+        case 16: return kernel_ptr<Cfg<D, BF, NH, 16, TPW, DMA>, SEL>();
         case 32:
-            if constexpr (NH == 2) return kernel_ptr<Cfg<D, BF, 2, 32, TPW, DMA>>();
+            if constexpr (NH == 2) return kernel_ptr<Cfg<D, BF, 2, 32, TPW, DMA>, SEL>();
             return nullptr;
         default: return nullptr;
     }
@@ -1352,20 +1353,20 @@ const void* pick_g(int G) {
 // The instantiation for (rows, G, tiles per wave, K path) of one operand type
 // and head dimension; TPW is tiles_per_wave(BF, D) or one more; the DMA path
 // exists for bf16 at the base tile count.
-template <int D, bool BF>
+template <int D, bool BF, bool SEL>
 const void* pick_kernel_for(int rows, int G, int tpw, bool dma) {
     constexpr int T0 = tiles_per_wave(BF, D);
     if (dma) {
         if constexpr (BF) {
-            if (tpw == T0) return rows == 32 ? pick_g<D, BF, 2, T0, true>(G) : pick_g<D, BF, 1, T0, true>(G);
+            if (tpw == T0) return rows == 32 ? pick_g<D, BF, 2, T0, true, SEL>(G) : pick_g<D, BF, 1, T0, true, SEL>(G);
             if (tpw == T0 + 1)
-                return rows == 32 ? pick_g<D, BF, 2, T0 + 1, true>(G) : pick_g<D, BF, 1, T0 + 1, true>(G);
+                return rows == 32 ? pick_g<D, BF, 2, T0 + 1, true, SEL>(G) : pick_g<D, BF, 1, T0 + 1, true, SEL>(G);
         }
         return nullptr;
     }
-    if (tpw == T0) return rows == 32 ? pick_g<D, BF, 2, T0, false>(G) : pick_g<D, BF, 1, T0, false>(G);
+    if (tpw == T0) return rows == 32 ? pick_g<D, BF, 2, T0, false, SEL>(G) : pick_g<D, BF, 1, T0, false, SEL>(G);
     if (tpw == T0 + 1)
-        return rows == 32 ? pick_g<D, BF, 2, T0 + 1, false>(G) : pick_g<D, BF, 1, T0 + 1, false>(G);
+        return rows == 32 ? pick_g<D, BF, 2, T0 + 1, false, SEL>(G) : pick_g<D, BF, 1, T0 + 1, false, SEL>(G);
     return nullptr;
 }
 

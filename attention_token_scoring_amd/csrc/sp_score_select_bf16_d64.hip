@@ -1,0 +1,10 @@
+// Instantiations of the fused scoring-and-selection kernel for bf16 operands, head dimension 64.
+#include "sp_score_kernel.h"
+
+namespace sp {
+
+const void* score_select_kernel_bf16_d64(int rows, int G, int tpw, bool dma) {
+    return pick_kernel_for<64, true, true>(rows, G, tpw, dma);
+}
+
+}  // namespace sp

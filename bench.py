@@ -103,7 +103,10 @@ def parse():
     return args
 
 
+# the scoring kernel's plain launch (sp_score); the fused launch
+# (sp_score_select) is the instantiation with true in its last place
 SCORE_KERNEL = "sp::score_kernel<"
+SCORE_KERNEL_PLAIN = ", false>(sp::ScoreArgs)"
 # the calibration probe is the run's only elementwise add
 PROBE_KERNEL_HINTS = ("elementwise", "add")
 
@@ -154,7 +157,7 @@ def write_traffic(fetch_db: str, write_db: str, workload: str, copy_mib: int):
     out = {"workload": workload, "source_sha": kernel_source_sha(), "copy_probe_mib": copy_mib}
     for key, db, counter in (("fetch", fetch_db, "FETCH_SIZE"), ("write", write_db, "WRITE_SIZE")):
         rows = pmc_per_dispatch(db, counter)
-        score = [v for n, v in rows if SCORE_KERNEL in n]
+        score = [v for n, v in rows if SCORE_KERNEL in n and SCORE_KERNEL_PLAIN in n]
         probes = [v for n, v in rows if all(h in n.lower() for h in PROBE_KERNEL_HINTS)]
         if not score or len(probes) != 1:
             raise SystemExit(f"{db}: no {counter} for the scoring kernel, or not exactly one probe")
