@@ -118,6 +118,32 @@ def test_score_several_units_per_group(case):
     check_importance(imp.cpu().numpy(), oracle.score(Qh, Kh), name)
 
 
+# Shapes whose cross-group merge takes the batch shapes the other cases do not:
+# at least 9 other groups with more than 512 values for some workgroup (4 values
+# per thread, 15 groups per batch), and more than 30 other groups (1 value per
+# thread, 60 groups per batch). (ngroups, values) follow from the plan: a
+# workgroup's share of its slice is ceil(keys / ngroups), times N steps.
+MERGE_CASES = [
+    ("merge-4x15-bf16-d64-N16", 8, 16, 8, 64, 16, 8192, BF, lambda ng, vals: ng >= 10 and max(vals) > 512),
+    ("merge-1x60-bf16-d128", 8, 32, 8, 128, 8, 3000, BF, lambda ng, vals: ng >= 32 and max(vals) <= 512),
+]
+
+
+@pytest.mark.parametrize("case", MERGE_CASES, ids=[c[0] for c in MERGE_CASES])
+def test_score_cross_group_merge_shapes(case):
+    name, L, H, Hkv, d, N, M, dt, covers = case
+    print(f"case {name}", flush=True)
+    plan = sp.sp_score_plan(sp.score_desc(L, H, Hkv, d, N, sp.SP_BF16 if dt else sp.SP_F32), M)
+    ng, g, kr = plan["ngroups"], plan["g"], plan["keys_per_wg"]
+    vals = [N * -(-max(min(r * kr + kr, M + N, M) - r * kr, 0) // ng) for r in range(g)]
+    assert covers(ng, vals), (plan, vals)
+    w = workload(L, H, Hkv, d, N, M, dt, seed=17)
+    Qh, Kh, _ = synth.make_request(w)
+    imp = sp.sp_score(to_dev(Qh), to_dev(Kh))
+    torch.cuda.synchronize()
+    check_importance(imp.cpu().numpy(), oracle.score(Qh, Kh), name)
+
+
 @pytest.mark.parametrize("case", SMALL_CASES, ids=[c[0] for c in SMALL_CASES])
 def test_score_small_shapes(case):
     name, L, H, Hkv, d, N, M, dt = case
