@@ -24,11 +24,17 @@ constexpr int kCombinerBatch = 16;
 constexpr int kMaxRanks = kWaves * 2 * kCombinerBatch;
 // The workspace header: the error word at byte 0, the last call's epoch at 8,
 // from byte 128 one 8-byte flag per streaming workgroup (rank x group: its
-// running maxima are in place), and from byte kDoneFlags one per streaming
-// workgroup (its scores are written; the fused selection waits for them).
+// running maxima are in place), and from byte kDoneFlags two 8-byte words per
+// streaming workgroup (the min and max of its scores once written; the fused
+// selection waits for them).
 constexpr int kHeaderBytes = 8192;
 constexpr int kDoneFlags = 4096;
 constexpr int kMaxFlags = (kDoneFlags - 128) / 8;
+constexpr int kMaxDone = (kHeaderBytes - kDoneFlags) / 16;
+// Per-prompt chunk limit of the selection (five per thread at 1024 threads:
+// 5120 covers the longest prompt the scoring kernel takes, 142,792 tokens, at
+// chunk 28 or more); the fused launch's chunk-mass slots are sized by it.
+constexpr int kSelMaxChunks = 5120;
 constexpr int kMaxDefer = 3;          // units between streaming and finishing a unit
 constexpr int kLdsBytes = 160 * 1024;  // LDS of one CU
 constexpr int kDefaultCUs = 256;       // MI355X; used when no device can be queried
@@ -162,7 +168,9 @@ struct ScoreArgs {
     int32_t* sel_kept;         // [M]
     int32_t* sel_pos;          // [M]
     int32_t* sel_n;            // [1]
-    unsigned long long* done;  // [streaming workgroups]: (epoch << 32) | epoch once its scores are written
+    unsigned long long* done;  // [streaming workgroups][2]: its scores' min | epoch, max | epoch, once written
+    unsigned long long* sel_sums;  // [chunks][2]: a chunk's fixed-point mass, low | epoch, high | epoch
+    int sel_dist;              // 1: the streaming workgroups sum the chunk masses
 };
 
 struct ScorePlan {
@@ -176,7 +184,7 @@ struct ScorePlan {
     int defer;
     int cus;       // compute units of the device planned for
     ScoreLds lds;
-    size_t ws_err, ws_part, ws_lse, ws_tg, ws_total;  // byte offsets / sizes in the workspace
+    size_t ws_err, ws_part, ws_lse, ws_sel, ws_tg, ws_total;  // byte offsets / sizes in the workspace
 };
 
 // Launch plan for one prompt of M keys on a device with cus compute units

@@ -355,6 +355,143 @@ __device__ __attribute__((noinline)) inline void fused_select(SelectParamsDev p,
                                                               int32_t* kept, int32_t* pos, int32_t* n) {
     select_prompt<kThreads>(*reinterpret_cast<SelectShared<kThreads>*>(fused_lds), p, x, M, 0, pb, kept, pos, n);
 }
+// Steps 4-7 only, from chunk masses already in the LDS.
+__device__ __attribute__((noinline)) inline void fused_select_ranked(SelectParamsDev p, int M, int pb, int32_t* kept,
+                                                                     int32_t* pos, int32_t* n) {
+    select_ranked<kThreads>(*reinterpret_cast<SelectShared<kThreads>*>(fused_lds), p, M, 0, pb, kept, pos, n);
+}
+
+// A share's min and max as published for the fused selection: the words
+// carry the epoch; a share holding a non-finite score publishes this max.
+constexpr unsigned kNonFiniteMark = 0xffffffffu;
+
+// The streaming workgroups' end of a fused launch. Without sel_dist the
+// workgroup raises a tagged flag once its scores are written. With it, the
+// workgroup publishes the min and max of the scores it wrote (complete before
+// the words), waits for every workgroup's, and sums the fixed-point masses of
+// chunks sw, sw + nstream, ... (sw = its index) over the scores (every token's
+// value and boosts as the selection computes them; the sums are exact, so the
+// split does not change them), each chunk's mass stored as two tagged words.
+// (what the tail reads of the launch's arguments, passed by value: a
+// reference to the kernel's arguments breaks the compiler's register
+// allocation when the tail is a function of its own, and as one its call
+// costs stack space and register saves)
+struct TailArgs {
+    unsigned long long* err;
+    unsigned long long* done;
+    unsigned long long* sel_sums;
+    const float* importance;
+    unsigned long long spin_ticks;
+    unsigned epoch, call_epoch;
+    int M;
+    int sel_dist;
+    SelectParamsDev selp;
+};
+__device__ __forceinline__ void fused_tail(TailArgs a, float smn, float smx, int snf, int nstream) {
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    __shared__ float mm[2 * kWaves];
+    __shared__ float gmm[2];
+    __shared__ int gbad;
+    const unsigned long long Et = (unsigned long long)a.epoch << 32;
+    if (!a.sel_dist) {
+        // (the selecting workgroup does every step: it only needs to know
+        // that the scores are written)
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (tid == 0) st64u(a.done + 2 * blockIdx.x, Et | a.epoch);
+        return;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        smn = fminf(smn, __shfl_xor(smn, o));
+        smx = fmaxf(smx, __shfl_xor(smx, o));
+    }
+    if (lane == 0) {
+        mm[w] = smn;
+        mm[kWaves + w] = smx;
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this workgroup's scores are written
+    const bool nf = __syncthreads_or(snf);
+    if (tid == 0) {
+        float m0 = mm[0], m1 = mm[kWaves];
+        for (int x = 1; x < kWaves; ++x) {
+            m0 = fminf(m0, mm[x]);
+            m1 = fmaxf(m1, mm[kWaves + x]);
+        }
+        st64u(a.done + 2 * blockIdx.x, Et | __float_as_uint(m0));
+        st64u(a.done + 2 * blockIdx.x + 1, Et | (nf ? kNonFiniteMark : __float_as_uint(m1)));
+    }
+    const int chunk = a.selp.chunk;
+    const int nc = (a.M + chunk - 1) / chunk;
+    const int sw = blockIdx.x;
+    const int nj = sw < nc ? (nc - sw + nstream - 1) / nstream : 0;  // this workgroup's chunks
+    if (nj == 0) return;
+    if (w == 0) {
+        // every workgroup's min and max; lane x watches workgroups x, x + 64, ...
+        float gmn = INFINITY, gmx = -INFINITY;
+        bool bad = false;
+        const unsigned long long t0 = wall_clock64();
+        while (true) {
+            bool miss = false, nfx = false;
+            gmn = INFINITY;
+            gmx = -INFINITY;
+            for (int x = lane; x < nstream; x += 64) {
+                const unsigned long long lo = ld64(a.done + 2 * x), hi = ld64(a.done + 2 * x + 1);
+                miss |= !(tag_is(lo, a.epoch) && tag_is(hi, a.epoch));
+                nfx |= (unsigned)hi == kNonFiniteMark;
+                gmn = fminf(gmn, tag_value(lo));
+                gmx = fmaxf(gmx, tag_value(hi));
+            }
+            if (__ballot(miss) == 0) {
+                bad = __ballot(nfx) != 0;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+            if (wait_expired(t0, a)) {
+                if (lane == 0) set_err(a);
+                bad = true;
+                break;
+            }
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            gmn = fminf(gmn, __shfl_xor(gmn, o));
+            gmx = fmaxf(gmx, __shfl_xor(gmx, o));
+        }
+        if (lane == 0) {
+            gmm[0] = gmn;
+            gmm[1] = gmx;
+            gbad = bad ? 1 : 0;
+        }
+    }
+    __syncthreads();
+    if (gbad) return;  // (the selecting workgroup reports it)
+    MinMaxNorm nm;
+    nm.init(gmm[0], gmm[1]);
+    unsigned long long* sums = fused_lds;  // (the launch's dynamic LDS: its K slots are free now)
+    constexpr int kB = 256;  // chunks per batch
+    for (int jb = 0; jb < nj; jb += kB) {
+        const int nb = min(kB, nj - jb);
+        for (int t = tid; t < nb; t += kThreads) sums[t] = 0ull;
+        __syncthreads();
+        for (int f = tid; f < nb * chunk; f += kThreads) {
+            const int j = f / chunk, e = f - j * chunk;
+            const int i = (sw + (jb + j) * nstream) * chunk + e;
+            // (agent-scope loads see the other workgroups' scores; an acquire
+            // fence in every workgroup instead costs more than the loads)
+            if (i < a.M)
+                atomicAdd(&sums[j], token_mass(nm.value(__uint_as_float(ld32(a.importance + i))), i, a.M, a.selp));
+        }
+        __syncthreads();
+        for (int t = tid; t < nb; t += kThreads) {
+            const unsigned long long v = sums[t];
+            unsigned long long* sl = a.sel_sums + 2 * (sw + (jb + t) * nstream);
+            st64u(sl, Et | (unsigned)v);
+            st64u(sl + 1, Et | (unsigned)(v >> 32));
+        }
+        __syncthreads();  // (sums is rewritten by the next batch)
+    }
+}
 
 // SEL: the fused launch (sp_score_select), which also selects from the scores.
 template <class C, bool SEL>
@@ -474,18 +611,36 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
             __syncthreads();  // (cred is rewritten for the next unit)
         }
         if (SEL && cg == ncg - 1) {
-            // Fused selection: once every streaming workgroup has written its
-            // scores (its done flag carries the epoch; an agent-scope acquire
-            // then makes them visible to this CU's plain loads), the selection
-            // of the prompt runs here, on the LDS the combiner no longer needs.
-            const unsigned long long mark = ((unsigned long long)a.epoch << 32) | a.epoch;
-            bool expired = false;
+            // Fused selection, once every streaming workgroup has written its
+            // scores (each raises a tagged flag). When the streaming
+            // workgroups sum the chunks' fixed-point masses between them
+            // (sel_dist: min-max normalisation, long prompts; exact integers,
+            // so the split does not change them), the flag is the min and max
+            // of the workgroup's scores (or a mark that one is not finite),
+            // and this workgroup gathers the masses and ranks; otherwise it
+            // runs every step itself on the scores (an agent-scope acquire
+            // makes them visible to this CU's plain loads). Either way on the
+            // LDS the combiner no longer needs.
+            bool expired = false, nonfinite = false;
             if (w == 0) {
                 const unsigned long long t0 = wall_clock64();
                 while (true) {
-                    bool miss = false;
-                    for (int x = lane; x < nstream; x += 64) miss |= ld64(a.done + x) != mark;
-                    if (__ballot(miss) == 0) break;
+                    bool miss = false, nf = false;
+                    if (a.sel_dist) {
+                        for (int x = lane; x < nstream; x += 64) {
+                            const unsigned long long lo = ld64(a.done + 2 * x), hi = ld64(a.done + 2 * x + 1);
+                            miss |= !(tag_is(lo, a.epoch) && tag_is(hi, a.epoch));
+                            nf |= (unsigned)hi == kNonFiniteMark;
+                        }
+                    } else {
+                        // (the scores' own check finds non-finite ones)
+                        const unsigned long long mark = ((unsigned long long)a.epoch << 32) | a.epoch;
+                        for (int x = lane; x < nstream; x += 64) miss |= ld64(a.done + 2 * x) != mark;
+                    }
+                    if (__ballot(miss) == 0) {
+                        nonfinite = __ballot(nf) != 0;
+                        break;
+                    }
                     __builtin_amdgcn_s_sleep(2);
                     if (wait_expired(t0, a)) {
                         if (lane == 0) set_err(a);
@@ -494,13 +649,57 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
                     }
                 }
             }
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-            if (__syncthreads_or(expired) || err_set(a)) {
-                // (scores missing or poisoned: no selection)
+            if (__syncthreads_or(expired || nonfinite) || err_set(a)) {
+                // (scores missing, poisoned or not finite: no selection)
                 if (tid == 0) *a.sel_n = -1;
                 return;
             }
-            fused_select(a.selp, a.importance, a.M, a.sel_pos_base, a.sel_kept, a.sel_pos, a.sel_n);
+            if (a.sel_dist) {
+                SelectShared<kThreads>& sh = *reinterpret_cast<SelectShared<kThreads>*>(fused_lds);
+                const int nc = (a.M + a.selp.chunk - 1) / a.selp.chunk;
+                constexpr int P = kSelMaxChunks / kThreads;  // chunks per thread
+                unsigned long long lo[P], hi[P];
+                unsigned pend = 0;  // bit e: chunk tid + e * kThreads not seen yet
+#pragma unroll
+                for (int e = 0; e < P; ++e) {
+                    lo[e] = hi[e] = 0ull;
+                    if (tid + e * kThreads < nc) pend |= 1u << e;
+                }
+                const unsigned long long t0 = wall_clock64();
+                while (true) {
+#pragma unroll
+                    for (int e = 0; e < P; ++e)
+                        if ((pend >> e) & 1) {
+                            const unsigned long long* sl = a.sel_sums + 2 * (tid + e * kThreads);
+                            lo[e] = ld64(sl);
+                            hi[e] = ld64(sl + 1);
+                        }
+                    unsigned np = 0;
+#pragma unroll
+                    for (int e = 0; e < P; ++e)
+                        if (((pend >> e) & 1) && !(tag_is(lo[e], a.epoch) && tag_is(hi[e], a.epoch))) np |= 1u << e;
+                    pend = np;
+                    if (__ballot(pend != 0) == 0) break;
+                    __builtin_amdgcn_s_sleep(2);
+                    if (wait_expired(t0, a)) {
+                        if (lane == 0) set_err(a);
+                        expired = true;
+                        break;
+                    }
+                }
+#pragma unroll
+                for (int e = 0; e < P; ++e)
+                    if (tid + e * kThreads < nc)
+                        sh.C[tid + e * kThreads] = (unsigned long long)(unsigned)lo[e] | (hi[e] << 32);
+                if (__syncthreads_or(expired) || err_set(a)) {
+                    if (tid == 0) *a.sel_n = -1;
+                    return;
+                }
+                fused_select_ranked(a.selp, a.M, a.sel_pos_base, a.sel_kept, a.sel_pos, a.sel_n);
+            } else {
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+                fused_select(a.selp, a.importance, a.M, a.sel_pos_base, a.sel_kept, a.sel_pos, a.sel_n);
+            }
         }
         return;
     }
@@ -1309,20 +1508,25 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
     // (With blend_n = n > 0 this call adds one more step to scores already
     // averaged over n steps: (n * importance + this step's score) / (n + 1).)
     const bool poisoned = err_set(a);
+    float smn = INFINITY, smx = -INFINITY;  // (fused selection: this share's min and max)
+    int snf = 0;                            //   and whether it holds a non-finite score
     for (int k = k_lo + tid; k < k_hi && r0 + k < a.M_out; k += kThreads) {
         float sum = 0.f;
         for (int jj = 0; jj < a.N; ++jj) sum += exp2_hw((float)Trun[jj * KRP + k] * kStep);
         float v = sum / (float)a.N;
         if (a.blend_n > 0) v = (a.importance[r0 + k] * (float)a.blend_n + v) / (float)(a.blend_n + 1);
-        __hip_atomic_store((unsigned*)a.importance + r0 + k, poisoned ? kNaNBits : __float_as_uint(v),
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const unsigned bits = poisoned ? kNaNBits : __float_as_uint(v);
+        __hip_atomic_store((unsigned*)a.importance + r0 + k, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if constexpr (SEL) {
+            snf |= (bits & 0x7f800000u) == 0x7f800000u;
+            smn = fminf(smn, __uint_as_float(bits));
+            smx = fmaxf(smx, __uint_as_float(bits));
+        }
     }
-    if constexpr (SEL) {
-        // this workgroup's scores are written (complete before the flag)
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        if (tid == 0) st64u(a.done + blockIdx.x, ((unsigned long long)a.epoch << 32) | a.epoch);
-    }
+    if constexpr (SEL)
+        fused_tail(TailArgs{a.err, a.done, a.sel_sums, a.importance, a.spin_ticks, a.epoch, a.call_epoch, a.M, a.sel_dist,
+                            a.selp},
+                   smn, smx, snf, nstream);
 }
 
 template <class C, bool SEL>

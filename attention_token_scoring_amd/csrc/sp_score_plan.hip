@@ -77,6 +77,7 @@ static sp_status plan_uncached(const sp_score_desc& d, long long M, int cus, Sco
             long long ng = (cus - 1) / g;
             if (ng > p.units) ng = p.units;
             if (ng > kMaxFlags / g) ng = kMaxFlags / g;
+            if (ng > kMaxDone / g) ng = kMaxDone / g;
             if (ng < 1) continue;
             const long long iters = (p.units + ng - 1) / ng;
             // where the kernel has a guard-free copy of the statistics for
@@ -132,7 +133,8 @@ static sp_status plan_uncached(const sp_score_desc& d, long long M, int cus, Sco
     p.ws_err = 0;
     p.ws_part = kHeaderBytes;
     p.ws_lse = p.ws_part + round_up((size_t)p.units * p.g * p.rows * 16, 256);
-    p.ws_tg = p.ws_lse + round_up((size_t)p.units * p.rows * 16, 256);
+    p.ws_sel = p.ws_lse + round_up((size_t)p.units * p.rows * 16, 256);
+    p.ws_tg = p.ws_sel + round_up((size_t)kSelMaxChunks * 16, 256);
     p.ws_total = p.ws_tg + round_up((size_t)p.ngroups * d.N * M * 4, 256);
     *out = p;
     return SP_OK;
@@ -206,7 +208,7 @@ size_t workspace_bound(const sp_score_desc& d, long long max_M, int cus) {
     if (tg_elems > (long long)cus * cap) tg_elems = (long long)cus * cap;
     tg_elems *= d.N;
     return kHeaderBytes + round_up((size_t)units * cus * rows * 16, 256) + round_up((size_t)units * rows * 16, 256) +
-           round_up((size_t)tg_elems * 4, 256);
+           round_up((size_t)kSelMaxChunks * 16, 256) + round_up((size_t)tg_elems * 4, 256);
 }
 
 }  // namespace sp

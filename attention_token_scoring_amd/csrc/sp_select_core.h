@@ -27,9 +27,6 @@
 
 namespace sp {
 
-// Per-prompt chunk limit (five per thread at 1024 threads: 5120 covers the
-// longest prompt the scoring kernel takes, 142,792 tokens, at chunk 28 or more).
-constexpr int kSelMaxChunks = 5120;
 constexpr int kLd = 16;         // importance loads in flight per thread
 constexpr int kSeg = 16;        // contiguous elements a thread quantises per tile
 constexpr int kDigit = 11;      // radix select: key bits per round
@@ -244,6 +241,51 @@ __device__ __forceinline__ double u128_to_f64(unsigned __int128 v) {
     return ldexp((double)m, sh);
 }
 
+// The min-max value u of one score: the correctly rounded quotient
+// (x - mn) / range by a reciprocal and one correction (Markstein): with
+// both operands scaled by a power of two taking range into [1, 2)
+// (a2 = (x - mn) * scale in one rounding), y = 1/range rounded,
+// q0 = a2 * y and the exact residual a2 - q0 * range, q0 + residual * y
+// rounds to the IEEE quotient (a quotient too small for that is too
+// small to survive the fixed point); a plain division when the range is
+// subnormal or near the top of the range; 1 when max == min.
+struct MinMaxNorm {
+    float mn, range, dscale, drange, dnms, drcp;
+    bool dfast;
+    __device__ __forceinline__ void init(float mn_, float mx_) {
+        mn = mn_;
+        range = mx_ - mn_;
+        const int rexp = (int)((__float_as_uint(range) >> 23) & 255);  // range's exponent field
+        dfast = range > 0.f && rexp >= 1 && rexp <= 253;                // normal, scale representable
+        dscale = dfast ? __uint_as_float((unsigned)(254 - rexp) << 23) : 1.f;
+        drange = range * dscale;
+        dnms = -mn * dscale;
+        drcp = __fdiv_rn(1.0f, drange);
+    }
+    __device__ __forceinline__ float value(float xv) const {
+        if (dfast) {
+            const float a2 = fmaf(xv, dscale, dnms);
+            const float q0 = a2 * drcp;
+            return fmaf(fmaf(-q0, drange, a2), drcp, q0);
+        }
+        return range > 0.f ? __fdiv_rn(xv - mn, range) : 1.0f;
+    }
+};
+
+// The fixed-point mass of token i (of M) with normalised value v: the boosts
+// (first, then last), then rint(v * 2^32) as uint64.
+__device__ __forceinline__ unsigned long long token_mass(float v, int i, int M, const SelectParamsDev& p) {
+    float q = v;
+    if (i < p.first_n) q = q * p.first_mult;
+    if (i >= M - p.last_n) q = q * p.last_mult;
+    return (unsigned long long)rintf(q * 4294967296.0f);
+}
+
+template <int NT>
+__device__ void select_ranked(SelectShared<NT>& sh, const SelectParamsDev& p, int M, int base, int pb,
+                              int32_t* __restrict__ kept, int32_t* __restrict__ pos,
+                              int32_t* __restrict__ nkept_out);
+
 // The selection of one prompt x[0..M) by a workgroup of NT threads, in the
 // steps above; sh is the workgroup's LDS. kept and pos receive the kept
 // tokens (kept[n] = base + i, pos[n] = pb + i), *nkept_out their count, or -1
@@ -308,31 +350,12 @@ __device__ void select_prompt(SelectShared<NT>& sh, const SelectParamsDev& p, co
         mn = fminf(mn, sh.fmin[x2]);
         mx = fmaxf(mx, sh.fmax[x2]);
     }
-    const float range = mx - mn;
-    // for the division below: a power of two taking range into [1, 2), the
-    // scaled range and its correctly rounded reciprocal
-    const int rexp = (int)((__float_as_uint(range) >> 23) & 255);  // range's exponent field
-    const bool dfast = range > 0.f && rexp >= 1 && rexp <= 253;    // normal, scale representable
-    const float dscale = dfast ? __uint_as_float((unsigned)(254 - rexp) << 23) : 1.f;
-    const float drange = range * dscale;
-    const float dnms = -mn * dscale;
-    const float drcp = __fdiv_rn(1.0f, drange);
-    // The min-max value u of one score: the correctly rounded quotient
-    // (x - mn) / range by a reciprocal and one correction (Markstein): with
-    // both operands scaled by a power of two taking range into [1, 2)
-    // (a2 = (x - mn) * scale in one rounding), y = 1/range rounded,
-    // q0 = a2 * y and the exact residual a2 - q0 * range, q0 + residual * y
-    // rounds to the IEEE quotient (a quotient too small for that is too
-    // small to survive the fixed point); a plain division when the range is
-    // subnormal or near the top of the range; 1 when max == min.
-    auto minmax_value = [&](float xv) __attribute__((always_inline)) {
-        if (dfast) {
-            const float a2 = fmaf(xv, dscale, dnms);
-            const float q0 = a2 * drcp;
-            return fmaf(fmaf(-q0, drange, a2), drcp, q0);
-        }
-        return range > 0.f ? __fdiv_rn(xv - mn, range) : 1.0f;
-    };
+    MinMaxNorm nm;
+    nm.init(mn, mx);
+    const float range = nm.range;
+    const bool dfast = nm.dfast;
+    const float dscale = nm.dscale, drange = nm.drange, dnms = nm.dnms, drcp = nm.drcp;
+    auto minmax_value = [&](float xv) __attribute__((always_inline)) { return nm.value(xv); };
 
     // Robust normalisations ("SpecPrefill - Implementation Guide",
     // Limitations item 5). Percentile clip: v = clamp((x - lo) / (hi - lo), 0, 1)
@@ -438,10 +461,7 @@ __device__ void select_prompt(SelectShared<NT>& sh, const SelectParamsDev& p, co
 #pragma unroll
                 for (int e = 0; e < kSeg; ++e) {
                     const int i = g0 + e;
-                    float q = vq[e];
-                    if (i < p.first_n) q = q * p.first_mult;
-                    if (i >= M - p.last_n) q = q * p.last_mult;
-                    qv[e] = i < M ? (unsigned long long)rintf(q * 4294967296.0f) : 0ull;
+                    qv[e] = i < M ? token_mass(vq[e], i, M, p) : 0ull;
                 }
                 int c = g0 / chunk;
                 int next = (c + 1) * chunk;  // first element of the next chunk
@@ -461,6 +481,21 @@ __device__ void select_prompt(SelectShared<NT>& sh, const SelectParamsDev& p, co
         }
         __syncthreads();
     }
+
+    select_ranked<NT>(sh, p, M, base, pb, kept, pos, nkept_out);
+}
+
+// Steps 4-7 from the chunk masses in sh.C[0..nc) (nc = ceil(M / chunk)): the
+// pooled keys, the ranking, the kept chunks and the kept tokens.
+template <int NT>
+__device__ void select_ranked(SelectShared<NT>& sh, const SelectParamsDev& p, int M, int base, int pb,
+                              int32_t* __restrict__ kept, int32_t* __restrict__ pos,
+                              int32_t* __restrict__ nkept_out) {
+    using C_ = SelCfg<NT>;
+    constexpr int kSelThreads = NT, kSelWaves = C_::kWaves;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int chunk = p.chunk;
+    const int nc = (M + chunk - 1) / chunk;
 
     // 4. pooled keys from prefix sums: key_c = (S[hi+1] - S[lo]) / tokens in
     // window, held as the bits of the (non-negative) double, which order like
