@@ -384,11 +384,13 @@ sp_status sp_profile_score_kernel(void* before, void* after);
 
 /*
  * sp_score and sp_select of one prompt in one launch (the computation of
- * each as cited there), for short prompts where a launch is a large part of
- * the time: once every workgroup of the scoring kernel has written its
- * scores, one of its workgroups (512 threads) runs the selection on them.
- * The outputs are those of sp_score followed by sp_select with the same
- * arguments, bit for bit.
+ * each as cited there): once every workgroup of the scoring kernel has
+ * written its scores, one of its workgroups (512 threads) runs the
+ * selection on them. For prompts of 16K tokens or more with min-max
+ * normalisation, the scoring workgroups first sum the chunks' fixed-point
+ * masses between them (exact integer sums), and that workgroup only pools,
+ * ranks and emits. The outputs are those of sp_score followed by sp_select
+ * with the same arguments, bit for bit.
  *   desc, Q, K, M, ws, ws_bytes, stream  as for sp_score (importance is
  *            written as well)
  *   params, pos_base, kept_idx, pos_ids, n_kept  as for sp_select; the
