@@ -372,22 +372,7 @@ constexpr unsigned kNonFiniteMark = 0xffffffffu;
 // chunks sw, sw + nstream, ... (sw = its index) over the scores (every token's
 // value and boosts as the selection computes them; the sums are exact, so the
 // split does not change them), each chunk's mass stored as two tagged words.
-// (what the tail reads of the launch's arguments, passed by value: a
-// reference to the kernel's arguments breaks the compiler's register
-// allocation when the tail is a function of its own, and as one its call
-// costs stack space and register saves)
-struct TailArgs {
-    unsigned long long* err;
-    unsigned long long* done;
-    unsigned long long* sel_sums;
-    const float* importance;
-    unsigned long long spin_ticks;
-    unsigned epoch, call_epoch;
-    int M;
-    int sel_dist;
-    SelectParamsDev selp;
-};
-__device__ __forceinline__ void fused_tail(TailArgs a, float smn, float smx, int snf, int nstream) {
+__device__ __forceinline__ void fused_tail(const ScoreArgs& a, float smn, float smx, int snf, int nstream) {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     __shared__ float mm[2 * kWaves];
     __shared__ float gmm[2];
@@ -1524,9 +1509,7 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
         }
     }
     if constexpr (SEL)
-        fused_tail(TailArgs{a.err, a.done, a.sel_sums, a.importance, a.spin_ticks, a.epoch, a.call_epoch, a.M, a.sel_dist,
-                            a.selp},
-                   smn, smx, snf, nstream);
+        fused_tail(a, smn, smx, snf, nstream);
 }
 
 template <class C, bool SEL>
