@@ -213,8 +213,9 @@ def sp_score_status(workspace, stream=None) -> bool:
 
 
 def sp_set_wait_limit(ticks: int = 0):
-    """Testing aid: limit of the scoring kernel's bounded waits for this
-    thread's later calls, in 100 MHz clock ticks (0: the default, 2 s)."""
+    """Testing aid: limit of the bounded waits (the scoring kernel's, and the
+    selection's by several workgroups) for this thread's later calls, in
+    100 MHz clock ticks (0: the default, 2 s)."""
     _check(load_library().sp_set_wait_limit(int(ticks)), "sp_set_wait_limit")
 
 
@@ -388,9 +389,11 @@ def sp_break_even(M: int, keep_fraction: float, spec_tps: float = 600.0,
 
 
 def sp_select(importance, params: SelectParams, pos_base: int = 0, kept_idx=None, pos_ids=None,
-              n_kept=None, stream=None):
+              n_kept=None, stream=None, workspace=None):
     """(kept_idx [M] int32, pos_ids [M] int32, n_kept [1] int32) on the device; the
-    first n_kept entries are valid."""
+    first n_kept entries are valid. workspace: None allocates what
+    sp_select_workspace_bytes asks for (several workgroups for long prompts),
+    False passes none (one workgroup), or a uint8 device tensor."""
     torch = _torch()
     _require_cuda(importance)
     M = importance.shape[0]
@@ -402,9 +405,17 @@ def sp_select(importance, params: SelectParams, pos_base: int = 0, kept_idx=None
     _check_out(kept_idx, torch.int32, M, "kept_idx")
     _check_out(pos_ids, torch.int32, M, "pos_ids")
     _check_out(n_kept, torch.int32, 1, "n_kept")
+    if workspace is None:
+        nbytes = sp_select_workspace_bytes(1, int(M), params)
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev) if nbytes > 0 else False
+    if workspace is False:
+        ws_ptr, ws_bytes = None, 0
+    else:
+        _check_out(workspace, torch.uint8, 0, "workspace")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
     st = load_library().sp_select(importance.data_ptr(), int(M), ctypes.byref(params),
                                   int(pos_base), kept_idx.data_ptr(), pos_ids.data_ptr(),
-                                  n_kept.data_ptr(), None, 0, _stream(stream))
+                                  n_kept.data_ptr(), ws_ptr, ws_bytes, _stream(stream))
     _check(st, "sp_select")
     return kept_idx, pos_ids, n_kept
 

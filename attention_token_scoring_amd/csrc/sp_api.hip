@@ -25,6 +25,10 @@ hipError_t launch_gather(const void* src, long long row_bytes, const int32_t* ke
 hipError_t launch_select(const SelectParamsDev& p, const int64_t* cu, const int32_t* pos_base,
                          int R, const float* importance, int32_t* kept_idx, int32_t* pos_ids,
                          int32_t* n_kept, hipStream_t stream);
+hipError_t launch_select_dist(const SelectParamsDev& p, const float* importance, int M, int pos_base,
+                              int32_t* kept_idx, int32_t* pos_ids, int32_t* n_kept, void* ws, unsigned epoch,
+                              unsigned long long spin, int cus, hipStream_t stream);
+unsigned long long wait_limit_ticks();
 
 namespace {
 
@@ -431,17 +435,22 @@ sp_status sp_break_even(int64_t M, float keep_fraction, float spec_tps, float ta
     return SP_OK;
 }
 
+// Whether sp_select may select one prompt of M tokens by several
+// workgroups (given a workspace): min-max normalisation, top-K or mass,
+// M >= kSelGridMin.
+static bool select_dist_eligible(int64_t M, const sp_select_params* params) {
+    return params->mode != SP_SELECT_THRESHOLD && params->norm == SP_NORM_MINMAX && M >= kSelGridMin;
+}
+
 size_t sp_select_workspace_bytes(int32_t R, int64_t total_prompt_len,
                                  const sp_select_params* params) {
     if (R < 1 || total_prompt_len < R || check_select_params(params) != SP_OK) return (size_t)-1;
-    return 0;
+    return R == 1 && select_dist_eligible(total_prompt_len, params) ? kSelDistBytes : 0;
 }
 
 sp_status sp_select(const float* importance, int32_t M, const sp_select_params* params,
                     int32_t pos_base, int32_t* kept_idx, int32_t* pos_ids, int32_t* n_kept,
                     void* ws, size_t ws_bytes, void* stream) {
-    (void)ws;
-    (void)ws_bytes;
     sp_status s = check_select_params(params);
     if (s != SP_OK) return s;
     if (!importance || !kept_idx || !pos_ids || !n_kept) return SP_EINVAL;
@@ -449,9 +458,19 @@ sp_status sp_select(const float* importance, int32_t M, const sp_select_params* 
     if (s != SP_OK) return s;
     if ((long long)pos_base + M > 2147483647ll || (long long)pos_base < -2147483647ll)
         return SP_EINVAL;
-    if (device_cus() < 1) return SP_EDEVICE;
-    const int64_t cu[2] = {0, M};
+    const int cus = device_cus();
+    if (cus < 1) return SP_EDEVICE;
     const SelectParamsDev p = to_dev(params);
+    if (select_dist_eligible(M, params) && ws && ws_bytes >= kSelDistBytes && aligned(ws, 16)) {
+        // several workgroups, unless the stream is being captured (their
+        // exchange slots carry a launch's epoch, which a graph would fix)
+        hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing((hipStream_t)stream, &cap) != hipSuccess) return SP_EDEVICE;
+        if (cap == hipStreamCaptureStatusNone)
+            return to_status(launch_select_dist(p, importance, M, pos_base, kept_idx, pos_ids, n_kept, ws,
+                                                next_epoch(), wait_limit_ticks(), cus, (hipStream_t)stream));
+    }
+    const int64_t cu[2] = {0, M};
     return to_status(launch_select(p, cu, &pos_base, 1, importance, kept_idx, pos_ids, n_kept,
                                    (hipStream_t)stream));
 }

@@ -35,6 +35,18 @@ constexpr int kMaxDone = (kHeaderBytes - kDoneFlags) / 16;
 // 5120 covers the longest prompt the scoring kernel takes, 142,792 tokens, at
 // chunk 28 or more); the fused launch's chunk-mass slots are sized by it.
 constexpr int kSelMaxChunks = 5120;
+// Prompts of at least this many tokens (min-max normalisation) have their
+// chunk masses summed by several workgroups: the fused launch's streaming
+// workgroups (from kSelDistMin, below which its one 512-thread workgroup
+// selects faster), or the selection kernel's grid when given a workspace
+// (from kSelGridMin: measured on the MI355X, one 1024-thread workgroup
+// selects 32K tokens in 17.1 us, a grid of 16 in 17.5 us; 128K tokens in
+// 37.7 against 20.5 us).
+constexpr int kSelDistMin = 16384;
+constexpr int kSelGridMin = 49152;
+// Workspace of the selection by several workgroups: 256 score ranges, then
+// the chunk masses (two 8-byte words each).
+constexpr size_t kSelDistBytes = (size_t)(2 * 256 + 2 * kSelMaxChunks) * 8;
 constexpr int kMaxDefer = 3;          // units between streaming and finishing a unit
 constexpr int kLdsBytes = 160 * 1024;  // LDS of one CU
 constexpr int kDefaultCUs = 256;       // MI355X; used when no device can be queried

@@ -37,7 +37,10 @@ static const void* pick_kernel(int dtype, int d, int rows, int G, int tpw, bool 
 
 static thread_local hipEvent_t t_ev_before = nullptr, t_ev_after = nullptr;
 static thread_local unsigned long long t_wait_limit = 0;
-constexpr int kSelDistMin = 16384;
+
+// The limit of a bounded wait, in ticks of the 100 MHz clock (the calling
+// thread's test setting, else the default).
+unsigned long long wait_limit_ticks() { return t_wait_limit > 0 ? t_wait_limit : kSpinTicks; }
 
 void set_profile_events(hipEvent_t before, hipEvent_t after) {
     t_ev_before = before;
@@ -107,7 +110,7 @@ hipError_t launch_score(const ScorePlan& p, const sp_score_desc& d, const void* 
     a.c = scale * 1.4426950408889634f;
     a.tail_n = tail_n;
     a.blend_n = blend_n;
-    a.spin_ticks = t_wait_limit > 0 ? t_wait_limit : kSpinTicks;
+    a.spin_ticks = wait_limit_ticks();
     a.done = (unsigned long long*)(base + p.ws_err + kDoneFlags);
     a.sel_sums = (unsigned long long*)(base + p.ws_sel);
     // The streaming workgroups sum the chunk masses (min-max normalisation)

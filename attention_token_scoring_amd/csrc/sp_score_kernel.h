@@ -143,25 +143,6 @@ __device__ __forceinline__ void st64(void* p, float x, float y) {
     __hip_atomic_store((unsigned long long*)p, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ unsigned long long ld64(const void* p) {
-    return __hip_atomic_load((unsigned long long*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ unsigned ld32(const void* p) {
-    return __hip_atomic_load((unsigned*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// A 32-bit value in the low half of a slot, the epoch of its launch in the high half.
-__device__ __forceinline__ unsigned long long tagged(float v, unsigned epoch) {
-    return (unsigned long long)__float_as_uint(v) | ((unsigned long long)epoch << 32);
-}
-__device__ __forceinline__ bool tag_is(unsigned long long v, unsigned epoch) {
-    return (unsigned)(v >> 32) == epoch;
-}
-__device__ __forceinline__ float tag_value(unsigned long long v) { return __uint_as_float((unsigned)v); }
-__device__ __forceinline__ void st64u(void* p, unsigned long long v) {
-    __hip_atomic_store((unsigned long long*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 // The call's error word: set once a bounded wait of any of its launches has
 // timed out.
@@ -360,10 +341,6 @@ __device__ __attribute__((noinline)) inline void fused_select_ranked(SelectParam
                                                                      int32_t* pos, int32_t* n) {
     select_ranked<kThreads>(*reinterpret_cast<SelectShared<kThreads>*>(fused_lds), p, M, 0, pb, kept, pos, n);
 }
-
-// A share's min and max as published for the fused selection: the words
-// carry the epoch; a share holding a non-finite score publishes this max.
-constexpr unsigned kNonFiniteMark = 0xffffffffu;
 
 // The streaming workgroups' end of a fused launch. Without sel_dist the
 // workgroup raises a tagged flag once its scores are written. With it, the

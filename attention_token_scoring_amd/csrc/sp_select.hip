@@ -235,7 +235,40 @@ __global__ __launch_bounds__(kSelThreads) void select_threshold_kernel(
     if (tid == 0) nkept_all[b.first + r] = n;
 }
 
+// One long prompt by several workgroups (min-max normalisation): see
+// select_distributed.
+__global__ __launch_bounds__(kSelThreads) void select_dist_kernel(SelectParamsDev p, const float* __restrict__ x,
+                                                                  int M, int pb, int32_t* __restrict__ kept,
+                                                                  int32_t* __restrict__ pos,
+                                                                  int32_t* __restrict__ nkept,
+                                                                  unsigned long long* slots, unsigned epoch,
+                                                                  unsigned long long spin) {
+    extern __shared__ unsigned long long smem_raw[];
+    SelectShared<kSelThreads>& sh = *reinterpret_cast<SelectShared<kSelThreads>*>(smem_raw);
+    select_distributed<kSelThreads>(sh, p, x, M, pb, kept, pos, nkept, slots, epoch, spin);
+}
+
 size_t select_shared_bytes() { return sizeof(SelectShared<kSelThreads>); }
+
+// Launches the selection of one prompt of M >= kSelGridMin tokens by a grid of
+// workgroups (about 2048 tokens each, 2 to 64 of them: one lane per range in
+// the exchange, and all resident at once on an idle device) on a workspace
+// of kSelDistBytes.
+hipError_t launch_select_dist(const SelectParamsDev& p, const float* importance, int M, int pos_base,
+                              int32_t* kept_idx, int32_t* pos_ids, int32_t* n_kept, void* ws, unsigned epoch,
+                              unsigned long long spin, int cus, hipStream_t stream) {
+    const size_t lds = sizeof(SelectShared<kSelThreads>);
+    hipError_t e = hipFuncSetAttribute((const void*)&select_dist_kernel,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    int W = (M + 2047) / 2048;
+    if (W > 64) W = 64;
+    if (W > cus) W = cus;
+    if (W < 2) W = 2;
+    hipLaunchKernelGGL(select_dist_kernel, dim3(W), dim3(kSelThreads), lds, stream, p, importance, M, pos_base,
+                       kept_idx, pos_ids, n_kept, (unsigned long long*)ws, epoch, spin);
+    return hipGetLastError();
+}
 
 // Launches the selection of requests [0, R) whose prompt offsets are cu[0..R].
 hipError_t launch_select(const SelectParamsDev& p, const int64_t* cu, const int32_t* pos_base,

@@ -24,6 +24,7 @@
 #include <math.h>
 
 #include "sp_internal.h"
+#include "sp_slots.h"
 
 namespace sp {
 
@@ -776,6 +777,160 @@ __device__ void select_ranked(SelectShared<NT>& sh, const SelectParamsDev& p, in
         pos[o] = pb + i;
     }
     if (tid == 0) *nkept_out = n_kept;
+}
+
+// The selection of one long prompt by a grid of W workgroups (W = gridDim.x,
+// all resident at once) with min-max normalisation: workgroup b takes chunks
+// [nc b / W, nc (b + 1) / W) and publishes the min and max of their scores
+// (or a mark that one is not finite); once all W are there, it sums those
+// chunks' fixed-point masses (exact, so the split does not change them) and
+// publishes each as two tagged words; workgroup 0 gathers every chunk's mass
+// and runs steps 4-7. slots: [0, 2 W) the ranges, from kSelDistChunkSlot the
+// masses (low, high) of chunk c at 2 c. Every wait gives up after spin ticks
+// of the 100 MHz clock (then n_kept = -1).
+constexpr int kSelDistChunkSlot = 2 * 256;
+
+template <int NT>
+__device__ void select_distributed(SelectShared<NT>& sh, const SelectParamsDev& p, const float* __restrict__ x,
+                                   int M, int pb, int32_t* __restrict__ kept, int32_t* __restrict__ pos,
+                                   int32_t* __restrict__ nkept_out, unsigned long long* slots, unsigned E,
+                                   unsigned long long spin) {
+    using C_ = SelCfg<NT>;
+    constexpr int kSelWaves = C_::kWaves;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int W = (int)gridDim.x, b = (int)blockIdx.x;
+    const int chunk = p.chunk;
+    const int nc = (M + chunk - 1) / chunk;
+    const int c0 = (int)((long long)nc * b / W), c1 = (int)((long long)nc * (b + 1) / W);
+    const int e0 = c0 * chunk, e1 = min(M, c1 * chunk);
+    const unsigned long long Et = (unsigned long long)E << 32;
+
+    // 1. this range's min and max (exact in any order)
+    float mn = INFINITY, mx = -INFINITY;
+    int nonfinite = 0;
+    for (int i = e0 + tid; i < e1; i += NT) {
+        const float v = x[i];
+        nonfinite |= (__float_as_uint(v) & 0x7f800000u) == 0x7f800000u;
+        mn = fminf(mn, v);
+        mx = fmaxf(mx, v);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        mn = fminf(mn, __shfl_xor(mn, o));
+        mx = fmaxf(mx, __shfl_xor(mx, o));
+    }
+    if (lane == 0) {
+        sh.fmin[w] = mn;
+        sh.fmax[w] = mx;
+    }
+    const bool nf = __syncthreads_or(nonfinite);
+    if (tid == 0) {
+        for (int x2 = 1; x2 < kSelWaves; ++x2) {
+            mn = fminf(mn, sh.fmin[x2]);
+            mx = fmaxf(mx, sh.fmax[x2]);
+        }
+        st64u(slots + 2 * b, Et | __float_as_uint(fminf(mn, sh.fmin[0])));
+        st64u(slots + 2 * b + 1, Et | (nf ? kNonFiniteMark : __float_as_uint(fmaxf(mx, sh.fmax[0]))));
+    }
+
+    // 2. the prompt's min and max from every range (lane x reads range x)
+    if (w == 0) {
+        float gmn = INFINITY, gmx = -INFINITY;
+        bool bad = false;
+        const unsigned long long t0 = wall_clock64();
+        while (true) {
+            bool miss = false, nfx = false;
+            gmn = INFINITY;
+            gmx = -INFINITY;
+            if (lane < W) {
+                const unsigned long long lo = ld64(slots + 2 * lane), hi = ld64(slots + 2 * lane + 1);
+                miss = !(tag_is(lo, E) && tag_is(hi, E));
+                nfx = (unsigned)hi == kNonFiniteMark;
+                gmn = tag_value(lo);
+                gmx = tag_value(hi);
+            }
+            if (__ballot(miss) == 0) {
+                bad = __ballot(nfx) != 0;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+            if (wall_clock64() - t0 > spin) {
+                bad = true;
+                break;
+            }
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            gmn = fminf(gmn, __shfl_xor(gmn, o));
+            gmx = fmaxf(gmx, __shfl_xor(gmx, o));
+        }
+        if (lane == 0) {
+            sh.pct[0] = gmn;
+            sh.pct[1] = gmx;
+            sh.ncand = bad ? 1 : 0;
+        }
+    }
+    __syncthreads();
+    if (sh.ncand) {
+        // (a non-finite score, or a range that never came)
+        if (b == 0 && tid == 0) *nkept_out = -1;
+        return;
+    }
+    MinMaxNorm nm;
+    nm.init(sh.pct[0], sh.pct[1]);
+
+    // 3. this range's chunk masses
+    for (int c = c0 + tid; c < c1; c += NT) sh.C[c - c0] = 0ull;
+    __syncthreads();
+    for (int i = e0 + tid; i < e1; i += NT) atomicAdd(&sh.C[i / chunk - c0], token_mass(nm.value(x[i]), i, M, p));
+    __syncthreads();
+    for (int c = c0 + tid; c < c1; c += NT) {
+        const unsigned long long v = sh.C[c - c0];
+        st64u(slots + kSelDistChunkSlot + 2 * c, Et | (unsigned)v);
+        st64u(slots + kSelDistChunkSlot + 2 * c + 1, Et | (unsigned)(v >> 32));
+    }
+    if (b != 0) return;
+    __syncthreads();  // (the gather rewrites C)
+
+    // 4. workgroup 0: every chunk's mass, then the ranking
+    constexpr int P = kSelMaxChunks / NT;  // chunks per thread
+    unsigned long long lo[P], hi[P];
+    unsigned pend = 0;  // bit e: chunk tid + e NT not seen yet
+#pragma unroll
+    for (int e = 0; e < P; ++e) {
+        lo[e] = hi[e] = 0ull;
+        if (tid + e * NT < nc) pend |= 1u << e;
+    }
+    bool expired = false;
+    const unsigned long long t0 = wall_clock64();
+    while (true) {
+#pragma unroll
+        for (int e = 0; e < P; ++e)
+            if ((pend >> e) & 1) {
+                const unsigned long long* sl = slots + kSelDistChunkSlot + 2 * (tid + e * NT);
+                lo[e] = ld64(sl);
+                hi[e] = ld64(sl + 1);
+            }
+        unsigned np = 0;
+#pragma unroll
+        for (int e = 0; e < P; ++e)
+            if (((pend >> e) & 1) && !(tag_is(lo[e], E) && tag_is(hi[e], E))) np |= 1u << e;
+        pend = np;
+        if (__ballot(pend != 0) == 0) break;
+        __builtin_amdgcn_s_sleep(2);
+        if (wall_clock64() - t0 > spin) {
+            expired = true;
+            break;
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < P; ++e)
+        if (tid + e * NT < nc) sh.C[tid + e * NT] = (unsigned long long)(unsigned)lo[e] | (hi[e] << 32);
+    if (__syncthreads_or(expired)) {
+        if (tid == 0) *nkept_out = -1;
+        return;
+    }
+    select_ranked<NT>(sh, p, M, 0, pb, kept, pos, nkept_out);
 }
 
 }  // namespace sp

@@ -397,6 +397,10 @@ def bench_single(args, w, sels, sp, torch, dev, steps, warmup, cpu_s):
         del a, b
 
     def make_step(params):
+        # (the selection's workspace: several workgroups select a long prompt)
+        nb = sp.sp_select_workspace_bytes(1, M, params)
+        sel_ws = torch.empty(nb, dtype=torch.uint8, device=dev) if nb > 0 else False
+
         def step(i, kev=None, sev=None, xev=None):
             if kev is not None:
                 sp.sp_profile_score_kernel(kev[0], kev[1])
@@ -409,7 +413,7 @@ def bench_single(args, w, sels, sp, torch, dev, steps, warmup, cpu_s):
                 sp.sp_profile_score_kernel()
             if xev is not None:
                 xev[0].record()
-            sp.sp_select(imp, params, kept_idx=kept, pos_ids=pos, n_kept=nk)
+            sp.sp_select(imp, params, kept_idx=kept, pos_ids=pos, n_kept=nk, workspace=sel_ws)
             if xev is not None:
                 xev[1].record()
         return step

@@ -239,8 +239,11 @@ sp_status sp_score_windows(const sp_score_desc* desc, int32_t R, const void* Q, 
                            const int64_t* cu_window_host, const int64_t* keep_host,
                            float* importance, void* ws, size_t ws_bytes, void* stream);
 
-/* Bytes of device workspace sp_select / sp_select_varlen need (currently 0 for
- * every valid argument set; (size_t)-1 if the arguments are invalid). */
+/* Bytes of device workspace sp_select / sp_select_varlen can use: for one
+ * prompt (R = 1) of at least 49152 tokens with min-max normalisation in the
+ * top-K or mass mode, 86016 (the exchange of selection by several
+ * workgroups, see sp_select); otherwise 0. (size_t)-1 if the arguments are
+ * invalid. */
 size_t sp_select_workspace_bytes(int32_t R, int64_t total_prompt_len,
                                  const sp_select_params* params);
 
@@ -295,6 +298,14 @@ size_t sp_select_workspace_bytes(int32_t R, int64_t total_prompt_len,
  *   n_kept      device, [1] int32 (written): the kept count, or -1 if some score
  *               is NaN or infinite (kept_idx and pos_ids are then not written;
  *               a scoring call whose bounded waits timed out leaves NaN scores)
+ *   ws, ws_bytes  device workspace, 16-byte aligned, or NULL / 0: with at
+ *               least sp_select_workspace_bytes(1, M, params) bytes, a prompt
+ *               of 49152 tokens or more with min-max normalisation is selected
+ *               by several workgroups (up to 64; each sums the exact chunk
+ *               masses of its share, one ranks), which must all be resident
+ *               at once (an otherwise idle device; a wait that gives up leaves
+ *               n_kept = -1); the outputs are the same as with one workgroup.
+ *               Not used while the stream is being captured into a graph.
  * Supported: M <= 2^24, nc = ceil(M/chunk) <= 5120 (4096 in threshold mode:
  * with chunk 32 that is 163,840 tokens, more than the longest prompt sp_score
  * takes, and 131,072 in threshold mode), and boost multipliers
@@ -421,8 +432,9 @@ sp_status sp_score_status(const void* ws, void* stream, int32_t* timed_out);
 
 /*
  * Testing aid: the limit, in ticks of the device's 100 MHz constant clock, of
- * every bounded wait in the scoring calls the calling thread makes from now on
- * (0 restores the default, 2 s). A tiny limit makes those waits give up at
+ * every bounded wait in the scoring calls, and in sp_select by several
+ * workgroups, that the calling thread makes from now on (0 restores the
+ * default, 2 s). A tiny limit makes those waits give up at
  * once, so that the time-out path (error word, NaN scores, n_kept = -1) can be
  * exercised with every kernel still ending normally. Always SP_OK.
  */

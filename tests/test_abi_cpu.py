@@ -199,6 +199,24 @@ def test_select_rejects_null_and_sizes(lib):
     assert sp.sp_select_workspace_bytes(1, 100, p) == 0
 
 
+def test_select_workspace_only_for_long_single_prompts_with_min_max():
+    # several workgroups select one prompt of >= 49152 tokens under min-max
+    # normalisation (top-K or mass); nothing else asks for a workspace
+    need = 8 * (2 * 256 + 2 * 5120)
+    topk = sp.select_params(chunk=32, pool_k=13, mode="topk", keep_rate=0.1)
+    mass = sp.select_params(chunk=32, pool_k=5, mode="mass", mass=0.85)
+    assert sp.sp_select_workspace_bytes(1, 49152, topk) == need
+    assert sp.sp_select_workspace_bytes(1, 131072, mass) == need
+    assert sp.sp_select_workspace_bytes(1, 49151, topk) == 0
+    assert sp.sp_select_workspace_bytes(1, 32768, mass) == 0
+    assert sp.sp_select_workspace_bytes(2, 100000, topk) == 0
+    pct = sp.select_params(chunk=32, pool_k=13, mode="topk", keep_rate=0.1, norm="percentile",
+                           norm_lo=0.01, norm_hi=0.99)
+    assert sp.sp_select_workspace_bytes(1, 100000, pct) == 0
+    thr = sp.select_params(chunk=32, mode="threshold", keep_rate=0.3, min_tok=64)
+    assert sp.sp_select_workspace_bytes(1, 100000, thr) == 0
+
+
 def test_score_status_rejects_null_pointers(lib):
     out = ctypes.c_int32(7)
     assert lib.sp_score_status(None, None, ctypes.byref(out)) == sp.SP_EINVAL
