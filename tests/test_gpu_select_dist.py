@@ -22,6 +22,9 @@ CASES = [
     ("65536-topk", 65536, dict(chunk=32, pool_k=13, mode="topk", keep_rate=0.1)),
     ("131072-topk", 131072, dict(chunk=64, pool_k=13, mode="topk", keep_rate=0.1)),
     ("142792-mass-chunk28", 142792, dict(chunk=28, pool_k=3, mode="mass", mass=0.9)),
+    # more workgroups (24) than chunks (13): some shares are empty
+    ("49153-topk-chunk4096", 49153, dict(chunk=4096, pool_k=3, mode="topk", keep_rate=0.3)),
+    ("50000-mass-chunk16", 50000, dict(chunk=16, pool_k=1, mode="mass", mass=0.5)),
 ]
 DISTS = ["powered", "ties", "constant"]
 
