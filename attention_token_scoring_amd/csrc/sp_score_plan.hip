@@ -129,7 +129,9 @@ static sp_status plan_uncached(const sp_score_desc& d, long long M, int cus, Sco
     p.grid = bg * bng + p.ncomb;
     p.cus = cus;
     p.lds = score_lds_layout(bdef + 1, btpw, p.rows, row_bytes, d.N, bkr, p.dma);
-    // the header (error word, last epoch, one flag per streaming workgroup)
+    // the header (error word, last epoch, the groups' flags, the fused
+    // call's words per streaming workgroup), the tagged partials and
+    // log-sum-exps, the fused call's chunk masses, the groups' running maxima
     p.ws_err = 0;
     p.ws_part = kHeaderBytes;
     p.ws_lse = p.ws_part + round_up((size_t)p.units * p.g * p.rows * 16, 256);
