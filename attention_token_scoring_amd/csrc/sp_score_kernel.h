@@ -47,6 +47,10 @@
 //    group) leave their running maxima in memory and raise epoch-tagged
 //    flags; then each takes the max over groups of its share of the slice's
 //    keys, exponentiates and averages over the steps.
+//  * The fused launch (sp_score_select, an instantiation of its own) then
+//    selects: one combiner workgroup runs the chunk selection on the scores,
+//    for long prompts on chunk masses the streaming workgroups have summed
+//    between them.
 #pragma once
 
 #include <math.h>
