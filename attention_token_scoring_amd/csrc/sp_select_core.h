@@ -1,6 +1,8 @@
-// Chunk selection of one prompt by one workgroup: the steps, shared by the
-// selection kernel (one workgroup of 1024 threads per request) and the fused
-// scoring launch (one workgroup of 512 threads after the scores).
+// Chunk selection of one prompt: the steps, shared by the selection kernel
+// (one workgroup of 1024 threads per request, or a grid of them for one long
+// prompt) and the fused scoring launch (one workgroup of 512 threads after
+// the scores, on chunk masses the streaming workgroups summed for long
+// prompts).
 //
 // Steps ("SpecPrefill - Implementation Guide": v3.1 item 5 min-max
 // normalisation, v3 item 2 structural boosts, v3 item 1 cumulative attention
@@ -16,9 +18,9 @@
 //   of the last kept rank, and ties on it are settled by index.
 // Every step is exact or a single IEEE-rounded operation (fp32 sub/div/mul,
 // u64 -> f64 conversion, f64 div and mul), and sums are integer, so the
-// result is the same however the work is split across threads: a CPU doing
-// the same steps in any order reproduces it bit for bit. Compiled with
-// -ffp-contract=off.
+// result is the same however the work is split across threads or
+// workgroups: a CPU doing the same steps in any order reproduces it bit for
+// bit. Compiled with -ffp-contract=off.
 #pragma once
 
 #include <math.h>
