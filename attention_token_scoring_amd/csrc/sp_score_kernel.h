@@ -316,7 +316,7 @@ __device__ __forceinline__ void mma(f32x4& acc, const i32x4& q, const i32x4& k) 
 // load in the plane (kOob for a tile past the slice: zeros; the buffer
 // descriptor bounds the plane, so reads past its end are zeros too).
 template <class C>
-__device__ __forceinline__ void load_k(Frag<C>& f, __amdgpu_buffer_rsrc_t rs, uint32_t off, int lane) {
+__device__ __forceinline__ void load_k(Frag<C>& f, __amdgpu_buffer_rsrc_t rs, uint32_t off) {
     // one offset register per tile; the 64-byte steps go in the instructions'
     // offset field (otherwise every (tile, step) offset is kept live)
     asm volatile("" : "+v"(off));
@@ -737,7 +737,7 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
         constexpr int S = C::S;                 // LDS slots of this wave
         constexpr int VM_AHEAD = (S - 1) * NLD; // loads issued after a tile's own
         static_assert(RPI * NLD == kTileKeys, "tile load shape");
-        static_assert(S <= TPW && NB % S == 0 || S == TPW, "slots must be static in the unrolled loop");
+        static_assert((S <= TPW && NB % S == 0) || S == TPW, "slots must be static in the unrolled loop");
         char* ring = smem + a.lds.bank + (size_t)w * S * TB;
         const int ntv = min(max((ntiles - w + SW - 1) / SW, 0), TPW);
         const int tpart = masked_tile(ntv, w, nall);
@@ -1022,7 +1022,7 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
         for (int P = 0; P < 2; ++P) {
             const auto rs = plane_rsrc(a, unit_of(P), plane_bytes, C::ESZ);
 #pragma unroll
-            for (int t = 0; t < TPW; ++t) load_k<C>(fb[P * TPW + t], rs, koff[t], lane);
+            for (int t = 0; t < TPW; ++t) load_k<C>(fb[P * TPW + t], rs, koff[t]);
         }
         __syncthreads();  // Q of unit 0 is staged
 
@@ -1050,7 +1050,7 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
             }
             // refill the slots with the same tiles of the unit two ahead
 #pragma unroll
-            for (int t = 0; t < TPW; ++t) load_k<C>(fb[P * TPW + t], rs2, koff[t], lane);
+            for (int t = 0; t < TPW; ++t) load_k<C>(fb[P * TPW + t], rs2, koff[t]);
             // Per wave-row statistics over this wave's keys of the slice (lanes
             // L, L^16, L^32, L^48 hold the same row): the max m, the shifted
             // log2 logits y = c x - c m (<= 0 on those keys) and their exp2
