@@ -7,7 +7,10 @@ too or left as the previous replay left it; every replay must reproduce the
 eager call bit for bit (the scoring kernel is deterministic; a launch's epoch
 is fixed into the graph, so a clearing kernel captured before it resets the
 workspace's tagged words on every replay, with no memset nodes in the graph:
-without it a replay would take the previous replay's slots for its own)."""
+without it a replay would take the previous replay's slots for its own). At
+65536 tokens the eager selection runs on a grid of workgroups and the
+captured one on one workgroup (a graph would fix the grid's epoch): the two
+must agree."""
 import numpy as np
 import pytest
 
@@ -23,7 +26,7 @@ from test_gpu_parity import to_dev  # noqa: E402
 
 @pytest.mark.parametrize("fused", [False, True], ids=["two-calls", "fused"])
 @pytest.mark.parametrize("refill", [True, False], ids=["ws-overwritten", "ws-kept"])
-@pytest.mark.parametrize("M", [3000, 20000])
+@pytest.mark.parametrize("M", [3000, 20000, 65536])
 def test_graph_replays_match_eager(M, refill, fused):
     w = synth.Workload("case", L=2, H=8, Hkv=2, d=128, N=8, dtype=synth.BF16, seed=9, M=M,
                        plant_frac=0.05, plant_chunk=32)
