@@ -9,7 +9,7 @@ library is missing, or a call fails, an exception says so.
 The call names follow the C ABI in ``include/specprefill.h``:
 ``sp_score``, ``sp_score_varlen``, ``sp_score_windows``, ``sp_window_layout``,
 ``sp_select``, ``sp_select_varlen``,
-``sp_score_workspace_bytes``, ``sp_select_workspace_bytes``,
+``sp_score_workspace_bytes``, ``sp_score_batch_workspace_bytes``, ``sp_select_workspace_bytes``,
 ``sp_score_plan`` and ``sp_status_string``.
 """
 from __future__ import annotations
@@ -30,7 +30,7 @@ SP_LAUNCH_RESIDENT, SP_LAUNCH_COOPERATIVE = 0, 1
 SP_NORM_MINMAX, SP_NORM_PERCENTILE, SP_NORM_ZSCORE = 0, 1, 2
 
 EXPORTED = ("sp_score", "sp_score_varlen", "sp_select", "sp_select_varlen",
-            "sp_score_workspace_bytes", "sp_select_workspace_bytes", "sp_score_plan",
+            "sp_score_workspace_bytes", "sp_score_batch_workspace_bytes", "sp_score_batch_plan", "sp_select_workspace_bytes", "sp_score_plan",
             "sp_status_string", "sp_profile_score_kernel", "sp_score_status",
             "sp_score_windows", "sp_window_layout", "sp_gather_rows", "sp_break_even",
             "sp_read_probe", "sp_set_wait_limit", "sp_score_lastrow", "sp_score_noalloc",
@@ -76,6 +76,10 @@ def load_library():
     lib.sp_status_string.restype = ctypes.c_char_p
     lib.sp_score_workspace_bytes.argtypes = [P(ScoreDesc), i64]
     lib.sp_score_workspace_bytes.restype = sz
+    lib.sp_score_batch_workspace_bytes.argtypes = [P(ScoreDesc), i32, P(ctypes.c_int64)]
+    lib.sp_score_batch_workspace_bytes.restype = sz
+    lib.sp_score_batch_plan.argtypes = [P(ScoreDesc), i32, P(ctypes.c_int64), sz,
+                                        P(ctypes.c_int32), P(ctypes.c_int32)]
     lib.sp_score_plan.argtypes = [P(ScoreDesc), i32, P(ctypes.c_int32)]
     lib.sp_score.argtypes = [P(ScoreDesc), vp, vp, i32, vp, vp, sz, vp]
     lib.sp_score_varlen.argtypes = [P(ScoreDesc), i32, vp, vp, P(ctypes.c_int64), vp, vp, sz, vp]
@@ -178,6 +182,36 @@ def select_params(chunk=32, pool_k=1, mode="topk", keep_rate=0.0, mass=0.0, boos
 
 def sp_score_workspace_bytes(desc: ScoreDesc, max_prompt_len: int) -> int:
     return int(load_library().sp_score_workspace_bytes(ctypes.byref(desc), int(max_prompt_len)))
+
+
+def sp_score_batch_workspace_bytes(desc: ScoreDesc, cu_prompt: Sequence[int]) -> int:
+    """Workspace with which sp_score_varlen / sp_score_windows pack requests
+    into shared launches wherever the planner finds it faster."""
+    cu = np.ascontiguousarray(np.asarray(cu_prompt, dtype=np.int64))
+    return int(load_library().sp_score_batch_workspace_bytes(
+        ctypes.byref(desc), int(cu.shape[0] - 1), cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))))
+
+
+def sp_score_batch_plan(desc: ScoreDesc, cu_prompt: Sequence[int], ws_bytes: int) -> np.ndarray:
+    """Each request's launch index under sp_score_varlen with a workspace of
+    ws_bytes (requests with one index share a launch)."""
+    cu = np.ascontiguousarray(np.asarray(cu_prompt, dtype=np.int64))
+    R = int(cu.shape[0] - 1)
+    out = np.zeros(max(R, 1), np.int32)
+    n = ctypes.c_int32(0)
+    _check(load_library().sp_score_batch_plan(
+        ctypes.byref(desc), R, cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), int(ws_bytes),
+        out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), ctypes.byref(n)), "sp_score_batch_plan")
+    return out[:R]
+
+
+def _batch_workspace(desc: ScoreDesc, cu, maxM: int, device, workspace):
+    """A given workspace must hold one request (smaller than the batch's packing
+    bound, the batch is scored in turn); else one of the packing bound."""
+    if workspace is None:
+        nbytes = max(sp_score_batch_workspace_bytes(desc, cu), sp_score_workspace_bytes(desc, maxM))
+        return _workspace(nbytes, device)
+    return _workspace(sp_score_workspace_bytes(desc, maxM), device, workspace)
 
 
 def sp_select_workspace_bytes(R: int, total_prompt_len: int, params: SelectParams) -> int:
@@ -296,7 +330,7 @@ def sp_score_varlen(Q, K, cu_prompt: Sequence[int], scale: float = 0.0, out=None
         out = torch.empty(int(cu[-1]), dtype=torch.float32, device=Q.device)
     _check_out(out, torch.float32, int(cu[-1]), "out")
     maxM = int(np.max(np.diff(cu))) if R else 1
-    ws = _workspace(sp_score_workspace_bytes(desc, maxM), Q.device, workspace)
+    ws = _batch_workspace(desc, cu, maxM, Q.device, workspace)
     st = load_library().sp_score_varlen(
         ctypes.byref(desc), int(R), Q.data_ptr(), K.data_ptr(),
         cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), out.data_ptr(), ws.data_ptr(),
@@ -340,7 +374,7 @@ def sp_score_windows(Q, K, cu_window: Sequence[int], keeps: Sequence[int], scale
         out = torch.empty(int(kp.sum()), dtype=torch.float32, device=Q.device)
     _check_out(out, torch.float32, int(kp.sum()), "out")
     maxM = int(np.max(np.diff(cu)))
-    ws = _workspace(sp_score_workspace_bytes(desc, maxM), Q.device, workspace)
+    ws = _batch_workspace(desc, cu, maxM, Q.device, workspace)
     p64 = ctypes.POINTER(ctypes.c_int64)
     st = load_library().sp_score_windows(
         ctypes.byref(desc), int(R), Q.data_ptr(), K.data_ptr(), cu.ctypes.data_as(p64),

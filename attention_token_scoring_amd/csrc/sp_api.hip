@@ -3,7 +3,9 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
+#include <vector>
 
 #include "sp_internal.h"
 
@@ -18,6 +20,8 @@ hipError_t launch_score(const ScorePlan& p, const sp_score_desc& d, const void* 
                         long long plane_stride, int M, int M_out, float* importance, void* ws,
                         unsigned call_epoch, bool first, int tail_n, int blend_n, const FusedSelect* fs,
                         hipStream_t stream);
+hipError_t launch_score_pack(const PackRequest* pk, int n, const sp_score_desc& d, long long plane_stride,
+                             unsigned call_epoch, bool first, hipStream_t stream);
 unsigned next_epoch();
 hipError_t launch_gather(const void* src, long long row_bytes, const int32_t* kept,
                          const int32_t* n_kept, int R, const int64_t* cu, long long max_rows,
@@ -150,9 +154,176 @@ SelectParamsDev to_dev(const sp_select_params* p) {
     return q;
 }
 
-// Requests r in [0, R) of a ragged batch, each scored alone; with keep, only the
-// first keep[r] scores of request r are written, packed one request after the
-// other (else all M_r scores at offset cu[r]).
+size_t round_up256(size_t x) { return (x + 255) / 256 * 256; }
+
+// The per-launch time the planner's estimates leave out (launch, pipeline
+// start, the end of the exchange; measured ~15-20 us on the MI355X), and the
+// streaming workgroups at which the kernel reaches the full read rate (the
+// planner's bandwidth model).
+constexpr double kLaunchFixedS = 15e-6;
+constexpr double kFullRateWgs = 200.0;
+// Which requests share a launch (measured on the MI355X at the 8B shape).
+// Packs of prompts of similar length gained 3-75 % (16 x 4K tokens 1.03 ->
+// 0.75 ms, 4 x 1000 0.170 -> 0.096 ms, 4 of 15K-53K 1.34 -> 1.30 ms); packs
+// that mixed lengths 5 to 50 times apart lost 5-20 % against estimates of
+// small gains (the smallest requests' few CUs, with one combining workgroup
+// for every unit, fall behind the plans' estimates), so the longest prompt
+// of a pack is at most kPackSpread times its shortest. The estimates also
+// favoured the smaller tile count where the larger measured faster: packs
+// are planned with the larger where the configuration has one. A pack must
+// be estimated at least kPackMargin faster than its requests in turn.
+constexpr long long kPackSpread = 4;
+constexpr double kPackMargin = 0.01;
+constexpr int kPackPasses = 4;
+
+// One launch for requests [r0, r0 + n), each on its own share of the CUs and
+// planned for that share with tpw tiles per wave (a launch runs one kernel
+// configuration). The shares start proportional to the requests' keys; each
+// further pass sets them in proportion to the last plans' estimated CU-time
+// (estimate x share), which evens out their estimates. Returns the best
+// pass's estimated time of the launch (plans and workspace offsets in pk), or
+// a negative number where no pass has plans that fit ws_bytes.
+double plan_one_pack(const sp_score_desc& d, const long long* Ms, int r0, int n, int cus, int tpw,
+                     size_t ws_bytes, PackRequest* pk) {
+    double w[kMaxPack], W = 0.0, best = -1.0;
+    for (int i = 0; i < n; ++i) {
+        w[i] = (double)(Ms[r0 + i] + d.N);
+        W += w[i];
+    }
+    int last[kMaxPack] = {};
+    PackRequest cand[kMaxPack];
+    for (int pass = 0; pass < kPackPasses; ++pass) {
+        // shares: at least 2 CUs (a streaming and a combining workgroup)
+        int c[kMaxPack], used = 0;
+        for (int i = 0; i < n; ++i) {
+            c[i] = (int)(cus * w[i] / W);
+            if (c[i] < 2) c[i] = 2;
+            used += c[i];
+        }
+        while (used > cus) {  // (the floors of 2 overshot: take from the largest)
+            int j = 0;
+            for (int i = 1; i < n; ++i) j = c[i] > c[j] ? i : j;
+            if (c[j] <= 2) return best;
+            --c[j];
+            --used;
+        }
+        for (; used < cus; ++used) {  // the rest to the largest weight per CU
+            int j = 0;
+            for (int i = 1; i < n; ++i) j = w[i] / c[i] > w[j] / c[j] ? i : j;
+            ++c[j];
+        }
+        bool same = true;
+        for (int i = 0; i < n; ++i) {
+            same = same && c[i] == last[i];
+            last[i] = c[i];
+        }
+        if (same) break;  // (the shares have settled)
+        int S = 0;
+        double worst = 0.0;
+        size_t off = 0;
+        for (int i = 0; i < n; ++i) {
+            ScorePlan& p = cand[i].plan;
+            if (make_plan(d, Ms[r0 + i], c[i], &p, tpw) != SP_OK || p.dma != cand[0].plan.dma)
+                return best;
+            S += p.g * p.ngroups;
+            worst = p.cost > worst ? p.cost : worst;
+            cand[i].ws = (void*)off;  // (an offset until the launch)
+            off += round_up256(p.ws_total);
+        }
+        if (off > ws_bytes) return best;
+        // (the plans model a request's bandwidth as its share of the full
+        // rate: the device's total caps it)
+        const double t = worst * (S > kFullRateWgs ? S / kFullRateWgs : 1.0) + kLaunchFixedS;
+        if (best < 0.0 || t < best) {
+            best = t;
+            for (int i = 0; i < n; ++i) pk[i] = cand[i];
+        }
+        W = 0.0;
+        for (int i = 0; i < n; ++i) {
+            w[i] = cand[i].plan.cost * cand[i].plan.cus;
+            W += w[i];
+        }
+    }
+    return best;
+}
+
+// Packing from request r0 on of R requests of prompt lengths Ms: the n (1 ..
+// kMaxPack) whose one launch (plan_one_pack) is estimated fastest per request
+// against scoring them one after the other, with the plans and workspace
+// offsets in pk (n = 1: no packing). full: each request's plan for the whole
+// device.
+int plan_pack(const sp_score_desc& d, const long long* Ms, int r0, int R, int cus, size_t ws_bytes,
+              const ScorePlan* full, PackRequest* pk) {
+    int best_n = 1;
+    double best_gain = 0.0;
+    PackRequest cand[kMaxPack];
+    const int tpw0 = tiles_per_wave(d.dtype == SP_BF16, d.d);
+    long long lo = Ms[r0], hi = lo;
+    for (int n = 2; n <= kMaxPack && r0 + n <= R; ++n) {
+        const long long M = Ms[r0 + n - 1];
+        lo = M < lo ? M : lo;
+        hi = M > hi ? M : hi;
+        if (hi > kPackSpread * lo) break;
+        double seq = 0.0;
+        for (int i = 0; i < n; ++i) seq += full[r0 + i].cost + kLaunchFixedS;
+        double t = plan_one_pack(d, Ms, r0, n, cus, tpw0 + 1, ws_bytes, cand);
+        if (t < 0.0) t = plan_one_pack(d, Ms, r0, n, cus, tpw0, ws_bytes, cand);
+        if (t < 0.0 || seq - t <= kPackMargin * seq) continue;
+        if ((seq - t) / n > best_gain) {
+            best_gain = (seq - t) / n;
+            best_n = n;
+            for (int i = 0; i < n; ++i) pk[i] = cand[i];
+        }
+    }
+    return best_n;
+}
+
+// The launches of a ragged batch: the requests in order of prompt length
+// (shortest first; launches are independent, and packs want lengths alike),
+// consecutive ones packed where plan_pack finds it pays. A launch of n = 1
+// scores request req[0] alone with its plan for the whole device.
+struct BatchLaunch {
+    int n;
+    int req[kMaxPack];
+    PackRequest pk[kMaxPack];  // (n > 1; ws holds the region's offset)
+};
+
+// Validates every request's plan for the whole device (into full) and
+// schedules the batch's launches.
+sp_status schedule_batch(const sp_score_desc& d, int R, const int64_t* cu, int cus, size_t ws_bytes,
+                         std::vector<ScorePlan>& full, std::vector<BatchLaunch>& launches) {
+    full.resize((size_t)R);
+    for (int r = 0; r < R; ++r) {
+        const sp_status s = make_plan(d, cu[r + 1] - cu[r], cus, &full[r]);
+        if (s != SP_OK) return s;
+        if (ws_bytes < full[r].ws_total) return SP_EWORKSPACE;
+    }
+    std::vector<int> order((size_t)R);
+    for (int r = 0; r < R; ++r) order[r] = r;
+    std::stable_sort(order.begin(), order.end(),
+                     [&](int a, int b) { return cu[a + 1] - cu[a] < cu[b + 1] - cu[b]; });
+    std::vector<long long> Ms((size_t)R);
+    std::vector<ScorePlan> fs((size_t)R);
+    for (int i = 0; i < R; ++i) {
+        Ms[i] = cu[order[i] + 1] - cu[order[i]];
+        fs[i] = full[order[i]];
+    }
+    launches.clear();
+    for (int i = 0; i < R;) {
+        BatchLaunch b;
+        b.n = plan_pack(d, Ms.data(), i, R, cus, ws_bytes, fs.data(), b.pk);
+        for (int j = 0; j < b.n; ++j) b.req[j] = order[i + j];
+        launches.push_back(b);
+        i += b.n;
+    }
+    return SP_OK;
+}
+
+// Requests r in [0, R) of a ragged batch, scored in the launches schedule_batch
+// makes (alone, or several in one launch on shares of the device where the
+// workspace holds their regions side by side); with keep, only the first
+// keep[r] scores of request r are written, packed one request after the
+// other in request order (else all M_r scores at offset cu[r]).
 sp_status score_batch(const sp_score_desc* desc, int32_t R, const void* Q, const void* K,
                       const int64_t* cu, const int64_t* keep, float* importance, void* ws,
                       size_t ws_bytes, void* stream) {
@@ -170,31 +341,60 @@ sp_status score_batch(const sp_score_desc* desc, int32_t R, const void* Q, const
     if (cus < 1) return SP_EDEVICE;
     if (!ws || !aligned(ws, 256)) return SP_EWORKSPACE;
     // validate every request's plan before enqueueing anything
-    for (int r = 0; r < R; ++r) {
-        ScorePlan p;
-        s = make_plan(*desc, cu[r + 1] - cu[r], cus, &p);
-        if (s != SP_OK) return s;
-        if (ws_bytes < p.ws_total) return SP_EWORKSPACE;
-    }
+    std::vector<ScorePlan> full;
+    std::vector<BatchLaunch> launches;
+    s = schedule_batch(*desc, R, cu, cus, ws_bytes, full, launches);
+    if (s != SP_OK) return s;
     const int es = esize(desc->dtype);
     const long long T = cu[R] + (long long)R * desc->N;
     const long long qsz = (long long)desc->L * desc->H * desc->N * desc->d * es;
-    long long out = 0;
-    const unsigned call = next_epoch();
+    std::vector<long long> out((size_t)R);  // where request r's scores go
+    long long o = 0;
     for (int r = 0; r < R; ++r) {
-        const long long M = cu[r + 1] - cu[r];
-        ScorePlan p;
-        make_plan(*desc, M, cus, &p);
-        const char* Qr = (const char*)Q + r * qsz;
-        const char* Kr = (const char*)K + (cu[r] + (long long)r * desc->N) * desc->d * es;
-        const long long M_out = keep ? keep[r] : M;
-        float* imp = importance + (keep ? out : cu[r]);
-        s = to_status(launch_score(p, *desc, Qr, Kr, T * desc->d, (int)M, (int)M_out, imp, ws, call,
-                                   r == 0, desc->N, 0, nullptr, (hipStream_t)stream));
+        out[r] = keep ? o : cu[r];
+        o += keep ? keep[r] : 0;
+    }
+    const unsigned call = next_epoch();
+    bool first = true;
+    for (BatchLaunch& b : launches) {
+        for (int i = 0; i < b.n; ++i) {
+            const int r = b.req[i];
+            const long long M = cu[r + 1] - cu[r];
+            PackRequest& q = b.pk[i];
+            q.Q = (const char*)Q + r * qsz;
+            q.K = (const char*)K + (cu[r] + (long long)r * desc->N) * desc->d * es;
+            q.M = (int)M;
+            q.M_out = (int)(keep ? keep[r] : M);
+            q.importance = importance + out[r];
+            if (b.n > 1) q.ws = (char*)ws + (size_t)q.ws;
+        }
+        if (b.n == 1) {
+            const PackRequest& q = b.pk[0];
+            s = to_status(launch_score(full[b.req[0]], *desc, q.Q, q.K, T * desc->d, q.M, q.M_out, q.importance, ws,
+                                       call, first, desc->N, 0, nullptr, (hipStream_t)stream));
+        } else {
+            s = to_status(launch_score_pack(b.pk, b.n, *desc, T * desc->d, call, first, (hipStream_t)stream));
+        }
         if (s != SP_OK) return s;
-        out += M_out;
+        first = false;
     }
     return SP_OK;
+}
+
+// The workspace with which score_batch packs as its plans allow (at least
+// what every request needs alone).
+size_t batch_workspace(const sp_score_desc& d, int R, const int64_t* cu, int cus) {
+    std::vector<ScorePlan> full;
+    std::vector<BatchLaunch> launches;
+    if (schedule_batch(d, R, cu, cus, (size_t)-1, full, launches) != SP_OK) return 0;
+    size_t need = 0;
+    for (const ScorePlan& p : full) need = p.ws_total > need ? p.ws_total : need;
+    for (const BatchLaunch& b : launches) {
+        if (b.n == 1) continue;
+        const size_t end = (size_t)b.pk[b.n - 1].ws + round_up256(b.pk[b.n - 1].plan.ws_total);
+        need = end > need ? end : need;
+    }
+    return need;
 }
 
 }  // namespace
@@ -226,6 +426,40 @@ size_t sp_score_workspace_bytes(const sp_score_desc* desc, int64_t max_prompt_le
     const size_t a = workspace_bound(*desc, max_prompt_len, device_cus());
     const size_t b = workspace_bound(d1, max_prompt_len, device_cus());
     return a > b ? a : b;
+}
+
+size_t sp_score_batch_workspace_bytes(const sp_score_desc* desc, int32_t R, const int64_t* cu) {
+    if (check_desc(desc) != SP_OK || R < 1 || !cu || cu[0] != 0) return 0;
+    long long maxM = 0;
+    for (int r = 0; r < R; ++r) {
+        const long long M = cu[r + 1] - cu[r];
+        if (M < 1) return 0;
+        maxM = M > maxM ? M : maxM;
+    }
+    const size_t one = sp_score_workspace_bytes(desc, maxM);
+    if (one == 0) return 0;
+    const size_t packed = batch_workspace(*desc, R, cu, device_cus() > 0 ? device_cus() : kDefaultCUs);
+    if (packed == 0) return 0;
+    return packed > one ? packed : one;
+}
+
+sp_status sp_score_batch_plan(const sp_score_desc* desc, int32_t R, const int64_t* cu, size_t ws_bytes,
+                              int32_t* launch_of, int32_t* n_launches) {
+    sp_status s = check_desc(desc);
+    if (s != SP_OK) return s;
+    if (R < 1 || !cu || cu[0] != 0 || !n_launches) return SP_EINVAL;
+    for (int r = 0; r < R; ++r)
+        if (cu[r + 1] - cu[r] < 1) return SP_EINVAL;
+    const int cus = device_cus() > 0 ? device_cus() : kDefaultCUs;
+    std::vector<ScorePlan> full;
+    std::vector<BatchLaunch> launches;
+    s = schedule_batch(*desc, R, cu, cus, ws_bytes, full, launches);
+    if (s != SP_OK) return s;
+    for (size_t l = 0; l < launches.size(); ++l)
+        for (int i = 0; i < launches[l].n; ++i)
+            if (launch_of) launch_of[launches[l].req[i]] = (int32_t)l;
+    *n_launches = (int32_t)launches.size();
+    return SP_OK;
 }
 
 sp_status sp_profile_score_kernel(void* before, void* after) {

@@ -185,6 +185,16 @@ struct ScoreArgs {
     int sel_dist;              // 1: the streaming workgroups sum the chunk masses
 };
 
+// Requests scored in one launch (sp_score_varlen): request r on blocks
+// [first[r], first[r + 1]).
+constexpr int kMaxPack = 4;
+constexpr int kLaunchPlain = 0, kLaunchFused = 1, kLaunchPack = 2;
+struct PackArgs {
+    int n;
+    int first[kMaxPack + 1];
+    ScoreArgs args[kMaxPack];
+};
+
 struct ScorePlan {
     int rows;      // 16 or 32
     int tpw;       // tiles per streaming wave and unit
@@ -195,13 +205,26 @@ struct ScorePlan {
     int grid;      // g * ngroups + ncomb
     int defer;
     int cus;       // compute units of the device planned for
+    double cost;   // the planner's estimate of the kernel's time (s) with cus CUs to itself
     ScoreLds lds;
     size_t ws_err, ws_part, ws_lse, ws_sel, ws_tg, ws_total;  // byte offsets / sizes in the workspace
 };
 
+// One request of a launch that scores several (launch_score_pack): its plan
+// (for its share of the CUs), operands, output and workspace region.
+struct PackRequest {
+    ScorePlan plan;
+    const void* Q;
+    const void* K;
+    int M, M_out;
+    float* importance;
+    void* ws;
+};
+
 // Launch plan for one prompt of M keys on a device with cus compute units
-// (SP_EINVAL for M < 1, SP_EUNSUPPORTED where no split fits).
-sp_status make_plan(const sp_score_desc& d, long long M, int cus, ScorePlan* out);
+// (SP_EINVAL for M < 1, SP_EUNSUPPORTED where no split fits); only_tpw > 0
+// restricts the plan to that many tiles per wave.
+sp_status make_plan(const sp_score_desc& d, long long M, int cus, ScorePlan* out, int only_tpw = 0);
 
 // Workspace bytes that cover every plan make_plan can choose for M <= max_M.
 size_t workspace_bound(const sp_score_desc& d, long long max_M, int cus);
@@ -224,5 +247,9 @@ const void* score_select_kernel_bf16_d128(int rows, int G, int tpw, bool dma);
 const void* score_select_kernel_bf16_d64(int rows, int G, int tpw, bool dma);
 const void* score_select_kernel_f32_d128(int rows, int G, int tpw, bool dma);
 const void* score_select_kernel_f32_d64(int rows, int G, int tpw, bool dma);
+const void* score_pack_kernel_bf16_d128(int rows, int G, int tpw, bool dma);
+const void* score_pack_kernel_bf16_d64(int rows, int G, int tpw, bool dma);
+const void* score_pack_kernel_f32_d128(int rows, int G, int tpw, bool dma);
+const void* score_pack_kernel_f32_d64(int rows, int G, int tpw, bool dma);
 
 }  // namespace sp

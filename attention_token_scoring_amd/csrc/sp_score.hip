@@ -19,20 +19,17 @@ __global__ __launch_bounds__(256) void clear_tags_kernel(uint4* p, size_t n16) {
 // ---------------------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------------------
-// The scoring kernel for a launch plan (sel: the fused launch that also selects).
-static const void* pick_kernel(int dtype, int d, int rows, int G, int tpw, bool dma, bool sel) {
-    if (dtype == SP_BF16) {
-        if (d == 128)
-            return sel ? score_select_kernel_bf16_d128(rows, G, tpw, dma) : score_kernel_bf16_d128(rows, G, tpw, dma);
-        if (d == 64)
-            return sel ? score_select_kernel_bf16_d64(rows, G, tpw, dma) : score_kernel_bf16_d64(rows, G, tpw, dma);
-    } else {
-        if (d == 128)
-            return sel ? score_select_kernel_f32_d128(rows, G, tpw, dma) : score_kernel_f32_d128(rows, G, tpw, dma);
-        if (d == 64)
-            return sel ? score_select_kernel_f32_d64(rows, G, tpw, dma) : score_kernel_f32_d64(rows, G, tpw, dma);
-    }
-    return nullptr;
+// The scoring kernel for a launch plan and launch mode (kLaunchPlain,
+// kLaunchFused: also selects, kLaunchPack: several requests).
+static const void* pick_kernel(int dtype, int d, int rows, int G, int tpw, bool dma, int mode) {
+    using Pick = const void* (*)(int, int, int, bool);
+    static const Pick table[2][2][3] = {
+        {{score_kernel_f32_d64, score_select_kernel_f32_d64, score_pack_kernel_f32_d64},
+         {score_kernel_f32_d128, score_select_kernel_f32_d128, score_pack_kernel_f32_d128}},
+        {{score_kernel_bf16_d64, score_select_kernel_bf16_d64, score_pack_kernel_bf16_d64},
+         {score_kernel_bf16_d128, score_select_kernel_bf16_d128, score_pack_kernel_bf16_d128}}};
+    if ((d != 64 && d != 128) || mode < kLaunchPlain || mode > kLaunchPack) return nullptr;
+    return table[dtype == SP_BF16 ? 1 : 0][d == 128 ? 1 : 0][mode](rows, G, tpw, dma);
 }
 
 static thread_local hipEvent_t t_ev_before = nullptr, t_ev_after = nullptr;
@@ -73,17 +70,16 @@ unsigned next_epoch() {
 // if the descriptor asks for it, a cooperative one. call_epoch tags the
 // call's error word (shared by all its launches); first: the call's first
 // launch.
-hipError_t launch_score(const ScorePlan& p, const sp_score_desc& d, const void* Q, const void* K,
-                        long long plane_stride, int M, int M_out, float* importance, void* ws,
-                        unsigned call_epoch, bool first, int tail_n, int blend_n, const FusedSelect* fs,
-                        hipStream_t stream) {
-    char* base = (char*)ws;
-    ScoreArgs a;
+// The kernel arguments of one request whose workspace region starts at base;
+// call_ws: the region of the call's error word and last epoch.
+static void fill_args(const ScorePlan& p, const sp_score_desc& d, const void* Q, const void* K,
+                      long long plane_stride, int M, int M_out, float* importance, char* base, char* call_ws,
+                      unsigned call_epoch, int tail_n, int blend_n, const FusedSelect* fs, ScoreArgs& a) {
     a.Q = Q;
     a.K = K;
     a.plane_stride = plane_stride;
-    a.err = (unsigned long long*)(base + p.ws_err);
-    a.hdr = (unsigned*)(base + p.ws_err + 8);
+    a.err = (unsigned long long*)(call_ws + p.ws_err);
+    a.hdr = (unsigned*)(call_ws + p.ws_err + 8);
     a.flags = (unsigned long long*)(base + p.ws_err + 128);
     a.importance = importance;
     a.M_out = M_out;
@@ -126,41 +122,36 @@ hipError_t launch_score(const ScorePlan& p, const sp_score_desc& d, const void* 
         a.sel_pos = fs->pos;
         a.sel_n = fs->n_kept;
     }
-    // (the fused selection reuses the combiner's LDS)
-    size_t lds = p.lds.total;
-    if (fs && lds < sizeof(SelectShared<kThreads>)) lds = sizeof(SelectShared<kThreads>);
+}
 
-    const void* fn = pick_kernel(d.dtype, d.d, p.rows, a.G, p.tpw, p.dma, fs != nullptr);
-    if (!fn) return hipErrorInvalidValue;
+// Under capture: the clearing of one workspace region's tagged words.
+static hipError_t clear_region(const ScorePlan& p, char* base, bool first, hipStream_t stream) {
+    const size_t lo = first ? 0 : 16;  // (keep the call's error word)
+    const size_t n16 = (p.ws_tg - lo) / 16;
+    hipLaunchKernelGGL(clear_tags_kernel, dim3((unsigned)((n16 + 255) / 256 < 1024 ? (n16 + 255) / 256 : 1024)),
+                       dim3(256), 0, stream, (uint4*)(base + lo), n16);
+    return hipGetLastError();
+}
+
+// The launch itself (grid workgroups of kThreads threads, lds bytes of
+// dynamic LDS), bracketed by the profiling events when they are set.
+static hipError_t launch_grid(const sp_score_desc& d, const void* fn, void** args, int grid, int cus, size_t lds,
+                              hipStream_t stream) {
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-
-    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-    e = hipStreamIsCapturing(stream, &cap);
-    if (e != hipSuccess) return e;
-    if (cap != hipStreamCaptureStatusNone) {
-        const size_t lo = first ? 0 : 16;  // (keep the call's error word)
-        const size_t n16 = (p.ws_tg - lo) / 16;
-        hipLaunchKernelGGL(clear_tags_kernel, dim3((unsigned)((n16 + 255) / 256 < 1024 ? (n16 + 255) / 256 : 1024)),
-                           dim3(256), 0, stream, (uint4*)(base + lo), n16);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    void* args[] = {&a};
     if (t_ev_before) {
         e = hipEventRecord(t_ev_before, stream);
         if (e != hipSuccess) return e;
     }
     if (d.launch == SP_LAUNCH_COOPERATIVE) {
-        e = hipLaunchCooperativeKernel(fn, dim3(p.grid), dim3(kThreads), args, (unsigned)lds, stream);
+        e = hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kThreads), args, (unsigned)lds, stream);
     } else {
         // every workgroup must fit on the device at once (one per unit here)
         int per_cu = 0;
         e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, lds);
         if (e != hipSuccess) return e;
-        if (per_cu < 1 || (long long)p.grid > (long long)per_cu * p.cus)
-            return hipErrorCooperativeLaunchTooLarge;
-        e = hipLaunchKernel(fn, dim3(p.grid), dim3(kThreads), args, (unsigned)lds, stream);
+        if (per_cu < 1 || (long long)grid > (long long)per_cu * cus) return hipErrorCooperativeLaunchTooLarge;
+        e = hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, (unsigned)lds, stream);
     }
     if (e != hipSuccess) return e;
     if (t_ev_after) {
@@ -168,6 +159,69 @@ hipError_t launch_score(const ScorePlan& p, const sp_score_desc& d, const void* 
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+hipError_t launch_score(const ScorePlan& p, const sp_score_desc& d, const void* Q, const void* K,
+                        long long plane_stride, int M, int M_out, float* importance, void* ws,
+                        unsigned call_epoch, bool first, int tail_n, int blend_n, const FusedSelect* fs,
+                        hipStream_t stream) {
+    char* base = (char*)ws;
+    ScoreArgs a;
+    fill_args(p, d, Q, K, plane_stride, M, M_out, importance, base, base, call_epoch, tail_n, blend_n, fs, a);
+    // (the fused selection reuses the combiner's LDS)
+    size_t lds = p.lds.total;
+    if (fs && lds < sizeof(SelectShared<kThreads>)) lds = sizeof(SelectShared<kThreads>);
+
+    const void* fn = pick_kernel(d.dtype, d.d, p.rows, a.G, p.tpw, p.dma, fs ? kLaunchFused : kLaunchPlain);
+    if (!fn) return hipErrorInvalidValue;
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    hipError_t e = hipStreamIsCapturing(stream, &cap);
+    if (e != hipSuccess) return e;
+    if (cap != hipStreamCaptureStatusNone) {
+        e = clear_region(p, base, first, stream);
+        if (e != hipSuccess) return e;
+    }
+    void* args[] = {&a};
+    return launch_grid(d, fn, args, p.grid, p.cus, lds, stream);
+}
+
+// n requests in one launch: request r with plan pk[r].plan on its own share of
+// the device's CUs and its own workspace region at pk[r].ws (all plans have
+// the same tiles per wave and K path); the call's error word is in pk[0]'s
+// region.
+hipError_t launch_score_pack(const PackRequest* pk, int n, const sp_score_desc& d, long long plane_stride,
+                             unsigned call_epoch, bool first, hipStream_t stream) {
+    if (n < 1 || n > kMaxPack) return hipErrorInvalidValue;
+    PackArgs m;
+    m.n = n;
+    m.first[0] = 0;
+    size_t lds = 0;
+    int cus = 0;
+    for (int r = 0; r < n; ++r) {
+        const ScorePlan& p = pk[r].plan;
+        if (p.tpw != pk[0].plan.tpw || p.dma != pk[0].plan.dma || p.rows != pk[0].plan.rows)
+            return hipErrorInvalidValue;
+        fill_args(p, d, pk[r].Q, pk[r].K, plane_stride, pk[r].M, pk[r].M_out, pk[r].importance, (char*)pk[r].ws,
+                  (char*)pk[0].ws, call_epoch, d.N, 0, nullptr, m.args[r]);
+        m.first[r + 1] = m.first[r] + p.grid;
+        if (p.lds.total > lds) lds = p.lds.total;
+        cus += p.cus;
+    }
+    for (int r = n; r < kMaxPack; ++r) m.first[r + 1] = m.first[n];
+    const ScorePlan& p0 = pk[0].plan;
+    const void* fn = pick_kernel(d.dtype, d.d, p0.rows, d.H / d.Hkv, p0.tpw, p0.dma, kLaunchPack);
+    if (!fn) return hipErrorInvalidValue;
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    hipError_t e = hipStreamIsCapturing(stream, &cap);
+    if (e != hipSuccess) return e;
+    if (cap != hipStreamCaptureStatusNone) {
+        for (int r = 0; r < n; ++r) {
+            e = clear_region(pk[r].plan, (char*)pk[r].ws, first && r == 0, stream);
+            if (e != hipSuccess) return e;
+        }
+    }
+    void* args[] = {&m};
+    return launch_grid(d, fn, args, m.first[n], cus, lds, stream);
 }
 
 }  // namespace sp

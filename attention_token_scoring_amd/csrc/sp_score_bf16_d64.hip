@@ -4,7 +4,7 @@
 namespace sp {
 
 const void* score_kernel_bf16_d64(int rows, int G, int tpw, bool dma) {
-    return pick_kernel_for<64, true, false>(rows, G, tpw, dma);
+    return pick_kernel_for<64, true, kLaunchPlain>(rows, G, tpw, dma);
 }
 
 }  // namespace sp

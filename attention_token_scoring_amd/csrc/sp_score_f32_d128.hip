@@ -4,7 +4,7 @@
 namespace sp {
 
 const void* score_kernel_f32_d128(int rows, int G, int tpw, bool dma) {
-    return pick_kernel_for<128, false, false>(rows, G, tpw, dma);
+    return pick_kernel_for<128, false, kLaunchPlain>(rows, G, tpw, dma);
 }
 
 }  // namespace sp

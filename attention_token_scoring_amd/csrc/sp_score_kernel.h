@@ -353,7 +353,8 @@ __device__ __attribute__((noinline)) inline void fused_select_ranked(SelectParam
 // chunks sw, sw + nstream, ... (sw = its index) over the scores (every token's
 // value and boosts as the selection computes them; the sums are exact, so the
 // split does not change them), each chunk's mass stored as two tagged words.
-__device__ __forceinline__ void fused_tail(const ScoreArgs& a, float smn, float smx, int snf, int nstream) {
+__device__ __forceinline__ void fused_tail(const ScoreArgs& a, float smn, float smx, int snf, int nstream,
+                                           const int bid) {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     __shared__ float mm[2 * kWaves];
     __shared__ float gmm[2];
@@ -364,7 +365,7 @@ __device__ __forceinline__ void fused_tail(const ScoreArgs& a, float smn, float 
         // that the scores are written)
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        if (tid == 0) st64u(a.done + 2 * blockIdx.x, Et | a.epoch);
+        if (tid == 0) st64u(a.done + 2 * bid, Et | a.epoch);
         return;
     }
 #pragma unroll
@@ -384,12 +385,12 @@ __device__ __forceinline__ void fused_tail(const ScoreArgs& a, float smn, float 
             m0 = fminf(m0, mm[x]);
             m1 = fmaxf(m1, mm[kWaves + x]);
         }
-        st64u(a.done + 2 * blockIdx.x, Et | __float_as_uint(m0));
-        st64u(a.done + 2 * blockIdx.x + 1, Et | (nf ? kNonFiniteMark : __float_as_uint(m1)));
+        st64u(a.done + 2 * bid, Et | __float_as_uint(m0));
+        st64u(a.done + 2 * bid + 1, Et | (nf ? kNonFiniteMark : __float_as_uint(m1)));
     }
     const int chunk = a.selp.chunk;
     const int nc = (a.M + chunk - 1) / chunk;
-    const int sw = blockIdx.x;
+    const int sw = bid;
     const int nj = sw < nc ? (nc - sw + nstream - 1) / nstream : 0;  // this workgroup's chunks
     if (nj == 0) return;
     if (w == 0) {
@@ -460,8 +461,28 @@ __device__ __forceinline__ void fused_tail(const ScoreArgs& a, float smn, float 
 }
 
 // SEL: the fused launch (sp_score_select), which also selects from the scores.
-template <class C, bool SEL>
-__global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
+// A: ScoreArgs (one request per launch: workgroup b of the grid is the
+// request's workgroup b) or PackArgs (several requests per launch, request r
+// on blocks [first[r], first[r + 1]) with its own workgroups, combiners and
+// workspace: the requests share nothing; not with SEL).
+template <class C, bool SEL, class A>
+__global__ __launch_bounds__(kThreads, 1) void score_kernel(A karg) {
+    // this workgroup's request, its index among the request's workgroups, and
+    // their count (-1: the whole grid, read where it is used rather than kept
+    // live)
+    int bid = (int)blockIdx.x, nblocks = -1;
+    const ScoreArgs* ap;
+    if constexpr (std::is_same<A, PackArgs>::value) {
+        static_assert(!SEL, "the fused selection scores one request per launch");
+        int r = 0;
+        for (int i = 1; i < karg.n; ++i) r = bid >= karg.first[i] ? i : r;
+        ap = &karg.args[r];
+        nblocks = karg.first[r + 1] - karg.first[r];
+        bid -= karg.first[r];
+    } else {
+        ap = &karg;
+    }
+    const ScoreArgs& a = *ap;
     constexpr int TPW = C::TPW, NH = C::NH, ROWS = C::ROWS, G = C::G, NLD = C::NLD;
     constexpr int SW = kStreamWaves;  // waves 0..SW-1 stream K; wave SW synchronises
     extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -474,7 +495,7 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
     const float c = a.c;
     const int nstream = a.g * a.ngroups;
     // (the workspace remembers the last call's epoch, for the status query)
-    if (blockIdx.x == 0 && tid == 0)
+    if (bid == 0 && tid == 0)
         __hip_atomic_store(a.hdr, a.call_epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
     // ---------------------------------------------------------------------------
@@ -484,8 +505,8 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
     // keys) and publish each row's log-sum-exp. Lane L handles row L % ROWS
     // for ranks L / ROWS, L / ROWS + SUBS, ... in batches of B.
     // ---------------------------------------------------------------------------
-    if ((int)blockIdx.x >= nstream) {
-        const int cg = (int)blockIdx.x - nstream, ncg = (int)gridDim.x - nstream;
+    if (bid >= nstream) {
+        const int cg = bid - nstream, ncg = (nblocks < 0 ? (int)gridDim.x : nblocks) - nstream;
         float2* cred = (float2*)smem;  // [kWaves][ROWS]
         constexpr int SUBS = 64 / ROWS;
         constexpr int B = kCombinerBatch;  // ranks polled per lane at once
@@ -673,7 +694,7 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
     // ---------------------------------------------------------------------------
     // Streaming workgroups.
     // ---------------------------------------------------------------------------
-    const int group = (int)blockIdx.x / a.g, rank = (int)blockIdx.x % a.g;
+    const int group = bid / a.g, rank = bid % a.g;
     const int KRP = row_stride(a.KR);
     // With K by DMA, the regions other than the K slots live in an array of
     // their own, so that the compiler can tell the waves' LDS stores there from
@@ -1490,29 +1511,32 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
         }
     }
     if constexpr (SEL)
-        fused_tail(a, smn, smx, snf, nstream);
+        fused_tail(a, smn, smx, snf, nstream, bid);
 }
 
-template <class C, bool SEL>
+// The kernels of one configuration: kLaunchPlain, kLaunchFused (with the
+// selection) or kLaunchPack (several requests).
+template <class C, int MODE>
 const void* kernel_ptr() {
-    return (const void*)&score_kernel<C, SEL>;
+    if constexpr (MODE == kLaunchPack) return (const void*)&score_kernel<C, false, PackArgs>;
+    else return (const void*)&score_kernel<C, MODE == kLaunchFused, ScoreArgs>;
 }
 
 // The instantiation for head-group size G (nullptr when unsupported).
-template <int D, bool BF, int NH, int TPW, bool DMA, bool SEL>
+template <int D, bool BF, int NH, int TPW, bool DMA, int MODE>
 const void* pick_g(int G) {
     switch (G) {
         case 1:
             // (one head per step and two halves keep 32 running maxima per
             // lane: only the base tile count fits the registers)
             if constexpr (NH == 2 && TPW > tiles_per_wave(BF, D)) return nullptr;
-            else return kernel_ptr<Cfg<D, BF, NH, 1, TPW, DMA>, SEL>();
-        case 2: return kernel_ptr<Cfg<D, BF, NH, 2, TPW, DMA>, SEL>();
-        case 4: return kernel_ptr<Cfg<D, BF, NH, 4, TPW, DMA>, SEL>();
-        case 8: return kernel_ptr<Cfg<D, BF, NH, 8, TPW, DMA>, SEL>();
-        case 16: return kernel_ptr<Cfg<D, BF, NH, 16, TPW, DMA>, SEL>();
+            else return kernel_ptr<Cfg<D, BF, NH, 1, TPW, DMA>, MODE>();
+        case 2: return kernel_ptr<Cfg<D, BF, NH, 2, TPW, DMA>, MODE>();
+        case 4: return kernel_ptr<Cfg<D, BF, NH, 4, TPW, DMA>, MODE>();
+        case 8: return kernel_ptr<Cfg<D, BF, NH, 8, TPW, DMA>, MODE>();
+        case 16: return kernel_ptr<Cfg<D, BF, NH, 16, TPW, DMA>, MODE>();
         case 32:
-            if constexpr (NH == 2) return kernel_ptr<Cfg<D, BF, 2, 32, TPW, DMA>, SEL>();
+            if constexpr (NH == 2) return kernel_ptr<Cfg<D, BF, 2, 32, TPW, DMA>, MODE>();
             return nullptr;
         default: return nullptr;
     }
@@ -1521,20 +1545,20 @@ const void* pick_g(int G) {
 // The instantiation for (rows, G, tiles per wave, K path) of one operand type
 // and head dimension; TPW is tiles_per_wave(BF, D) or one more; the DMA path
 // exists for bf16 at the base tile count.
-template <int D, bool BF, bool SEL>
+template <int D, bool BF, int MODE>
 const void* pick_kernel_for(int rows, int G, int tpw, bool dma) {
     constexpr int T0 = tiles_per_wave(BF, D);
     if (dma) {
         if constexpr (BF) {
-            if (tpw == T0) return rows == 32 ? pick_g<D, BF, 2, T0, true, SEL>(G) : pick_g<D, BF, 1, T0, true, SEL>(G);
+            if (tpw == T0) return rows == 32 ? pick_g<D, BF, 2, T0, true, MODE>(G) : pick_g<D, BF, 1, T0, true, MODE>(G);
             if (tpw == T0 + 1)
-                return rows == 32 ? pick_g<D, BF, 2, T0 + 1, true, SEL>(G) : pick_g<D, BF, 1, T0 + 1, true, SEL>(G);
+                return rows == 32 ? pick_g<D, BF, 2, T0 + 1, true, MODE>(G) : pick_g<D, BF, 1, T0 + 1, true, MODE>(G);
         }
         return nullptr;
     }
-    if (tpw == T0) return rows == 32 ? pick_g<D, BF, 2, T0, false, SEL>(G) : pick_g<D, BF, 1, T0, false, SEL>(G);
+    if (tpw == T0) return rows == 32 ? pick_g<D, BF, 2, T0, false, MODE>(G) : pick_g<D, BF, 1, T0, false, MODE>(G);
     if (tpw == T0 + 1)
-        return rows == 32 ? pick_g<D, BF, 2, T0 + 1, false, SEL>(G) : pick_g<D, BF, 1, T0 + 1, false, SEL>(G);
+        return rows == 32 ? pick_g<D, BF, 2, T0 + 1, false, MODE>(G) : pick_g<D, BF, 1, T0 + 1, false, MODE>(G);
     return nullptr;
 }
 

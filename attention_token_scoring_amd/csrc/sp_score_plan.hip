@@ -21,7 +21,7 @@ int esize(sp_dtype t) { return t == SP_BF16 ? 2 : 4; }
 // keep in flight and park (registers and LDS), the groups fill the device with
 // at least one CU left for combining, and the per-unit exchanges stay few;
 // then lay out LDS and the workspace.
-static sp_status plan_uncached(const sp_score_desc& d, long long M, int cus, ScorePlan* out) {
+static sp_status plan_uncached(const sp_score_desc& d, long long M, int cus, int only_tpw, ScorePlan* out) {
     ScorePlan p;
     const int G = d.H / d.Hkv;
     const bool bf = d.dtype == SP_BF16;
@@ -50,6 +50,7 @@ static sp_status plan_uncached(const sp_score_desc& d, long long M, int cus, Sco
     // (one head per step over two halves: the base tile count only)
     const int tpw1 = (G == 1 && p.rows == 32) ? tpw0 : tpw0 + 1;
     for (int tpw = tpw0; tpw <= tpw1; ++tpw) {
+        if (only_tpw > 0 && tpw != only_tpw) continue;
         const int cap = kStreamWaves * tpw * kTileKeys;
         const long long gmin = (MK + cap - 1) / cap;
         const bool roomy = score_roomy(row_bytes, tpw, p.rows / 16);
@@ -128,6 +129,7 @@ static sp_status plan_uncached(const sp_score_desc& d, long long M, int cus, Sco
     if (p.ncomb > kMaxCombiners) p.ncomb = kMaxCombiners;
     p.grid = bg * bng + p.ncomb;
     p.cus = cus;
+    p.cost = best;
     p.lds = score_lds_layout(bdef + 1, btpw, p.rows, row_bytes, d.N, bkr, p.dma);
     // the header (error word, last epoch, the groups' flags, the fused
     // call's words per streaming workgroup), the tagged partials and
@@ -149,11 +151,11 @@ static sp_status plan_uncached(const sp_score_desc& d, long long M, int cus, Sco
 namespace {
 
 struct PlanKey {
-    int L, H, Hkv, d, N, dtype, cus;
+    int L, H, Hkv, d, N, dtype, cus, tpw;
     long long M;
     bool operator==(const PlanKey& o) const {
         return L == o.L && H == o.H && Hkv == o.Hkv && d == o.d && N == o.N && dtype == o.dtype &&
-               cus == o.cus && M == o.M;
+               cus == o.cus && tpw == o.tpw && M == o.M;
     }
 };
 
@@ -168,15 +170,15 @@ std::mutex g_plans_mu;
 
 unsigned plan_slot(const PlanKey& k) {
     unsigned long long h = 1469598103934665603ull;
-    const long long f[8] = {k.L, k.H, k.Hkv, k.d, k.N, k.dtype, k.cus, k.M};
+    const long long f[9] = {k.L, k.H, k.Hkv, k.d, k.N, k.dtype, k.cus, k.tpw, k.M};
     for (long long v : f) h = (h ^ (unsigned long long)v) * 1099511628211ull;
     return (unsigned)(h ^ (h >> 29)) % kPlanSlots;
 }
 
 }  // namespace
 
-sp_status make_plan(const sp_score_desc& d, long long M, int cus, ScorePlan* out) {
-    const PlanKey k{d.L, d.H, d.Hkv, d.d, d.N, (int)d.dtype, cus, M};
+sp_status make_plan(const sp_score_desc& d, long long M, int cus, ScorePlan* out, int only_tpw) {
+    const PlanKey k{d.L, d.H, d.Hkv, d.d, d.N, (int)d.dtype, cus, only_tpw, M};
     const unsigned slot = plan_slot(k);
     {
         std::lock_guard<std::mutex> lk(g_plans_mu);
@@ -186,7 +188,7 @@ sp_status make_plan(const sp_score_desc& d, long long M, int cus, ScorePlan* out
         }
     }
     ScorePlan p;
-    const sp_status s = plan_uncached(d, M, cus, &p);
+    const sp_status s = plan_uncached(d, M, cus, only_tpw, &p);
     if (s != SP_OK) return s;
     {
         std::lock_guard<std::mutex> lk(g_plans_mu);

@@ -4,7 +4,7 @@
 namespace sp {
 
 const void* score_select_kernel_bf16_d128(int rows, int G, int tpw, bool dma) {
-    return pick_kernel_for<128, true, true>(rows, G, tpw, dma);
+    return pick_kernel_for<128, true, kLaunchFused>(rows, G, tpw, dma);
 }
 
 }  // namespace sp

@@ -4,7 +4,7 @@
 namespace sp {
 
 const void* score_select_kernel_f32_d64(int rows, int G, int tpw, bool dma) {
-    return pick_kernel_for<64, false, true>(rows, G, tpw, dma);
+    return pick_kernel_for<64, false, kLaunchFused>(rows, G, tpw, dma);
 }
 
 }  // namespace sp

@@ -106,9 +106,10 @@ def parse():
 
 
 # the scoring kernel's plain launch (sp_score); the fused launch
-# (sp_score_select) is the instantiation with true in its last place
+# (sp_score_select) is the instantiation with true in its second place, the
+# launch of several requests (sp_score_varlen) the one that takes PackArgs
 SCORE_KERNEL = "sp::score_kernel<"
-SCORE_KERNEL_PLAIN = ", false>(sp::ScoreArgs)"
+SCORE_KERNEL_PLAIN = ", false, sp::ScoreArgs>(sp::ScoreArgs)"
 # the calibration probe is the run's only elementwise add
 PROBE_KERNEL_HINTS = ("elementwise", "add")
 
@@ -480,8 +481,9 @@ def bench_ragged(args, w, sel, sp, torch, dev, steps, warmup, cpu_s):
     """A batch of R prompts of different lengths: one step is sp_score_varlen
     + sp_select_varlen over the whole batch. The batch's keys (tens of GB) are
     far larger than the Infinity Cache, so one copy suffices. The roofline
-    figure uses the sp_score_varlen call's duration (one scoring kernel per
-    request), a lower bound for the kernels' rate."""
+    figure uses the sp_score_varlen call's duration (its scoring launches:
+    requests alone, or several of similar length in one launch), a lower
+    bound for the kernels' rate."""
     import synth
 
     Qh, Kh, cu = synth.make_ragged(w)
@@ -493,8 +495,9 @@ def bench_ragged(args, w, sel, sp, torch, dev, steps, warmup, cpu_s):
     launch = sp.SP_LAUNCH_COOPERATIVE if args.cooperative else sp.SP_LAUNCH_RESIDENT
     desc = sp.score_desc(w.L, w.H, w.Hkv, w.d, w.N, sp.SP_BF16 if w.dtype else sp.SP_F32, 0.0,
                          launch)
-    ws = torch.empty(sp.sp_score_workspace_bytes(desc, int(Ms.max())), dtype=torch.uint8,
-                     device=dev)
+    ws_bytes = sp.sp_score_batch_workspace_bytes(desc, cu)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    launches = int(sp.sp_score_batch_plan(desc, cu, ws_bytes).max()) + 1
     imp = torch.empty(total, dtype=torch.float32, device=dev)
     kept = torch.empty(total, dtype=torch.int32, device=dev)
     pos = torch.empty(total, dtype=torch.int32, device=dev)
@@ -519,8 +522,8 @@ def bench_ragged(args, w, sel, sp, torch, dev, steps, warmup, cpu_s):
     alg = alg_bytes_of(w, Ms)
     out = {"value": total / (res["ms_per_step"] / 1e3), "unit": "tokens/s", "M": total,
            "roofline": roofline(alg, res["kernel_ms_mean"] / 1e3, None),
-           "roofline_basis": "sp_score_varlen call (every request's scoring kernel)",
-           "timing": res, "alg_bytes_per_step": alg, "requests": R,
+           "roofline_basis": "sp_score_varlen call (all its scoring launches)",
+           "timing": res, "alg_bytes_per_step": alg, "requests": R, "score_launches": launches,
            "config": dict(workload_desc(w, sel), M=total,
                           workload=f"{w.name}: R={R} prompts, M in [{int(Ms.min())}, "
                                    f"{int(Ms.max())}], sum {total}; L={w.L} H={w.H} "
@@ -544,8 +547,8 @@ def bench_windowed(args, w, sel, sp, torch, dev):
     """One prompt of the workload scored in sliding windows (each window with
     its own synthetic queries and keys, as a speculator run per window gives):
     one step is sp_score_windows + sp_select over the prompt's M tokens. The
-    roofline figure uses the sp_score_windows call's duration (one scoring
-    kernel per window)."""
+    roofline figure uses the sp_score_windows call's duration (its scoring
+    launches: windows are of one length, so several share a launch)."""
     import synth
 
     starts, lens, keeps = sp.sp_window_layout(w.M, args.window, args.stride)
@@ -558,8 +561,9 @@ def bench_windowed(args, w, sel, sp, torch, dev):
     launch = sp.SP_LAUNCH_COOPERATIVE if args.cooperative else sp.SP_LAUNCH_RESIDENT
     desc = sp.score_desc(w.L, w.H, w.Hkv, w.d, w.N, sp.SP_BF16 if w.dtype else sp.SP_F32, 0.0,
                          launch)
-    ws = torch.empty(sp.sp_score_workspace_bytes(desc, int(lens.max())), dtype=torch.uint8,
-                     device=dev)
+    ws_bytes = sp.sp_score_batch_workspace_bytes(desc, cu)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    launches = int(sp.sp_score_batch_plan(desc, cu, ws_bytes).max()) + 1
     imp = torch.empty(w.M, dtype=torch.float32, device=dev)
     kept = torch.empty(w.M, dtype=torch.int32, device=dev)
     pos = torch.empty(w.M, dtype=torch.int32, device=dev)
@@ -589,8 +593,8 @@ def bench_windowed(args, w, sel, sp, torch, dev):
                                     f"stride {args.stride}: {R} windows",
                            window=args.window, stride=args.stride),
             "detail": {"timing": res, "alg_bytes_per_step": alg, "windows": R,
-                       "roofline_basis": "sp_score_windows call (every window's "
-                                         "scoring kernel)",
+                       "score_launches": launches,
+                       "roofline_basis": "sp_score_windows call (all its scoring launches)",
                        "n_kept": int(nk.cpu()[0])}}
 
 

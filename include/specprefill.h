@@ -190,8 +190,10 @@ sp_status sp_score_lastrow(const sp_score_desc* desc, const void* Q, const void*
                            size_t ws_bytes, void* stream);
 
 /*
- * sp_score for a ragged batch of R requests (R >= 1), each scored exactly as
- * sp_score would score it alone.
+ * sp_score for a ragged batch of R requests (R >= 1), each scored as sp_score
+ * would score it alone (bit for bit where it has a launch to itself; a request
+ * that shares a launch has its own split of the keys over workgroups, so its
+ * scores can differ in rounding).
  *   Q              device, [R][L][H][N][d]
  *   K              device, [L][Hkv][T][d], T = sum_r (M_r + N); request r's
  *                  M_r prompt keys followed by its N look-ahead keys start at
@@ -200,11 +202,36 @@ sp_status sp_score_lastrow(const sp_score_desc* desc, const void* Q, const void*
  *                  M_r = cu_prompt_host[r+1] - cu_prompt_host[r] >= 1
  *   importance     device, [cu_prompt_host[R]] float32; request r's scores at
  *                  offset cu_prompt_host[r]
- *   ws             as for sp_score with max_prompt_len = max_r M_r
+ *   ws             as for sp_score with max_prompt_len = max_r M_r; with
+ *                  ws_bytes >= sp_score_batch_workspace_bytes(desc, R,
+ *                  cu_prompt_host), requests of similar length (up to 4, the
+ *                  longest at most 4 times the shortest) whose one launch the
+ *                  planner estimates faster than their launches in turn are
+ *                  scored in one launch, each on its own share of the CUs and
+ *                  its own part of the workspace (launches go in order of
+ *                  prompt length; each request's scores are those sp_score
+ *                  computes, up to rounding; a smaller workspace scores in
+ *                  turn what does not fit)
  */
 sp_status sp_score_varlen(const sp_score_desc* desc, int32_t R, const void* Q, const void* K,
                           const int64_t* cu_prompt_host, float* importance, void* ws,
                           size_t ws_bytes, void* stream);
+
+/* Bytes of device workspace with which sp_score_varlen / sp_score_windows score
+ * the batch cu_prompt_host[0..R] (host, as for sp_score_varlen) with every
+ * launch that packs several requests (at least sp_score_workspace_bytes of the
+ * longest request); 0 if the arguments are invalid or a request has no plan. */
+size_t sp_score_batch_workspace_bytes(const sp_score_desc* desc, int32_t R,
+                                      const int64_t* cu_prompt_host);
+
+/* The launches sp_score_varlen / sp_score_windows would make for the batch
+ * cu_prompt_host[0..R] with a workspace of ws_bytes (for reports and tests; no
+ * device work): launch_of (host, [R], or NULL) gets each request's launch
+ * index, requests with the same index sharing one launch; n_launches (host,
+ * [1]) the number of launches. SP_EWORKSPACE if ws_bytes is below what a
+ * request needs alone. */
+sp_status sp_score_batch_plan(const sp_score_desc* desc, int32_t R, const int64_t* cu_prompt_host,
+                              size_t ws_bytes, int32_t* launch_of, int32_t* n_launches);
 
 /*
  * Sliding-window scoring ([SP-G] Sliding Window, "Sliding Window Solution";
@@ -387,7 +414,7 @@ sp_status sp_score_plan(const sp_score_desc* desc, int32_t M, int32_t info[9]);
  * its stream immediately before and after each launch of the
  * scoring kernel, so that hipEventElapsedTime gives that kernel's duration
  * apart from the small kernels around it (for sp_score_varlen the events end
- * up around the last request's kernel). Pass NULL, NULL to stop. The setting
+ * up around its last launch). Pass NULL, NULL to stop. The setting
  * is per thread; the library never creates, waits on or destroys the events.
  * Returns SP_EINVAL if exactly one of the two is NULL.
  */
