@@ -721,7 +721,8 @@ def summary(r):
          "roofline": r["roofline"], "score_kernel_ms_mean": t["kernel_ms_mean"],
          "score_kernel_ms_median": t["kernel_ms_median"], "sp_score_ms_mean": t["sp_score_ms_mean"],
          "select_ms_mean": t["select_ms_mean"]}
-    for k in ("plan", "select_modes", "fused", "cpu_baseline", "cpu_baseline_1thread", "roofline_basis"):
+    for k in ("plan", "select_modes", "fused", "cpu_baseline", "cpu_baseline_1thread", "roofline_basis",
+              "requests", "score_launches"):
         if k in r:
             s[k] = r[k]
     return s
