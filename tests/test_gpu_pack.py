@@ -135,3 +135,23 @@ def test_packed_batch_graph_replays_match_eager(refill):
         print(f"packed graph refill={refill} replay {rep}", flush=True)
         assert torch.equal(imp, eager[rep % 2]), rep
         assert not sp.sp_score_status(ws), rep
+
+
+def test_packed_batch_cooperative_launch_matches():
+    """The packed launches as cooperative launches: the same schedule and plans,
+    so the same scores bit for bit."""
+    L, H, Hkv, d, N = 8, 32, 8, 128, 8
+    lens = [3000, 2000, 2500, 4000, 1, 5, 9000]
+    desc = sp.score_desc(L, H, Hkv, d, N)
+    cu, _ = _layout(lens, N)
+    launch = sp.sp_score_batch_plan(desc, cu, sp.sp_score_batch_workspace_bytes(desc, cu))
+    assert int(launch.max()) + 1 < len(lens)
+    w = synth.Workload("coop", L=L, H=H, Hkv=Hkv, d=d, N=N, dtype=BF, seed=47, R=len(lens),
+                       plant_frac=0.05, plant_chunk=32)
+    Qh, Kh, _ = synth.make_ragged(w, lens)
+    Q, K = to_dev(Qh), to_dev(Kh)
+    print("packed batch, cooperative launch", flush=True)
+    a = sp.sp_score_varlen(Q, K, cu)
+    b = sp.sp_score_varlen(Q, K, cu, launch=sp.SP_LAUNCH_COOPERATIVE)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
