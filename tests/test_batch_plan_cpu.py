@@ -100,3 +100,34 @@ def test_schedules_for_other_configurations(dtype, dd, H, Hkv, N):
     for l in range(int(launch.max()) + 1):
         m = np.asarray(lens)[launch == l]
         assert 1 <= len(m) <= 4 and m.max() <= 4 * m.min()
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_batches_schedule_validly(seed):
+    """Seeded random batches (1 to 40 requests of 1 to 100000 tokens, some of
+    equal length): the schedule's invariants hold, and it is the same on a
+    second query (the plans are cached)."""
+    rng = np.random.default_rng(seed)
+    d = _desc()
+    for _ in range(10):
+        R = int(rng.integers(1, 41))
+        lens = rng.integers(1, 100001, R)
+        if R > 4:
+            lens[rng.integers(0, R, R // 4)] = int(rng.integers(1, 20000))
+        cu = _cu(lens)
+        ws = sp.sp_score_batch_workspace_bytes(d, cu)
+        assert ws >= sp.sp_score_workspace_bytes(d, int(lens.max()))
+        launch = sp.sp_score_batch_plan(d, cu, ws)
+        assert np.array_equal(launch, sp.sp_score_batch_plan(d, cu, ws))
+        nl = int(launch.max()) + 1
+        assert sorted(set(launch.tolist())) == list(range(nl))
+        prev_hi = 0
+        for l in range(nl):
+            m = lens[launch == l]
+            assert 1 <= len(m) <= 4 and m.max() <= 4 * m.min()
+            assert m.min() >= prev_hi
+            prev_hi = m.max()
+        # a workspace that fits one request at a time still schedules every request
+        one = sp.sp_score_workspace_bytes(d, int(lens.max()))
+        small = sp.sp_score_batch_plan(d, cu, one)
+        assert int(small.max()) + 1 >= 1 and small.shape == (R,)
