@@ -29,6 +29,9 @@ CASES = [
     ("bf16-d64-G1", 4, 8, 8, 64, 4, BF, [3000, 2000, 2500, 4000]),
     ("bf16-d128-G1-N32", 4, 4, 4, 128, 32, BF, [3000, 2000, 2500, 4000]),
     ("8b-shape", 32, 32, 8, 128, 8, BF, [4096, 3000, 5000, 4500, 1, 2, 3, 6000, 100]),
+    # four long prompts in one launch, about 64 CUs each (the 24000-token one
+    # needs 43 workgroups per unit: one group)
+    ("8b-shape-4x-long", 32, 32, 8, 128, 8, BF, [20000, 18000, 24000, 22000]),
 ]
 
 
