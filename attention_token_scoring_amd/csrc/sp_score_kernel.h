@@ -51,6 +51,10 @@
 //    selects: one combiner workgroup runs the chunk selection on the scores,
 //    for long prompts on chunk masses the streaming workgroups have summed
 //    between them.
+//  * A packed launch (sp_score_varlen, also an instantiation of its own)
+//    scores up to four requests side by side: each workgroup finds its request
+//    from its block index and runs the one-request code above on that
+//    request's workgroups, plan and workspace region.
 #pragma once
 
 #include <math.h>
