@@ -164,7 +164,10 @@ constexpr double kLaunchFixedS = 15e-6;
 constexpr double kFullRateWgs = 200.0;
 // Which requests share a launch (measured on the MI355X at the 8B shape).
 // Packs of prompts of similar length gained 3-75 % (16 x 4K tokens 1.03 ->
-// 0.75 ms, 4 x 1000 0.170 -> 0.096 ms, 4 of 15K-53K 1.34 -> 1.30 ms); packs
+// 0.75 ms, 4 x 1000 0.170 -> 0.096 ms, 4 of 15K-53K 1.34 -> 1.30 ms), and
+// packs of up to 8 more than packs of up to 4 (32 x 1000 0.80 -> 0.50 ms,
+// 16 x 2048 0.46 -> 0.42 ms, the ragged 16 prompts of 5K-61K 4.93 -> 4.86 ms;
+// 16 x 4096 0.77 -> 0.78 ms); packs
 // that mixed lengths 5 to 50 times apart lost 5-20 % against estimates of
 // small gains (the smallest requests' few CUs, with one combining workgroup
 // for every unit, fall behind the plans' estimates), so the longest prompt

@@ -187,13 +187,14 @@ struct ScoreArgs {
 
 // Requests scored in one launch (sp_score_varlen): request r on blocks
 // [first[r], first[r + 1]).
-constexpr int kMaxPack = 4;
+constexpr int kMaxPack = 8;
 constexpr int kLaunchPlain = 0, kLaunchFused = 1, kLaunchPack = 2;
 struct PackArgs {
     int n;
     int first[kMaxPack + 1];
     ScoreArgs args[kMaxPack];
 };
+static_assert(sizeof(PackArgs) <= 4096, "kernel arguments are limited to 4 KiB");
 
 struct ScorePlan {
     int rows;      // 16 or 32

@@ -52,7 +52,7 @@
 //    for long prompts on chunk masses the streaming workgroups have summed
 //    between them.
 //  * A packed launch (sp_score_varlen, also an instantiation of its own)
-//    scores up to four requests side by side: each workgroup finds its request
+//    scores up to eight requests side by side: each workgroup finds its request
 //    from its block index and runs the one-request code above on that
 //    request's workgroups, plan and workspace region.
 #pragma once

@@ -204,7 +204,7 @@ sp_status sp_score_lastrow(const sp_score_desc* desc, const void* Q, const void*
  *                  offset cu_prompt_host[r]
  *   ws             as for sp_score with max_prompt_len = max_r M_r; with
  *                  ws_bytes >= sp_score_batch_workspace_bytes(desc, R,
- *                  cu_prompt_host), requests of similar length (up to 4, the
+ *                  cu_prompt_host), requests of similar length (up to 8, the
  *                  longest at most 4 times the shortest) whose one launch the
  *                  planner estimates faster than their launches in turn are
  *                  scored in one launch, each on its own share of the CUs and

@@ -32,6 +32,9 @@ CASES = [
     # four long prompts in one launch, about 64 CUs each (the 24000-token one
     # needs 43 workgroups per unit: one group)
     ("8b-shape-4x-long", 32, 32, 8, 128, 8, BF, [20000, 18000, 24000, 22000]),
+    # eight requests in one launch
+    ("8b-shape-8-short", 32, 32, 8, 128, 8, BF, [2048, 2000, 1900, 2100, 2048, 1500, 1800, 2047, 3000]),
+    ("bf16-d128-units16-8", 4, 16, 4, 128, 8, BF, [3000, 2000, 2500, 4000, 3500, 2200, 2700, 3900]),
 ]
 
 
