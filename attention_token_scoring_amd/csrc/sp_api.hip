@@ -291,39 +291,54 @@ struct BatchLaunch {
     PackRequest pk[kMaxPack];  // (n > 1; ws holds the region's offset)
 };
 
-// Validates every request's plan for the whole device (into full) and
-// schedules the batch's launches.
-sp_status schedule_batch(const sp_score_desc& d, int R, const int64_t* cu, int cus, size_t ws_bytes,
-                         std::vector<ScorePlan>& full, std::vector<BatchLaunch>& launches) {
-    full.resize((size_t)R);
-    for (int r = 0; r < R; ++r) {
-        const sp_status s = make_plan(d, cu[r + 1] - cu[r], cus, &full[r]);
-        if (s != SP_OK) return s;
-        if (ws_bytes < full[r].ws_total) return SP_EWORKSPACE;
-    }
-    std::vector<int> order((size_t)R);
-    for (int r = 0; r < R; ++r) order[r] = r;
-    std::stable_sort(order.begin(), order.end(),
-                     [&](int a, int b) { return cu[a + 1] - cu[a] < cu[b + 1] - cu[b]; });
-    std::vector<long long> Ms((size_t)R);
-    std::vector<ScorePlan> fs((size_t)R);
-    for (int i = 0; i < R; ++i) {
-        Ms[i] = cu[order[i] + 1] - cu[order[i]];
-        fs[i] = full[order[i]];
-    }
-    launches.clear();
-    for (int i = 0; i < R;) {
-        BatchLaunch b;
-        b.n = plan_pack(d, Ms.data(), i, R, cus, ws_bytes, fs.data(), b.pk);
-        for (int j = 0; j < b.n; ++j) b.req[j] = order[i + j];
-        launches.push_back(b);
-        i += b.n;
-    }
-    return SP_OK;
-}
+// A batch's launches, planned one at a time (so that a caller can enqueue each
+// as soon as it is planned): init validates every request's plan for the
+// whole device (full, by request) and orders the requests by length; next
+// plans the launch from the next unscheduled request on.
+struct BatchSchedule {
+    const sp_score_desc* d = nullptr;
+    int R = 0, cus = 0, done = 0;
+    size_t ws_bytes = 0;
+    std::vector<ScorePlan> full;
+    std::vector<int> order;
+    std::vector<long long> Ms;      // prompt lengths in order
+    std::vector<ScorePlan> fs;      // full plans in order
 
-// Requests r in [0, R) of a ragged batch, scored in the launches schedule_batch
-// makes (alone, or several in one launch on shares of the device where the
+    sp_status init(const sp_score_desc& desc, int nreq, const int64_t* cu, int ncus, size_t wsb) {
+        d = &desc;
+        R = nreq;
+        cus = ncus;
+        ws_bytes = wsb;
+        done = 0;
+        full.resize((size_t)R);
+        for (int r = 0; r < R; ++r) {
+            const sp_status s = make_plan(desc, cu[r + 1] - cu[r], cus, &full[r]);
+            if (s != SP_OK) return s;
+            if (ws_bytes < full[r].ws_total) return SP_EWORKSPACE;
+        }
+        order.resize((size_t)R);
+        for (int r = 0; r < R; ++r) order[r] = r;
+        std::stable_sort(order.begin(), order.end(),
+                         [&](int a, int b) { return cu[a + 1] - cu[a] < cu[b + 1] - cu[b]; });
+        Ms.resize((size_t)R);
+        fs.resize((size_t)R);
+        for (int i = 0; i < R; ++i) {
+            Ms[i] = cu[order[i] + 1] - cu[order[i]];
+            fs[i] = full[order[i]];
+        }
+        return SP_OK;
+    }
+    bool next(BatchLaunch& b) {
+        if (done >= R) return false;
+        b.n = plan_pack(*d, Ms.data(), done, R, cus, ws_bytes, fs.data(), b.pk);
+        for (int j = 0; j < b.n; ++j) b.req[j] = order[done + j];
+        done += b.n;
+        return true;
+    }
+};
+
+// Requests r in [0, R) of a ragged batch, scored in the launches BatchSchedule
+// plans (alone, or several in one launch on shares of the device where the
 // workspace holds their regions side by side); with keep, only the first
 // keep[r] scores of request r are written, packed one request after the
 // other in request order (else all M_r scores at offset cu[r]).
@@ -343,10 +358,11 @@ sp_status score_batch(const sp_score_desc* desc, int32_t R, const void* Q, const
     const int cus = device_cus();
     if (cus < 1) return SP_EDEVICE;
     if (!ws || !aligned(ws, 256)) return SP_EWORKSPACE;
-    // validate every request's plan before enqueueing anything
-    std::vector<ScorePlan> full;
-    std::vector<BatchLaunch> launches;
-    s = schedule_batch(*desc, R, cu, cus, ws_bytes, full, launches);
+    // validate every request's plan before enqueueing anything (the packs are
+    // planned launch by launch below: a pack that does not pay or fit falls
+    // back to the request alone, so their planning fails nothing)
+    BatchSchedule sched;
+    s = sched.init(*desc, R, cu, cus, ws_bytes);
     if (s != SP_OK) return s;
     const int es = esize(desc->dtype);
     const long long T = cu[R] + (long long)R * desc->N;
@@ -359,7 +375,8 @@ sp_status score_batch(const sp_score_desc* desc, int32_t R, const void* Q, const
     }
     const unsigned call = next_epoch();
     bool first = true;
-    for (BatchLaunch& b : launches) {
+    BatchLaunch b;
+    while (sched.next(b)) {
         for (int i = 0; i < b.n; ++i) {
             const int r = b.req[i];
             const long long M = cu[r + 1] - cu[r];
@@ -373,8 +390,8 @@ sp_status score_batch(const sp_score_desc* desc, int32_t R, const void* Q, const
         }
         if (b.n == 1) {
             const PackRequest& q = b.pk[0];
-            s = to_status(launch_score(full[b.req[0]], *desc, q.Q, q.K, T * desc->d, q.M, q.M_out, q.importance, ws,
-                                       call, first, desc->N, 0, nullptr, (hipStream_t)stream));
+            s = to_status(launch_score(sched.full[b.req[0]], *desc, q.Q, q.K, T * desc->d, q.M, q.M_out,
+                                       q.importance, ws, call, first, desc->N, 0, nullptr, (hipStream_t)stream));
         } else {
             s = to_status(launch_score_pack(b.pk, b.n, *desc, T * desc->d, call, first, (hipStream_t)stream));
         }
@@ -387,12 +404,12 @@ sp_status score_batch(const sp_score_desc* desc, int32_t R, const void* Q, const
 // The workspace with which score_batch packs as its plans allow (at least
 // what every request needs alone).
 size_t batch_workspace(const sp_score_desc& d, int R, const int64_t* cu, int cus) {
-    std::vector<ScorePlan> full;
-    std::vector<BatchLaunch> launches;
-    if (schedule_batch(d, R, cu, cus, (size_t)-1, full, launches) != SP_OK) return 0;
+    BatchSchedule sched;
+    if (sched.init(d, R, cu, cus, (size_t)-1) != SP_OK) return 0;
     size_t need = 0;
-    for (const ScorePlan& p : full) need = p.ws_total > need ? p.ws_total : need;
-    for (const BatchLaunch& b : launches) {
+    for (const ScorePlan& p : sched.full) need = p.ws_total > need ? p.ws_total : need;
+    BatchLaunch b;
+    while (sched.next(b)) {
         if (b.n == 1) continue;
         const size_t end = (size_t)b.pk[b.n - 1].ws + round_up256(b.pk[b.n - 1].plan.ws_total);
         need = end > need ? end : need;
@@ -454,14 +471,15 @@ sp_status sp_score_batch_plan(const sp_score_desc* desc, int32_t R, const int64_
     for (int r = 0; r < R; ++r)
         if (cu[r + 1] - cu[r] < 1) return SP_EINVAL;
     const int cus = device_cus() > 0 ? device_cus() : kDefaultCUs;
-    std::vector<ScorePlan> full;
-    std::vector<BatchLaunch> launches;
-    s = schedule_batch(*desc, R, cu, cus, ws_bytes, full, launches);
+    BatchSchedule sched;
+    s = sched.init(*desc, R, cu, cus, ws_bytes);
     if (s != SP_OK) return s;
-    for (size_t l = 0; l < launches.size(); ++l)
-        for (int i = 0; i < launches[l].n; ++i)
-            if (launch_of) launch_of[launches[l].req[i]] = (int32_t)l;
-    *n_launches = (int32_t)launches.size();
+    int32_t l = 0;
+    BatchLaunch b;
+    for (; sched.next(b); ++l)
+        for (int i = 0; i < b.n; ++i)
+            if (launch_of) launch_of[b.req[i]] = l;
+    *n_launches = l;
     return SP_OK;
 }
 
